@@ -1,0 +1,24 @@
+"""CPU oracle for the MoE expert-MLP path.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
+definition of what the GPU path computes, evaluated in float64 with numpy.
+Only the test suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+(``mixture_experts_expert_top_amd``) never does and shares no code with it.
+
+Sources (cited by page title and section):
+  * "Efficient MoE Training for Biological Foundation Models" (NVIDIA
+    Developer Blog, mirrored) -- Challenge 1 (per-expert loop, split_sizes,
+    GroupedLinear gate_up of width 2*intermediate), Challenge 2 (MXFP8: one
+    scale per 32 consecutive values), Challenge 3 (GroupedLinear ->
+    ScaledSwiGLU -> GroupedLinear, the routing probabilities act as scales).
+  * "How MoE Architecture Cuts Costs and Boosts Efficiency: Efficient
+    Training of Biological Foundation Models" -- section "Why Biology Is
+    Especially Well-Suited for MoE" (top-K router over per-expert scores).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
+closed forms, library routines, finite differences, exhaustive codec
+sweeps).  See each module header for what is and is not pinned.
+"""
+
+from . import moe_ref, mx_ref  # noqa: F401

@@ -1,0 +1,296 @@
+"""Plain float64 definition of the MoE expert-MLP layer (routing, dispatch,
+expert SwiGLU MLP, combine) and of its backward pass.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Nothing here is
+blocked, fused or reordered: each step is the per-expert loop the pages
+describe, written out with numpy matmuls as the only library primitive.
+
+Layout conventions (fixed by the library's C-ABI and restated here so the
+oracle can be read on its own):
+  x      [T, d]        tokens
+  logits [T, E]        router scores
+  w_gu   [E, 2f, d]    per-expert gate_up weight, rows 0..f-1 gate (W1),
+                       rows f..2f-1 up (W3); out_features = 2*intermediate
+  w2     [E, d, f]     per-expert down weight (out_features x in_features)
+  idx, p [T, k]        chosen experts (descending score, ties -> lower id)
+                       and their routing weights
+  counts [E], offsets [E+1], pos [T, k], src [T*k]   the dispatch plan
+  permuted tensors have one row per (token, slot) pair, rows of expert e
+  in [offsets[e], offsets[e+1]), token-ascending inside an expert.
+
+Pinned by tests/test_oracle_pins.py: routing against a pure-Python sort,
+softmax against scipy, dispatch against its invariants, the forward against
+a dense masked brute force and the E=1,k=1 plain SwiGLU MLP, hand-derived
+closed forms (tests/golden/closed_forms.json), the backward against torch
+autograd (float64) and central finite differences.
+"""
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Router.  "How MoE Architecture Cuts Costs ...", section "Why Biology Is
+# Especially Well-Suited for MoE": the router emits one score per expert and
+# only the K best-scoring experts run for a token.
+# --------------------------------------------------------------------------
+
+def router_logits(x, w_g, bias=None):
+    """Router scores L = x . W_g^T (+ per-expert bias), float64.
+
+    x [T, d], w_g [E, d], bias [E] or None.  Returns [T, E].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w_g = np.asarray(w_g, dtype=np.float64)
+    logits = x @ w_g.T
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+    return logits
+
+
+def topk_route(logits, k, renorm=True):
+    """Top-k expert choice and routing weights for every token.
+
+    Selection compares the given score values exactly (float32 scores are
+    exact in float64): experts are ordered by descending score, equal scores
+    by ascending expert id, and the first k are kept.  Weights are the
+    softmax of the scores; with ``renorm`` they are renormalised over the k
+    chosen experts, which equals a softmax over the chosen scores alone.
+    Returns idx [T, k] int32 and p [T, k] float64.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # a stable sort on the negated score keeps the lower id first among ties
+    order = np.argsort(-L, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    chosen = np.take_along_axis(L, idx.astype(np.int64), axis=1)
+    top = chosen[:, :1]                      # the largest score of the row
+    if renorm:
+        z = np.exp(chosen - top)
+        p = z / z.sum(axis=1, keepdims=True)
+    else:
+        z_all = np.exp(L - top)
+        p = np.exp(chosen - top) / z_all.sum(axis=1, keepdims=True)
+    return idx, p
+
+
+# --------------------------------------------------------------------------
+# Dispatch plan.  "Efficient MoE Training ...", Challenge 1: each expert
+# gathers the tokens that chose it; GroupedLinear takes the per-expert token
+# counts (split_sizes).  Rows are grouped expert by expert, tokens ascending.
+# --------------------------------------------------------------------------
+
+def dispatch_plan(idx, E):
+    """counts[E], offsets[E+1], pos[T,k], src[T*k] for the expert grouping.
+
+    pos[t, j] is the permuted row of slot j of token t; src[r] is the token
+    of permuted row r.  Inside an expert, rows follow ascending token id.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    pos = np.full((T, k), -1, dtype=np.int64)
+    src = np.full(T * k, -1, dtype=np.int64)
+    row = 0
+    for e in range(E):
+        offsets[e] = row
+        # row-major scan of the [T, k] mask: ascending token, one slot each
+        tokens, slots = np.nonzero(idx == e)
+        n = tokens.shape[0]
+        counts[e] = n
+        rows = row + np.arange(n)
+        pos[tokens, slots] = rows
+        src[rows] = tokens
+        row += n
+    offsets[E] = row
+    return counts, offsets, pos, src
+
+
+def permute_rows(x, src):
+    """Permuted copy of token rows: Xp[r] = x[src[r]]."""
+    return np.asarray(x, dtype=np.float64)[np.asarray(src)]
+
+
+def permuted_weights(p, pos):
+    """w_perm[pos[t, j]] = p[t, j]."""
+    p = np.asarray(p, dtype=np.float64)
+    out = np.zeros(p.size, dtype=np.float64)
+    out[np.asarray(pos).reshape(-1)] = p.reshape(-1)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Expert MLP.  "Efficient MoE Training ...", Challenge 1 (gate_up projection
+# with out_features = 2 * intermediate_size, bias=False) and Challenge 3
+# (GroupedLinear(gate_up) -> ScaledSwiGLU -> GroupedLinear(down); the routing
+# probabilities are the SwiGLU's scales).
+# --------------------------------------------------------------------------
+
+def silu(a):
+    """silu(a) = a / (1 + exp(-a))."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def expert_forward(xp_e, w_gu_e, w2_e, w_e):
+    """One expert on its rows: returns (AB, S, O).
+
+    AB = Xp_e . W_gu_e^T  (gate pre-activations first, then up)
+    S  = w * silu(A_g) * A_u       (scaled SwiGLU, one weight per row)
+    O  = S . W2_e^T
+    """
+    f = w_gu_e.shape[0] // 2
+    ab = xp_e @ w_gu_e.T
+    a_g, a_u = ab[:, :f], ab[:, f:]
+    h = silu(a_g) * a_u
+    s = np.asarray(w_e, dtype=np.float64)[:, None] * h
+    o = s @ w2_e.T
+    return ab, s, o
+
+
+def combine(o_perm, pos, idx):
+    """y[t] = sum over the token's k slots, ascending expert id, of O[pos]."""
+    pos = np.asarray(pos)
+    idx = np.asarray(idx)
+    T, k = pos.shape
+    y = np.zeros((T, o_perm.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in np.argsort(idx[t], kind="stable"):
+            y[t] += o_perm[pos[t, j]]
+    return y
+
+
+def experts_forward(x, idx, p, w_gu, w2):
+    """The layer forward with routing given (idx, p).  Returns a dict with
+    the plan, the permuted intermediates and the output y [T, d]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_gu = np.asarray(w_gu, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    E = w_gu.shape[0]
+    f = w_gu.shape[1] // 2
+    d = x.shape[1]
+    counts, offsets, pos, src = dispatch_plan(idx, E)
+    xp = permute_rows(x, src)
+    w_perm = permuted_weights(p, pos)
+    Tk = xp.shape[0]
+    ab = np.zeros((Tk, 2 * f))
+    s = np.zeros((Tk, f))
+    o = np.zeros((Tk, d))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        ab[r0:r1], s[r0:r1], o[r0:r1] = expert_forward(
+            xp[r0:r1], w_gu[e], w2[e], w_perm[r0:r1])
+    y = combine(o, pos, idx)
+    return dict(idx=np.asarray(idx), p=np.asarray(p, dtype=np.float64),
+                counts=counts, offsets=offsets, pos=pos, src=src,
+                xp=xp, w_perm=w_perm, ab=ab, s=s, o=o, y=y)
+
+
+def moe_forward(x, logits, w_gu, w2, k, renorm=True):
+    """Route on the given scores, then run the experts and combine."""
+    idx, p = topk_route(logits, k, renorm)
+    return experts_forward(x, idx, p, w_gu, w2)
+
+
+def moe_backward(fwd, dy, w_gu, w2):
+    """Backward of ``experts_forward`` for upstream gradient dy [T, d].
+
+    Routing (idx) is held fixed; the gradient with respect to the routing
+    weights is returned as dp [T, k].  Returns dict(dx, dw_gu, dw2, dp,
+    dab, do) with dab/do in permuted row order.  Experts that received no
+    rows get exactly zero weight gradients.
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    w_gu = np.asarray(w_gu, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    E, two_f, d = w_gu.shape
+    f = two_f // 2
+    offsets, pos, src = fwd["offsets"], fwd["pos"], fwd["src"]
+    ab, s, xp, w_perm = fwd["ab"], fwd["s"], fwd["xp"], fwd["w_perm"]
+    Tk = xp.shape[0]
+    do = dy[src]                                  # dO[r] = dY[src[r]]
+    dab = np.zeros((Tk, 2 * f))
+    dxp = np.zeros((Tk, d))
+    dw_gu = np.zeros_like(w_gu)
+    dw2 = np.zeros_like(w2)
+    dp_perm = np.zeros(Tk)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        do_e = do[r0:r1]
+        a_g, a_u = ab[r0:r1, :f], ab[r0:r1, f:]
+        h = silu(a_g) * a_u
+        dw2[e] = do_e.T @ s[r0:r1]                # dW2 = dO^T S
+        ds = do_e @ w2[e]                         # dS = dO W2
+        dp_perm[r0:r1] = np.sum(ds * h, axis=1)   # d/dp of S = p H
+        dh = w_perm[r0:r1, None] * ds
+        sg = sigmoid(a_g)
+        da_g = dh * a_u * sg * (1.0 + a_g * (1.0 - sg))
+        da_u = dh * silu(a_g)
+        dab[r0:r1, :f] = da_g
+        dab[r0:r1, f:] = da_u
+        dw_gu[e] = dab[r0:r1].T @ xp[r0:r1]       # dW_gu = dAB^T Xp
+        dxp[r0:r1] = dab[r0:r1] @ w_gu[e]         # dXp = dAB W_gu
+    T, k = pos.shape
+    dx = np.zeros((T, d))
+    dp = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            dx[t] += dxp[pos[t, j]]
+            dp[t, j] = dp_perm[pos[t, j]]
+    return dict(dx=dx, dw_gu=dw_gu, dw2=dw2, dp=dp, dab=dab, do=do,
+                dxp=dxp)
+
+
+# --------------------------------------------------------------------------
+# Sampled evaluation for full-size parity checks: the same definition,
+# evaluated for single outputs so that Mixtral-sized layers stay cheap.
+# --------------------------------------------------------------------------
+
+def token_forward(x_t, idx_t, p_t, w_gu, w2):
+    """y[t] for one token: sum over its chosen experts (ascending id) of
+    p * (silu(x W1^T) * (x W3^T)) W2^T.  ``w_gu``/``w2`` may be any indexable
+    stack of per-expert weights (each item converted to float64 here)."""
+    x_t = np.asarray(x_t, dtype=np.float64)
+    y = np.zeros(x_t.shape[0])
+    for j in np.argsort(np.asarray(idx_t), kind="stable"):
+        e = int(idx_t[j])
+        wgu = np.asarray(w_gu[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        _, _, o = expert_forward(x_t[None, :], wgu, w2e,
+                                 np.array([float(p_t[j])]))
+        y += o[0]
+    return y
+
+
+def row_backward(x_t, dy_t, p_r, w_gu_e, w2_e):
+    """Backward of one permuted row (one token through one expert).
+
+    Returns (dab_row [2f], dxp_row [d], dp_r scalar, ab_row, s_row).
+    """
+    x_t = np.asarray(x_t, dtype=np.float64)
+    dy_t = np.asarray(dy_t, dtype=np.float64)
+    w_gu_e = np.asarray(w_gu_e, dtype=np.float64)
+    w2_e = np.asarray(w2_e, dtype=np.float64)
+    f = w_gu_e.shape[0] // 2
+    ab, s, _ = expert_forward(x_t[None, :], w_gu_e, w2_e, np.array([p_r]))
+    a_g, a_u = ab[0, :f], ab[0, f:]
+    h = silu(a_g) * a_u
+    ds = dy_t @ w2_e
+    dp_r = float(np.dot(ds, h))
+    dh = p_r * ds
+    sg = sigmoid(a_g)
+    dab = np.concatenate([dh * a_u * sg * (1.0 + a_g * (1.0 - sg)),
+                          dh * silu(a_g)])
+    dxp = dab @ w_gu_e
+    return dab, dxp, dp_r, ab[0], s[0]
