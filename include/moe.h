@@ -1,0 +1,248 @@
+/*
+ * moe.h -- C-ABI of libmoe.so: the mixture-of-experts expert-MLP hot path
+ * (top-k routing, permutation by expert, grouped GEMM with fused SwiGLU and
+ * routing-weight scaling, optional MXFP8 block quantization, un-permute
+ * combine; forward and backward) as hand-written HIP kernels for gfx950.
+ *
+ * Sources, cited by page title and section:
+ *  [P1] "Efficient MoE Training for Biological Foundation Models" (NVIDIA
+ *       Developer Blog): Challenge 1 (per-expert loop; GroupedLinear takes
+ *       per-expert token counts, split_sizes, gate_up has out_features =
+ *       2 * intermediate_size, bias=False), Challenge 2 (MXFP8: one scaling
+ *       factor per block of 32 consecutive values), Challenge 3
+ *       (GroupedLinear(gate_up) -> ScaledSwiGLU -> GroupedLinear(down), the
+ *       routing probabilities are the SwiGLU's scales; a matching fused
+ *       backward; quantization folded into the fused path).
+ *  [P4] "How MoE Architecture Cuts Costs and Boosts Efficiency: Efficient
+ *       Training of Biological Foundation Models", section "Why Biology Is
+ *       Especially Well-Suited for MoE" (top-K router over per-expert
+ *       scores).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates or frees memory and keeps no mutable global
+ *    state.  Scratch memory is the caller's `workspace` (size from
+ *    moe_workspace_bytes); it need not be zeroed.
+ *  - Row-major layouts.  bf16 tensors are passed as `void*` holding IEEE
+ *    bfloat16 bit patterns.  Every tensor pointer must be 16-byte aligned.
+ *  - Work is enqueued on `stream` and the call returns without waiting.
+ *    Counts and offsets stay on the device (no host synchronisation).
+ *  - Errors: arguments are validated on the host before anything is
+ *    launched.  On a validation failure the call returns a non-zero
+ *    moe_status, launches nothing and leaves every output untouched;
+ *    moe_last_error() then describes the failure (thread-local).  A failed
+ *    kernel launch returns MOE_ERR_HIP.  No exception crosses the ABI.
+ *  - Limits: 1 <= k <= E <= 1024, k <= 32, T >= 1, d and f >= 8 and
+ *    multiples of 8 (bf16) or of 32 (MXFP8); every tensor smaller than
+ *    2 GiB.
+ *  - Deterministic: identical inputs give bitwise identical outputs (no
+ *    floating-point atomics; all reductions run in a fixed order).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment      */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request outside the supported set  */
+  MOE_ERR_WORKSPACE = 3,    /* workspace smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = 4           /* a HIP launch failed                       */
+} moe_status;
+
+typedef enum moe_prec {
+  MOE_BF16 = 0,   /* bf16 operands, fp32 accumulation                    */
+  MOE_MXFP8 = 1   /* E4M3 codes + one E8M0 scale byte per 32 values       */
+} moe_prec;
+
+/* Entry ids for moe_workspace_bytes. */
+typedef enum moe_entry {
+  MOE_ENTRY_PERMUTE = 0,
+  MOE_ENTRY_MLP_FWD = 1,
+  MOE_ENTRY_MLP_BWD = 2
+} moe_entry;
+
+/* Short name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+
+/* Description of the last failure of a call made by this thread. */
+const char* moe_last_error(void);
+
+/* Version string of the library build. */
+const char* moe_version(void);
+
+/*
+ * moe_router_logits -- router scores, [P4] (the router emits one score per
+ * expert):  logits[t][e] = sum_i x[t][i] * w_g[e][i] (+ bias[e]).
+ *   x       [T][d]  bf16        w_g   [E][d] bf16
+ *   bias    [E]     fp32 or NULL
+ *   logits  [T][E]  fp32 out    (fp32 accumulation on bf16 MFMA)
+ */
+moe_status moe_router_logits(const void* x, const void* w_g, const float* bias,
+                             int64_t T, int64_t d, int32_t E, float* logits,
+                             hipStream_t stream);
+
+/*
+ * moe_route -- top-k expert choice and routing weights, [P4] (only the K
+ * best-scoring experts run) and [P1] Challenge 1 (routing weights scale the
+ * expert outputs).  Per token: experts ordered by descending score, equal
+ * scores by ascending id (+0.0 and -0.0 are equal); the first k are kept in
+ * that order.  renorm != 0: weights are the softmax over the k chosen
+ * scores (softmax then renormalisation over the chosen k); renorm == 0:
+ * the softmax over all E scores, taken at the chosen experts.
+ *   logits   [T][E] fp32 (finite)
+ *   topk_idx [T][k] int32 out,  topk_w [T][k] fp32 out
+ */
+moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
+                     int32_t renorm, int32_t* topk_idx, float* topk_w,
+                     hipStream_t stream);
+
+/*
+ * moe_permute -- dispatch plan and token permutation, [P1] Challenge 1
+ * (each expert gathers its tokens; split_sizes are the per-expert counts).
+ *   counts[e]   = number of (t, j) with topk_idx[t][j] == e       [E]
+ *   offsets[e]  = sum of counts[e'] for e' < e; offsets[E] = T*k   [E+1]
+ *   pos[t][j]   = offsets[e] + #{t' < t : e in topk_idx[t']}      [T][k]
+ *                 (rows of an expert follow ascending token id)
+ *   src[r]      = token of permuted row r                          [T*k]
+ *   w_perm[r]   = topk_w of the slot that maps to row r            [T*k]
+ *   x_perm[r]   = x[src[r]]                                        [T*k][d]
+ * prec == MOE_BF16: x and x_perm are bf16, x_scales/x_perm_scales unused.
+ * prec == MOE_MXFP8: x/x_perm are E4M3 codes (uint8 [.][d]) with E8M0
+ *   scales x_scales/x_perm_scales (uint8 [.][d/32]) moved along.
+ * topk_w may be NULL (then w_perm may be NULL too).  Integer outputs are
+ * exact and deterministic.  Workspace: MOE_ENTRY_PERMUTE.
+ */
+moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
+                       const float* topk_w, int64_t T, int32_t E, int32_t k,
+                       const void* x, const uint8_t* x_scales, int64_t d,
+                       int32_t* counts, int32_t* offsets, int32_t* pos,
+                       int32_t* src, float* w_perm, void* x_perm,
+                       uint8_t* x_perm_scales, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_permute_rows -- row permutation with an existing plan (used for the
+ * upstream gradient in the backward pass): x_perm[pos[t][j]] = x[t].
+ * Same dtype rules as moe_permute.
+ */
+moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
+                            int32_t k, const void* x, const uint8_t* x_scales,
+                            int64_t d, void* x_perm, uint8_t* x_perm_scales,
+                            hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_fwd -- all experts' SwiGLU MLPs as grouped GEMMs over the
+ * permuted rows, [P1] Challenge 1 (one grouped submission, per-expert
+ * weights) and Challenge 3 (gate_up -> ScaledSwiGLU -> down, fused).  For
+ * every expert e and row r in [offsets[e], offsets[e+1]):
+ *   AB[r]  = x_perm[r] . w_gu[e]^T                 (gate: first f columns)
+ *   S[r]   = w_perm[r] * silu(AB[r][:f]) * AB[r][f:]
+ *   O[r]   = S[r] . w2[e]^T
+ *   w_gu [E][2f][d], w2 [E][d][f]; ab_saved [T*k][2f] bf16 out,
+ *   s_saved [T*k][f] bf16 out, out_perm [T*k][d] bf16 out.
+ * prec == MOE_MXFP8: x_perm is E4M3 codes + scales along d (from
+ *   moe_permute), w_gu/w2 are codes with scales along their last axis (from
+ *   moe_mxfp8_quantize, axis 0); S is requantized along f inside the
+ *   epilogue for the second GEMM; ab_saved/s_saved/out_perm stay bf16.
+ * w_perm may be NULL (weight 1).  Workspace: MOE_ENTRY_MLP_FWD.
+ */
+moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
+                               const uint8_t* x_perm_scales,
+                               const int32_t* offsets, int32_t E, int64_t Tk,
+                               int64_t d, int64_t f, const void* w_gu,
+                               const uint8_t* w_gu_scales, const void* w2,
+                               const uint8_t* w2_scales, const float* w_perm,
+                               void* ab_saved, void* s_saved, void* out_perm,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_bwd -- backward of moe_grouped_mlp_fwd ([P1] Challenge 3
+ * names a matching fused backward).  With dO = dout_perm (rows permuted
+ * like x_perm) and H = silu(A_g) * A_u recomputed from ab_saved:
+ *   dW2[e]   = dO_e^T . S_e            (K = rows of e; zero if none)
+ *   dS       = dO . w2[e]
+ *   dp[t][j] = <dS[r], H[r]>, r = pos[t][j]      (fp32, fixed-order sums)
+ *   dA_g     = w*dS * A_u * sig(A_g) * (1 + A_g*(1 - sig(A_g)))
+ *   dA_u     = w*dS * silu(A_g)
+ *   dW_gu[e] = dAB_e^T . x_perm_e
+ *   dx_perm  = dAB . w_gu[e]
+ *   dout_perm [T*k][d] bf16, x_perm [T*k][d] bf16, ab_saved, s_saved as
+ *   written by the forward; dx_perm [T*k][d], dw_gu [E][2f][d],
+ *   dw2 [E][d][f] bf16 out; dp [T][k] fp32 out (needs pos).
+ * prec == MOE_MXFP8: the same operands are quantized inside the call along
+ *   each GEMM's reduction axis (d, 2f, or rows of an expert, restarting at
+ *   each expert's first row); inputs and outputs stay bf16.
+ * Workspace: MOE_ENTRY_MLP_BWD.
+ */
+moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
+                               const void* x_perm, const int32_t* offsets,
+                               const int32_t* pos, int64_t T, int32_t k,
+                               int32_t E, int64_t d, int64_t f,
+                               const void* w_gu, const void* w2,
+                               const void* ab_saved, const void* s_saved,
+                               const float* w_perm, void* dx_perm,
+                               void* dw_gu, void* dw2, float* dp,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * moe_unpermute -- combine, [P1] Challenge 1 (the loop index-adds each
+ * expert's rows back into the token's output).  Gather form, no atomics:
+ *   y[t] = sum over j, in ascending expert id, of wt * o_perm[pos[t][j]]
+ * with wt = w[t][j] (or 1 when w is NULL); fp32 accumulation, one final
+ * rounding.  o_perm [T*k][d] bf16; y [T][d] bf16 (y_fp32 == 0) or fp32
+ * (y_fp32 != 0).
+ */
+moe_status moe_unpermute(const void* o_perm, const int32_t* pos,
+                         const float* w, int64_t T, int32_t k, int64_t d,
+                         int32_t y_fp32, void* y, hipStream_t stream);
+
+/*
+ * moe_mxfp8_quantize -- MX block quantization, [P1] Challenge 2 (8-bit
+ * values, one scale per block of 32 consecutive values).  Per block:
+ * amax = max|v|; e = clamp(floor(log2 amax) - 8, -127, 127) (e = -127 for
+ * an all-zero block); scale byte = e + 127; code = E4M3(v / 2^e), rounded
+ * to nearest with ties to even mantissa and saturated to +-448, sign kept.
+ *   src [rows][cols] bf16.
+ *   axis == 0: blocks of 32 consecutive columns (cols % 32 == 0);
+ *     codes [rows][cols], scales [rows][cols/32].
+ *   axis == 1: blocks of 32 consecutive rows that restart at every segment
+ *     start seg_offsets[s] (nseg segments, seg_offsets [nseg+1] on the
+ *     device, seg_offsets[nseg] == rows; NULL means one segment); the last
+ *     block of a segment covers the rows left.  Output is transposed so
+ *     that each block is contiguous: codes [cols][rows_pad],
+ *     scales [cols][rows_pad/32], where row r of segment s lands at column
+ *     pad_off[s] + (r - seg_offsets[s]) and pad_off[s] is the sum of the
+ *     previous segments' lengths rounded up to 32; pad columns hold code 0.
+ *     rows_pad = moe_mxfp8_padded_rows(...) (host-side bound: rows +
+ *     31 * nseg rounded up to 32).
+ */
+moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
+                              int32_t axis, const int32_t* seg_offsets,
+                              int32_t nseg, uint8_t* codes, uint8_t* scales,
+                              int64_t rows_pad, hipStream_t stream);
+
+/* Host-side bound on rows_pad for axis == 1 quantization. */
+int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg);
+
+/*
+ * moe_workspace_bytes -- workspace size an entry point needs for the given
+ * problem (0 when none).  Returns 0 for invalid arguments.
+ */
+size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
+                           int32_t E, int32_t k, int64_t d, int64_t f);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,372 @@
+// C-ABI of libmoe: argument validation, workspace layout and launch order.
+// Semantics of every entry point are documented in include/moe.h.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "internal.h"
+
+using moe::bf16_t;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxBytes = (int64_t{1} << 31) - 1;
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+#define REQUIRE(cond, st, ...)               \
+  do {                                       \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p)                                                      \
+  do {                                                                      \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, #p " is NULL");    \
+    if (!aligned16(p))                                                      \
+      return fail(MOE_ERR_INVALID_ARG, #p " is not 16-byte aligned");       \
+  } while (0)
+
+#define REQUIRE_OPT_PTR(p)                                                  \
+  do {                                                                      \
+    if ((p) != nullptr && !aligned16(p))                                    \
+      return fail(MOE_ERR_INVALID_ARG, #p " is not 16-byte aligned");       \
+  } while (0)
+
+moe_status check_route_dims(int64_t T, int32_t E, int32_t k) {
+  REQUIRE(T >= 1, MOE_ERR_INVALID_ARG, "T must be >= 1 (got %lld)",
+          static_cast<long long>(T));
+  REQUIRE(T <= (int64_t{1} << 30), MOE_ERR_UNSUPPORTED, "T too large");
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d] (got %d)", moe::kMaxExperts, E);
+  REQUIRE(k >= 1 && k <= E, MOE_ERR_INVALID_ARG,
+          "k must be in [1, E] (got k=%d, E=%d)", k, E);
+  REQUIRE(k <= moe::kMaxTopK, MOE_ERR_UNSUPPORTED, "k must be <= %d",
+          moe::kMaxTopK);
+  REQUIRE(T * k <= (int64_t{1} << 31) - 1, MOE_ERR_UNSUPPORTED,
+          "T*k too large");
+  return MOE_OK;
+}
+
+moe_status check_prec(moe_prec prec) {
+  REQUIRE(prec == MOE_BF16 || prec == MOE_MXFP8, MOE_ERR_INVALID_ARG,
+          "unknown precision %d", static_cast<int>(prec));
+  return MOE_OK;
+}
+
+moe_status check_feature(const char* name, int64_t v, moe_prec prec) {
+  const int64_t q = (prec == MOE_MXFP8) ? 32 : 8;
+  REQUIRE(v >= q && v % q == 0, MOE_ERR_INVALID_ARG,
+          "%s must be a positive multiple of %lld (got %lld)", name,
+          static_cast<long long>(q), static_cast<long long>(v));
+  return MOE_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+struct BwdWorkspace {
+  size_t dab = 0, dp_part = 0, total = 0;
+};
+
+BwdWorkspace bwd_layout(int64_t Tk, int64_t f) {
+  BwdWorkspace w;
+  w.dab = 0;
+  size_t off = align256(static_cast<size_t>(Tk * 2 * f * 2));
+  w.dp_part = off;
+  off += align256(static_cast<size_t>(Tk * moe::gemm_dp_tiles(f) * 4));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
+                           int32_t E, int32_t k, int64_t d, int64_t f) {
+  (void)d;
+  if (T < 1 || E < 1 || E > moe::kMaxExperts || k < 1 || k > E) return 0;
+  const int64_t Tk = T * k;
+  switch (entry) {
+    case MOE_ENTRY_PERMUTE:
+      return moe::plan_workspace_bytes(Tk, E);
+    case MOE_ENTRY_MLP_FWD:
+      return 0;
+    case MOE_ENTRY_MLP_BWD:
+      if (prec != MOE_BF16 || f < 1) return 0;
+      return bwd_layout(Tk, f).total;
+  }
+  return 0;
+}
+
+moe_status moe_router_logits(const void* x, const void* w_g, const float* bias,
+                             int64_t T, int64_t d, int32_t E, float* logits,
+                             hipStream_t stream) {
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_g);
+  REQUIRE_OPT_PTR(bias);
+  REQUIRE_PTR(logits);
+  REQUIRE(T >= 1, MOE_ERR_INVALID_ARG, "T must be >= 1");
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d]", moe::kMaxExperts);
+  if (moe_status st = check_feature("d", d, MOE_BF16)) return st;
+  REQUIRE(T * d * 2 <= kMaxBytes && E * d * 2 <= kMaxBytes,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  return hip_status(moe::launch_router_logits(static_cast<const bf16_t*>(x),
+                                              static_cast<const bf16_t*>(w_g),
+                                              bias, T, d, E, logits, stream),
+                    "moe_router_logits");
+}
+
+moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
+                     int32_t renorm, int32_t* topk_idx, float* topk_w,
+                     hipStream_t stream) {
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  if (moe_status st = check_route_dims(T, E, k)) return st;
+  return hip_status(
+      moe::launch_route(logits, T, E, k, renorm ? 1 : 0, topk_idx, topk_w,
+                        stream),
+      "moe_route");
+}
+
+moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
+                       const float* topk_w, int64_t T, int32_t E, int32_t k,
+                       const void* x, const uint8_t* x_scales, int64_t d,
+                       int32_t* counts, int32_t* offsets, int32_t* pos,
+                       int32_t* src, float* w_perm, void* x_perm,
+                       uint8_t* x_perm_scales, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status st = check_prec(prec)) return st;
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_OPT_PTR(topk_w);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(src);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(x_perm);
+  REQUIRE(!(w_perm && !topk_w), MOE_ERR_INVALID_ARG,
+          "w_perm given without topk_w");
+  if (moe_status st = check_route_dims(T, E, k)) return st;
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  const int64_t row_bytes = (prec == MOE_BF16) ? d * 2 : d;
+  REQUIRE(T * k * row_bytes <= kMaxBytes * 4, MOE_ERR_UNSUPPORTED,
+          "permuted tensor too large");
+  if (prec == MOE_MXFP8) {
+    REQUIRE_PTR(x_scales);
+    REQUIRE_PTR(x_perm_scales);
+  }
+  const size_t need = moe::plan_workspace_bytes(T * k, E);
+  REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+  hipError_t e = moe::launch_plan(topk_idx, T, E, k, counts, offsets, pos,
+                                  workspace, stream);
+  if (e != hipSuccess) return hip_status(e, "moe_permute/plan");
+  const bool mx = prec == MOE_MXFP8;
+  e = moe::launch_scatter(topk_idx, topk_w, T, E, k, offsets, pos, src,
+                          topk_w ? w_perm : nullptr, x, row_bytes, x_perm,
+                          mx ? x_scales : nullptr, mx ? d / 32 : 0,
+                          mx ? x_perm_scales : nullptr, workspace, stream);
+  return hip_status(e, "moe_permute/scatter");
+}
+
+moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
+                            int32_t k, const void* x, const uint8_t* x_scales,
+                            int64_t d, void* x_perm, uint8_t* x_perm_scales,
+                            hipStream_t stream) {
+  if (moe_status st = check_prec(prec)) return st;
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(x_perm);
+  REQUIRE(T >= 1, MOE_ERR_INVALID_ARG, "T must be >= 1");
+  REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
+          "k must be in [1, %d]", moe::kMaxTopK);
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  const bool mx = prec == MOE_MXFP8;
+  if (mx) {
+    REQUIRE_PTR(x_scales);
+    REQUIRE_PTR(x_perm_scales);
+  }
+  const int64_t row_bytes = mx ? d : d * 2;
+  return hip_status(
+      moe::launch_permute_rows(pos, T, k, x, row_bytes, x_perm,
+                               mx ? x_scales : nullptr, mx ? d / 32 : 0,
+                               mx ? x_perm_scales : nullptr, stream),
+      "moe_permute_rows");
+}
+
+moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
+                               const uint8_t* x_perm_scales,
+                               const int32_t* offsets, int32_t E, int64_t Tk,
+                               int64_t d, int64_t f, const void* w_gu,
+                               const uint8_t* w_gu_scales, const void* w2,
+                               const uint8_t* w2_scales, const float* w_perm,
+                               void* ab_saved, void* s_saved, void* out_perm,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  (void)x_perm_scales; (void)w_gu_scales; (void)w2_scales;
+  (void)workspace; (void)workspace_bytes;
+  if (moe_status st = check_prec(prec)) return st;
+  REQUIRE(prec == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "MXFP8 grouped MLP is not available in this build");
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w_gu);
+  REQUIRE_PTR(w2);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(ab_saved);
+  REQUIRE_PTR(s_saved);
+  REQUIRE_PTR(out_perm);
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  if (moe_status st = check_feature("f", f, prec)) return st;
+  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 2 <= kMaxBytes &&
+              2 * f * d * 2 <= kMaxBytes,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  hipError_t e = moe::gemm_fc1_fwd(
+      static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(w_gu),
+      offsets, E, Tk, d, f, w_perm, static_cast<bf16_t*>(ab_saved),
+      static_cast<bf16_t*>(s_saved), stream);
+  if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_fwd/fc1");
+  e = moe::gemm_fc2_fwd(static_cast<const bf16_t*>(s_saved),
+                        static_cast<const bf16_t*>(w2), offsets, E, Tk, d, f,
+                        static_cast<bf16_t*>(out_perm), stream);
+  return hip_status(e, "moe_grouped_mlp_fwd/fc2");
+}
+
+moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
+                               const void* x_perm, const int32_t* offsets,
+                               const int32_t* pos, int64_t T, int32_t k,
+                               int32_t E, int64_t d, int64_t f,
+                               const void* w_gu, const void* w2,
+                               const void* ab_saved, const void* s_saved,
+                               const float* w_perm, void* dx_perm,
+                               void* dw_gu, void* dw2, float* dp,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (moe_status st = check_prec(prec)) return st;
+  REQUIRE(prec == MOE_BF16, MOE_ERR_UNSUPPORTED,
+          "MXFP8 grouped MLP backward is not available in this build");
+  REQUIRE_PTR(dout_perm);
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(w_gu);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(ab_saved);
+  REQUIRE_PTR(s_saved);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(dx_perm);
+  REQUIRE_PTR(dw_gu);
+  REQUIRE_PTR(dw2);
+  REQUIRE_PTR(dp);
+  if (moe_status st = check_route_dims(T, E, k)) return st;
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  if (moe_status st = check_feature("f", f, prec)) return st;
+  const int64_t Tk = T * k;
+  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 2 <= kMaxBytes &&
+              2 * f * d * 2 <= kMaxBytes,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  const BwdWorkspace L = bwd_layout(Tk, f);
+  REQUIRE(workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
+          "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+  REQUIRE_PTR(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  bf16_t* dab = reinterpret_cast<bf16_t*>(ws + L.dab);
+  float* dp_part = reinterpret_cast<float*>(ws + L.dp_part);
+  const bf16_t* dO = static_cast<const bf16_t*>(dout_perm);
+  const bf16_t* xp = static_cast<const bf16_t*>(x_perm);
+  hipError_t e = moe::gemm_fc2_dgrad(
+      dO, static_cast<const bf16_t*>(w2), offsets, E, Tk, d, f,
+      static_cast<const bf16_t*>(ab_saved), w_perm, dab, dp_part, stream);
+  if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/fc2_dgrad");
+  e = moe::launch_dp_reduce(dp_part, moe::gemm_dp_tiles(f), pos, T, k, dp,
+                            stream);
+  if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/dp");
+  e = moe::gemm_wgrad(dO, d, static_cast<const bf16_t*>(s_saved), f, offsets,
+                      E, Tk, d, f, static_cast<bf16_t*>(dw2), stream);
+  if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/dw2");
+  e = moe::gemm_fc1_dgrad(dab, static_cast<const bf16_t*>(w_gu), offsets, E,
+                          Tk, d, f, static_cast<bf16_t*>(dx_perm), stream);
+  if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/fc1_dgrad");
+  e = moe::gemm_wgrad(dab, 2 * f, xp, d, offsets, E, Tk, 2 * f, d,
+                      static_cast<bf16_t*>(dw_gu), stream);
+  return hip_status(e, "moe_grouped_mlp_bwd/dw_gu");
+}
+
+moe_status moe_unpermute(const void* o_perm, const int32_t* pos,
+                         const float* w, int64_t T, int32_t k, int64_t d,
+                         int32_t y_fp32, void* y, hipStream_t stream) {
+  REQUIRE_PTR(o_perm);
+  REQUIRE_PTR(pos);
+  REQUIRE_OPT_PTR(w);
+  REQUIRE_PTR(y);
+  REQUIRE(T >= 1, MOE_ERR_INVALID_ARG, "T must be >= 1");
+  REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
+          "k must be in [1, %d]", moe::kMaxTopK);
+  if (moe_status st = check_feature("d", d, MOE_BF16)) return st;
+  return hip_status(moe::launch_unpermute(static_cast<const bf16_t*>(o_perm),
+                                          pos, w, T, k, d, y_fp32 ? 1 : 0, y,
+                                          stream),
+                    "moe_unpermute");
+}
+
+int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg) {
+  if (rows < 0 || nseg < 1) return 0;
+  return ((rows + 31 * static_cast<int64_t>(nseg)) + 31) / 32 * 32;
+}
+
+moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
+                              int32_t axis, const int32_t* seg_offsets,
+                              int32_t nseg, uint8_t* codes, uint8_t* scales,
+                              int64_t rows_pad, hipStream_t stream) {
+  (void)src; (void)rows; (void)cols; (void)axis; (void)seg_offsets;
+  (void)nseg; (void)codes; (void)scales; (void)rows_pad; (void)stream;
+  return fail(MOE_ERR_UNSUPPORTED, "MXFP8 quantize is not available in this build");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Launchers shared between the kernel translation units and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kPlanChunk = 512;   // slots per block of the counting pass
+
+// routing (route.hip)
+hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
+                                const float* bias, int64_t T, int64_t d, int E,
+                                float* logits, hipStream_t s);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k,
+                        int renorm, int32_t* idx, float* w, hipStream_t s);
+
+// dispatch plan and row movement (permute.hip)
+size_t plan_workspace_bytes(int64_t Tk, int E);
+hipError_t launch_plan(const int32_t* idx, int64_t T, int E, int k,
+                       int32_t* counts, int32_t* offsets, int32_t* pos,
+                       void* ws, hipStream_t s);
+// pos/src/w_perm from the plan + the rows of x (row_bytes each) and an
+// optional side array of side_bytes per row (MX scales).
+hipError_t launch_scatter(const int32_t* idx, const float* topk_w, int64_t T,
+                          int E, int k, const int32_t* offsets, int32_t* pos,
+                          int32_t* src, float* w_perm, const void* x,
+                          int64_t row_bytes, void* x_perm,
+                          const void* side, int64_t side_bytes, void* side_perm,
+                          const void* ws, hipStream_t s);
+hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
+                               const void* x, int64_t row_bytes, void* x_perm,
+                               const void* side, int64_t side_bytes,
+                               void* side_perm, hipStream_t s);
+hipError_t launch_unpermute(const bf16_t* o, const int32_t* pos,
+                            const float* w, int64_t T, int k, int64_t d,
+                            int y_fp32, void* y, hipStream_t s);
+hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
+                            int64_t T, int k, float* dp, hipStream_t s);
+
+// grouped GEMMs (gemm.hip)
+int gemm_dp_tiles(int64_t f);
+hipError_t gemm_fc1_fwd(const bf16_t* xp, const bf16_t* w_gu,
+                        const int32_t* offsets, int E, int64_t Tk, int64_t d,
+                        int64_t f, const float* w_perm, bf16_t* ab, bf16_t* s,
+                        hipStream_t st);
+hipError_t gemm_fc2_fwd(const bf16_t* s, const bf16_t* w2,
+                        const int32_t* offsets, int E, int64_t Tk, int64_t d,
+                        int64_t f, bf16_t* o, hipStream_t st);
+hipError_t gemm_fc2_dgrad(const bf16_t* dO, const bf16_t* w2,
+                          const int32_t* offsets, int E, int64_t Tk,
+                          int64_t d, int64_t f, const bf16_t* ab,
+                          const float* w_perm, bf16_t* dab, float* dp_part,
+                          hipStream_t st);
+hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
+                          const int32_t* offsets, int E, int64_t Tk,
+                          int64_t d, int64_t f, bf16_t* dxp, hipStream_t st);
+hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
+                      int64_t ldb, const int32_t* offsets, int E, int64_t Tk,
+                      int64_t M, int64_t N, bf16_t* c, hipStream_t st);
+
+}  // namespace moe

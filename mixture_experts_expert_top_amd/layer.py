@@ -1,0 +1,93 @@
+"""One MoE expert-MLP layer driven through the C-ABI.
+
+``MoEPath`` owns the device buffers of one problem size (allocated once
+with torch, reused every step) and issues the library calls in order:
+
+  forward : moe_router_logits -> moe_route -> moe_permute
+            -> moe_grouped_mlp_fwd -> moe_unpermute
+  backward: moe_permute_rows (dY) -> moe_grouped_mlp_bwd -> moe_unpermute
+
+No arithmetic happens here: every step runs in the library's kernels.
+"""
+
+import torch
+
+from . import moe
+from .moe import MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_PERMUTE
+
+
+class MoEPath:
+    def __init__(self, T, d, f, E, k, renorm=True, prec=MOE_BF16,
+                 device="cuda", y_fp32=False):
+        if prec != MOE_BF16:
+            raise NotImplementedError("use MoEPathMX for the MXFP8 path")
+        self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
+        self.renorm = renorm
+        self.prec = prec
+        Tk = T * k
+        dev = torch.device(device)
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        z = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        self.logits = z(T, E, dt=f32)
+        self.topk_idx = z(T, k, dt=i32)
+        self.topk_w = z(T, k, dt=f32)
+        self.counts = z(E, dt=i32)
+        self.offsets = z(E + 1, dt=i32)
+        self.pos = z(T, k, dt=i32)
+        self.src = z(Tk, dt=i32)
+        self.w_perm = z(Tk, dt=f32)
+        self.x_perm = z(Tk, d, dt=bf)
+        self.ab = z(Tk, 2 * f, dt=bf)
+        self.s = z(Tk, f, dt=bf)
+        self.o = z(Tk, d, dt=bf)
+        self.y = z(T, d, dt=f32 if y_fp32 else bf)
+        ws_p = moe.moe_workspace_bytes(MOE_ENTRY_PERMUTE, prec, T, E, k, d, f)
+        self.ws_permute = z(max(ws_p, 16), dt=torch.uint8)
+        self._bwd_ready = False
+
+    def _alloc_bwd(self):
+        T, d, f, E, k = self.T, self.d, self.f, self.E, self.k
+        Tk = T * k
+        dev = self.x_perm.device
+        bf = torch.bfloat16
+        self.dout_perm = torch.empty(Tk, d, dtype=bf, device=dev)
+        self.dx_perm = torch.empty(Tk, d, dtype=bf, device=dev)
+        self.dw_gu = torch.empty(E, 2 * f, d, dtype=bf, device=dev)
+        self.dw2 = torch.empty(E, d, f, dtype=bf, device=dev)
+        self.dp = torch.empty(T, k, dtype=torch.float32, device=dev)
+        self.dx = torch.empty(T, d, dtype=bf, device=dev)
+        ws_b = moe.moe_workspace_bytes(MOE_ENTRY_MLP_BWD, self.prec, T, E, k,
+                                       d, f)
+        self.ws_bwd = torch.empty(max(ws_b, 16), dtype=torch.uint8,
+                                  device=dev)
+        self._bwd_ready = True
+
+    # ------------------------------------------------------------------
+    def route(self, x=None, w_g=None, bias=None, logits=None):
+        if logits is None:
+            moe.moe_router_logits(x, w_g, bias, self.logits)
+            logits = self.logits
+        moe.moe_route(logits, self.k, self.renorm, self.topk_idx, self.topk_w)
+
+    def forward(self, x, w_gu, w2, w_g=None, bias=None, logits=None):
+        self.route(x, w_g, bias, logits)
+        moe.moe_permute(self.prec, self.topk_idx, self.topk_w, self.E, x,
+                        None, self.counts, self.offsets, self.pos, self.src,
+                        self.w_perm, self.x_perm, None, self.ws_permute)
+        moe.moe_grouped_mlp_fwd(self.prec, self.x_perm, None, self.offsets,
+                                w_gu, None, w2, None, self.w_perm, self.ab,
+                                self.s, self.o)
+        moe.moe_unpermute(self.o, self.pos, None, self.y)
+        return self.y
+
+    def backward(self, dy, w_gu, w2):
+        if not self._bwd_ready:
+            self._alloc_bwd()
+        moe.moe_permute_rows(self.prec, self.pos, dy, None, self.dout_perm,
+                             None)
+        moe.moe_grouped_mlp_bwd(self.prec, self.dout_perm, self.x_perm,
+                                self.offsets, self.pos, w_gu, w2, self.ab,
+                                self.s, self.w_perm, self.dx_perm, self.dw_gu,
+                                self.dw2, self.dp, self.ws_bwd)
+        moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+        return self.dx, self.dw_gu, self.dw2, self.dp

@@ -1,0 +1,254 @@
+"""Python binding of libmoe.so (see include/moe.h for the semantics).
+
+Argument marshalling only: each function checks that the torch tensors have
+the dtype, device and contiguity the C-ABI expects, passes their device
+pointers and the current HIP stream, and raises MoeError on a non-zero
+status.  All compute happens in the library's kernels.  Importing this
+module fails loudly when libmoe.so has not been built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_BF16 = 0
+MOE_MXFP8 = 1
+MOE_ENTRY_PERMUTE = 0
+MOE_ENTRY_MLP_FWD = 1
+MOE_ENTRY_MLP_BWD = 2
+
+EXPORTED = [
+    "moe_status_str", "moe_last_error", "moe_version", "moe_router_logits",
+    "moe_route", "moe_permute", "moe_permute_rows", "moe_grouped_mlp_fwd",
+    "moe_grouped_mlp_bwd", "moe_unpermute", "moe_mxfp8_quantize",
+    "moe_mxfp8_padded_rows", "moe_workspace_bytes",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name, status, status_str, message):
+        super().__init__(f"{name} failed: {status_str}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m mixture_experts_expert_top_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                       ctypes.c_size_t)
+    sig = {
+        "moe_status_str": (ctypes.c_char_p, [I32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_version": (ctypes.c_char_p, []),
+        "moe_router_logits": (I32, [P, P, P, I64, I64, I32, P, P]),
+        "moe_route": (I32, [P, I64, I32, I32, I32, P, P, P]),
+        "moe_permute": (I32, [I32, P, P, I64, I32, I32, P, P, I64, P, P, P,
+                              P, P, P, P, P, SZ, P]),
+        "moe_permute_rows": (I32, [I32, P, I64, I32, P, P, I64, P, P, P]),
+        "moe_grouped_mlp_fwd": (I32, [I32, P, P, P, I32, I64, I64, I64, P, P,
+                                      P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
+                                      I64, P, P, P, P, P, P, P, P, P, P, SZ,
+                                      P]),
+        "moe_unpermute": (I32, [P, P, P, I64, I32, I64, I32, P, P]),
+        "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
+        "moe_mxfp8_padded_rows": (I64, [I64, I32]),
+        "moe_workspace_bytes": (SZ, [I32, I32, I64, I32, I32, I64, I64]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _p(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name, status):
+    if status != 0:
+        raise MoeError(name, status, lib.moe_status_str(status).decode(),
+                       lib.moe_last_error().decode())
+
+
+def _want(t, name, dtype, shape=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def version():
+    return lib.moe_version().decode()
+
+
+def moe_workspace_bytes(entry, prec, T, E, k, d, f):
+    return int(lib.moe_workspace_bytes(entry, prec, T, E, k, d, f))
+
+
+def moe_router_logits(x, w_g, bias, logits, stream=None):
+    T, d = x.shape
+    E = w_g.shape[0]
+    _want(x, "x", torch.bfloat16)
+    _want(w_g, "w_g", torch.bfloat16, (E, d))
+    _want(bias, "bias", torch.float32, (E,), allow_none=True)
+    _want(logits, "logits", torch.float32, (T, E))
+    _check("moe_router_logits", lib.moe_router_logits(
+        _p(x), _p(w_g), _p(bias), T, d, E, _p(logits), _stream(stream)))
+
+
+def moe_route(logits, k, renorm, topk_idx, topk_w, stream=None):
+    T, E = logits.shape
+    _want(logits, "logits", torch.float32)
+    _want(topk_idx, "topk_idx", torch.int32, (T, k))
+    _want(topk_w, "topk_w", torch.float32, (T, k))
+    _check("moe_route", lib.moe_route(_p(logits), T, E, k, int(renorm),
+                                      _p(topk_idx), _p(topk_w),
+                                      _stream(stream)))
+
+
+def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
+                src, w_perm, x_perm, x_perm_scales, workspace, stream=None):
+    T, k = topk_idx.shape
+    d = x.shape[1]
+    _want(topk_idx, "topk_idx", torch.int32)
+    _want(topk_w, "topk_w", torch.float32, (T, k), allow_none=True)
+    xdt = torch.bfloat16 if prec == MOE_BF16 else torch.uint8
+    _want(x, "x", xdt, (T, d))
+    _want(x_perm, "x_perm", xdt, (T * k, d))
+    if prec == MOE_MXFP8:
+        _want(x_scales, "x_scales", torch.uint8, (T, d // 32))
+        _want(x_perm_scales, "x_perm_scales", torch.uint8, (T * k, d // 32))
+    for n, t, shp in (("counts", counts, (E,)), ("offsets", offsets, (E + 1,)),
+                      ("pos", pos, (T, k)), ("src", src, (T * k,))):
+        _want(t, n, torch.int32, shp)
+    _want(w_perm, "w_perm", torch.float32, (T * k,), allow_none=True)
+    nbytes = workspace.numel() * workspace.element_size() if workspace \
+        is not None else 0
+    _check("moe_permute", lib.moe_permute(
+        prec, _p(topk_idx), _p(topk_w), T, E, k, _p(x), _p(x_scales), d,
+        _p(counts), _p(offsets), _p(pos), _p(src), _p(w_perm), _p(x_perm),
+        _p(x_perm_scales), _p(workspace), nbytes, _stream(stream)))
+
+
+def moe_permute_rows(prec, pos, x, x_scales, x_perm, x_perm_scales,
+                     stream=None):
+    T, k = pos.shape
+    d = x.shape[1]
+    _want(pos, "pos", torch.int32)
+    xdt = torch.bfloat16 if prec == MOE_BF16 else torch.uint8
+    _want(x, "x", xdt, (T, d))
+    _want(x_perm, "x_perm", xdt, (T * k, d))
+    _check("moe_permute_rows", lib.moe_permute_rows(
+        prec, _p(pos), T, k, _p(x), _p(x_scales), d, _p(x_perm),
+        _p(x_perm_scales), _stream(stream)))
+
+
+def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
+                        w_gu_scales, w2, w2_scales, w_perm, ab_saved, s_saved,
+                        out_perm, workspace=None, stream=None):
+    Tk, d = x_perm.shape
+    E, two_f, _ = w_gu.shape
+    f = two_f // 2
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    if prec == MOE_BF16:
+        _want(x_perm, "x_perm", torch.bfloat16)
+        _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
+        _want(w2, "w2", torch.bfloat16, (E, d, f))
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
+    _want(out_perm, "out_perm", torch.bfloat16, (Tk, d))
+    nbytes = workspace.numel() * workspace.element_size() if workspace \
+        is not None else 0
+    _check("moe_grouped_mlp_fwd", lib.moe_grouped_mlp_fwd(
+        prec, _p(x_perm), _p(x_perm_scales), _p(offsets), E, Tk, d, f,
+        _p(w_gu), _p(w_gu_scales), _p(w2), _p(w2_scales), _p(w_perm),
+        _p(ab_saved), _p(s_saved), _p(out_perm), _p(workspace), nbytes,
+        _stream(stream)))
+
+
+def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
+                        ab_saved, s_saved, w_perm, dx_perm, dw_gu, dw2, dp,
+                        workspace, stream=None):
+    Tk, d = x_perm.shape
+    T, k = pos.shape
+    E, two_f, _ = w_gu.shape
+    f = two_f // 2
+    for n, t, shp in (("dout_perm", dout_perm, (Tk, d)),
+                      ("x_perm", x_perm, (Tk, d)),
+                      ("w_gu", w_gu, (E, 2 * f, d)), ("w2", w2, (E, d, f)),
+                      ("ab_saved", ab_saved, (Tk, 2 * f)),
+                      ("s_saved", s_saved, (Tk, f)),
+                      ("dx_perm", dx_perm, (Tk, d)),
+                      ("dw_gu", dw_gu, (E, 2 * f, d)), ("dw2", dw2, (E, d, f))):
+        _want(t, n, torch.bfloat16, shp)
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(pos, "pos", torch.int32)
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(dp, "dp", torch.float32, (T, k))
+    nbytes = workspace.numel() * workspace.element_size() if workspace \
+        is not None else 0
+    _check("moe_grouped_mlp_bwd", lib.moe_grouped_mlp_bwd(
+        prec, _p(dout_perm), _p(x_perm), _p(offsets), _p(pos), T, k, E, d, f,
+        _p(w_gu), _p(w2), _p(ab_saved), _p(s_saved), _p(w_perm),
+        _p(dx_perm), _p(dw_gu), _p(dw2), _p(dp), _p(workspace), nbytes,
+        _stream(stream)))
+
+
+def moe_unpermute(o_perm, pos, w, y, stream=None):
+    T, k = pos.shape
+    d = o_perm.shape[1]
+    _want(o_perm, "o_perm", torch.bfloat16, (T * k, d))
+    _want(pos, "pos", torch.int32)
+    _want(w, "w", torch.float32, (T, k), allow_none=True)
+    if y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("y must be bfloat16 or float32")
+    _want(y, "y", y.dtype, (T, d))
+    _check("moe_unpermute", lib.moe_unpermute(
+        _p(o_perm), _p(pos), _p(w), T, k, d,
+        1 if y.dtype == torch.float32 else 0, _p(y), _stream(stream)))
+
+
+def moe_mxfp8_padded_rows(rows, nseg):
+    return int(lib.moe_mxfp8_padded_rows(rows, nseg))
+
+
+def moe_mxfp8_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,
+                       stream=None):
+    rows, cols = src.shape
+    _want(src, "src", torch.bfloat16)
+    _want(codes, "codes", torch.uint8)
+    _want(scales, "scales", torch.uint8)
+    nseg = 1 if seg_offsets is None else seg_offsets.numel() - 1
+    if seg_offsets is not None:
+        _want(seg_offsets, "seg_offsets", torch.int32)
+    _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(
+        _p(src), rows, cols, axis, _p(seg_offsets), nseg, _p(codes),
+        _p(scales), rows_pad, _stream(stream)))

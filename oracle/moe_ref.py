@@ -294,3 +294,36 @@ def row_backward(x_t, dy_t, p_r, w_gu_e, w2_e):
                           dh * silu(a_g)])
     dxp = dab @ w_gu_e
     return dab, dxp, dp_r, ab[0], s[0]
+
+
+def dw2_column(xp_e, do_e, w_e, w_gu_e, j):
+    """Column j of dW2_e = sum over the expert's rows of dO[r] * S[r, j],
+    with S[r, j] = w_r * silu(Xp[r] . W1[j]) * (Xp[r] . W3[j]).
+    xp_e [n, d], do_e [n, d], w_e [n], w_gu_e [2f, d]."""
+    xp_e = np.asarray(xp_e, dtype=np.float64)
+    do_e = np.asarray(do_e, dtype=np.float64)
+    f = w_gu_e.shape[0] // 2
+    g = xp_e @ np.asarray(w_gu_e[j], dtype=np.float64)
+    u = xp_e @ np.asarray(w_gu_e[f + j], dtype=np.float64)
+    s = np.asarray(w_e, dtype=np.float64) * silu(g) * u
+    return do_e.T @ s
+
+
+def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i):
+    """Row i (of 2f) of dW_gu_e = sum over the expert's rows of
+    dAB[r, i] * Xp[r]; dAB[:, i] needs only column i mod f of dS, gate and
+    up.  xp_e, do_e [n, d]; w_e [n]; w_gu_e [2f, d]; w2_e [d, f]."""
+    xp_e = np.asarray(xp_e, dtype=np.float64)
+    do_e = np.asarray(do_e, dtype=np.float64)
+    f = w_gu_e.shape[0] // 2
+    c = i % f
+    g = xp_e @ np.asarray(w_gu_e[c], dtype=np.float64)
+    u = xp_e @ np.asarray(w_gu_e[f + c], dtype=np.float64)
+    ds = do_e @ np.asarray(w2_e[:, c], dtype=np.float64)
+    dh = np.asarray(w_e, dtype=np.float64) * ds
+    if i < f:
+        sg = sigmoid(g)
+        col = dh * u * sg * (1.0 + g * (1.0 - sg))
+    else:
+        col = dh * silu(g)
+    return col @ xp_e

@@ -1,0 +1,128 @@
+"""Host-side checks of libmoe.so that need no GPU: the library loads, it
+exports every entry point include/moe.h declares, and argument validation
+rejects bad calls before anything is launched (fake device pointers are
+safe here because validation fails first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_expert_top_amd import moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "moe.h")
+L = moe.lib
+
+OK, INVALID, UNSUP, WS = 0, 1, 2, 3
+BF16, MX = 0, 1
+A = 4096          # a fake, 16-byte-aligned "device" address
+MIS = 4096 + 4    # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert L.moe_status_str(0) == b"MOE_OK"
+    assert L.moe_status_str(3) == b"MOE_ERR_WORKSPACE"
+    assert b"gfx950" in L.moe_version()
+
+
+def _route(logits, T, E, k, idx, w):
+    return L.moe_route(logits, T, E, k, 1, idx, w, None)
+
+
+@pytest.mark.parametrize("T,E,k,want", [
+    (0, 8, 2, INVALID), (16, 0, 1, INVALID), (16, 8, 0, INVALID),
+    (16, 8, 9, INVALID), (16, 2000, 2, INVALID), (16, 64, 33, UNSUP)])
+def test_route_rejects_bad_dims(T, E, k, want):
+    assert _route(A, T, E, k, A, A) == want
+    assert L.moe_last_error()
+
+
+def test_route_rejects_null_and_misaligned():
+    assert _route(None, 16, 8, 2, A, A) == INVALID
+    assert b"logits" in L.moe_last_error()
+    assert _route(A, 16, 8, 2, MIS, A) == INVALID
+    assert b"aligned" in L.moe_last_error()
+
+
+def test_router_logits_rejects_bad_d():
+    assert L.moe_router_logits(A, A, None, 8, 12, 4, A, None) == INVALID
+    assert L.moe_router_logits(A, A, None, 8, 0, 4, A, None) == INVALID
+    assert L.moe_router_logits(None, A, None, 8, 16, 4, A, None) == INVALID
+
+
+def _permute(prec=BF16, T=16, E=4, k=2, d=64, ws_bytes=None, x_scales=None,
+             xp_scales=None, ws=A, w=A, w_perm=A):
+    if ws_bytes is None:
+        ws_bytes = L.moe_workspace_bytes(0, prec, T, E, k, d, 64)
+    return L.moe_permute(prec, A, w, T, E, k, A, x_scales, d, A, A, A, A,
+                         w_perm, A, xp_scales, ws, ws_bytes, None)
+
+
+def test_permute_validation():
+    assert _permute(ws_bytes=0) == WS
+    assert b"workspace" in L.moe_last_error()
+    assert _permute(d=12) == INVALID
+    assert _permute(prec=7) == INVALID
+    assert _permute(prec=MX, d=48) == INVALID          # MX needs d % 32
+    assert _permute(prec=MX, d=64) == INVALID          # scales missing
+    assert _permute(w=None) == INVALID                 # w_perm without w
+    assert _permute(ws=None) == INVALID
+
+
+def test_workspace_sizes():
+    assert L.moe_workspace_bytes(0, BF16, 8192, 8, 2, 4096, 14336) > 0
+    assert L.moe_workspace_bytes(1, BF16, 8192, 8, 2, 4096, 14336) == 0
+    bwd = L.moe_workspace_bytes(2, BF16, 8192, 8, 2, 4096, 14336)
+    assert bwd >= 16384 * 2 * 14336 * 2               # holds dAB
+    assert L.moe_workspace_bytes(0, BF16, 0, 8, 2, 64, 64) == 0
+    assert L.moe_workspace_bytes(0, BF16, 8, 8, 9, 64, 64) == 0
+
+
+def test_mlp_fwd_validation():
+    f = L.moe_grouped_mlp_fwd
+    # f not a multiple of 8
+    assert f(BF16, A, None, A, 4, 128, 32, 60, A, None, A, None, A, A, A, A,
+             None, 0, None) == INVALID
+    # too large for 32-bit buffer offsets
+    assert f(BF16, A, None, A, 8, 1 << 20, 4096, 14336, A, None, A, None, A,
+             A, A, A, None, 0, None) == UNSUP
+    assert f(BF16, None, None, A, 4, 128, 32, 64, A, None, A, None, A, A, A,
+             A, None, 0, None) == INVALID
+
+
+def test_mlp_bwd_validation():
+    f = L.moe_grouped_mlp_bwd
+    ws = L.moe_workspace_bytes(2, BF16, 64, 4, 2, 32, 64)
+    args = [BF16, A, A, A, A, 64, 2, 4, 32, 64, A, A, A, A, A, A, A, A, A, A]
+    assert f(*args, ws - 1, None) == WS
+    bad = list(args)
+    bad[7] = 1                          # E < k
+    assert f(*bad, ws, None) == INVALID
+
+
+def test_unpermute_validation():
+    assert L.moe_unpermute(A, A, None, 8, 0, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, A, None, 8, 2, 60, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, None, None, 8, 2, 64, 0, A, None) == INVALID
+
+
+def test_padded_rows():
+    assert L.moe_mxfp8_padded_rows(100, 1) == 160
+    assert L.moe_mxfp8_padded_rows(64, 4) == 192
+    assert L.moe_mxfp8_padded_rows(-1, 1) == 0

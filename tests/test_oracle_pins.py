@@ -341,3 +341,24 @@ def test_sampled_helpers_match_full_layer():
             assert abs(dp_r - bwd["dp"][t, j]) <= 1e-13 * max(1, abs(dp_r))
             np.testing.assert_allclose(ab, fwd["ab"][r], rtol=1e-13)
             np.testing.assert_allclose(s, fwd["s"][r], rtol=1e-13)
+
+
+def test_sampled_weight_grads_match_full_layer():
+    T, d, f, E, k = 30, 16, 12, 4, 2
+    a = _tiny(T, d, f, E, k, seed=21)
+    a["w_gu"] *= 25.0
+    fwd = R.moe_forward(a["x"], a["logits"], a["w_gu"], a["w2"], k)
+    bwd = R.moe_backward(fwd, a["dy"], a["w_gu"], a["w2"])
+    for e in range(E):
+        r0, r1 = fwd["offsets"][e], fwd["offsets"][e + 1]
+        xp_e = fwd["xp"][r0:r1]
+        do_e = bwd["do"][r0:r1]
+        w_e = fwd["w_perm"][r0:r1]
+        for j in (0, 5, f - 1):
+            np.testing.assert_allclose(
+                R.dw2_column(xp_e, do_e, w_e, a["w_gu"][e], j),
+                bwd["dw2"][e][:, j], rtol=1e-12, atol=1e-14)
+        for i in (0, 3, f, 2 * f - 1):
+            np.testing.assert_allclose(
+                R.dw_gu_row(xp_e, do_e, w_e, a["w_gu"][e], a["w2"][e], i),
+                bwd["dw_gu"][e][i], rtol=1e-12, atol=1e-14)
