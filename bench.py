@@ -1,0 +1,196 @@
+"""Benchmark of the MoE expert-MLP hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, forward and
+backward: router scores (x . W_g), top-k routing, permutation, the grouped
+gate_up GEMM with the fused ScaledSwiGLU epilogue, the grouped down GEMM,
+the combine, the permutation of dY, the fused down-projection backward
+(dS, dSwiGLU, routing-weight gradient partials), their reduction, both
+variable-K weight-gradient GEMMs, the gate_up data gradient and the combine
+of dX.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer,
+forward+backward in bf16 (T=8192 tokens as 2 x 4096, d=4096, f=14336, E=8,
+top-2, renormalised), random weights and inputs.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("MoE-layer fwd+bwd tokens/s & TFLOP/s (% MFMA peak), "
+          "Mixtral shape, 1 MI355X")
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+GEMM_STAGES = ("gate_up_swiglu_fwd", "down_fwd", "down_swiglu_bwd",
+               "wgrad_down", "gate_up_dgrad", "wgrad_gate_up")
+
+
+def stage_flops(name, T, d, f, E, k):
+    Tk = T * k
+    return {
+        "router_logits": 2.0 * T * d * E,
+        "gate_up_swiglu_fwd": 4.0 * Tk * d * f,
+        "down_fwd": 2.0 * Tk * d * f,
+        "down_swiglu_bwd": 2.0 * Tk * d * f,
+        "wgrad_down": 2.0 * Tk * d * f,
+        "gate_up_dgrad": 4.0 * Tk * d * f,
+        "wgrad_gate_up": 4.0 * Tk * d * f,
+    }.get(name, 0.0)
+
+
+def stage_bytes(name, T, d, f, E, k):
+    """Algorithmic HBM bytes of the memory-bound stages (each tensor read
+    or written once)."""
+    Tk = T * k
+    return {
+        "route": T * E * 4 + Tk * 8,
+        "permute": Tk * 8 + T * d * 2 + Tk * d * 2 + Tk * 12 + E * 8,
+        "unpermute_y": Tk * 4 + Tk * d * 4 + T * d * 2,
+        "permute_dy": Tk * 4 + T * d * 2 + Tk * d * 2,
+        "unpermute_dx": Tk * 4 + Tk * d * 4 + T * d * 2,
+    }.get(name, 0)
+
+
+def cpu_baseline(inp, wl, n_tokens):
+    """The float64 oracle, untuned, on the first n_tokens tokens of the same
+    workload (router scores, routing, experts, combine and backward)."""
+    import numpy as np
+    from oracle import moe_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    h = lambda t: t.double().cpu().numpy()  # noqa: E731
+    x = h(inp["x"][:n_tokens])
+    dy = h(inp["dy"][:n_tokens])
+    w_g = h(inp["w_g"])
+    bias = None if inp["bias"] is None else h(inp["bias"])
+    w_gu = h(inp["w_gu"])
+    w2 = h(inp["w2"])
+    t0 = time.perf_counter()
+    logits = moe_ref.router_logits(x, w_g, bias)
+    fwd = moe_ref.moe_forward(x, logits, w_gu, w2, wl.k)
+    moe_ref.moe_backward(fwd, dy, w_gu, w2)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens of the {wl.name} workload, "
+                       "fwd+bwd, float64 numpy per-expert loop with the full "
+                       f"weights ({dt:.1f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral",
+                    help="mixtral (default), finegrain, tiny")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
+              "supported (this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_expert_top_amd import inputs
+    from mixture_experts_expert_top_amd.layer import MoEPath, StageTimers
+
+    wl = inputs.WORKLOADS[args.workload]
+    if wl.prec != "bf16":
+        raise SystemExit("the bench drives the bf16 path")
+    T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
+    dev = torch.device("cuda:0")
+    inp = inputs.make_inputs(wl, seed=0, device=dev)
+    path = MoEPath(T, d, f, E, k, device=dev)
+
+    def step(timers=None):
+        path.forward(inp["x"], inp["w_gu"], inp["w2"], w_g=inp["w_g"],
+                     bias=inp["bias"], timers=timers)
+        path.backward(inp["dy"], inp["w_gu"], inp["w2"], timers=timers)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timers = StageTimers()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step(timers)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end) / args.steps
+
+    stage_ms = timers.mean_ms()
+    gemm_flops = sum(stage_flops(n, T, d, f, E, k) for n in GEMM_STAGES)
+    all_flops = gemm_flops + stage_flops("router_logits", T, d, f, E, k)
+    tokens_s = T / (ms / 1e3)
+    dom = max(GEMM_STAGES, key=lambda n: stage_ms[n])
+    dom_tflops = stage_flops(dom, T, d, f, E, k) / (stage_ms[dom] / 1e3) / 1e12
+    gemm_ms = sum(stage_ms[n] for n in GEMM_STAGES)
+    stages = {}
+    for n, v in stage_ms.items():
+        e = {"ms": round(v, 4)}
+        fl = stage_flops(n, T, d, f, E, k)
+        by = stage_bytes(n, T, d, f, E, k)
+        if fl:
+            e["tflops"] = round(fl / (v / 1e3) / 1e12, 1)
+        if by:
+            e["gbs"] = round(by / (v / 1e3) / 1e9, 1)
+        stages[n] = e
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} fwd+bwd", "T": T, "d": d, "f": f,
+                   "E": E, "k": k, "renorm": wl.renorm,
+                   "router_bias": wl.router_bias},
+        "tflops": round(all_flops / (ms / 1e3) / 1e12, 1),
+        "pct_mfma_peak": round(100.0 * all_flops / (ms / 1e3) / 1e12
+                               / PEAK_BF16_TFLOPS, 2),
+        "gemm_tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(dom_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "stages": stages,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_tokens, T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -147,7 +147,8 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   S[r]   = w_perm[r] * silu(AB[r][:f]) * AB[r][f:]
  *   O[r]   = S[r] . w2[e]^T
  *   w_gu [E][2f][d], w2 [E][d][f]; ab_saved [T*k][2f] bf16 out,
- *   s_saved [T*k][f] bf16 out, out_perm [T*k][d] bf16 out.
+ *   s_saved [T*k][f] bf16 out, out_perm [T*k][d] fp32 out (kept in fp32
+ *   so that the combine rounds each output once).
  * prec == MOE_MXFP8: x_perm is E4M3 codes + scales along d (from
  *   moe_permute), w_gu/w2 are codes with scales along their last axis (from
  *   moe_mxfp8_quantize, axis 0); S is requantized along f inside the
@@ -176,7 +177,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   dW_gu[e] = dAB_e^T . x_perm_e
  *   dx_perm  = dAB . w_gu[e]
  *   dout_perm [T*k][d] bf16, x_perm [T*k][d] bf16, ab_saved, s_saved as
- *   written by the forward; dx_perm [T*k][d], dw_gu [E][2f][d],
+ *   written by the forward; dx_perm [T*k][d] fp32 out; dw_gu [E][2f][d],
  *   dw2 [E][d][f] bf16 out; dp [T][k] fp32 out (needs pos).
  * prec == MOE_MXFP8: the same operands are quantized inside the call along
  *   each GEMM's reduction axis (d, 2f, or rows of an expert, restarting at
@@ -195,16 +196,71 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                hipStream_t stream);
 
 /*
+ * Stage entry points: the single grouped GEMMs that moe_grouped_mlp_fwd and
+ * moe_grouped_mlp_bwd are made of ([P1] Challenge 1: GroupedLinear as one
+ * grouped submission per projection; Challenge 3: ScaledSwiGLU fused into
+ * the gate_up projection and a matching backward).  Each launches exactly
+ * one kernel, so callers can time, overlap or reorder the pieces.  Shapes
+ * and dtypes are those of the fused entry points.
+ *
+ * moe_gate_up_swiglu_fwd: ab_saved = x_perm . w_gu[e]^T (bf16) and
+ *   s_saved = w_perm * silu(gate) * up (bf16).
+ * moe_down_fwd: out_perm = s_saved . w2[e]^T (fp32).
+ * moe_down_swiglu_bwd: dS = dout_perm . w2[e]; writes dab [T*k][2f] bf16
+ *   (dA_g, dA_u as in moe_grouped_mlp_bwd) and dp_part [T*k][ntiles] fp32,
+ *   the per-tile sums of dS * H, ntiles = moe_dp_tiles(f).
+ * moe_gate_up_dgrad: dx_perm = dab . w_gu[e] (fp32).
+ * moe_grouped_wgrad: for each expert e, c[e] (M x N, bf16) = sum over the
+ *   expert's rows r of a[r][m] * b[r][n]; a [T*k][lda], b [T*k][ldb]
+ *   row-major; experts without rows get exact zeros.  (dW2: a = dout_perm,
+ *   b = s_saved, M = d, N = f; dW_gu: a = dab, b = x_perm, M = 2f, N = d.)
+ * moe_dp_reduce: dp[t][j] = sum over tiles, in order, of
+ *   dp_part[pos[t][j]][tile].
+ */
+int32_t moe_dp_tiles(int64_t f);
+
+moe_status moe_gate_up_swiglu_fwd(const void* x_perm, const int32_t* offsets,
+                                  int32_t E, int64_t Tk, int64_t d, int64_t f,
+                                  const void* w_gu, const float* w_perm,
+                                  void* ab_saved, void* s_saved,
+                                  hipStream_t stream);
+
+moe_status moe_down_fwd(const void* s_saved, const int32_t* offsets,
+                        int32_t E, int64_t Tk, int64_t d, int64_t f,
+                        const void* w2, float* out_perm, hipStream_t stream);
+
+moe_status moe_down_swiglu_bwd(const void* dout_perm, const int32_t* offsets,
+                               int32_t E, int64_t Tk, int64_t d, int64_t f,
+                               const void* w2, const void* ab_saved,
+                               const float* w_perm, void* dab, float* dp_part,
+                               hipStream_t stream);
+
+moe_status moe_gate_up_dgrad(const void* dab, const int32_t* offsets,
+                             int32_t E, int64_t Tk, int64_t d, int64_t f,
+                             const void* w_gu, float* dx_perm,
+                             hipStream_t stream);
+
+moe_status moe_grouped_wgrad(const void* a, int64_t lda, const void* b,
+                             int64_t ldb, const int32_t* offsets, int32_t E,
+                             int64_t Tk, int64_t M, int64_t N, void* c,
+                             hipStream_t stream);
+
+moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
+                         const int32_t* pos, int64_t T, int32_t k, float* dp,
+                         hipStream_t stream);
+
+/*
  * moe_unpermute -- combine, [P1] Challenge 1 (the loop index-adds each
  * expert's rows back into the token's output).  Gather form, no atomics:
  *   y[t] = sum over j, in ascending expert id, of wt * o_perm[pos[t][j]]
  * with wt = w[t][j] (or 1 when w is NULL); fp32 accumulation, one final
- * rounding.  o_perm [T*k][d] bf16; y [T][d] bf16 (y_fp32 == 0) or fp32
- * (y_fp32 != 0).
+ * rounding.  o_perm [T*k][d] bf16 (o_fp32 == 0) or fp32 (o_fp32 != 0);
+ * y [T][d] bf16 (y_fp32 == 0) or fp32 (y_fp32 != 0).
  */
-moe_status moe_unpermute(const void* o_perm, const int32_t* pos,
-                         const float* w, int64_t T, int32_t k, int64_t d,
-                         int32_t y_fp32, void* y, hipStream_t stream);
+moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
+                         const int32_t* pos, const float* w, int64_t T,
+                         int32_t k, int64_t d, int32_t y_fp32, void* y,
+                         hipStream_t stream);
 
 /*
  * moe_mxfp8_quantize -- MX block quantization, [P1] Challenge 2 (8-bit

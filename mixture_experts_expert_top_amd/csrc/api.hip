@@ -85,6 +85,19 @@ moe_status check_feature(const char* name, int64_t v, moe_prec prec) {
   return MOE_OK;
 }
 
+moe_status check_mlp_dims(int32_t E, int64_t Tk, int64_t d, int64_t f,
+                          moe_prec prec) {
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  if (moe_status st = check_feature("f", f, prec)) return st;
+  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
+              2 * f * d * 2 <= kMaxBytes,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  return MOE_OK;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct BwdWorkspace {
@@ -264,7 +277,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
   if (moe_status st = check_feature("d", d, prec)) return st;
   if (moe_status st = check_feature("f", f, prec)) return st;
-  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 2 <= kMaxBytes &&
+  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
   hipError_t e = moe::gemm_fc1_fwd(
@@ -274,7 +287,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_fwd/fc1");
   e = moe::gemm_fc2_fwd(static_cast<const bf16_t*>(s_saved),
                         static_cast<const bf16_t*>(w2), offsets, E, Tk, d, f,
-                        static_cast<bf16_t*>(out_perm), stream);
+                        static_cast<float*>(out_perm), stream);
   return hip_status(e, "moe_grouped_mlp_fwd/fc2");
 }
 
@@ -308,7 +321,7 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   if (moe_status st = check_feature("d", d, prec)) return st;
   if (moe_status st = check_feature("f", f, prec)) return st;
   const int64_t Tk = T * k;
-  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 2 <= kMaxBytes &&
+  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
   const BwdWorkspace L = bwd_layout(Tk, f);
@@ -331,16 +344,17 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                       E, Tk, d, f, static_cast<bf16_t*>(dw2), stream);
   if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/dw2");
   e = moe::gemm_fc1_dgrad(dab, static_cast<const bf16_t*>(w_gu), offsets, E,
-                          Tk, d, f, static_cast<bf16_t*>(dx_perm), stream);
+                          Tk, d, f, static_cast<float*>(dx_perm), stream);
   if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/fc1_dgrad");
   e = moe::gemm_wgrad(dab, 2 * f, xp, d, offsets, E, Tk, 2 * f, d,
                       static_cast<bf16_t*>(dw_gu), stream);
   return hip_status(e, "moe_grouped_mlp_bwd/dw_gu");
 }
 
-moe_status moe_unpermute(const void* o_perm, const int32_t* pos,
-                         const float* w, int64_t T, int32_t k, int64_t d,
-                         int32_t y_fp32, void* y, hipStream_t stream) {
+moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
+                         const int32_t* pos, const float* w, int64_t T,
+                         int32_t k, int64_t d, int32_t y_fp32, void* y,
+                         hipStream_t stream) {
   REQUIRE_PTR(o_perm);
   REQUIRE_PTR(pos);
   REQUIRE_OPT_PTR(w);
@@ -349,10 +363,123 @@ moe_status moe_unpermute(const void* o_perm, const int32_t* pos,
   REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
           "k must be in [1, %d]", moe::kMaxTopK);
   if (moe_status st = check_feature("d", d, MOE_BF16)) return st;
-  return hip_status(moe::launch_unpermute(static_cast<const bf16_t*>(o_perm),
-                                          pos, w, T, k, d, y_fp32 ? 1 : 0, y,
-                                          stream),
+  return hip_status(moe::launch_unpermute(o_perm, o_fp32 ? 1 : 0, pos, w, T,
+                                          k, d, y_fp32 ? 1 : 0, y, stream),
                     "moe_unpermute");
+}
+
+int32_t moe_dp_tiles(int64_t f) {
+  return f >= 1 ? moe::gemm_dp_tiles(f) : 0;
+}
+
+moe_status moe_gate_up_swiglu_fwd(const void* x_perm, const int32_t* offsets,
+                                  int32_t E, int64_t Tk, int64_t d, int64_t f,
+                                  const void* w_gu, const float* w_perm,
+                                  void* ab_saved, void* s_saved,
+                                  hipStream_t stream) {
+  REQUIRE_PTR(x_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w_gu);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(ab_saved);
+  REQUIRE_PTR(s_saved);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_BF16)) return st;
+  return hip_status(
+      moe::gemm_fc1_fwd(static_cast<const bf16_t*>(x_perm),
+                        static_cast<const bf16_t*>(w_gu), offsets, E, Tk, d, f,
+                        w_perm, static_cast<bf16_t*>(ab_saved),
+                        static_cast<bf16_t*>(s_saved), stream),
+      "moe_gate_up_swiglu_fwd");
+}
+
+moe_status moe_down_fwd(const void* s_saved, const int32_t* offsets,
+                        int32_t E, int64_t Tk, int64_t d, int64_t f,
+                        const void* w2, float* out_perm, hipStream_t stream) {
+  REQUIRE_PTR(s_saved);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(out_perm);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_BF16)) return st;
+  return hip_status(
+      moe::gemm_fc2_fwd(static_cast<const bf16_t*>(s_saved),
+                        static_cast<const bf16_t*>(w2), offsets, E, Tk, d, f,
+                        out_perm, stream),
+      "moe_down_fwd");
+}
+
+moe_status moe_down_swiglu_bwd(const void* dout_perm, const int32_t* offsets,
+                               int32_t E, int64_t Tk, int64_t d, int64_t f,
+                               const void* w2, const void* ab_saved,
+                               const float* w_perm, void* dab, float* dp_part,
+                               hipStream_t stream) {
+  REQUIRE_PTR(dout_perm);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(ab_saved);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(dab);
+  REQUIRE_PTR(dp_part);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_BF16)) return st;
+  return hip_status(
+      moe::gemm_fc2_dgrad(static_cast<const bf16_t*>(dout_perm),
+                          static_cast<const bf16_t*>(w2), offsets, E, Tk, d, f,
+                          static_cast<const bf16_t*>(ab_saved), w_perm,
+                          static_cast<bf16_t*>(dab), dp_part, stream),
+      "moe_down_swiglu_bwd");
+}
+
+moe_status moe_gate_up_dgrad(const void* dab, const int32_t* offsets,
+                             int32_t E, int64_t Tk, int64_t d, int64_t f,
+                             const void* w_gu, float* dx_perm,
+                             hipStream_t stream) {
+  REQUIRE_PTR(dab);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w_gu);
+  REQUIRE_PTR(dx_perm);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_BF16)) return st;
+  return hip_status(
+      moe::gemm_fc1_dgrad(static_cast<const bf16_t*>(dab),
+                          static_cast<const bf16_t*>(w_gu), offsets, E, Tk, d,
+                          f, dx_perm, stream),
+      "moe_gate_up_dgrad");
+}
+
+moe_status moe_grouped_wgrad(const void* a, int64_t lda, const void* b,
+                             int64_t ldb, const int32_t* offsets, int32_t E,
+                             int64_t Tk, int64_t M, int64_t N, void* c,
+                             hipStream_t stream) {
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(b);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(c);
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
+  if (moe_status st = check_feature("M", M, MOE_BF16)) return st;
+  if (moe_status st = check_feature("N", N, MOE_BF16)) return st;
+  REQUIRE(lda >= M && lda % 8 == 0 && ldb >= N && ldb % 8 == 0,
+          MOE_ERR_INVALID_ARG, "need lda >= M, ldb >= N, both multiples of 8");
+  REQUIRE(Tk * lda * 2 <= kMaxBytes && Tk * ldb * 2 <= kMaxBytes &&
+              M * N * 2 * static_cast<int64_t>(E) <= kMaxBytes * 8,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  return hip_status(
+      moe::gemm_wgrad(static_cast<const bf16_t*>(a), lda,
+                      static_cast<const bf16_t*>(b), ldb, offsets, E, Tk, M, N,
+                      static_cast<bf16_t*>(c), stream),
+      "moe_grouped_wgrad");
+}
+
+moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
+                         const int32_t* pos, int64_t T, int32_t k, float* dp,
+                         hipStream_t stream) {
+  REQUIRE_PTR(dp_part);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(dp);
+  REQUIRE(T >= 1 && k >= 1 && ntiles >= 1, MOE_ERR_INVALID_ARG,
+          "T, k and ntiles must be >= 1");
+  return hip_status(moe::launch_dp_reduce(dp_part, ntiles, pos, T, k, dp,
+                                          stream),
+                    "moe_dp_reduce");
 }
 
 int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg) {

@@ -20,6 +20,7 @@
 // with the routing probabilities as the SwiGLU scales, plus a matching
 // fused backward):
 //   kStore   : C = bf16(acc)
+//   kStoreF32: C = acc (fp32; rows later summed by the combine)
 //   kSwiglu  : dual-B tile (gate and up columns of the same index in one
 //              workgroup); stores AB (bf16) and S = w * silu(gate) * up
 //   kDSwiglu : acc = dS; reads AB and w, writes dAB = (dA_g, dA_u) and
@@ -48,7 +49,7 @@ constexpr int kEpiLd = 132;               // fp32 row stride of the epilogue sta
 constexpr int kSmemBytes = 4 * 64 * kEpiLd * 4;  // >= the two operand stages
 
 enum Mode { kSegM = 0, kSegK = 1 };
-enum Epi { kStore = 0, kSwiglu = 1, kDSwiglu = 2 };
+enum Epi { kStore = 0, kSwiglu = 1, kDSwiglu = 2, kStoreF32 = 3 };
 
 struct Params {
   const bf16_t* A;
@@ -56,7 +57,8 @@ struct Params {
   const bf16_t* B;
   int64_t ldb;
   int64_t b_stride;  // elements between experts' B
-  bf16_t* C;
+  bf16_t* C;         // bf16 output (kStore, kSwiglu, kDSwiglu)
+  float* Cf;         // fp32 output (kStoreF32)
   int64_t ldc;
   int64_t c_stride;  // SegK: elements between experts' C
   const int32_t* offsets;
@@ -341,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params P) {
   float* stage = reinterpret_cast<float*>(smem) + wave * (64 * kEpiLd);
   const int64_t cbase = (MODE == kSegM) ? seg0 * P.ldc
                                         : static_cast<int64_t>(e) * P.c_stride;
-  const float* w = (EPI != kStore && P.w) ? P.w + seg0 : nullptr;
+  const float* w = ((EPI == kSwiglu || EPI == kDSwiglu) && P.w) ? P.w + seg0
+                                                                : nullptr;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -368,6 +371,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params P) {
           o.y = pack_bf16x2(x[2], x[3]);
           *reinterpret_cast<uint2*>(P.C + cbase + static_cast<int64_t>(row) * P.ldc + col) = o;
         }
+      }
+    } else if (EPI == kStoreF32) {
+      const int c4 = (lane & 31) * 4;
+      const int col = n0 + wn * 128 + c4;
+      for (int r = lane >> 5; r < 64; r += 2) {
+        const int row = row_base + r;
+        if (row < Mvalid && col < P.N)
+          *reinterpret_cast<f32x4*>(P.Cf + cbase + static_cast<int64_t>(row) * P.ldc + col) =
+              *reinterpret_cast<const f32x4*>(stage + r * kEpiLd + c4);
       }
     } else if (EPI == kSwiglu) {
       // stage columns [0,64) are gate, [64,128) the matching up columns
@@ -480,18 +492,18 @@ hipError_t gemm_fc1_fwd(const bf16_t* xp, const bf16_t* w_gu,
   return launch<kSegM, true, true, kSwiglu>(P, segm_grid(Tk, E, P.ntn), st);
 }
 
-// fc2 forward: O = S . W2^T
+// fc2 forward: O = S . W2^T (fp32 rows)
 hipError_t gemm_fc2_fwd(const bf16_t* s, const bf16_t* w2,
                         const int32_t* offsets, int E, int64_t Tk, int64_t d,
-                        int64_t f, bf16_t* o, hipStream_t st) {
+                        int64_t f, float* o, hipStream_t st) {
   Params P{};
   P.A = s; P.lda = f;
   P.B = w2; P.ldb = f; P.b_stride = d * f; P.b_rows = d;
-  P.C = o; P.ldc = d;
+  P.Cf = o; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = f; P.f = f;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
-  return launch<kSegM, true, true, kStore>(P, segm_grid(Tk, E, P.ntn), st);
+  return launch<kSegM, true, true, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }
 
 // fc2 dgrad + dSwiGLU: dS = dO . W2 (W2 is [d][f]: MN-contiguous B)
@@ -511,18 +523,18 @@ hipError_t gemm_fc2_dgrad(const bf16_t* dO, const bf16_t* w2,
   return launch<kSegM, true, false, kDSwiglu>(P, segm_grid(Tk, E, P.ntn), st);
 }
 
-// fc1 dgrad: dXp = dAB . W_gu (W_gu is [2f][d]: MN-contiguous B)
+// fc1 dgrad: dXp = dAB . W_gu (W_gu is [2f][d]: MN-contiguous B), fp32 rows
 hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
                           const int32_t* offsets, int E, int64_t Tk,
-                          int64_t d, int64_t f, bf16_t* dxp, hipStream_t st) {
+                          int64_t d, int64_t f, float* dxp, hipStream_t st) {
   Params P{};
   P.A = dab; P.lda = 2 * f;
   P.B = w_gu; P.ldb = d; P.b_stride = 2 * f * d; P.b_rows = 2 * f;
-  P.C = dxp; P.ldc = d;
+  P.Cf = dxp; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = 2 * f; P.f = f;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
-  return launch<kSegM, true, false, kStore>(P, segm_grid(Tk, E, P.ntn), st);
+  return launch<kSegM, true, false, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }
 
 // wgrad: C[e] (M x N) = sum over the expert's rows r of A[r][m] * B[r][n]

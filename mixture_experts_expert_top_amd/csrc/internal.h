@@ -37,7 +37,7 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
                                const void* x, int64_t row_bytes, void* x_perm,
                                const void* side, int64_t side_bytes,
                                void* side_perm, hipStream_t s);
-hipError_t launch_unpermute(const bf16_t* o, const int32_t* pos,
+hipError_t launch_unpermute(const void* o, int o_fp32, const int32_t* pos,
                             const float* w, int64_t T, int k, int64_t d,
                             int y_fp32, void* y, hipStream_t s);
 hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
@@ -51,7 +51,7 @@ hipError_t gemm_fc1_fwd(const bf16_t* xp, const bf16_t* w_gu,
                         hipStream_t st);
 hipError_t gemm_fc2_fwd(const bf16_t* s, const bf16_t* w2,
                         const int32_t* offsets, int E, int64_t Tk, int64_t d,
-                        int64_t f, bf16_t* o, hipStream_t st);
+                        int64_t f, float* o, hipStream_t st);
 hipError_t gemm_fc2_dgrad(const bf16_t* dO, const bf16_t* w2,
                           const int32_t* offsets, int E, int64_t Tk,
                           int64_t d, int64_t f, const bf16_t* ab,
@@ -59,7 +59,7 @@ hipError_t gemm_fc2_dgrad(const bf16_t* dO, const bf16_t* w2,
                           hipStream_t st);
 hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
                           const int32_t* offsets, int E, int64_t Tk,
-                          int64_t d, int64_t f, bf16_t* dxp, hipStream_t st);
+                          int64_t d, int64_t f, float* dxp, hipStream_t st);
 hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
                       int64_t ldb, const int32_t* offsets, int E, int64_t Tk,
                       int64_t M, int64_t N, bf16_t* c, hipStream_t st);

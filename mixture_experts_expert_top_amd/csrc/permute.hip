@@ -169,9 +169,30 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
 // ---------------------------------------------------------------- combine
 // y[t] = sum_j wt_j * O[pos[t][j]] with the slots taken in ascending
 // permuted row (= ascending expert id).  One workgroup per token; a thread
-// owns 8 consecutive columns.
+// owns 8 consecutive columns.  O rows are bf16 or fp32 (OF32).
+template <bool OF32>
+__device__ __forceinline__ void load8(const void* o, int64_t row, int64_t d,
+                                      int64_t q, float* v) {
+  if (OF32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(
+                         static_cast<const float*>(o) + row * d) + 2 * q;
+    const f32x4 a = p[0], b = p[1];
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const i32x4 x = reinterpret_cast<const i32x4*>(
+        static_cast<const bf16_t*>(o) + row * d)[q];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[2 * c] = bf_lo(static_cast<uint32_t>(x[c]));
+      v[2 * c + 1] = bf_hi(static_cast<uint32_t>(x[c]));
+    }
+  }
+}
+
+template <bool OF32>
 __global__ __launch_bounds__(256) void unpermute_kernel(
-    const bf16_t* __restrict__ o, const int32_t* __restrict__ pos,
+    const void* __restrict__ o, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int k, int64_t d, int y_fp32,
     void* __restrict__ y) {
   __shared__ int s_pos[kMaxTopK];
@@ -180,8 +201,8 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
   if (threadIdx.x == 0) {
     // insertion sort of the token's k rows (k <= 32)
     for (int j = 0; j < k; ++j) {
-      int p = pos[t * k + j];
-      float wj = w ? w[t * k + j] : 1.0f;
+      const int p = pos[t * k + j];
+      const float wj = w ? w[t * k + j] : 1.0f;
       int i = j;
       while (i > 0 && s_pos[i - 1] > p) {
         s_pos[i] = s_pos[i - 1];
@@ -197,19 +218,15 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
   for (int64_t q = threadIdx.x; q < n8; q += blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
-      const i32x4 v = reinterpret_cast<const i32x4*>(
-          o + static_cast<int64_t>(s_pos[j]) * d)[q];
-      const float wj = s_w[j];
+      float v[8];
+      load8<OF32>(o, s_pos[j], d, q, v);
+      if (w) {
+        const float wj = s_w[j];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t u = static_cast<uint32_t>(v[c]);
-        if (w) {
-          acc[2 * c] += wj * bf_lo(u);
-          acc[2 * c + 1] += wj * bf_hi(u);
-        } else {
-          acc[2 * c] += bf_lo(u);
-          acc[2 * c + 1] += bf_hi(u);
-        }
+        for (int c = 0; c < 8; ++c) acc[c] += wj * v[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += v[c];
       }
     }
     if (y_fp32) {
@@ -288,11 +305,15 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
   return hipGetLastError();
 }
 
-hipError_t launch_unpermute(const bf16_t* o, const int32_t* pos,
+hipError_t launch_unpermute(const void* o, int o_fp32, const int32_t* pos,
                             const float* w, int64_t T, int k, int64_t d,
                             int y_fp32, void* y, hipStream_t s) {
-  hipLaunchKernelGGL(unpermute_kernel, dim3(static_cast<unsigned>(T)),
-                     dim3(256), 0, s, o, pos, w, k, d, y_fp32, y);
+  if (o_fp32)
+    hipLaunchKernelGGL(unpermute_kernel<true>, dim3(static_cast<unsigned>(T)),
+                       dim3(256), 0, s, o, pos, w, k, d, y_fp32, y);
+  else
+    hipLaunchKernelGGL(unpermute_kernel<false>, dim3(static_cast<unsigned>(T)),
+                       dim3(256), 0, s, o, pos, w, k, d, y_fp32, y);
   return hipGetLastError();
 }
 

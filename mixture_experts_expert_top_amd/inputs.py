@@ -130,3 +130,11 @@ def make_tied_logits(T, E, seed=0, levels=3, device="cpu"):
     vals = torch.where((vals == 0) & (sign == 1),
                        torch.full_like(vals, -0.0), vals)
     return vals
+
+
+def make_tensor(shape, seed, scale=1.0, dtype=torch.bfloat16, device="cpu"):
+    """N(0, scale^2) values of the given shape, rounded to dtype."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    return (t * scale).to(dtype)

@@ -7,13 +7,48 @@ with torch, reused every step) and issues the library calls in order:
             -> moe_grouped_mlp_fwd -> moe_unpermute
   backward: moe_permute_rows (dY) -> moe_grouped_mlp_bwd -> moe_unpermute
 
+With a ``timers`` object (see ``StageTimers``) the GEMMs are issued
+through the per-GEMM stage entry points instead of the fused ones, with
+HIP events recorded around each stage on the stream it runs on.
+
 No arithmetic happens here: every step runs in the library's kernels.
 """
+
+import contextlib
 
 import torch
 
 from . import moe
 from .moe import MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_PERMUTE
+
+
+class StageTimers:
+    """Pairs of HIP events recorded around named stages on the current
+    stream; ``mean_ms()`` gives each stage's average duration."""
+
+    def __init__(self):
+        self.events = {}
+
+    @contextlib.contextmanager
+    def around(self, name):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.events.setdefault(name, []).append((a, b))
+
+    def mean_ms(self):
+        return {n: sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+                for n, ev in self.events.items()}
+
+    def counts(self):
+        return {n: len(ev) for n, ev in self.events.items()}
+
+
+def _around(timers, name):
+    return timers.around(name) if timers is not None else \
+        contextlib.nullcontext()
 
 
 class MoEPath:
@@ -39,7 +74,7 @@ class MoEPath:
         self.x_perm = z(Tk, d, dt=bf)
         self.ab = z(Tk, 2 * f, dt=bf)
         self.s = z(Tk, f, dt=bf)
-        self.o = z(Tk, d, dt=bf)
+        self.o = z(Tk, d, dt=f32)
         self.y = z(T, d, dt=f32 if y_fp32 else bf)
         ws_p = moe.moe_workspace_bytes(MOE_ENTRY_PERMUTE, prec, T, E, k, d, f)
         self.ws_permute = z(max(ws_p, 16), dt=torch.uint8)
@@ -51,11 +86,14 @@ class MoEPath:
         dev = self.x_perm.device
         bf = torch.bfloat16
         self.dout_perm = torch.empty(Tk, d, dtype=bf, device=dev)
-        self.dx_perm = torch.empty(Tk, d, dtype=bf, device=dev)
+        self.dx_perm = torch.empty(Tk, d, dtype=torch.float32, device=dev)
         self.dw_gu = torch.empty(E, 2 * f, d, dtype=bf, device=dev)
         self.dw2 = torch.empty(E, d, f, dtype=bf, device=dev)
         self.dp = torch.empty(T, k, dtype=torch.float32, device=dev)
         self.dx = torch.empty(T, d, dtype=bf, device=dev)
+        self.dab = torch.empty(Tk, 2 * f, dtype=bf, device=dev)
+        self.dp_part = torch.empty(Tk, moe.moe_dp_tiles(f),
+                                   dtype=torch.float32, device=dev)
         ws_b = moe.moe_workspace_bytes(MOE_ENTRY_MLP_BWD, self.prec, T, E, k,
                                        d, f)
         self.ws_bwd = torch.empty(max(ws_b, 16), dtype=torch.uint8,
@@ -63,31 +101,66 @@ class MoEPath:
         self._bwd_ready = True
 
     # ------------------------------------------------------------------
-    def route(self, x=None, w_g=None, bias=None, logits=None):
+    def route(self, x=None, w_g=None, bias=None, logits=None, timers=None):
         if logits is None:
-            moe.moe_router_logits(x, w_g, bias, self.logits)
+            with _around(timers, "router_logits"):
+                moe.moe_router_logits(x, w_g, bias, self.logits)
             logits = self.logits
-        moe.moe_route(logits, self.k, self.renorm, self.topk_idx, self.topk_w)
+        with _around(timers, "route"):
+            moe.moe_route(logits, self.k, self.renorm, self.topk_idx,
+                          self.topk_w)
 
-    def forward(self, x, w_gu, w2, w_g=None, bias=None, logits=None):
-        self.route(x, w_g, bias, logits)
-        moe.moe_permute(self.prec, self.topk_idx, self.topk_w, self.E, x,
-                        None, self.counts, self.offsets, self.pos, self.src,
-                        self.w_perm, self.x_perm, None, self.ws_permute)
-        moe.moe_grouped_mlp_fwd(self.prec, self.x_perm, None, self.offsets,
-                                w_gu, None, w2, None, self.w_perm, self.ab,
-                                self.s, self.o)
-        moe.moe_unpermute(self.o, self.pos, None, self.y)
+    def forward(self, x, w_gu, w2, w_g=None, bias=None, logits=None,
+                timers=None):
+        self.route(x, w_g, bias, logits, timers)
+        with _around(timers, "permute"):
+            moe.moe_permute(self.prec, self.topk_idx, self.topk_w, self.E, x,
+                            None, self.counts, self.offsets, self.pos,
+                            self.src, self.w_perm, self.x_perm, None,
+                            self.ws_permute)
+        if timers is None:
+            moe.moe_grouped_mlp_fwd(self.prec, self.x_perm, None,
+                                    self.offsets, w_gu, None, w2, None,
+                                    self.w_perm, self.ab, self.s, self.o)
+        else:
+            with timers.around("gate_up_swiglu_fwd"):
+                moe.moe_gate_up_swiglu_fwd(self.x_perm, self.offsets, w_gu,
+                                           self.w_perm, self.ab, self.s)
+            with timers.around("down_fwd"):
+                moe.moe_down_fwd(self.s, self.offsets, w2, self.o)
+        with _around(timers, "unpermute_y"):
+            moe.moe_unpermute(self.o, self.pos, None, self.y)
         return self.y
 
-    def backward(self, dy, w_gu, w2):
+    def backward(self, dy, w_gu, w2, timers=None):
         if not self._bwd_ready:
             self._alloc_bwd()
-        moe.moe_permute_rows(self.prec, self.pos, dy, None, self.dout_perm,
-                             None)
-        moe.moe_grouped_mlp_bwd(self.prec, self.dout_perm, self.x_perm,
-                                self.offsets, self.pos, w_gu, w2, self.ab,
-                                self.s, self.w_perm, self.dx_perm, self.dw_gu,
-                                self.dw2, self.dp, self.ws_bwd)
-        moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+        with _around(timers, "permute_dy"):
+            moe.moe_permute_rows(self.prec, self.pos, dy, None,
+                                 self.dout_perm, None)
+        if timers is None:
+            moe.moe_grouped_mlp_bwd(self.prec, self.dout_perm, self.x_perm,
+                                    self.offsets, self.pos, w_gu, w2, self.ab,
+                                    self.s, self.w_perm, self.dx_perm,
+                                    self.dw_gu, self.dw2, self.dp,
+                                    self.ws_bwd)
+        else:
+            # the same kernels in the same order as moe_grouped_mlp_bwd
+            with timers.around("down_swiglu_bwd"):
+                moe.moe_down_swiglu_bwd(self.dout_perm, self.offsets, w2,
+                                        self.ab, self.w_perm, self.dab,
+                                        self.dp_part)
+            with timers.around("dp_reduce"):
+                moe.moe_dp_reduce(self.dp_part, self.pos, self.dp)
+            with timers.around("wgrad_down"):
+                moe.moe_grouped_wgrad(self.dout_perm, self.s, self.offsets,
+                                      self.dw2)
+            with timers.around("gate_up_dgrad"):
+                moe.moe_gate_up_dgrad(self.dab, self.offsets, w_gu,
+                                      self.dx_perm)
+            with timers.around("wgrad_gate_up"):
+                moe.moe_grouped_wgrad(self.dab, self.x_perm, self.offsets,
+                                      self.dw_gu)
+        with _around(timers, "unpermute_dx"):
+            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
         return self.dx, self.dw_gu, self.dw2, self.dp

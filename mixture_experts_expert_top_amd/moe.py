@@ -25,7 +25,9 @@ EXPORTED = [
     "moe_status_str", "moe_last_error", "moe_version", "moe_router_logits",
     "moe_route", "moe_permute", "moe_permute_rows", "moe_grouped_mlp_fwd",
     "moe_grouped_mlp_bwd", "moe_unpermute", "moe_mxfp8_quantize",
-    "moe_mxfp8_padded_rows", "moe_workspace_bytes",
+    "moe_mxfp8_padded_rows", "moe_workspace_bytes", "moe_dp_tiles",
+    "moe_gate_up_swiglu_fwd", "moe_down_fwd", "moe_down_swiglu_bwd",
+    "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
 ]
 
 
@@ -57,10 +59,20 @@ def _load():
         "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
                                       I64, P, P, P, P, P, P, P, P, P, P, SZ,
                                       P]),
-        "moe_unpermute": (I32, [P, P, P, I64, I32, I64, I32, P, P]),
+        "moe_unpermute": (I32, [P, I32, P, P, I64, I32, I64, I32, P, P]),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
         "moe_mxfp8_padded_rows": (I64, [I64, I32]),
         "moe_workspace_bytes": (SZ, [I32, I32, I64, I32, I32, I64, I64]),
+        "moe_dp_tiles": (I32, [I64]),
+        "moe_gate_up_swiglu_fwd": (I32, [P, P, I32, I64, I64, I64, P, P, P,
+                                         P, P]),
+        "moe_down_fwd": (I32, [P, P, I32, I64, I64, I64, P, P, P]),
+        "moe_down_swiglu_bwd": (I32, [P, P, I32, I64, I64, I64, P, P, P, P,
+                                      P, P]),
+        "moe_gate_up_dgrad": (I32, [P, P, I32, I64, I64, I64, P, P, P]),
+        "moe_grouped_wgrad": (I32, [P, I64, P, I64, P, I32, I64, I64, I64, P,
+                                    P]),
+        "moe_dp_reduce": (I32, [P, I32, P, I64, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,7 +196,7 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
     _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
-    _want(out_perm, "out_perm", torch.bfloat16, (Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (Tk, d))
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
     _check("moe_grouped_mlp_fwd", lib.moe_grouped_mlp_fwd(
@@ -206,9 +218,9 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                       ("w_gu", w_gu, (E, 2 * f, d)), ("w2", w2, (E, d, f)),
                       ("ab_saved", ab_saved, (Tk, 2 * f)),
                       ("s_saved", s_saved, (Tk, f)),
-                      ("dx_perm", dx_perm, (Tk, d)),
                       ("dw_gu", dw_gu, (E, 2 * f, d)), ("dw2", dw2, (E, d, f))):
         _want(t, n, torch.bfloat16, shp)
+    _want(dx_perm, "dx_perm", torch.float32, (Tk, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
     _want(pos, "pos", torch.int32)
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
@@ -225,14 +237,17 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
 def moe_unpermute(o_perm, pos, w, y, stream=None):
     T, k = pos.shape
     d = o_perm.shape[1]
-    _want(o_perm, "o_perm", torch.bfloat16, (T * k, d))
+    if o_perm.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("o_perm must be bfloat16 or float32")
+    _want(o_perm, "o_perm", o_perm.dtype, (T * k, d))
     _want(pos, "pos", torch.int32)
     _want(w, "w", torch.float32, (T, k), allow_none=True)
     if y.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("y must be bfloat16 or float32")
     _want(y, "y", y.dtype, (T, d))
     _check("moe_unpermute", lib.moe_unpermute(
-        _p(o_perm), _p(pos), _p(w), T, k, d,
+        _p(o_perm), 1 if o_perm.dtype == torch.float32 else 0, _p(pos),
+        _p(w), T, k, d,
         1 if y.dtype == torch.float32 else 0, _p(y), _stream(stream)))
 
 
@@ -252,3 +267,93 @@ def moe_mxfp8_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,
     _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(
         _p(src), rows, cols, axis, _p(seg_offsets), nseg, _p(codes),
         _p(scales), rows_pad, _stream(stream)))
+
+
+# ---------------------------------------------------------------- stages
+
+def moe_dp_tiles(f):
+    return int(lib.moe_dp_tiles(f))
+
+
+def _mlp_dims(x_perm, w_gu):
+    Tk, d = x_perm.shape
+    E, two_f, _ = w_gu.shape
+    return Tk, d, E, two_f // 2
+
+
+def moe_gate_up_swiglu_fwd(x_perm, offsets, w_gu, w_perm, ab_saved, s_saved,
+                           stream=None):
+    Tk, d, E, f = _mlp_dims(x_perm, w_gu)
+    _want(x_perm, "x_perm", torch.bfloat16)
+    _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
+    _check("moe_gate_up_swiglu_fwd", lib.moe_gate_up_swiglu_fwd(
+        _p(x_perm), _p(offsets), E, Tk, d, f, _p(w_gu), _p(w_perm),
+        _p(ab_saved), _p(s_saved), _stream(stream)))
+
+
+def moe_down_fwd(s_saved, offsets, w2, out_perm, stream=None):
+    Tk, f = s_saved.shape
+    E, d, _ = w2.shape
+    _want(s_saved, "s_saved", torch.bfloat16)
+    _want(w2, "w2", torch.bfloat16, (E, d, f))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(out_perm, "out_perm", torch.float32, (Tk, d))
+    _check("moe_down_fwd", lib.moe_down_fwd(
+        _p(s_saved), _p(offsets), E, Tk, d, f, _p(w2), _p(out_perm),
+        _stream(stream)))
+
+
+def moe_down_swiglu_bwd(dout_perm, offsets, w2, ab_saved, w_perm, dab,
+                        dp_part, stream=None):
+    Tk, d = dout_perm.shape
+    E, _, f = w2.shape
+    _want(dout_perm, "dout_perm", torch.bfloat16)
+    _want(w2, "w2", torch.bfloat16, (E, d, f))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(dab, "dab", torch.bfloat16, (Tk, 2 * f))
+    _want(dp_part, "dp_part", torch.float32, (Tk, moe_dp_tiles(f)))
+    _check("moe_down_swiglu_bwd", lib.moe_down_swiglu_bwd(
+        _p(dout_perm), _p(offsets), E, Tk, d, f, _p(w2), _p(ab_saved),
+        _p(w_perm), _p(dab), _p(dp_part), _stream(stream)))
+
+
+def moe_gate_up_dgrad(dab, offsets, w_gu, dx_perm, stream=None):
+    Tk, two_f = dab.shape
+    E, _, d = w_gu.shape
+    f = two_f // 2
+    _want(dab, "dab", torch.bfloat16)
+    _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(dx_perm, "dx_perm", torch.float32, (Tk, d))
+    _check("moe_gate_up_dgrad", lib.moe_gate_up_dgrad(
+        _p(dab), _p(offsets), E, Tk, d, f, _p(w_gu), _p(dx_perm),
+        _stream(stream)))
+
+
+def moe_grouped_wgrad(a, b, offsets, c, stream=None):
+    Tk, M = a.shape
+    _, N = b.shape
+    E = offsets.numel() - 1
+    _want(a, "a", torch.bfloat16)
+    _want(b, "b", torch.bfloat16, (Tk, N))
+    _want(offsets, "offsets", torch.int32)
+    _want(c, "c", torch.bfloat16, (E, M, N))
+    _check("moe_grouped_wgrad", lib.moe_grouped_wgrad(
+        _p(a), M, _p(b), N, _p(offsets), E, Tk, M, N, _p(c),
+        _stream(stream)))
+
+
+def moe_dp_reduce(dp_part, pos, dp, stream=None):
+    T, k = pos.shape
+    _want(dp_part, "dp_part", torch.float32)
+    _want(pos, "pos", torch.int32)
+    _want(dp, "dp", torch.float32, (T, k))
+    _check("moe_dp_reduce", lib.moe_dp_reduce(
+        _p(dp_part), dp_part.shape[1], _p(pos), T, k, _p(dp),
+        _stream(stream)))

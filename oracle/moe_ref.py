@@ -139,20 +139,94 @@ def sigmoid(a):
         return 1.0 / (1.0 + np.exp(-a))
 
 
-def expert_forward(xp_e, w_gu_e, w2_e, w_e):
+def bf16_round(v):
+    """Nearest bfloat16 value of v (ties to even), returned as float64.
+
+    "Efficient MoE Training for Biological Foundation Models", Challenge 2:
+    BF16 training represents every weight and activation with 16 bits.  With
+    ``bf16_act`` the functions below store the activations the path keeps
+    (gate/up pre-activations, the SwiGLU output S and its gradient dAB) in
+    that format at the points where they are stored."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    binade = np.maximum(ex - 1, -126)     # subnormals share the 2^-126 binade
+    spacing = np.ldexp(1.0, binade - 7)   # 7 stored mantissa bits
+    return np.copysign(np.rint(a / spacing) * spacing, v)
+
+
+def _keep(v, bf16_act):
+    return bf16_round(v) if bf16_act else v
+
+
+# One function per step of the expert MLP, each the plain definition.
+
+def gate_up(xp_e, w_gu_e):
+    """AB = Xp . W_gu^T: gate pre-activations in columns [0, f), up in
+    [f, 2f)."""
+    return np.asarray(xp_e, dtype=np.float64) @ \
+        np.asarray(w_gu_e, dtype=np.float64).T
+
+
+def scaled_swiglu(ab_e, w_e):
+    """S = w * silu(A_g) * A_u, one routing weight per row."""
+    ab_e = np.asarray(ab_e, dtype=np.float64)
+    f = ab_e.shape[1] // 2
+    return np.asarray(w_e, dtype=np.float64)[:, None] * \
+        (silu(ab_e[:, :f]) * ab_e[:, f:])
+
+
+def down(s_e, w2_e):
+    """O = S . W2^T."""
+    return np.asarray(s_e, dtype=np.float64) @ \
+        np.asarray(w2_e, dtype=np.float64).T
+
+
+def down_backward(do_e, ab_e, w_e, w2_e):
+    """Backward through down and the scaled SwiGLU for one expert's rows:
+    dS = dO . W2; dp = <dS, H> per row (H = silu(A_g) A_u); dH = w dS;
+    dA_g = dH A_u sig(A_g)(1 + A_g(1 - sig(A_g))); dA_u = dH silu(A_g).
+    Returns (dAB, dp)."""
+    do_e = np.asarray(do_e, dtype=np.float64)
+    ab_e = np.asarray(ab_e, dtype=np.float64)
+    f = ab_e.shape[1] // 2
+    a_g, a_u = ab_e[:, :f], ab_e[:, f:]
+    ds = do_e @ np.asarray(w2_e, dtype=np.float64)
+    h = silu(a_g) * a_u
+    dp = np.sum(ds * h, axis=1)
+    dh = np.asarray(w_e, dtype=np.float64)[:, None] * ds
+    sg = sigmoid(a_g)
+    dab = np.concatenate([dh * a_u * sg * (1.0 + a_g * (1.0 - sg)),
+                          dh * silu(a_g)], axis=1)
+    return dab, dp
+
+
+def gate_up_dgrad(dab_e, w_gu_e):
+    """dXp = dAB . W_gu."""
+    return np.asarray(dab_e, dtype=np.float64) @ \
+        np.asarray(w_gu_e, dtype=np.float64)
+
+
+def wgrad(a_e, b_e):
+    """Weight gradient over an expert's rows: sum_r a[r]^T b[r]."""
+    return np.asarray(a_e, dtype=np.float64).T @ \
+        np.asarray(b_e, dtype=np.float64)
+
+
+def expert_forward(xp_e, w_gu_e, w2_e, w_e, bf16_act=False):
     """One expert on its rows: returns (AB, S, O).
 
     AB = Xp_e . W_gu_e^T  (gate pre-activations first, then up)
     S  = w * silu(A_g) * A_u       (scaled SwiGLU, one weight per row)
     O  = S . W2_e^T
+    With bf16_act the returned AB (kept for the backward pass) and S (the
+    input of the down projection) are stored as bfloat16; S is formed from
+    the unrounded A_g, A_u.
     """
-    f = w_gu_e.shape[0] // 2
-    ab = xp_e @ w_gu_e.T
-    a_g, a_u = ab[:, :f], ab[:, f:]
-    h = silu(a_g) * a_u
-    s = np.asarray(w_e, dtype=np.float64)[:, None] * h
-    o = s @ w2_e.T
-    return ab, s, o
+    ab = gate_up(xp_e, w_gu_e)
+    s = _keep(scaled_swiglu(ab, w_e), bf16_act)
+    o = down(s, w2_e)
+    return _keep(ab, bf16_act), s, o
 
 
 def combine(o_perm, pos, idx):
@@ -167,7 +241,7 @@ def combine(o_perm, pos, idx):
     return y
 
 
-def experts_forward(x, idx, p, w_gu, w2):
+def experts_forward(x, idx, p, w_gu, w2, bf16_act=False):
     """The layer forward with routing given (idx, p).  Returns a dict with
     the plan, the permuted intermediates and the output y [T, d]."""
     x = np.asarray(x, dtype=np.float64)
@@ -188,37 +262,38 @@ def experts_forward(x, idx, p, w_gu, w2):
         if r1 == r0:
             continue
         ab[r0:r1], s[r0:r1], o[r0:r1] = expert_forward(
-            xp[r0:r1], w_gu[e], w2[e], w_perm[r0:r1])
+            xp[r0:r1], w_gu[e], w2[e], w_perm[r0:r1], bf16_act)
     y = combine(o, pos, idx)
     return dict(idx=np.asarray(idx), p=np.asarray(p, dtype=np.float64),
                 counts=counts, offsets=offsets, pos=pos, src=src,
                 xp=xp, w_perm=w_perm, ab=ab, s=s, o=o, y=y)
 
 
-def moe_forward(x, logits, w_gu, w2, k, renorm=True):
+def moe_forward(x, logits, w_gu, w2, k, renorm=True, bf16_act=False):
     """Route on the given scores, then run the experts and combine."""
     idx, p = topk_route(logits, k, renorm)
-    return experts_forward(x, idx, p, w_gu, w2)
+    return experts_forward(x, idx, p, w_gu, w2, bf16_act)
 
 
-def moe_backward(fwd, dy, w_gu, w2):
+def moe_backward(fwd, dy, w_gu, w2, bf16_act=False):
     """Backward of ``experts_forward`` for upstream gradient dy [T, d].
 
     Routing (idx) is held fixed; the gradient with respect to the routing
     weights is returned as dp [T, k].  Returns dict(dx, dw_gu, dw2, dp,
     dab, do) with dab/do in permuted row order.  Experts that received no
-    rows get exactly zero weight gradients.
+    rows get exactly zero weight gradients.  With bf16_act, fwd must come
+    from experts_forward(..., bf16_act=True) and dAB is stored as bfloat16
+    before it feeds the two GEMMs that consume it.
     """
     dy = np.asarray(dy, dtype=np.float64)
     w_gu = np.asarray(w_gu, dtype=np.float64)
     w2 = np.asarray(w2, dtype=np.float64)
     E, two_f, d = w_gu.shape
-    f = two_f // 2
     offsets, pos, src = fwd["offsets"], fwd["pos"], fwd["src"]
     ab, s, xp, w_perm = fwd["ab"], fwd["s"], fwd["xp"], fwd["w_perm"]
     Tk = xp.shape[0]
     do = dy[src]                                  # dO[r] = dY[src[r]]
-    dab = np.zeros((Tk, 2 * f))
+    dab = np.zeros((Tk, two_f))
     dxp = np.zeros((Tk, d))
     dw_gu = np.zeros_like(w_gu)
     dw2 = np.zeros_like(w2)
@@ -228,19 +303,12 @@ def moe_backward(fwd, dy, w_gu, w2):
         if r1 == r0:
             continue
         do_e = do[r0:r1]
-        a_g, a_u = ab[r0:r1, :f], ab[r0:r1, f:]
-        h = silu(a_g) * a_u
-        dw2[e] = do_e.T @ s[r0:r1]                # dW2 = dO^T S
-        ds = do_e @ w2[e]                         # dS = dO W2
-        dp_perm[r0:r1] = np.sum(ds * h, axis=1)   # d/dp of S = p H
-        dh = w_perm[r0:r1, None] * ds
-        sg = sigmoid(a_g)
-        da_g = dh * a_u * sg * (1.0 + a_g * (1.0 - sg))
-        da_u = dh * silu(a_g)
-        dab[r0:r1, :f] = da_g
-        dab[r0:r1, f:] = da_u
-        dw_gu[e] = dab[r0:r1].T @ xp[r0:r1]       # dW_gu = dAB^T Xp
-        dxp[r0:r1] = dab[r0:r1] @ w_gu[e]         # dXp = dAB W_gu
+        dw2[e] = wgrad(do_e, s[r0:r1])                       # dO^T S
+        dab_e, dp_perm[r0:r1] = down_backward(do_e, ab[r0:r1],
+                                              w_perm[r0:r1], w2[e])
+        dab[r0:r1] = _keep(dab_e, bf16_act)
+        dw_gu[e] = wgrad(dab[r0:r1], xp[r0:r1])              # dAB^T Xp
+        dxp[r0:r1] = gate_up_dgrad(dab[r0:r1], w_gu[e])      # dAB W_gu
     T, k = pos.shape
     dx = np.zeros((T, d))
     dp = np.zeros((T, k))
@@ -257,7 +325,7 @@ def moe_backward(fwd, dy, w_gu, w2):
 # evaluated for single outputs so that Mixtral-sized layers stay cheap.
 # --------------------------------------------------------------------------
 
-def token_forward(x_t, idx_t, p_t, w_gu, w2):
+def token_forward(x_t, idx_t, p_t, w_gu, w2, bf16_act=False):
     """y[t] for one token: sum over its chosen experts (ascending id) of
     p * (silu(x W1^T) * (x W3^T)) W2^T.  ``w_gu``/``w2`` may be any indexable
     stack of per-expert weights (each item converted to float64 here)."""
@@ -268,12 +336,12 @@ def token_forward(x_t, idx_t, p_t, w_gu, w2):
         wgu = np.asarray(w_gu[e], dtype=np.float64)
         w2e = np.asarray(w2[e], dtype=np.float64)
         _, _, o = expert_forward(x_t[None, :], wgu, w2e,
-                                 np.array([float(p_t[j])]))
+                                 np.array([float(p_t[j])]), bf16_act)
         y += o[0]
     return y
 
 
-def row_backward(x_t, dy_t, p_r, w_gu_e, w2_e):
+def row_backward(x_t, dy_t, p_r, w_gu_e, w2_e, bf16_act=False):
     """Backward of one permuted row (one token through one expert).
 
     Returns (dab_row [2f], dxp_row [d], dp_r scalar, ab_row, s_row).
@@ -282,21 +350,16 @@ def row_backward(x_t, dy_t, p_r, w_gu_e, w2_e):
     dy_t = np.asarray(dy_t, dtype=np.float64)
     w_gu_e = np.asarray(w_gu_e, dtype=np.float64)
     w2_e = np.asarray(w2_e, dtype=np.float64)
-    f = w_gu_e.shape[0] // 2
-    ab, s, _ = expert_forward(x_t[None, :], w_gu_e, w2_e, np.array([p_r]))
-    a_g, a_u = ab[0, :f], ab[0, f:]
-    h = silu(a_g) * a_u
-    ds = dy_t @ w2_e
-    dp_r = float(np.dot(ds, h))
-    dh = p_r * ds
-    sg = sigmoid(a_g)
-    dab = np.concatenate([dh * a_u * sg * (1.0 + a_g * (1.0 - sg)),
-                          dh * silu(a_g)])
-    dxp = dab @ w_gu_e
+    ab, s, _ = expert_forward(x_t[None, :], w_gu_e, w2_e, np.array([p_r]),
+                              bf16_act)
+    dab, dp = down_backward(dy_t[None, :], ab, np.array([p_r]), w2_e)
+    dab = _keep(dab[0], bf16_act)
+    dp_r = float(dp[0])
+    dxp = gate_up_dgrad(dab[None, :], w_gu_e)[0]
     return dab, dxp, dp_r, ab[0], s[0]
 
 
-def dw2_column(xp_e, do_e, w_e, w_gu_e, j):
+def dw2_column(xp_e, do_e, w_e, w_gu_e, j, bf16_act=False):
     """Column j of dW2_e = sum over the expert's rows of dO[r] * S[r, j],
     with S[r, j] = w_r * silu(Xp[r] . W1[j]) * (Xp[r] . W3[j]).
     xp_e [n, d], do_e [n, d], w_e [n], w_gu_e [2f, d]."""
@@ -305,11 +368,11 @@ def dw2_column(xp_e, do_e, w_e, w_gu_e, j):
     f = w_gu_e.shape[0] // 2
     g = xp_e @ np.asarray(w_gu_e[j], dtype=np.float64)
     u = xp_e @ np.asarray(w_gu_e[f + j], dtype=np.float64)
-    s = np.asarray(w_e, dtype=np.float64) * silu(g) * u
+    s = _keep(np.asarray(w_e, dtype=np.float64) * silu(g) * u, bf16_act)
     return do_e.T @ s
 
 
-def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i):
+def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i, bf16_act=False):
     """Row i (of 2f) of dW_gu_e = sum over the expert's rows of
     dAB[r, i] * Xp[r]; dAB[:, i] needs only column i mod f of dS, gate and
     up.  xp_e, do_e [n, d]; w_e [n]; w_gu_e [2f, d]; w2_e [d, f]."""
@@ -317,8 +380,8 @@ def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i):
     do_e = np.asarray(do_e, dtype=np.float64)
     f = w_gu_e.shape[0] // 2
     c = i % f
-    g = xp_e @ np.asarray(w_gu_e[c], dtype=np.float64)
-    u = xp_e @ np.asarray(w_gu_e[f + c], dtype=np.float64)
+    g = _keep(xp_e @ np.asarray(w_gu_e[c], dtype=np.float64), bf16_act)
+    u = _keep(xp_e @ np.asarray(w_gu_e[f + c], dtype=np.float64), bf16_act)
     ds = do_e @ np.asarray(w2_e[:, c], dtype=np.float64)
     dh = np.asarray(w_e, dtype=np.float64) * ds
     if i < f:
@@ -326,4 +389,4 @@ def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i):
         col = dh * u * sg * (1.0 + g * (1.0 - sg))
     else:
         col = dh * silu(g)
-    return col @ xp_e
+    return _keep(col, bf16_act) @ xp_e

@@ -117,9 +117,9 @@ def test_mlp_bwd_validation():
 
 
 def test_unpermute_validation():
-    assert L.moe_unpermute(A, A, None, 8, 0, 64, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, A, None, 8, 2, 60, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, None, None, 8, 2, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 0, A, None, 8, 0, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 1, A, None, 8, 2, 60, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 0, None, None, 8, 2, 64, 0, A, None) == INVALID
 
 
 def test_padded_rows():

@@ -362,3 +362,71 @@ def test_sampled_weight_grads_match_full_layer():
             np.testing.assert_allclose(
                 R.dw_gu_row(xp_e, do_e, w_e, a["w_gu"][e], a["w2"][e], i),
                 bwd["dw_gu"][e][i], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- bf16 mode
+
+def test_bf16_round_matches_torch_on_float32_values():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([
+        rng.standard_normal(200000) * 2.0 ** rng.integers(-60, 60, 200000),
+        [0.0, -0.0, 1.0, 1.00390625, 1.01171875, 2.0 ** -126, 2.0 ** -130,
+         -3.0e38, 1.0e-40]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    got = R.bf16_round(v.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_bf16_round_is_nearest_for_float64_values():
+    """Brute force: the nearest of the bfloat16 neighbours of v (found by
+    stepping the bit pattern), ties to the even pattern."""
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(20000) * 2.0 ** rng.integers(-20, 20, 20000)
+    v[:100] = (np.arange(100) + 0.5) * 2.0 ** -7 + 1.0     # exact ties
+    got = R.bf16_round(v)
+    base = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    bits = base.view(torch.int16).numpy().astype(np.int32)
+    for i in range(v.size):
+        cands = []
+        for db in (-1, 0, 1):
+            b = np.array([bits[i] + db], dtype=np.int32).astype(np.int16)
+            c = torch.from_numpy(b).view(torch.bfloat16).double().item()
+            cands.append((abs(c - v[i]), (bits[i] + db) & 1, c))
+        best = min(cands)[0]
+        tied = [c for c in cands if c[0] == best]
+        want = min(tied, key=lambda c: c[1])[2]
+        assert got[i] == want, (v[i], got[i], want)
+
+
+def test_bf16_activation_mode_stores_bf16_values():
+    T, d, f, E, k = 40, 16, 24, 4, 2
+    a = _tiny(T, d, f, E, k, seed=31)
+    a["w_gu"] *= 25.0
+    fwd = R.moe_forward(a["x"], a["logits"], a["w_gu"], a["w2"], k,
+                        bf16_act=True)
+    bwd = R.moe_backward(fwd, a["dy"], a["w_gu"], a["w2"], bf16_act=True)
+    for name, arr in (("ab", fwd["ab"]), ("s", fwd["s"]),
+                      ("dab", bwd["dab"])):
+        np.testing.assert_array_equal(R.bf16_round(arr), arr, err_msg=name)
+    exact = R.moe_forward(a["x"], a["logits"], a["w_gu"], a["w2"], k)
+    # S is the rounded exact S; AB is the rounded exact AB
+    np.testing.assert_array_equal(fwd["s"], R.bf16_round(exact["s"]))
+    np.testing.assert_array_equal(fwd["ab"], R.bf16_round(exact["ab"]))
+    # the output moves by no more than the storage roundings allow
+    assert rel_err(fwd["y"], exact["y"]) < 2e-2
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
+
+
+def test_bf16_activation_closed_form():
+    """k1_two_tokens of the closed forms with S stored as bfloat16:
+    silu(1) = 0.731058... rounds to 187/256 and 1.0757... (= silu(-1)*(-4))
+    to 138/128, so y = (187/256, 3*138/128)."""
+    case = [c for c in _golden_cases() if c["name"] == "k1_two_tokens"][0]
+    fwd = R.moe_forward(np.array(case["x"]), np.array(case["logits"]),
+                        np.array(case["w_gu"]), np.array(case["w2"]), 1,
+                        bf16_act=True)
+    np.testing.assert_array_equal(fwd["y"], [[187 / 256], [3 * 138 / 128]])
