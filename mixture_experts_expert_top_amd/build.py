@@ -51,7 +51,8 @@ def build(verbose=False):
             print(warn, file=sys.stderr)
     objs = [o for o, _ in results]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           "-Wl,--no-undefined", "-o", tmp,
            *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
