@@ -45,16 +45,17 @@ def stage_flops(name, T, d, f, E, k):
     }.get(name, 0.0)
 
 
-def stage_bytes(name, T, d, f, E, k):
+def stage_bytes(name, T, d, f, E, k, planes=1):
     """Algorithmic HBM bytes of the memory-bound stages (each tensor read
-    or written once)."""
+    or written once; the fp32 rows the combines read come as `planes`
+    partial-sum planes)."""
     Tk = T * k
     return {
         "route": T * E * 4 + Tk * 8,
         "permute": Tk * 8 + T * d * 2 + Tk * d * 2 + Tk * 12 + E * 8,
-        "unpermute_y": Tk * 4 + Tk * d * 4 + T * d * 2,
+        "unpermute_y": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
         "permute_dy": Tk * 4 + T * d * 2 + Tk * d * 2,
-        "unpermute_dx": Tk * 4 + Tk * d * 4 + T * d * 2,
+        "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
     }.get(name, 0)
 
 
@@ -95,7 +96,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
                     help="mixtral (default), finegrain, tiny")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -104,7 +105,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from mixture_experts_expert_top_amd import inputs
+    from mixture_experts_expert_top_amd import inputs, moe
     from mixture_experts_expert_top_amd.layer import MoEPath, StageTimers
 
     wl = inputs.WORKLOADS[args.workload]
@@ -148,7 +149,7 @@ def main():
     for n, v in stage_ms.items():
         e = {"ms": round(v, 4)}
         fl = stage_flops(n, T, d, f, E, k)
-        by = stage_bytes(n, T, d, f, E, k)
+        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES)
         if fl:
             e["tflops"] = round(fl / (v / 1e3) / 1e12, 1)
         if by:

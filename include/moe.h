@@ -147,8 +147,10 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   S[r]   = w_perm[r] * silu(AB[r][:f]) * AB[r][f:]
  *   O[r]   = S[r] . w2[e]^T
  *   w_gu [E][2f][d], w2 [E][d][f]; ab_saved [T*k][2f] bf16 out,
- *   s_saved [T*k][f] bf16 out, out_perm [T*k][d] fp32 out (kept in fp32
- *   so that the combine rounds each output once).
+ *   s_saved [T*k][f] bf16 out; out_perm [P][T*k][d] fp32 out, P =
+ *   moe_row_planes(): O as P partial sums over consecutive ranges of the
+ *   reduction (kept in fp32 and summed, in plane order, by moe_unpermute,
+ *   so that each output is rounded once).
  * prec == MOE_MXFP8: x_perm is E4M3 codes + scales along d (from
  *   moe_permute), w_gu/w2 are codes with scales along their last axis (from
  *   moe_mxfp8_quantize, axis 0); S is requantized along f inside the
@@ -177,8 +179,9 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   dW_gu[e] = dAB_e^T . x_perm_e
  *   dx_perm  = dAB . w_gu[e]
  *   dout_perm [T*k][d] bf16, x_perm [T*k][d] bf16, ab_saved, s_saved as
- *   written by the forward; dx_perm [T*k][d] fp32 out; dw_gu [E][2f][d],
- *   dw2 [E][d][f] bf16 out; dp [T][k] fp32 out (needs pos).
+ *   written by the forward; dx_perm [P][T*k][d] fp32 out (P partial-sum
+ *   planes as out_perm); dw_gu [E][2f][d], dw2 [E][d][f] bf16 out;
+ *   dp [T][k] fp32 out (needs pos).
  * prec == MOE_MXFP8: the same operands are quantized inside the call along
  *   each GEMM's reduction axis (d, 2f, or rows of an expert, restarting at
  *   each expert's first row); inputs and outputs stay bf16.
@@ -205,11 +208,11 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
  *
  * moe_gate_up_swiglu_fwd: ab_saved = x_perm . w_gu[e]^T (bf16) and
  *   s_saved = w_perm * silu(gate) * up (bf16).
- * moe_down_fwd: out_perm = s_saved . w2[e]^T (fp32).
+ * moe_down_fwd: out_perm = s_saved . w2[e]^T (fp32, P planes).
  * moe_down_swiglu_bwd: dS = dout_perm . w2[e]; writes dab [T*k][2f] bf16
  *   (dA_g, dA_u as in moe_grouped_mlp_bwd) and dp_part [T*k][ntiles] fp32,
  *   the per-tile sums of dS * H, ntiles = moe_dp_tiles(f).
- * moe_gate_up_dgrad: dx_perm = dab . w_gu[e] (fp32).
+ * moe_gate_up_dgrad: dx_perm = dab . w_gu[e] (fp32, P planes).
  * moe_grouped_wgrad: for each expert e, c[e] (M x N, bf16) = sum over the
  *   expert's rows r of a[r][m] * b[r][n]; a [T*k][lda], b [T*k][ldb]
  *   row-major; experts without rows get exact zeros.  (dW2: a = dout_perm,
@@ -254,13 +257,18 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
  * expert's rows back into the token's output).  Gather form, no atomics:
  *   y[t] = sum over j, in ascending expert id, of wt * o_perm[pos[t][j]]
  * with wt = w[t][j] (or 1 when w is NULL); fp32 accumulation, one final
- * rounding.  o_perm [T*k][d] bf16 (o_fp32 == 0) or fp32 (o_fp32 != 0);
- * y [T][d] bf16 (y_fp32 == 0) or fp32 (y_fp32 != 0).
+ * rounding.  o_perm [o_planes][T*k][d] fp32 (o_fp32 != 0; a row is the
+ * sum of its planes, added in plane order) or [T*k][d] bf16 (o_fp32 == 0,
+ * o_planes must be 1); y [T][d] bf16 (y_fp32 == 0) or fp32 (y_fp32 != 0).
  */
 moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
-                         const int32_t* pos, const float* w, int64_t T,
-                         int32_t k, int64_t d, int32_t y_fp32, void* y,
-                         hipStream_t stream);
+                         int32_t o_planes, const int32_t* pos, const float* w,
+                         int64_t T, int32_t k, int64_t d, int32_t y_fp32,
+                         void* y, hipStream_t stream);
+
+/* Number of partial-sum planes in out_perm and dx_perm (fixed by the
+ * library build). */
+int32_t moe_row_planes(void);
 
 /*
  * moe_mxfp8_quantize -- MX block quantization, [P1] Challenge 2 (8-bit

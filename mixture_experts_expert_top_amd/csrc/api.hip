@@ -351,10 +351,12 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   return hip_status(e, "moe_grouped_mlp_bwd/dw_gu");
 }
 
+int32_t moe_row_planes(void) { return moe::kOutPlanes; }
+
 moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
-                         const int32_t* pos, const float* w, int64_t T,
-                         int32_t k, int64_t d, int32_t y_fp32, void* y,
-                         hipStream_t stream) {
+                         int32_t o_planes, const int32_t* pos, const float* w,
+                         int64_t T, int32_t k, int64_t d, int32_t y_fp32,
+                         void* y, hipStream_t stream) {
   REQUIRE_PTR(o_perm);
   REQUIRE_PTR(pos);
   REQUIRE_OPT_PTR(w);
@@ -363,8 +365,14 @@ moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
   REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
           "k must be in [1, %d]", moe::kMaxTopK);
   if (moe_status st = check_feature("d", d, MOE_BF16)) return st;
-  return hip_status(moe::launch_unpermute(o_perm, o_fp32 ? 1 : 0, pos, w, T,
-                                          k, d, y_fp32 ? 1 : 0, y, stream),
+  REQUIRE(o_planes >= 1 && o_planes <= 8 && (o_fp32 || o_planes == 1),
+          MOE_ERR_INVALID_ARG,
+          "o_planes must be in [1, 8] (1 for bf16 rows), got %d", o_planes);
+  REQUIRE(T * k * d * 4 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+          "plane larger than 4 GiB");
+  return hip_status(moe::launch_unpermute(o_perm, o_fp32 ? 1 : 0, o_planes,
+                                          pos, w, T, k, d, y_fp32 ? 1 : 0, y,
+                                          stream),
                     "moe_unpermute");
 }
 

@@ -97,6 +97,11 @@ struct Params {
   const bf16_t* AB;  // kDSwiglu: saved [Tk][2f]
   float* dp_part;    // kDSwiglu: [Tk][ntn]
   int f;
+  // SegM split-K (kStoreF32 only): the reduction is cut into ksplit
+  // contiguous ranges; range s writes its partial sums to plane s of C
+  // (plane = elements between planes).  The combine adds the planes.
+  int ksplit;
+  int64_t plane;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -253,7 +258,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int E = P.E;
 
   // ---------------------------------------------------------- tile decode
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // SegM grids hold ksplit copies of an upper bound on the tile count;
+  // copy s (the slowest index) computes reduction range s.
+  const int lbid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_split = gridDim.x / P.ksplit;
+  const int split = lbid / per_split;
+  const int bid = lbid - split * per_split;
   int e, mt, nt;
   int64_t seg0;      // first permuted row of the expert
   int seg_len;       // rows of the expert
@@ -318,7 +328,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int m0 = mt * BM;
   const int n0 = nt * BN;               // kSwiglu: gate column tile = nt*BN/2
   const int Mvalid = (MODE == kSegM) ? seg_len : P.M;
-  const int Kdim = (MODE == kSegM) ? P.K : seg_len;
+  // reduction range [kbeg, Kdim) of this workgroup
+  const int kchunk =
+      (MODE == kSegM) ? ((P.K + P.ksplit * BK - 1) / (P.ksplit * BK)) * BK : 0;
+  const int kbeg = (MODE == kSegM) ? min(P.K, split * kchunk) : 0;
+  const int Kdim = (MODE == kSegM) ? min(P.K, kbeg + kchunk) : seg_len;
 
   // ---------------------------------------------------------- operands
   __amdgpu_buffer_rsrc_t rsA, rsB;
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const bool mv_a = !C::kSplitLoad ||
                     __builtin_amdgcn_readfirstlane(tid) < kMoveThreads;
   const int lt = tid & (kMoveThreads - 1);
-  const int nk = (Kdim + BK - 1) / BK;
+  const int nk = (Kdim - kbeg + BK - 1) / BK;
   Mover<AKC> ma;
   Mover<BKC> mb;
   ma.init(lt, P.lda);
@@ -457,19 +471,19 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per slice
     bf16x8_v a0[BI], b0[BJ], a1[BI], b1[BJ];
     if (nk > 0) {
-      gload(0, 0);
-      gload(0, 1);
+      gload(kbeg, 0);
+      gload(kbeg, 1);
       lstore(smem, 0);
       lstore(smem, 1);
-      gload(BK, 0);
-      gload(BK, 1);
+      gload(kbeg + BK, 0);
+      gload(kbeg + BK, 1);
       __syncthreads();
       read_frags(smem, 0, a0, b0);
     }
     for (int kt = 0; kt < nk; ++kt) {
       const bf16_t* cur = smem + (kt & 1) * kStageElems;
       bf16_t* nxt = smem + ((kt + 1) & 1) * kStageElems;
-      const int k2 = (kt + 2) * BK;
+      const int k2 = kbeg + (kt + 2) * BK;
       // slice 0: MFMAs on (a0,b0); reads of slice 1; stores of stage kt+1
       read_frags(cur, 1, a1, b1);
       lstore(nxt, 0);
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const f32x4 x = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
           const int64_t o = cbase + static_cast<int64_t>(row) * P.ldc + col;
           if (EPI == kStoreF32) {
-            *reinterpret_cast<f32x4*>(P.Cf + o) = x;
+            *reinterpret_cast<f32x4*>(P.Cf + split * P.plane + o) = x;
           } else {
             uint2 u;
             u.x = pack_bf16x2(x[0], x[1]);
@@ -671,8 +685,10 @@ using CfgDgrad = std::conditional_t<MOE_DGRAD_WAVES == 8, Cfg8, Cfg4>;
 using CfgWgrad = Cfg8;
 
 template <class C, int MODE, bool AKC, bool BKC, int EPI>
-hipError_t launch(const Params& P, int grid, hipStream_t s) {
+hipError_t launch(Params P, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  if (P.ksplit < 1) P.ksplit = 1;
+  grid *= P.ksplit;
   hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI>),
                      dim3(grid), dim3(C::kThreads), 0, s, P);
   return hipGetLastError();
@@ -713,6 +729,7 @@ hipError_t gemm_fc2_fwd(const bf16_t* s, const bf16_t* w2,
   P.Cf = o; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = f; P.f = f;
+  P.ksplit = kOutPlanes; P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgFwd, kSegM, true, true, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }
@@ -744,6 +761,7 @@ hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
   P.Cf = dxp; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = 2 * f; P.f = f;
+  P.ksplit = kOutPlanes; P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgDgrad, kSegM, true, false, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }

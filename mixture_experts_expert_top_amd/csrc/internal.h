@@ -12,6 +12,10 @@ typedef uint16_t bf16_t;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPlanChunk = 512;   // slots per block of the counting pass
+// fp32 row outputs of the down projection and of the gate_up data
+// gradient are written as this many partial-sum planes [planes][T*k][d]
+// (split reduction); the combine adds them in plane order.
+constexpr int kOutPlanes = 2;
 
 // routing (route.hip)
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
@@ -37,9 +41,10 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
                                const void* x, int64_t row_bytes, void* x_perm,
                                const void* side, int64_t side_bytes,
                                void* side_perm, hipStream_t s);
-hipError_t launch_unpermute(const void* o, int o_fp32, const int32_t* pos,
-                            const float* w, int64_t T, int k, int64_t d,
-                            int y_fp32, void* y, hipStream_t s);
+hipError_t launch_unpermute(const void* o, int o_fp32, int o_planes,
+                            const int32_t* pos, const float* w, int64_t T,
+                            int k, int64_t d, int y_fp32, void* y,
+                            hipStream_t s);
 hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
                             int64_t T, int k, float* dp, hipStream_t s);
 

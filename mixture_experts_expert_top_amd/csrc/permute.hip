@@ -192,9 +192,9 @@ __device__ __forceinline__ void load8(const void* o, int64_t row, int64_t d,
 
 template <bool OF32>
 __global__ __launch_bounds__(256) void unpermute_kernel(
-    const void* __restrict__ o, const int32_t* __restrict__ pos,
-    const float* __restrict__ w, int k, int64_t d, int y_fp32,
-    void* __restrict__ y) {
+    const void* __restrict__ o, int planes, int64_t plane,
+    const int32_t* __restrict__ pos, const float* __restrict__ w, int k,
+    int64_t d, int y_fp32, void* __restrict__ y) {
   __shared__ int s_pos[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   const int64_t t = blockIdx.x;
@@ -220,6 +220,14 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
     for (int j = 0; j < k; ++j) {
       float v[8];
       load8<OF32>(o, s_pos[j], d, q, v);
+      // further partial-sum planes of the same row, in plane order
+      for (int pl = 1; pl < planes; ++pl) {
+        float u[8];
+        load8<OF32>(static_cast<const float*>(o) + pl * plane, s_pos[j], d, q,
+                    u);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] += u[c];
+      }
       if (w) {
         const float wj = s_w[j];
 #pragma unroll
@@ -305,15 +313,18 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
   return hipGetLastError();
 }
 
-hipError_t launch_unpermute(const void* o, int o_fp32, const int32_t* pos,
-                            const float* w, int64_t T, int k, int64_t d,
-                            int y_fp32, void* y, hipStream_t s) {
+hipError_t launch_unpermute(const void* o, int o_fp32, int o_planes,
+                            const int32_t* pos, const float* w, int64_t T,
+                            int k, int64_t d, int y_fp32, void* y,
+                            hipStream_t s) {
+  const int64_t plane = T * k * d;
   if (o_fp32)
     hipLaunchKernelGGL(unpermute_kernel<true>, dim3(static_cast<unsigned>(T)),
-                       dim3(256), 0, s, o, pos, w, k, d, y_fp32, y);
+                       dim3(256), 0, s, o, o_planes, plane, pos, w, k, d,
+                       y_fp32, y);
   else
     hipLaunchKernelGGL(unpermute_kernel<false>, dim3(static_cast<unsigned>(T)),
-                       dim3(256), 0, s, o, pos, w, k, d, y_fp32, y);
+                       dim3(256), 0, s, o, 1, plane, pos, w, k, d, y_fp32, y);
   return hipGetLastError();
 }
 

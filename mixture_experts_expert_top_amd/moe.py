@@ -28,6 +28,7 @@ EXPORTED = [
     "moe_mxfp8_padded_rows", "moe_workspace_bytes", "moe_dp_tiles",
     "moe_gate_up_swiglu_fwd", "moe_down_fwd", "moe_down_swiglu_bwd",
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
+    "moe_row_planes",
 ]
 
 
@@ -59,7 +60,9 @@ def _load():
         "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
                                       I64, P, P, P, P, P, P, P, P, P, P, SZ,
                                       P]),
-        "moe_unpermute": (I32, [P, I32, P, P, I64, I32, I64, I32, P, P]),
+        "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
+                                P]),
+        "moe_row_planes": (I32, []),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
         "moe_mxfp8_padded_rows": (I64, [I64, I32]),
         "moe_workspace_bytes": (SZ, [I32, I32, I64, I32, I32, I64, I64]),
@@ -118,6 +121,9 @@ def _want(t, name, dtype, shape=None, allow_none=False):
 
 def version():
     return lib.moe_version().decode()
+
+
+ROW_PLANES = int(lib.moe_row_planes())
 
 
 def moe_workspace_bytes(entry, prec, T, E, k, d, f):
@@ -196,7 +202,7 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
     _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
-    _want(out_perm, "out_perm", torch.float32, (Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
     _check("moe_grouped_mlp_fwd", lib.moe_grouped_mlp_fwd(
@@ -220,7 +226,7 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                       ("s_saved", s_saved, (Tk, f)),
                       ("dw_gu", dw_gu, (E, 2 * f, d)), ("dw2", dw2, (E, d, f))):
         _want(t, n, torch.bfloat16, shp)
-    _want(dx_perm, "dx_perm", torch.float32, (Tk, d))
+    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
     _want(pos, "pos", torch.int32)
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
@@ -235,19 +241,22 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
 
 
 def moe_unpermute(o_perm, pos, w, y, stream=None):
+    """o_perm: bf16 [T*k, d] rows, or fp32 [T*k, d] / [planes, T*k, d]."""
     T, k = pos.shape
-    d = o_perm.shape[1]
+    d = o_perm.shape[-1]
     if o_perm.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("o_perm must be bfloat16 or float32")
-    _want(o_perm, "o_perm", o_perm.dtype, (T * k, d))
+    planes = o_perm.shape[0] if o_perm.dim() == 3 else 1
+    _want(o_perm, "o_perm", o_perm.dtype,
+          (planes, T * k, d) if o_perm.dim() == 3 else (T * k, d))
     _want(pos, "pos", torch.int32)
     _want(w, "w", torch.float32, (T, k), allow_none=True)
     if y.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("y must be bfloat16 or float32")
     _want(y, "y", y.dtype, (T, d))
     _check("moe_unpermute", lib.moe_unpermute(
-        _p(o_perm), 1 if o_perm.dtype == torch.float32 else 0, _p(pos),
-        _p(w), T, k, d,
+        _p(o_perm), 1 if o_perm.dtype == torch.float32 else 0, planes,
+        _p(pos), _p(w), T, k, d,
         1 if y.dtype == torch.float32 else 0, _p(y), _stream(stream)))
 
 
@@ -301,7 +310,7 @@ def moe_down_fwd(s_saved, offsets, w2, out_perm, stream=None):
     _want(s_saved, "s_saved", torch.bfloat16)
     _want(w2, "w2", torch.bfloat16, (E, d, f))
     _want(offsets, "offsets", torch.int32, (E + 1,))
-    _want(out_perm, "out_perm", torch.float32, (Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
     _check("moe_down_fwd", lib.moe_down_fwd(
         _p(s_saved), _p(offsets), E, Tk, d, f, _p(w2), _p(out_perm),
         _stream(stream)))
@@ -330,7 +339,7 @@ def moe_gate_up_dgrad(dab, offsets, w_gu, dx_perm, stream=None):
     _want(dab, "dab", torch.bfloat16)
     _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
-    _want(dx_perm, "dx_perm", torch.float32, (Tk, d))
+    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
     _check("moe_gate_up_dgrad", lib.moe_gate_up_dgrad(
         _p(dab), _p(offsets), E, Tk, d, f, _p(w_gu), _p(dx_perm),
         _stream(stream)))

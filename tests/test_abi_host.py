@@ -117,9 +117,14 @@ def test_mlp_bwd_validation():
 
 
 def test_unpermute_validation():
-    assert L.moe_unpermute(A, 0, A, None, 8, 0, 64, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, 1, A, None, 8, 2, 60, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, 0, None, None, 8, 2, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 0, 1, A, None, 8, 0, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 1, 1, A, None, 8, 2, 60, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 0, 1, None, None, 8, 2, 64, 0, A,
+                           None) == INVALID
+    # bf16 rows come as one plane; planes must be in [1, 8]
+    assert L.moe_unpermute(A, 0, 2, A, None, 8, 2, 64, 0, A, None) == INVALID
+    assert L.moe_unpermute(A, 1, 0, A, None, 8, 2, 64, 0, A, None) == INVALID
+    assert L.moe_row_planes() >= 1
 
 
 def test_padded_rows():

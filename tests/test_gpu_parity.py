@@ -243,7 +243,8 @@ def test_layer_parity(name, T, d, f, E, k, bias):
     np.testing.assert_array_equal(path.offsets.cpu().numpy(), fwd["offsets"])
     np.testing.assert_array_equal(path.pos.cpu().numpy(), fwd["pos"])
     np.testing.assert_array_equal(path.src.cpu().numpy(), fwd["src"])
-    gpu = {"ab": path.ab, "s": path.s, "o": path.o, "y": path.y,
+    gpu = {"ab": path.ab, "s": path.s, "o": path.o.double().sum(dim=0),
+           "y": path.y,
            "dx": path.dx, "dw_gu": path.dw_gu, "dw2": path.dw2, "dp": path.dp}
     ref = {"ab": fwd["ab"], "s": fwd["s"], "o": fwd["o"], "y": fwd["y"],
            "dx": bwd["dx"], "dw_gu": bwd["dw_gu"], "dw2": bwd["dw2"],
