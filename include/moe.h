@@ -281,21 +281,25 @@ int32_t moe_row_planes(void);
  *     codes [rows][cols], scales [rows][cols/32].
  *   axis == 1: blocks of 32 consecutive rows that restart at every segment
  *     start seg_offsets[s] (nseg segments, seg_offsets [nseg+1] on the
- *     device, seg_offsets[nseg] == rows; NULL means one segment); the last
- *     block of a segment covers the rows left.  Output is transposed so
- *     that each block is contiguous: codes [cols][rows_pad],
- *     scales [cols][rows_pad/32], where row r of segment s lands at column
- *     pad_off[s] + (r - seg_offsets[s]) and pad_off[s] is the sum of the
- *     previous segments' lengths rounded up to 32; pad columns hold code 0.
- *     rows_pad = moe_mxfp8_padded_rows(...) (host-side bound: rows +
- *     31 * nseg rounded up to 32).
+ *     device, seg_offsets[0] == 0, seg_offsets[nseg] == rows; NULL means
+ *     one segment); the last block of a segment covers the rows left.
+ *     Output is transposed so that each block is contiguous: codes
+ *     [cols][rows_pad], scales [cols][rows_pad/32]; row r of segment s
+ *     lands at column pad_off[s] + (r - seg_offsets[s]) where pad_off[s]
+ *     is the sum of the previous segments' lengths, each rounded up to 128
+ *     (so every segment starts on a multiple of 128).  Padding holds code
+ *     0 with scale byte 0.  rows_pad: a multiple of 128, at least
+ *     moe_mxfp8_padded_rows(rows, nseg).
+ * Inputs are finite.  Codes and scales are exact (bit-identical to the
+ * definition above).
  */
 moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                               int32_t axis, const int32_t* seg_offsets,
                               int32_t nseg, uint8_t* codes, uint8_t* scales,
                               int64_t rows_pad, hipStream_t stream);
 
-/* Host-side bound on rows_pad for axis == 1 quantization. */
+/* Host-side bound on rows_pad for axis == 1 quantization:
+ * rows + 127 * nseg rounded up to 128. */
 int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg);
 
 /*

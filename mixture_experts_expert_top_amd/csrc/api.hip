@@ -492,16 +492,48 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
 
 int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg) {
   if (rows < 0 || nseg < 1) return 0;
-  return ((rows + 31 * static_cast<int64_t>(nseg)) + 31) / 32 * 32;
+  const int64_t p = moe::kMxPad;
+  return (rows + (p - 1) * static_cast<int64_t>(nseg) + p - 1) / p * p;
 }
 
 moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                               int32_t axis, const int32_t* seg_offsets,
                               int32_t nseg, uint8_t* codes, uint8_t* scales,
                               int64_t rows_pad, hipStream_t stream) {
-  (void)src; (void)rows; (void)cols; (void)axis; (void)seg_offsets;
-  (void)nseg; (void)codes; (void)scales; (void)rows_pad; (void)stream;
-  return fail(MOE_ERR_UNSUPPORTED, "MXFP8 quantize is not available in this build");
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE(rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG,
+          "rows and cols must be >= 1");
+  REQUIRE(rows * cols * 2 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+          "source larger than 4 GiB");
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  if (axis == 0) {
+    REQUIRE(cols % 32 == 0, MOE_ERR_INVALID_ARG,
+            "axis 0 needs cols %% 32 == 0 (got %lld)",
+            static_cast<long long>(cols));
+    return hip_status(moe::launch_mx_quant_rows(s, rows, cols, codes, scales,
+                                                stream),
+                      "moe_mxfp8_quantize/rows");
+  }
+  REQUIRE(axis == 1, MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
+  REQUIRE(nseg >= 1 && nseg <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "nseg must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(seg_offsets != nullptr || nseg == 1, MOE_ERR_INVALID_ARG,
+          "seg_offsets may be NULL only for one segment");
+  REQUIRE_OPT_PTR(seg_offsets);
+  REQUIRE(cols % 8 == 0, MOE_ERR_INVALID_ARG, "axis 1 needs cols %% 8 == 0");
+  REQUIRE(rows_pad >= moe_mxfp8_padded_rows(rows, nseg) &&
+              rows_pad % moe::kMxPad == 0,
+          MOE_ERR_INVALID_ARG,
+          "rows_pad must be a multiple of %d and >= moe_mxfp8_padded_rows",
+          moe::kMxPad);
+  REQUIRE(cols * rows_pad <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+          "output larger than 4 GiB");
+  return hip_status(moe::launch_mx_quant_tokens(s, rows, cols, seg_offsets,
+                                                nseg, codes, scales, rows_pad,
+                                                stream),
+                    "moe_mxfp8_quantize/tokens");
 }
 
 }  // extern "C"

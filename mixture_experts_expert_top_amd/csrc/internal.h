@@ -16,6 +16,9 @@ constexpr int kPlanChunk = 512;   // slots per block of the counting pass
 // gradient are written as this many partial-sum planes [planes][T*k][d]
 // (split reduction); the combine adds them in plane order.
 constexpr int kOutPlanes = 2;
+// MXFP8 along tokens: every expert segment is padded to a multiple of this
+// many rows so that each starts on a whole k-step of the MX GEMMs.
+constexpr int kMxPad = 128;
 
 // routing (route.hip)
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
@@ -47,6 +50,15 @@ hipError_t launch_unpermute(const void* o, int o_fp32, int o_planes,
                             hipStream_t s);
 hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
                             int64_t T, int k, float* dp, hipStream_t s);
+
+// MXFP8 quantization (mxfp8.hip)
+hipError_t launch_mx_quant_rows(const bf16_t* src, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales,
+                                hipStream_t s);
+hipError_t launch_mx_quant_tokens(const bf16_t* src, int64_t rows,
+                                  int64_t cols, const int32_t* seg, int nseg,
+                                  uint8_t* codes, uint8_t* scales,
+                                  int64_t rows_pad, hipStream_t s);
 
 // grouped GEMMs (gemm.hip)
 int gemm_dp_tiles(int64_t f);

@@ -128,6 +128,16 @@ def test_unpermute_validation():
 
 
 def test_padded_rows():
-    assert L.moe_mxfp8_padded_rows(100, 1) == 160
-    assert L.moe_mxfp8_padded_rows(64, 4) == 192
+    assert L.moe_mxfp8_padded_rows(100, 1) == 256
+    assert L.moe_mxfp8_padded_rows(64, 4) == 640
+    assert L.moe_mxfp8_padded_rows(128, 1) == 256
     assert L.moe_mxfp8_padded_rows(-1, 1) == 0
+
+
+def test_quantize_validation():
+    q = L.moe_mxfp8_quantize
+    assert q(A, 8, 48, 0, None, 1, A, A, 0, None) == INVALID   # cols % 32
+    assert q(A, 8, 64, 2, None, 1, A, A, 0, None) == INVALID   # axis
+    assert q(A, 8, 64, 1, None, 2, A, A, 1024, None) == INVALID  # NULL segs
+    assert q(A, 100, 64, 1, None, 1, A, A, 128, None) == INVALID  # rows_pad
+    assert q(None, 8, 64, 0, None, 1, A, A, 0, None) == INVALID
