@@ -16,9 +16,10 @@ Sources (cited by page title and section):
     Training of Biological Foundation Models" -- section "Why Biology Is
     Especially Well-Suited for MoE" (top-K router over per-expert scores).
 
-Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
-closed forms, library routines, finite differences, exhaustive codec
-sweeps).  See each module header for what is and is not pinned.
+Every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_mx_pins.py`` and ``tests/test_oracle_mx_layer_pins.py``
+(brute force, closed forms, library routines, finite differences,
+exhaustive codec sweeps, an independent formulation of the MXFP8 layer).  See each module header for what is and is not pinned.
 """
 
-from . import moe_ref, mx_ref  # noqa: F401
+from . import moe_mx, moe_ref, mx_ref  # noqa: F401
