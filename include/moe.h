@@ -151,11 +151,15 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   moe_row_planes(): O as P partial sums over consecutive ranges of the
  *   reduction (kept in fp32 and summed, in plane order, by moe_unpermute,
  *   so that each output is rounded once).
- * prec == MOE_MXFP8: x_perm is E4M3 codes + scales along d (from
- *   moe_permute), w_gu/w2 are codes with scales along their last axis (from
- *   moe_mxfp8_quantize, axis 0); S is requantized along f inside the
- *   epilogue for the second GEMM; ab_saved/s_saved/out_perm stay bf16.
- * w_perm may be NULL (weight 1).  Workspace: MOE_ENTRY_MLP_FWD.
+ * prec == MOE_MXFP8 ([P1] Challenge 2: blocks of 32 along each GEMM's
+ *   reduction axis, E4M3 codes with E8M0 scales): x_perm is codes + scales
+ *   along d (from moe_permute), w_gu/w2 are codes with scales along their
+ *   last axis (from moe_mxfp8_quantize, axis 0); S is quantized along f
+ *   inside the gate_up epilogue, from its fp32 value, for the down GEMM
+ *   (held in the workspace); ab_saved/s_saved stay bf16, out_perm fp32.
+ *   d and f must be multiples of 128.
+ * w_perm may be NULL (weight 1).  Workspace: MOE_ENTRY_MLP_FWD (none for
+ * bf16).
  */
 moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
                                const uint8_t* x_perm_scales,
@@ -182,9 +186,13 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   written by the forward; dx_perm [P][T*k][d] fp32 out (P partial-sum
  *   planes as out_perm); dw_gu [E][2f][d], dw2 [E][d][f] bf16 out;
  *   dp [T][k] fp32 out (needs pos).
- * prec == MOE_MXFP8: the same operands are quantized inside the call along
- *   each GEMM's reduction axis (d, 2f, or rows of an expert, restarting at
- *   each expert's first row); inputs and outputs stay bf16.
+ * prec == MOE_MXFP8: inputs and outputs stay bf16; every GEMM operand is
+ *   quantized inside the call along that GEMM's reduction axis: dO along
+ *   d, w2 along d and w_gu along 2f (per expert), dAB along 2f (in the
+ *   epilogue that produces it, from fp32), and for the weight gradients
+ *   dO, s_saved, dAB (its bf16 value) and x_perm along the rows of each
+ *   expert, blocks restarting at the expert's first row.  d and f must be
+ *   multiples of 128.
  * Workspace: MOE_ENTRY_MLP_BWD.
  */
 moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
@@ -253,6 +261,63 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
                          hipStream_t stream);
 
 /*
+ * MXFP8 stage entry points ([P1] Challenge 2): the block-scaled versions
+ * of the stage GEMMs above, one kernel each, on E4M3 codes (uint8) with
+ * one E8M0 scale byte per 32 codes along the reduction axis.  d and f must
+ * be multiples of 128; outputs as in the bf16 stages.
+ *
+ * moe_mx_gate_up_swiglu_fwd: xq [T*k][d], xs [T*k][d/32]; wq [E][2f][d],
+ *   ws [E][2f][d/32]; writes ab_saved, s_saved (bf16) and S quantized
+ *   along f from its fp32 value: sq [T*k][f], ss [T*k][f/32].
+ * moe_mx_down_fwd: sq/ss as written above; wq [E][d][f], ws [E][d][f/32];
+ *   out_perm [P][T*k][d] fp32.
+ * moe_mx_down_swiglu_bwd: doq [T*k][d], dos [T*k][d/32] (dout_perm along
+ *   d); w2tq [f][E*d], w2ts [f][E*d/32] (w2 viewed as [E*d][f] quantized
+ *   with moe_mxfp8_quantize axis 1, one segment, rows_pad E*d: expert e
+ *   in columns [e*d, (e+1)*d)); writes dab (bf16), dAB quantized along 2f
+ *   from fp32 (dabq [T*k][2f], dabs [T*k][2f/32]) and dp_part.
+ * moe_mx_gate_up_dgrad: dabq/dabs as written above; wgutq [d][E*2f],
+ *   wguts [d][E*2f/32] (w_gu viewed as [E*2f][d], axis 1, one segment,
+ *   rows_pad E*2f); dx_perm [P][T*k][d] fp32.
+ * moe_mx_grouped_wgrad: c[e] (M x N, bf16) = sum over expert e's padded
+ *   token range of a[m][t] * b[n][t], where aq [M][ldt], as [M][ldt/32],
+ *   bq [N][ldt], bs [N][ldt/32] come from moe_mxfp8_quantize axis 1 with
+ *   seg_offsets = offsets (nseg = E) and rows_pad = ldt (a multiple of 128,
+ *   at least moe_mxfp8_padded_rows(T*k, E)).  Experts without rows get
+ *   exact zeros.
+ */
+moe_status moe_mx_gate_up_swiglu_fwd(
+    const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
+    int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
+    const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
+    uint8_t* ss, hipStream_t stream);
+
+moe_status moe_mx_down_fwd(const uint8_t* sq, const uint8_t* ss,
+                           const int32_t* offsets, int32_t E, int64_t Tk,
+                           int64_t d, int64_t f, const uint8_t* wq,
+                           const uint8_t* ws, float* out_perm,
+                           hipStream_t stream);
+
+moe_status moe_mx_down_swiglu_bwd(
+    const uint8_t* doq, const uint8_t* dos, const int32_t* offsets,
+    int32_t E, int64_t Tk, int64_t d, int64_t f, const uint8_t* w2tq,
+    const uint8_t* w2ts, const void* ab_saved, const float* w_perm,
+    void* dab, uint8_t* dabq, uint8_t* dabs, float* dp_part,
+    hipStream_t stream);
+
+moe_status moe_mx_gate_up_dgrad(const uint8_t* dabq, const uint8_t* dabs,
+                                const int32_t* offsets, int32_t E, int64_t Tk,
+                                int64_t d, int64_t f, const uint8_t* wgutq,
+                                const uint8_t* wguts, float* dx_perm,
+                                hipStream_t stream);
+
+moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
+                                const uint8_t* bq, const uint8_t* bs,
+                                int64_t ldt, const int32_t* offsets,
+                                int32_t E, int64_t Tk, int64_t M, int64_t N,
+                                void* c, hipStream_t stream);
+
+/*
  * moe_unpermute -- combine, [P1] Challenge 1 (the loop index-adds each
  * expert's rows back into the token's output).  Gather form, no atomics:
  *   y[t] = sum over j, in ascending expert id, of wt * o_perm[pos[t][j]]
@@ -298,8 +363,10 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                               int32_t nseg, uint8_t* codes, uint8_t* scales,
                               int64_t rows_pad, hipStream_t stream);
 
-/* Host-side bound on rows_pad for axis == 1 quantization:
- * rows + 127 * nseg rounded up to 128. */
+/* Host-side bound on rows_pad for axis == 1 quantization: the padded
+ * segment lengths sum to a multiple of 128 that is at most rows + 127 *
+ * nseg, so the bound is that number rounded down to a multiple of 128
+ * (exact for one segment). */
 int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg);
 
 /*

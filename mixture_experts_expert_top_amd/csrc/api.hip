@@ -100,6 +100,72 @@ moe_status check_mlp_dims(int32_t E, int64_t Tk, int64_t d, int64_t f,
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
+// The MX GEMMs read one scale dword (4 blocks of 32) per row and stage of
+// 128 codes: every reduction length and scale row must be a multiple of
+// 128 codes.
+moe_status check_mx_dims(int64_t d, int64_t f) {
+  REQUIRE(d % moe::kMxPad == 0 && f % moe::kMxPad == 0, MOE_ERR_INVALID_ARG,
+          "MXFP8 grouped MLP needs d and f multiples of %d (got %lld, %lld)",
+          moe::kMxPad, static_cast<long long>(d), static_cast<long long>(f));
+  return MOE_OK;
+}
+
+int64_t padded_tokens(int64_t Tk, int32_t E) {
+  const int64_t p = moe::kMxPad;
+  return (Tk + (p - 1) * static_cast<int64_t>(E)) / p * p;
+}
+
+// Forward MX workspace: S as codes [Tk][f] and scales [Tk][f/32].
+struct MxFwdWorkspace {
+  size_t sq = 0, ss = 0, total = 0;
+};
+
+MxFwdWorkspace mx_fwd_layout(int64_t Tk, int64_t f) {
+  MxFwdWorkspace w;
+  size_t off = 0;
+  w.sq = off; off += align256(static_cast<size_t>(Tk * f));
+  w.ss = off; off += align256(static_cast<size_t>(Tk * f / 32));
+  w.total = off;
+  return w;
+}
+
+// Backward MX workspace: every backward GEMM operand in MX form.
+//   doq/dos   dO rows along d           [Tk][d], [Tk][d/32]
+//   w2t*      W2 along d, transposed    [f][E d], [f][E d/32]
+//   wgut*     W_gu along 2f, transposed [d][E 2f], [d][E 2f/32]
+//   dabq/dabs dAB rows along 2f         [Tk][2f], [Tk][2f/32]
+//   *t        token-axis operands of the weight gradients, transposed
+//             [cols][Tk_pad] codes and [cols][Tk_pad/32] scales
+struct MxBwdWorkspace {
+  size_t doq, dos, w2tq, w2ts, wgutq, wguts, dabq, dabs;
+  size_t dot, dots, st, sts, dabt, dabts, xpt, xpts;
+  size_t total;
+  int64_t tk_pad;
+};
+
+MxBwdWorkspace mx_bwd_layout(int64_t Tk, int32_t E, int64_t d, int64_t f,
+                             size_t base) {
+  MxBwdWorkspace w;
+  size_t off = base;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += align256(static_cast<size_t>(bytes));
+    return o;
+  };
+  const int64_t tp = padded_tokens(Tk, E);
+  w.tk_pad = tp;
+  w.doq = take(Tk * d);            w.dos = take(Tk * d / 32);
+  w.w2tq = take(E * d * f);        w.w2ts = take(E * d * f / 32);
+  w.wgutq = take(E * 2 * f * d);   w.wguts = take(E * 2 * f * d / 32);
+  w.dabq = take(Tk * 2 * f);       w.dabs = take(Tk * 2 * f / 32);
+  w.dot = take(d * tp);            w.dots = take(d * tp / 32);
+  w.st = take(f * tp);             w.sts = take(f * tp / 32);
+  w.dabt = take(2 * f * tp);       w.dabts = take(2 * f * tp / 32);
+  w.xpt = take(d * tp);            w.xpts = take(d * tp / 32);
+  w.total = off;
+  return w;
+}
+
 struct BwdWorkspace {
   size_t dab = 0, dp_part = 0, total = 0;
 };
@@ -135,17 +201,19 @@ const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
 
 size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
                            int32_t E, int32_t k, int64_t d, int64_t f) {
-  (void)d;
   if (T < 1 || E < 1 || E > moe::kMaxExperts || k < 1 || k > E) return 0;
+  if (prec != MOE_BF16 && prec != MOE_MXFP8) return 0;
   const int64_t Tk = T * k;
   switch (entry) {
     case MOE_ENTRY_PERMUTE:
       return moe::plan_workspace_bytes(Tk, E);
     case MOE_ENTRY_MLP_FWD:
-      return 0;
+      if (prec == MOE_BF16 || f < 1) return 0;
+      return mx_fwd_layout(Tk, f).total;
     case MOE_ENTRY_MLP_BWD:
-      if (prec != MOE_BF16 || f < 1) return 0;
-      return bwd_layout(Tk, f).total;
+      if (f < 1 || d < 1) return 0;
+      if (prec == MOE_BF16) return bwd_layout(Tk, f).total;
+      return mx_bwd_layout(Tk, E, d, f, bwd_layout(Tk, f).total).total;
   }
   return 0;
 }
@@ -259,11 +327,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
                                void* ab_saved, void* s_saved, void* out_perm,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  (void)x_perm_scales; (void)w_gu_scales; (void)w2_scales;
-  (void)workspace; (void)workspace_bytes;
   if (moe_status st = check_prec(prec)) return st;
-  REQUIRE(prec == MOE_BF16, MOE_ERR_UNSUPPORTED,
-          "MXFP8 grouped MLP is not available in this build");
   REQUIRE_PTR(x_perm);
   REQUIRE_PTR(offsets);
   REQUIRE_PTR(w_gu);
@@ -280,6 +344,28 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  if (prec == MOE_MXFP8) {
+    if (moe_status st = check_mx_dims(d, f)) return st;
+    REQUIRE_PTR(x_perm_scales);
+    REQUIRE_PTR(w_gu_scales);
+    REQUIRE_PTR(w2_scales);
+    const MxFwdWorkspace L = mx_fwd_layout(Tk, f);
+    REQUIRE(workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+    REQUIRE_PTR(workspace);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    hipError_t e = moe::gemm_mx_fc1_fwd(
+        static_cast<const uint8_t*>(x_perm), x_perm_scales,
+        static_cast<const uint8_t*>(w_gu), w_gu_scales, offsets, E, Tk, d, f,
+        w_perm, static_cast<bf16_t*>(ab_saved), static_cast<bf16_t*>(s_saved),
+        ws + L.sq, ws + L.ss, stream);
+    if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_fwd/mx_fc1");
+    e = moe::gemm_mx_fc2_fwd(ws + L.sq, ws + L.ss,
+                             static_cast<const uint8_t*>(w2), w2_scales,
+                             offsets, E, Tk, d, f,
+                             static_cast<float*>(out_perm), stream);
+    return hip_status(e, "moe_grouped_mlp_fwd/mx_fc2");
+  }
   hipError_t e = moe::gemm_fc1_fwd(
       static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(w_gu),
       offsets, E, Tk, d, f, w_perm, static_cast<bf16_t*>(ab_saved),
@@ -302,8 +388,6 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (moe_status st = check_prec(prec)) return st;
-  REQUIRE(prec == MOE_BF16, MOE_ERR_UNSUPPORTED,
-          "MXFP8 grouped MLP backward is not available in this build");
   REQUIRE_PTR(dout_perm);
   REQUIRE_PTR(x_perm);
   REQUIRE_PTR(offsets);
@@ -325,6 +409,71 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
   const BwdWorkspace L = bwd_layout(Tk, f);
+  if (prec == MOE_MXFP8) {
+    if (moe_status st = check_mx_dims(d, f)) return st;
+    const MxBwdWorkspace X = mx_bwd_layout(Tk, E, d, f, L.total);
+    REQUIRE(2 * f * X.tk_pad <= kMaxBytes && E * 2 * f * d <= kMaxBytes,
+            MOE_ERR_UNSUPPORTED, "MX operand larger than 2 GiB");
+    REQUIRE(workspace_bytes >= X.total, MOE_ERR_WORKSPACE,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, X.total);
+    REQUIRE_PTR(workspace);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    bf16_t* dab = reinterpret_cast<bf16_t*>(ws + L.dab);
+    float* dp_part = reinterpret_cast<float*>(ws + L.dp_part);
+    const bf16_t* dO = static_cast<const bf16_t*>(dout_perm);
+    const int64_t tp = X.tk_pad;
+    hipError_t e;
+#define MX_STEP(call, what)                                           \
+    e = (call);                                                       \
+    if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/" what)
+    // operands of the data gradients
+    MX_STEP(moe::launch_mx_quant_rows(dO, Tk, d, ws + X.doq, ws + X.dos,
+                                      stream), "quant_dO");
+    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w2),
+                                        nullptr, E * d, f, nullptr, 1,
+                                        ws + X.w2tq, ws + X.w2ts, E * d,
+                                        stream), "quant_W2");
+    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w_gu),
+                                        nullptr, E * 2 * f, d, nullptr, 1,
+                                        ws + X.wgutq, ws + X.wguts,
+                                        E * 2 * f, stream), "quant_W_gu");
+    MX_STEP(moe::gemm_mx_fc2_dgrad(ws + X.doq, ws + X.dos, ws + X.w2tq,
+                                   ws + X.w2ts, E * d, offsets, E, Tk, d, f,
+                                   static_cast<const bf16_t*>(ab_saved),
+                                   w_perm, dab, ws + X.dabq, ws + X.dabs,
+                                   dp_part, stream), "mx_fc2_dgrad");
+    MX_STEP(moe::launch_dp_reduce(dp_part, moe::gemm_dp_tiles(f), pos, T, k,
+                                  dp, stream), "dp");
+    MX_STEP(moe::gemm_mx_fc1_dgrad(ws + X.dabq, ws + X.dabs, ws + X.wgutq,
+                                   ws + X.wguts, E * 2 * f, offsets, E, Tk, d,
+                                   f, static_cast<float*>(dx_perm), stream),
+            "mx_fc1_dgrad");
+    // token-axis operands of the weight gradients
+    MX_STEP(moe::launch_mx_quant_tokens(dO, nullptr, Tk, d, offsets, E,
+                                        ws + X.dot, ws + X.dots, tp, stream),
+            "quant_dO_tokens");
+    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(s_saved),
+                                        nullptr, Tk, f, offsets, E,
+                                        ws + X.st, ws + X.sts, tp, stream),
+            "quant_S_tokens");
+    MX_STEP(moe::gemm_mx_wgrad(ws + X.dot, ws + X.dots, ws + X.st,
+                               ws + X.sts, tp, offsets, E, d, f,
+                               static_cast<bf16_t*>(dw2), stream),
+            "mx_dw2");
+    MX_STEP(moe::launch_mx_quant_tokens(dab, nullptr, Tk, 2 * f, offsets, E,
+                                        ws + X.dabt, ws + X.dabts, tp,
+                                        stream), "quant_dAB_tokens");
+    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(x_perm),
+                                        nullptr, Tk, d, offsets, E,
+                                        ws + X.xpt, ws + X.xpts, tp, stream),
+            "quant_Xp_tokens");
+    MX_STEP(moe::gemm_mx_wgrad(ws + X.dabt, ws + X.dabts, ws + X.xpt,
+                               ws + X.xpts, tp, offsets, E, 2 * f, d,
+                               static_cast<bf16_t*>(dw_gu), stream),
+            "mx_dw_gu");
+#undef MX_STEP
+    return ok();
+  }
   REQUIRE(workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
           "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
   REQUIRE_PTR(workspace);
@@ -490,10 +639,103 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
                     "moe_dp_reduce");
 }
 
+// ------------------------------------------------------------ MX stages
+
+moe_status moe_mx_gate_up_swiglu_fwd(
+    const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
+    int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
+    const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
+    uint8_t* ss, hipStream_t stream) {
+  REQUIRE_PTR(xq); REQUIRE_PTR(xs); REQUIRE_PTR(offsets);
+  REQUIRE_PTR(wq); REQUIRE_PTR(ws); REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(ab_saved); REQUIRE_PTR(s_saved); REQUIRE_PTR(sq);
+  REQUIRE_PTR(ss);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
+  if (moe_status st = check_mx_dims(d, f)) return st;
+  return hip_status(
+      moe::gemm_mx_fc1_fwd(xq, xs, wq, ws, offsets, E, Tk, d, f, w_perm,
+                           static_cast<bf16_t*>(ab_saved),
+                           static_cast<bf16_t*>(s_saved), sq, ss, stream),
+      "moe_mx_gate_up_swiglu_fwd");
+}
+
+moe_status moe_mx_down_fwd(const uint8_t* sq, const uint8_t* ss,
+                           const int32_t* offsets, int32_t E, int64_t Tk,
+                           int64_t d, int64_t f, const uint8_t* wq,
+                           const uint8_t* ws, float* out_perm,
+                           hipStream_t stream) {
+  REQUIRE_PTR(sq); REQUIRE_PTR(ss); REQUIRE_PTR(offsets);
+  REQUIRE_PTR(wq); REQUIRE_PTR(ws); REQUIRE_PTR(out_perm);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
+  if (moe_status st = check_mx_dims(d, f)) return st;
+  return hip_status(moe::gemm_mx_fc2_fwd(sq, ss, wq, ws, offsets, E, Tk, d,
+                                         f, out_perm, stream),
+                    "moe_mx_down_fwd");
+}
+
+moe_status moe_mx_down_swiglu_bwd(
+    const uint8_t* doq, const uint8_t* dos, const int32_t* offsets,
+    int32_t E, int64_t Tk, int64_t d, int64_t f, const uint8_t* w2tq,
+    const uint8_t* w2ts, const void* ab_saved, const float* w_perm,
+    void* dab, uint8_t* dabq, uint8_t* dabs, float* dp_part,
+    hipStream_t stream) {
+  REQUIRE_PTR(doq); REQUIRE_PTR(dos); REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w2tq); REQUIRE_PTR(w2ts); REQUIRE_PTR(ab_saved);
+  REQUIRE_OPT_PTR(w_perm); REQUIRE_PTR(dab); REQUIRE_PTR(dabq);
+  REQUIRE_PTR(dabs); REQUIRE_PTR(dp_part);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
+  if (moe_status st = check_mx_dims(d, f)) return st;
+  return hip_status(
+      moe::gemm_mx_fc2_dgrad(doq, dos, w2tq, w2ts, E * d, offsets, E, Tk, d,
+                             f, static_cast<const bf16_t*>(ab_saved), w_perm,
+                             static_cast<bf16_t*>(dab), dabq, dabs, dp_part,
+                             stream),
+      "moe_mx_down_swiglu_bwd");
+}
+
+moe_status moe_mx_gate_up_dgrad(const uint8_t* dabq, const uint8_t* dabs,
+                                const int32_t* offsets, int32_t E, int64_t Tk,
+                                int64_t d, int64_t f, const uint8_t* wgutq,
+                                const uint8_t* wguts, float* dx_perm,
+                                hipStream_t stream) {
+  REQUIRE_PTR(dabq); REQUIRE_PTR(dabs); REQUIRE_PTR(offsets);
+  REQUIRE_PTR(wgutq); REQUIRE_PTR(wguts); REQUIRE_PTR(dx_perm);
+  if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
+  if (moe_status st = check_mx_dims(d, f)) return st;
+  return hip_status(
+      moe::gemm_mx_fc1_dgrad(dabq, dabs, wgutq, wguts, E * 2 * f, offsets, E,
+                             Tk, d, f, dx_perm, stream),
+      "moe_mx_gate_up_dgrad");
+}
+
+moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
+                                const uint8_t* bq, const uint8_t* bs,
+                                int64_t ldt, const int32_t* offsets,
+                                int32_t E, int64_t Tk, int64_t M, int64_t N,
+                                void* c, hipStream_t stream) {
+  REQUIRE_PTR(aq); REQUIRE_PTR(as); REQUIRE_PTR(bq); REQUIRE_PTR(bs);
+  REQUIRE_PTR(offsets); REQUIRE_PTR(c);
+  REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "E must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
+  if (moe_status st = check_feature("M", M, MOE_BF16)) return st;
+  if (moe_status st = check_feature("N", N, MOE_BF16)) return st;
+  REQUIRE(ldt % moe::kMxPad == 0 && ldt >= padded_tokens(Tk, E),
+          MOE_ERR_INVALID_ARG,
+          "ldt must be a multiple of %d and >= moe_mxfp8_padded_rows(Tk, E)",
+          moe::kMxPad);
+  REQUIRE(M * ldt <= kMaxBytes && N * ldt <= kMaxBytes &&
+              M * N * 2 * static_cast<int64_t>(E) <= kMaxBytes * 8,
+          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  return hip_status(moe::gemm_mx_wgrad(aq, as, bq, bs, ldt, offsets, E, M, N,
+                                       static_cast<bf16_t*>(c), stream),
+                    "moe_mx_grouped_wgrad");
+}
+
 int64_t moe_mxfp8_padded_rows(int64_t rows, int32_t nseg) {
   if (rows < 0 || nseg < 1) return 0;
   const int64_t p = moe::kMxPad;
-  return (rows + (p - 1) * static_cast<int64_t>(nseg) + p - 1) / p * p;
+  return (rows + (p - 1) * static_cast<int64_t>(nseg)) / p * p;
 }
 
 moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
@@ -530,9 +772,9 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
           moe::kMxPad);
   REQUIRE(cols * rows_pad <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
           "output larger than 4 GiB");
-  return hip_status(moe::launch_mx_quant_tokens(s, rows, cols, seg_offsets,
-                                                nseg, codes, scales, rows_pad,
-                                                stream),
+  return hip_status(moe::launch_mx_quant_tokens(s, nullptr, rows, cols,
+                                                seg_offsets, nseg, codes,
+                                                scales, rows_pad, stream),
                     "moe_mxfp8_quantize/tokens");
 }
 

@@ -33,11 +33,28 @@
 // overlaps the other's MFMAs).  LDS: two stages of (256 + 256) x 64 bf16,
 // rows of 128 B with a 16-byte-chunk XOR swizzle that keeps both the tile
 // stores and the MFMA fragment reads free of bank conflicts.
+//
+// MXFP8 (Challenge 2 of the same page: 8-bit values, one scale per block
+// of 32 along the reduction axis): the same kernel with MX = true runs on
+// E4M3 codes and E8M0 scale bytes through gfx950's block-scaled MFMA
+// (32x32x64: per operand and row, lanes 0-31 supply the scale byte of the
+// slice's first 32-block and lanes 32-63 that of its second; every lane
+// holds 16 codes of each block).  Both operands are K-contiguous; their addresses and K
+// coordinates count pairs of codes, so a 64-unit stage holds 128 codes and
+// the movers and LDS tiles are shared unchanged with the bf16 kernel.  Each
+// lane loads the scale dwords of its fragment rows (4 blocks = one stage)
+// straight from global memory one stage ahead.  The epilogues can also
+// emit their bf16 result MX-quantized along the columns (S for the down
+// GEMM, dAB for the gate_up data gradient).  A third grouping mode serves
+// the MX weight gradients: operands transposed by the token-axis quantizer
+// ([rows][padded tokens], blocks restarting at every expert), reduced over
+// each expert's padded token range.
 
 #include <type_traits>
 
 #include "common.cuh"
 #include "internal.h"
+#include "mx.cuh"
 
 namespace moe {
 namespace {
@@ -50,7 +67,7 @@ constexpr int kStageElems = 2 * kTileElems;
 constexpr int kGroupN = 4;                // n-tiles per scheduling group
 constexpr int kEpiRows = 64;              // rows per epilogue pass of a wave
 
-enum Mode { kSegM = 0, kSegK = 1 };
+enum Mode { kSegM = 0, kSegK = 1, kSegKT = 2 };
 enum Epi { kStore = 0, kSwiglu = 1, kDSwiglu = 2, kStoreF32 = 3 };
 
 template <int WM_, int WN_>
@@ -102,6 +119,17 @@ struct Params {
   // (plane = elements between planes).  The combine adds the planes.
   int ksplit;
   int64_t plane;
+  // MX operands: scale bytes [rows][lds_*] (one per 32 codes along K),
+  // bs_stride = bytes between experts' B scales (SegM)
+  const uint8_t* sA;
+  int64_t lds_a;
+  const uint8_t* sB;
+  int64_t lds_b;
+  int64_t bs_stride;
+  // MX epilogue outputs: codes [rows][ldq] and scales [rows][ldq / 32] of
+  // S (kSwiglu, ldq = f) or dAB (kDSwiglu, ldq = 2f); null to skip
+  uint8_t* Qc;
+  uint8_t* Qs;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -242,7 +270,43 @@ __device__ __forceinline__ int find_segment(const int* pref, int E, int key) {
   return lo;
 }
 
-template <class C, int MODE, bool AKC, bool BKC, int EPI>
+// E4M3 codes of 4 values of one row and the scale byte of their 32-block,
+// the block being held by 8 consecutive lanes (4 values each).  All 64
+// lanes must call it; lanes with valid == false contribute zeros.
+__device__ __forceinline__ uint32_t mx_quant4(const float* v, bool valid,
+                                              uint32_t* scale_byte) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) amax = fmaxf(amax, valid ? fabsf(v[c]) : 0.0f);
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const int e = mx_scale_exp(amax);
+  const float inv = mx_inv_scale(e);
+  uint32_t word = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) word |= e4m3_encode(v[c] * inv) << (8 * c);
+  *scale_byte = static_cast<uint32_t>(e + 127);
+  return word;
+}
+
+// Scaled MFMAs of one 64-code k-slice for A fragment rows [I0, I0 + NI)
+// (af holds those NI fragments): the lane's scale byte is byte OPS of its
+// (pre-shifted) scale dword.
+template <int OPS, int I0, int NI, int BI, int BJ>
+__device__ __forceinline__ void mx_mfmas(f32x16 (&acc)[BI][BJ],
+                                         const i32x8* af, const i32x8* bf,
+                                         const uint32_t* sa,
+                                         const uint32_t* sb) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
+      acc[I0 + i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          af[i], bf[j], acc[I0 + i][j], 0, 0, OPS,
+          static_cast<int>(sa[I0 + i]), OPS, static_cast<int>(sb[j]));
+}
+
+template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX>
 __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     Params P) {
   constexpr int NT = C::kThreads;
@@ -250,6 +314,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmemBytes / 2];
   __shared__ int s_pref[kMaxExperts + 1];
   __shared__ float s_dp[C::WN * BM];
+  // MX: scale dwords of the tile rows, [stage][A rows, B rows]
+  __shared__ uint32_t s_scl[MX ? 2 * 2 * BM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -267,11 +333,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   int e, mt, nt;
   int64_t seg0;      // first permuted row of the expert
   int seg_len;       // rows of the expert
-  if (MODE == kSegM) {
-    // prefix of m-tiles per expert
+  if (MODE == kSegM || MODE == kSegKT) {
+    // SegM: prefix of m-tiles per expert; SegKT: prefix of the experts'
+    // padded token ranges (units of two codes)
     for (int i = tid; i <= E; i += NT) {
       int c = 0;
-      if (i < E) c = (P.offsets[i + 1] - P.offsets[i] + BM - 1) / BM;
+      if (i < E) {
+        const int n = P.offsets[i + 1] - P.offsets[i];
+        c = (MODE == kSegM) ? (n + BM - 1) / BM
+                            : (n + kMxPad - 1) / kMxPad * (kMxPad / 2);
+      }
       s_pref[i] = c;
     }
     __syncthreads();
@@ -301,6 +372,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
     }
     __syncthreads();
+  }
+  if (MODE == kSegM) {
     const int total = s_pref[E] * P.ntn;
     if (bid >= total) return;
     e = find_segment(s_pref, E, bid / P.ntn);
@@ -331,18 +404,41 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   // reduction range [kbeg, Kdim) of this workgroup
   const int kchunk =
       (MODE == kSegM) ? ((P.K + P.ksplit * BK - 1) / (P.ksplit * BK)) * BK : 0;
-  const int kbeg = (MODE == kSegM) ? min(P.K, split * kchunk) : 0;
-  const int Kdim = (MODE == kSegM) ? min(P.K, kbeg + kchunk) : seg_len;
+  const int kbeg = (MODE == kSegM)    ? min(P.K, split * kchunk)
+                   : (MODE == kSegKT) ? s_pref[e]
+                                      : 0;
+  const int Kdim = (MODE == kSegM)    ? min(P.K, kbeg + kchunk)
+                   : (MODE == kSegKT) ? s_pref[e + 1]
+                                      : seg_len;
 
   // ---------------------------------------------------------- operands
   __amdgpu_buffer_rsrc_t rsA, rsB;
+  // MX scale bytes (empty resources in the bf16 kernels)
+  __amdgpu_buffer_rsrc_t rsSA = make_rsrc(P.sA, 0), rsSB = make_rsrc(P.sB, 0);
   if (MODE == kSegM) {
     const bf16_t* a = P.A + seg0 * P.lda;
     const int64_t bytes = (P.Tk - seg0) * P.lda * 2;
     rsA = make_rsrc(a, static_cast<uint32_t>(bytes));
     const bf16_t* b = P.B + static_cast<int64_t>(e) * P.b_stride;
-    rsB = make_rsrc(b, static_cast<uint32_t>(static_cast<int64_t>(P.b_rows) *
-                                             P.ldb * 2));
+    // MX B may be a column range of a transposed weight: bound it by the
+    // last byte the expert's rows reach
+    const int64_t bbytes =
+        MX ? ((static_cast<int64_t>(P.b_rows) - 1) * P.ldb + P.K) * 2
+           : static_cast<int64_t>(P.b_rows) * P.ldb * 2;
+    rsB = make_rsrc(b, static_cast<uint32_t>(bbytes));
+    if (MX) {
+      rsSA = make_rsrc(P.sA + seg0 * P.lds_a,
+                       static_cast<uint32_t>((P.Tk - seg0) * P.lds_a));
+      rsSB = make_rsrc(
+          P.sB + static_cast<int64_t>(e) * P.bs_stride,
+          static_cast<uint32_t>((static_cast<int64_t>(P.b_rows) - 1) *
+                                    P.lds_b + P.K / 16));
+    }
+  } else if (MODE == kSegKT) {
+    rsA = make_rsrc(P.A, static_cast<uint32_t>(P.M * P.lda * 2));
+    rsB = make_rsrc(P.B, static_cast<uint32_t>(P.N * P.ldb * 2));
+    rsSA = make_rsrc(P.sA, static_cast<uint32_t>(P.M * P.lds_a));
+    rsSB = make_rsrc(P.sB, static_cast<uint32_t>(P.N * P.lds_b));
   } else {
     const bf16_t* a = P.A + seg0 * P.lda;
     rsA = make_rsrc(a, static_cast<uint32_t>(seg_len * P.lda * 2));
@@ -392,12 +488,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     for (int j = 0; j < BJ; ++j) acc[i][j] = f32x16{};
 
   const int fr = lane & 31;      // fragment row inside a 32-block
-  const int fk = lane >> 5;      // which 8-wide k half
+  const int fk = lane >> 5;      // which half of the fragment's k range
 
-  // Fragments of k-slice kk (16 wide) of one LDS stage.
-  auto read_frags = [&](const bf16_t* sa, int kk, bf16x8_v* af,
-                        bf16x8_v* bf) {
-    const bf16_t* sb = sa + kTileElems;
+  // LDS tiles: [A stage 0][A stage 1][B stage 0][B stage 1].
+  auto atile = [&](int st) { return smem + st * kTileElems; };
+  auto btile = [&](int st) { return smem + (2 + st) * kTileElems; };
+
+  // bf16 fragments of k-slice kk (16 wide) of one LDS stage.
+  auto read_frags = [&](int st, int kk, bf16x8_v* af, bf16x8_v* bf) {
+    const bf16_t* sa = atile(st);
+    const bf16_t* sb = btile(st);
     const int chunk = kk * 2 + fk;
 #pragma unroll
     for (int i = 0; i < BI; ++i)
@@ -435,12 +535,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       load_one<BKC>(mb, vb, rsB, P.ldb, k0, part, blk_b, n0, Kdim);
     }
   };
-  auto lstore = [&](bf16_t* st, int part) {
+  auto lstore = [&](int st, int part) {
     if (C::kSplitLoad) {
-      Mover<AKC>::store(va, st + (mv_a ? 0 : kTileElems), lt, part);
+      Mover<AKC>::store(va, mv_a ? atile(st) : btile(st), lt, part);
     } else {
-      Mover<AKC>::store(va, st, lt, part);
-      Mover<BKC>::store(vb, st + kTileElems, lt, part);
+      Mover<AKC>::store(va, atile(st), lt, part);
+      Mover<BKC>::store(vb, btile(st), lt, part);
     }
   };
   // 8 waves with different layouts: each wave role gets its own copy of
@@ -448,14 +548,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   auto gload_a = [&](int k0, int part) {
     load_one<AKC>(ma, va, rsA, P.lda, k0, part, blk_a, m0, Kdim);
   };
-  auto lstore_a = [&](bf16_t* st, int part) {
-    Mover<AKC>::store(va, st, lt, part);
+  auto lstore_a = [&](int st, int part) {
+    Mover<AKC>::store(va, atile(st), lt, part);
   };
   auto gload_b = [&](int k0, int part) {
     load_one<BKC>(mb, va, rsB, P.ldb, k0, part, blk_b, n0, Kdim);
   };
-  auto lstore_b = [&](bf16_t* st, int part) {
-    Mover<BKC>::store(va, st + kTileElems, lt, part);
+  auto lstore_b = [&](int st, int part) {
+    Mover<BKC>::store(va, btile(st), lt, part);
   };
 
   // Software pipeline over k-steps of BK.  At iteration kt the mover
@@ -473,22 +573,21 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     if (nk > 0) {
       gload(kbeg, 0);
       gload(kbeg, 1);
-      lstore(smem, 0);
-      lstore(smem, 1);
+      lstore(0, 0);
+      lstore(0, 1);
       gload(kbeg + BK, 0);
       gload(kbeg + BK, 1);
       __syncthreads();
-      read_frags(smem, 0, a0, b0);
+      read_frags(0, 0, a0, b0);
     }
     for (int kt = 0; kt < nk; ++kt) {
-      const bf16_t* cur = smem + (kt & 1) * kStageElems;
-      bf16_t* nxt = smem + ((kt + 1) & 1) * kStageElems;
+      const int cs = kt & 1, ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
       // slice 0: MFMAs on (a0,b0); reads of slice 1; stores of stage kt+1
-      read_frags(cur, 1, a1, b1);
-      lstore(nxt, 0);
+      read_frags(cs, 1, a1, b1);
+      lstore(ns, 0);
       mfmas(a0, b0);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
@@ -496,10 +595,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
       // slice 1: MFMAs on (a1,b1); reads of slice 2; stores of stage kt+1
-      read_frags(cur, 2, a0, b0);
-      lstore(nxt, 1);
+      read_frags(cs, 2, a0, b0);
+      lstore(ns, 1);
       mfmas(a1, b1);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
@@ -507,10 +606,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
       // slice 2: MFMAs on (a0,b0); reads of slice 3; loads of stage kt+2
-      read_frags(cur, 3, a1, b1);
+      read_frags(cs, 3, a1, b1);
       gload(k2, 0);
       mfmas(a0, b0);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
@@ -520,18 +619,179 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       // slice 3: MFMAs on (a1,b1); loads of stage kt+2
       gload(k2, 1);
       mfmas(a1, b1);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-      read_frags(nxt, 0, a0, b0);
+      read_frags(ns, 0, a0, b0);
     }
   };
 
-  if constexpr (C::kSplitLoad && AKC != BKC) {
+  // MX K-loop: two 64-code k-slices per stage.  The stage's movers work
+  // as in the bf16 loop (stores of stage kt+1 in slice 0, loads of stage
+  // kt+2 in slice 1); with part 0 each mover thread also moves the scale
+  // dword (4 blocks of 32 codes) of its own tile row into the stage's scale
+  // area of LDS.  After the barrier each lane reads the dwords of its
+  // fragment rows and shifts them by its lane half: lanes 0-31 supply the
+  // scale of the slice's first block and lanes 32-63 that of its second,
+  // i.e. block 2 kk + fk, which is byte 2 kk of the shifted dword (the
+  // MFMA's opsel).  Fragments are
+  // read right before the MFMAs that use them; with 8 waves (two a SIMD)
+  // only half of the wave's A fragments are held at a time, and each
+  // wave's LDS waits are covered by the other wave of its SIMD.
+  auto kloop_mx = [&]() {
+    constexpr int kHalves = (C::kWaves == 4) ? 1 : 2;
+    constexpr int kAH = BI / kHalves;             // A fragments held at once
+    constexpr int kMfH = kAH * BJ;                // MFMAs per half-slice
+    constexpr int kMv = C::kSplitLoad ? 4 : 8;    // moves per part
+    const uint32_t srow_a = static_cast<uint32_t>((m0 + lt) * P.lds_a);
+    const uint32_t srow_b =
+        static_cast<uint32_t>((blk_b(lt >> 5) + (lt & 31)) * P.lds_b);
+    uint32_t vsa = 0, vsb = 0;
+    auto gload_mx = [&](int k0, int part) {
+      gload(k0, part);
+      if (part == 0) {
+        const bool ok = k0 < Kdim;
+        const uint32_t kb = static_cast<uint32_t>(k0 >> 4);   // 32-blocks
+        if (C::kSplitLoad) {
+          vsa = mv_a ? buf_load4(rsSA, ok ? srow_a + kb : kOob)
+                     : buf_load4(rsSB, ok ? srow_b + kb : kOob);
+        } else {
+          vsa = buf_load4(rsSA, ok ? srow_a + kb : kOob);
+          vsb = buf_load4(rsSB, ok ? srow_b + kb : kOob);
+        }
+      }
+    };
+    auto lstore_mx = [&](int st, int part) {
+      lstore(st, part);
+      if (part == 0) {
+        uint32_t* sc = s_scl + st * (2 * BM);
+        if (C::kSplitLoad) {
+          sc[(mv_a ? 0 : BM) + lt] = vsa;
+        } else {
+          sc[lt] = vsa;
+          sc[BM + lt] = vsb;
+        }
+      }
+    };
+    auto read_scales = [&](int st, uint32_t* sa, uint32_t* sb) {
+      const uint32_t* sc = s_scl + st * (2 * BM);
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        sa[i] = sc[wm * TM + i * 32 + fr] >> (8 * fk);
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+        sb[j] = sc[BM + wn * TN + j * 32 + fr] >> (8 * fk);
+    };
+    // The lane's 32 codes of k-slice kk (codes 64 kk .. 64 kk + 63 of the
+    // stage, scale blocks 2 kk and 2 kk + 1) of a tile row.  The block-
+    // scaled MFMA takes bytes 0-15 of every lane from the first 32-block
+    // (scaled by the byte that lanes 0-31 supply) and bytes 16-31 from the
+    // second (scaled by lanes 32-63), so lane half fk holds 16 codes of each
+    // block: chunks 4 kk + fk and 4 kk + 2 + fk.
+    auto frag = [&](const bf16_t* tile, int row, int kk) {
+      const int c0 = kk * 4 + fk;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + lds_off(row, c0));
+      const i32x4 hi =
+          *reinterpret_cast<const i32x4*>(tile + lds_off(row, c0 + 2));
+      return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto read_a = [&](int st, int kk, int h, i32x8* af) {
+#pragma unroll
+      for (int i = 0; i < kAH; ++i)
+        af[i] = frag(atile(st), wm * TM + (h * kAH + i) * 32 + fr, kk);
+    };
+    auto read_b = [&](int st, int kk, i32x8* bf) {
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+        bf[j] = frag(btile(st), wn * TN + j * 32 + fr, kk);
+    };
+    i32x8 af[kAH], bf[BJ];
+    uint32_t sa[BI], sb[BJ];
+    if (nk > 0) {
+      gload_mx(kbeg, 0);
+      gload_mx(kbeg, 1);
+      lstore_mx(0, 0);
+      lstore_mx(0, 1);
+      gload_mx(kbeg + BK, 0);
+      gload_mx(kbeg + BK, 1);
+      __syncthreads();
+      read_b(0, 0, bf);
+      read_a(0, 0, 0, af);
+      read_scales(0, sa, sb);
+    }
+    auto step = [&](int cs, int ns, int kt) {
+      const int k2 = kbeg + (kt + 2) * BK;
+      // slice 0 (fragments of half 0 already read): stores of stage kt+1
+      if constexpr (kHalves == 1) {
+        lstore_mx(ns, 0);
+        lstore_mx(ns, 1);
+        mx_mfmas<0, 0, kAH>(acc, af, bf, sa, sb);
+#pragma unroll
+        for (int i = 0; i < kMfH; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < 2 * kMv + 2) sched_group(kSgDsWrite, 1);
+        }
+      } else {
+        lstore_mx(ns, 0);
+        mx_mfmas<0, 0, kAH>(acc, af, bf, sa, sb);
+#pragma unroll
+        for (int i = 0; i < kMfH; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < kMv + 1) sched_group(kSgDsWrite, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(cs, 0, 1, af);
+        lstore_mx(ns, 1);
+        mx_mfmas<0, kAH, kAH>(acc, af, bf, sa, sb);
+        sched_group(kSgDsRead, 2 * kAH);
+#pragma unroll
+        for (int i = 0; i < kMfH; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < kMv) sched_group(kSgDsWrite, 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // slice 1: loads of stage kt+2
+      read_b(cs, 1, bf);
+      read_a(cs, 1, 0, af);
+      gload_mx(k2, 0);
+      mx_mfmas<2, 0, kAH>(acc, af, bf, sa, sb);
+      sched_group(kSgDsRead, 2 * (kAH + BJ));
+#pragma unroll
+      for (int i = 0; i < kMfH; ++i) {
+        sched_group(kSgMfma, 1);
+        if (i < kMv + 1) sched_group(kSgVmemRead, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kHalves == 2) {
+        read_a(cs, 1, 1, af);
+        gload_mx(k2, 1);
+        mx_mfmas<2, kAH, kAH>(acc, af, bf, sa, sb);
+        sched_group(kSgDsRead, 2 * kAH);
+#pragma unroll
+        for (int i = 0; i < kMfH; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < kMv) sched_group(kSgVmemRead, 1);
+        }
+      } else {
+        gload_mx(k2, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      read_b(ns, 0, bf);
+      read_a(ns, 0, 0, af);
+      read_scales(ns, sa, sb);
+    };
+    for (int kt = 0; kt < nk; ++kt) step(kt & 1, (kt & 1) ^ 1, kt);
+  };
+
+  if constexpr (MX) {
+    kloop_mx();
+  } else if constexpr (C::kSplitLoad && AKC != BKC) {
     if (mv_a) kloop(gload_a, lstore_a);
     else kloop(gload_b, lstore_b);
   } else {
@@ -593,16 +853,29 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       const int col = n0g + wn * (TN / 2) + c4;       // gate column
       for (int r = lane / kLanesG; r < kEpiRows; r += kRowsG) {
         const int row = row_base + r;
-        if (row < Mvalid && col < f) {
-          const f32x4 g = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
-          const f32x4 u =
-              *reinterpret_cast<const f32x4*>(stage + r * LD + TN / 2 + c4);
-          const float wr = w ? w[row] : 1.0f;
-          float sv[4];
+        const bool ok = row < Mvalid && col < f;
+        const int64_t ro = static_cast<int64_t>(row);
+        const f32x4 g = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
+        const f32x4 u =
+            *reinterpret_cast<const f32x4*>(stage + r * LD + TN / 2 + c4);
+        const float wr = (w && ok) ? w[row] : 1.0f;
+        float sv[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sv[c] = wr * (g[c] * sigmoidf_(g[c]) * u[c]);
-          const int64_t ro = static_cast<int64_t>(row);
+        for (int c = 0; c < 4; ++c)
+          sv[c] = wr * (g[c] * sigmoidf_(g[c]) * u[c]);
+        if constexpr (MX) {
+          // S along f: one 32-column block per 8 lanes of the row
+          uint32_t sbyte;
+          const uint32_t q = mx_quant4(sv, ok, &sbyte);
+          if (ok) {
+            const int64_t qr = (seg0 + ro) * f;
+            *reinterpret_cast<uint32_t*>(P.Qc + qr + col) = q;
+            if ((lane & 7) == 0)
+              P.Qs[qr / kMxBlock + col / kMxBlock] =
+                  static_cast<uint8_t>(sbyte);
+          }
+        }
+        if (ok) {
           uint2 og, ou, os;
           og.x = pack_bf16x2(g[0], g[1]); og.y = pack_bf16x2(g[2], g[3]);
           ou.x = pack_bf16x2(u[0], u[1]); ou.y = pack_bf16x2(u[2], u[3]);
@@ -620,8 +893,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       for (int r = lane / kLanesPerRow; r < kEpiRows; r += kRowsPerPass) {
         const int row = row_base + r;
         float part = 0.0f;
-        if (row < Mvalid && col < f) {
-          const int64_t ro = static_cast<int64_t>(row);
+        const bool ok = row < Mvalid && col < f;
+        const int64_t ro = static_cast<int64_t>(row);
+        float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float du[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok) {
           const f32x4 ds = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
           const uint2 gb = *reinterpret_cast<const uint2*>(AB + ro * 2 * f + col);
           const uint2 ub =
@@ -631,7 +907,6 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const float u[4] = {bf_lo(ub.x), bf_hi(ub.x), bf_lo(ub.y),
                               bf_hi(ub.y)};
           const float wr = w ? w[row] : 1.0f;
-          float dg[4], du[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const float sg = sigmoidf_(g[c]);
@@ -646,6 +921,22 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           ou.x = pack_bf16x2(du[0], du[1]); ou.y = pack_bf16x2(du[2], du[3]);
           *reinterpret_cast<uint2*>(dAB + ro * P.ldc + col) = og;
           *reinterpret_cast<uint2*>(dAB + ro * P.ldc + f + col) = ou;
+        }
+        if constexpr (MX) {
+          // dAB along 2f: gate and up blocks of 32 columns, 8 lanes each
+          uint32_t sg_byte, su_byte;
+          const uint32_t qg = mx_quant4(dg, ok, &sg_byte);
+          const uint32_t qu = mx_quant4(du, ok, &su_byte);
+          if (ok) {
+            const int64_t qr = (seg0 + ro) * (2 * f);
+            *reinterpret_cast<uint32_t*>(P.Qc + qr + col) = qg;
+            *reinterpret_cast<uint32_t*>(P.Qc + qr + f + col) = qu;
+            if ((lane & 7) == 0) {
+              uint8_t* srow = P.Qs + qr / kMxBlock;
+              srow[col / kMxBlock] = static_cast<uint8_t>(sg_byte);
+              srow[(f + col) / kMxBlock] = static_cast<uint8_t>(su_byte);
+            }
+          }
         }
         // row sum over the lanes of this row, fixed butterfly order
 #pragma unroll
@@ -683,13 +974,17 @@ using CfgFwd = std::conditional_t<MOE_GEMM_WAVES == 4, Cfg4, Cfg8>;
 #endif
 using CfgDgrad = std::conditional_t<MOE_DGRAD_WAVES == 8, Cfg8, Cfg4>;
 using CfgWgrad = Cfg8;
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 8
+#endif
+using CfgMx = std::conditional_t<MOE_MX_WAVES == 4, Cfg4, Cfg8>;
 
-template <class C, int MODE, bool AKC, bool BKC, int EPI>
+template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX = false>
 hipError_t launch(Params P, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (P.ksplit < 1) P.ksplit = 1;
   grid *= P.ksplit;
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI, MX>),
                      dim3(grid), dim3(C::kThreads), 0, s, P);
   return hipGetLastError();
 }
@@ -780,6 +1075,121 @@ hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
   const int64_t mtiles = (M + BM - 1) / BM;
   const int grid = static_cast<int>(E * mtiles * P.ntn);
   return launch<CfgWgrad, kSegK, false, false, kStore>(P, grid, st);
+}
+
+// ------------------------------------------------------------------ MXFP8
+// Operands are E4M3 codes with one E8M0 byte per 32 codes along K; the
+// kernel addresses codes in pairs, so leading dimensions and K are halved.
+
+// fc1 forward: AB = Xp . W_gu^T, S = w*silu(g)*u as bf16 and as MX codes
+// along f (the down GEMM's A)
+hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
+                           const uint8_t* wq, const uint8_t* ws,
+                           const int32_t* offsets, int E, int64_t Tk,
+                           int64_t d, int64_t f, const float* w_perm,
+                           bf16_t* ab, bf16_t* s, uint8_t* sq, uint8_t* ss,
+                           hipStream_t st) {
+  Params P{};
+  P.A = reinterpret_cast<const bf16_t*>(xq); P.lda = d / 2;
+  P.sA = xs; P.lds_a = d / kMxBlock;
+  P.B = reinterpret_cast<const bf16_t*>(wq); P.ldb = d / 2;
+  P.b_stride = f * d; P.b_rows = 2 * f;
+  P.sB = ws; P.lds_b = d / kMxBlock; P.bs_stride = 2 * f * d / kMxBlock;
+  P.C = ab; P.ldc = 2 * f;
+  P.offsets = offsets; P.E = E; P.Tk = Tk;
+  P.N = f; P.K = d / 2; P.f = f;
+  P.ntn = static_cast<int>((f + BN / 2 - 1) / (BN / 2));
+  P.w = w_perm; P.S = s; P.Qc = sq; P.Qs = ss;
+  return launch<CfgMx, kSegM, true, true, kSwiglu, true>(
+      P, segm_grid(Tk, E, P.ntn), st);
+}
+
+// fc2 forward: O = S . W2^T (fp32 partial planes)
+hipError_t gemm_mx_fc2_fwd(const uint8_t* sq, const uint8_t* ss,
+                           const uint8_t* wq, const uint8_t* ws,
+                           const int32_t* offsets, int E, int64_t Tk,
+                           int64_t d, int64_t f, float* o, hipStream_t st) {
+  Params P{};
+  P.A = reinterpret_cast<const bf16_t*>(sq); P.lda = f / 2;
+  P.sA = ss; P.lds_a = f / kMxBlock;
+  P.B = reinterpret_cast<const bf16_t*>(wq); P.ldb = f / 2;
+  P.b_stride = d * f / 2; P.b_rows = d;
+  P.sB = ws; P.lds_b = f / kMxBlock; P.bs_stride = d * f / kMxBlock;
+  P.Cf = o; P.ldc = d;
+  P.offsets = offsets; P.E = E; P.Tk = Tk;
+  P.N = d; P.K = f / 2; P.f = f;
+  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ntn = static_cast<int>((d + BN - 1) / BN);
+  return launch<CfgMx, kSegM, true, true, kStoreF32, true>(
+      P, segm_grid(Tk, E, P.ntn), st);
+}
+
+// fc2 dgrad + dSwiGLU: dS = dO . W2 with W2 quantized along d and stored
+// transposed ([f][ldw] codes, expert e in columns [e d, (e+1) d)); dAB as
+// bf16 and as MX codes along 2f (the gate_up data gradient's A)
+hipError_t gemm_mx_fc2_dgrad(const uint8_t* doq, const uint8_t* dos,
+                             const uint8_t* wtq, const uint8_t* wts,
+                             int64_t ldw, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t d, int64_t f,
+                             const bf16_t* ab, const float* w_perm,
+                             bf16_t* dab, uint8_t* dabq, uint8_t* dabs,
+                             float* dp_part, hipStream_t st) {
+  Params P{};
+  P.A = reinterpret_cast<const bf16_t*>(doq); P.lda = d / 2;
+  P.sA = dos; P.lds_a = d / kMxBlock;
+  P.B = reinterpret_cast<const bf16_t*>(wtq); P.ldb = ldw / 2;
+  P.b_stride = d / 2; P.b_rows = f;
+  P.sB = wts; P.lds_b = ldw / kMxBlock; P.bs_stride = d / kMxBlock;
+  P.C = dab; P.ldc = 2 * f;
+  P.offsets = offsets; P.E = E; P.Tk = Tk;
+  P.N = f; P.K = d / 2; P.f = f;
+  P.ntn = gemm_dp_tiles(f);
+  P.AB = ab; P.w = w_perm; P.dp_part = dp_part; P.Qc = dabq; P.Qs = dabs;
+  return launch<CfgMx, kSegM, true, true, kDSwiglu, true>(
+      P, segm_grid(Tk, E, P.ntn), st);
+}
+
+// fc1 dgrad: dXp = dAB . W_gu with W_gu quantized along 2f and stored
+// transposed ([d][ldw] codes, expert e in columns [2 e f, 2 (e+1) f))
+hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
+                             const uint8_t* wtq, const uint8_t* wts,
+                             int64_t ldw, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t d, int64_t f, float* dxp,
+                             hipStream_t st) {
+  Params P{};
+  P.A = reinterpret_cast<const bf16_t*>(dabq); P.lda = f;
+  P.sA = dabs; P.lds_a = 2 * f / kMxBlock;
+  P.B = reinterpret_cast<const bf16_t*>(wtq); P.ldb = ldw / 2;
+  P.b_stride = f; P.b_rows = d;
+  P.sB = wts; P.lds_b = ldw / kMxBlock; P.bs_stride = 2 * f / kMxBlock;
+  P.Cf = dxp; P.ldc = d;
+  P.offsets = offsets; P.E = E; P.Tk = Tk;
+  P.N = d; P.K = f; P.f = f;
+  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ntn = static_cast<int>((d + BN - 1) / BN);
+  return launch<CfgMx, kSegM, true, true, kStoreF32, true>(
+      P, segm_grid(Tk, E, P.ntn), st);
+}
+
+// wgrad: C[e] (M x N) = sum over the expert's padded token range of
+// A[m][t] B[n][t], both operands quantized along tokens and transposed
+// ([rows][ldt] codes, [rows][ldt / 32] scales)
+hipError_t gemm_mx_wgrad(const uint8_t* aq, const uint8_t* as,
+                         const uint8_t* bq, const uint8_t* bs, int64_t ldt,
+                         const int32_t* offsets, int E, int64_t M, int64_t N,
+                         bf16_t* c, hipStream_t st) {
+  Params P{};
+  P.A = reinterpret_cast<const bf16_t*>(aq); P.lda = ldt / 2;
+  P.sA = as; P.lds_a = ldt / kMxBlock;
+  P.B = reinterpret_cast<const bf16_t*>(bq); P.ldb = ldt / 2;
+  P.sB = bs; P.lds_b = ldt / kMxBlock;
+  P.C = c; P.ldc = N; P.c_stride = M * N;
+  P.offsets = offsets; P.E = E;
+  P.M = static_cast<int>(M); P.N = static_cast<int>(N);
+  P.ntn = static_cast<int>((N + BN - 1) / BN);
+  const int64_t mtiles = (M + BM - 1) / BM;
+  const int grid = static_cast<int>(E * mtiles * P.ntn);
+  return launch<CfgMx, kSegKT, true, true, kStore, true>(P, grid, st);
 }
 
 }  // namespace moe

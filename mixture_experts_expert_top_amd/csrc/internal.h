@@ -55,8 +55,10 @@ hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
 hipError_t launch_mx_quant_rows(const bf16_t* src, int64_t rows, int64_t cols,
                                 uint8_t* codes, uint8_t* scales,
                                 hipStream_t s);
-hipError_t launch_mx_quant_tokens(const bf16_t* src, int64_t rows,
-                                  int64_t cols, const int32_t* seg, int nseg,
+// token-axis blocks; logical row r is src row gather[r] (gather may be null)
+hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
+                                  int64_t rows, int64_t cols,
+                                  const int32_t* seg, int nseg,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s);
 
@@ -80,5 +82,33 @@ hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
 hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
                       int64_t ldb, const int32_t* offsets, int E, int64_t Tk,
                       int64_t M, int64_t N, bf16_t* c, hipStream_t st);
+
+// MXFP8 grouped GEMMs (gemm.hip): codes + scale bytes, see the definitions
+hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
+                           const uint8_t* wq, const uint8_t* ws,
+                           const int32_t* offsets, int E, int64_t Tk,
+                           int64_t d, int64_t f, const float* w_perm,
+                           bf16_t* ab, bf16_t* s, uint8_t* sq, uint8_t* ss,
+                           hipStream_t st);
+hipError_t gemm_mx_fc2_fwd(const uint8_t* sq, const uint8_t* ss,
+                           const uint8_t* wq, const uint8_t* ws,
+                           const int32_t* offsets, int E, int64_t Tk,
+                           int64_t d, int64_t f, float* o, hipStream_t st);
+hipError_t gemm_mx_fc2_dgrad(const uint8_t* doq, const uint8_t* dos,
+                             const uint8_t* wtq, const uint8_t* wts,
+                             int64_t ldw, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t d, int64_t f,
+                             const bf16_t* ab, const float* w_perm,
+                             bf16_t* dab, uint8_t* dabq, uint8_t* dabs,
+                             float* dp_part, hipStream_t st);
+hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
+                             const uint8_t* wtq, const uint8_t* wts,
+                             int64_t ldw, const int32_t* offsets, int E,
+                             int64_t Tk, int64_t d, int64_t f, float* dxp,
+                             hipStream_t st);
+hipError_t gemm_mx_wgrad(const uint8_t* aq, const uint8_t* as,
+                         const uint8_t* bq, const uint8_t* bs, int64_t ldt,
+                         const int32_t* offsets, int E, int64_t M, int64_t N,
+                         bf16_t* c, hipStream_t st);
 
 }  // namespace moe

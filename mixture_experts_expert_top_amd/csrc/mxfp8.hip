@@ -96,7 +96,8 @@ __device__ void padded_prefix(const int32_t* seg, int nseg, int64_t rows,
 
 // Workgroup = one padded 32-row block x 256 columns; thread = column.
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
-    const bf16_t* __restrict__ src, int64_t rows, int64_t cols,
+    const bf16_t* __restrict__ src, const int32_t* __restrict__ gather,
+    int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg, int nseg, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t rows_pad) {
   __shared__ int s_pad[kMaxExperts + 1];
@@ -125,7 +126,12 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
 #pragma unroll
   for (int i = 0; i < kMxBlock; ++i) {
     const int64_t r = r0 + i;
-    v[i] = (r < r_end) ? bf2f(src[r * cols + c]) : 0.0f;
+    float x = 0.0f;
+    if (r < r_end) {
+      const int64_t sr = gather ? static_cast<int64_t>(gather[r]) : r;
+      x = bf2f(src[sr * cols + c]);
+    }
+    v[i] = x;
     amax = fmaxf(amax, fabsf(v[i]));
   }
   const int e = mx_scale_exp(amax);
@@ -162,14 +168,15 @@ hipError_t launch_mx_quant_rows(const bf16_t* src, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
-hipError_t launch_mx_quant_tokens(const bf16_t* src, int64_t rows,
-                                  int64_t cols, const int32_t* seg, int nseg,
+hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
+                                  int64_t rows, int64_t cols,
+                                  const int32_t* seg, int nseg,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(rows_pad / kMxBlock),
             static_cast<unsigned>((cols + 255) / 256));
-  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, s, src, rows,
-                     cols, seg, nseg, codes, scales, rows_pad);
+  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, s, src, gather,
+                     rows, cols, seg, nseg, codes, scales, rows_pad);
   return hipGetLastError();
 }
 

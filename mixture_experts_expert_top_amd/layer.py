@@ -11,6 +11,12 @@ With a ``timers`` object (see ``StageTimers``) the GEMMs are issued
 through the per-GEMM stage entry points instead of the fused ones, with
 HIP events recorded around each stage on the stream it runs on.
 
+``MoEPathMX`` is the same layer with MXFP8 GEMM operands: x is quantized
+along d before the permutation, the weights along their rows once per step
+(forward) and along their columns inside the backward, S and dAB inside the
+GEMM epilogues that produce them, and the weight-gradient operands along
+the rows of each expert.
+
 No arithmetic happens here: every step runs in the library's kernels.
 """
 
@@ -19,7 +25,8 @@ import contextlib
 import torch
 
 from . import moe
-from .moe import MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_PERMUTE
+from .moe import (MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_MLP_FWD,
+                  MOE_ENTRY_PERMUTE, MOE_MXFP8)
 
 
 class StageTimers:
@@ -162,6 +169,144 @@ class MoEPath:
             with timers.around("wgrad_gate_up"):
                 moe.moe_grouped_wgrad(self.dab, self.x_perm, self.offsets,
                                       self.dw_gu)
+        with _around(timers, "unpermute_dx"):
+            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+        return self.dx, self.dw_gu, self.dw2, self.dp
+
+
+class MoEPathMX(MoEPath):
+    """The layer with MXFP8 GEMM operands (see the module docstring)."""
+
+    def __init__(self, T, d, f, E, k, renorm=True, device="cuda",
+                 y_fp32=False):
+        super().__init__(T, d, f, E, k, renorm=renorm, prec=MOE_BF16,
+                         device=device, y_fp32=y_fp32)
+        self.prec = MOE_MXFP8
+        Tk = T * k
+        dev = self.x_perm.device
+        u8 = torch.uint8
+        z = lambda *s: torch.empty(*s, dtype=u8, device=dev)  # noqa: E731
+        self.xq, self.xs = z(T, d), z(T, d // 32)
+        self.xpq, self.xps = z(Tk, d), z(Tk, d // 32)
+        self.wguq, self.wgus = z(E, 2 * f, d), z(E, 2 * f, d // 32)
+        self.w2q, self.w2s = z(E, d, f), z(E, d, f // 32)
+        self.sq, self.ss = z(Tk, f), z(Tk, f // 32)
+        ws_f = moe.moe_workspace_bytes(MOE_ENTRY_MLP_FWD, MOE_MXFP8, T, E, k,
+                                       d, f)
+        self.ws_fwd = z(max(ws_f, 16))
+
+    def _alloc_bwd(self):
+        super()._alloc_bwd()
+        T, d, f, E, k = self.T, self.d, self.f, self.E, self.k
+        Tk = T * k
+        dev = self.x_perm.device
+        u8 = torch.uint8
+        z = lambda *s: torch.empty(*s, dtype=u8, device=dev)  # noqa: E731
+        tp = moe.moe_mxfp8_padded_rows(Tk, E)
+        self.tk_pad = tp
+        self.doq, self.dos = z(Tk, d), z(Tk, d // 32)
+        self.w2tq, self.w2ts = z(f, E * d), z(f, E * d // 32)
+        self.wgutq, self.wguts = z(d, E * 2 * f), z(d, E * 2 * f // 32)
+        self.dabq, self.dabs = z(Tk, 2 * f), z(Tk, 2 * f // 32)
+        self.dot, self.dots = z(d, tp), z(d, tp // 32)
+        self.st, self.sts = z(f, tp), z(f, tp // 32)
+        self.dabt, self.dabts = z(2 * f, tp), z(2 * f, tp // 32)
+        self.xpt, self.xpts = z(d, tp), z(d, tp // 32)
+        ws_b = moe.moe_workspace_bytes(MOE_ENTRY_MLP_BWD, MOE_MXFP8, T, E, k,
+                                       d, f)
+        self.ws_bwd = z(max(ws_b, 16))
+
+    def quantize_weights(self, w_gu, w2, timers=None):
+        """Row-wise MX codes of the weights for the forward GEMMs (done once
+        per optimizer step)."""
+        E, d, f = self.E, self.d, self.f
+        with _around(timers, "quant_weights"):
+            moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 0, None,
+                                   self.wguq.view(E * 2 * f, d),
+                                   self.wgus.view(E * 2 * f, d // 32))
+            moe.moe_mxfp8_quantize(w2.view(E * d, f), 0, None,
+                                   self.w2q.view(E * d, f),
+                                   self.w2s.view(E * d, f // 32))
+
+    def forward(self, x, w_gu, w2, w_g=None, bias=None, logits=None,
+                timers=None):
+        self.route(x, w_g, bias, logits, timers)
+        with _around(timers, "quant_x"):
+            moe.moe_mxfp8_quantize(x, 0, None, self.xq, self.xs)
+        with _around(timers, "permute"):
+            moe.moe_permute(MOE_MXFP8, self.topk_idx, self.topk_w, self.E,
+                            self.xq, self.xs, self.counts, self.offsets,
+                            self.pos, self.src, self.w_perm, self.xpq,
+                            self.xps, self.ws_permute)
+        self.quantize_weights(w_gu, w2, timers)
+        if timers is None:
+            moe.moe_grouped_mlp_fwd(MOE_MXFP8, self.xpq, self.xps,
+                                    self.offsets, self.wguq, self.wgus,
+                                    self.w2q, self.w2s, self.w_perm, self.ab,
+                                    self.s, self.o, self.ws_fwd)
+        else:
+            with timers.around("gate_up_swiglu_fwd"):
+                moe.moe_mx_gate_up_swiglu_fwd(
+                    self.xpq, self.xps, self.offsets, self.wguq, self.wgus,
+                    self.w_perm, self.ab, self.s, self.sq, self.ss)
+            with timers.around("down_fwd"):
+                moe.moe_mx_down_fwd(self.sq, self.ss, self.offsets, self.w2q,
+                                    self.w2s, self.o)
+        with _around(timers, "unpermute_y"):
+            moe.moe_unpermute(self.o, self.pos, None, self.y)
+        self._x = x
+        return self.y
+
+    def backward(self, dy, w_gu, w2, timers=None):
+        if not self._bwd_ready:
+            self._alloc_bwd()
+        E, d, f = self.E, self.d, self.f
+        with _around(timers, "permute_dy"):
+            moe.moe_permute_rows(MOE_BF16, self.pos, dy, None,
+                                 self.dout_perm, None)
+        with _around(timers, "permute_x"):
+            moe.moe_permute_rows(MOE_BF16, self.pos, self._x, None,
+                                 self.x_perm, None)
+        if timers is None:
+            moe.moe_grouped_mlp_bwd(MOE_MXFP8, self.dout_perm, self.x_perm,
+                                    self.offsets, self.pos, w_gu, w2, self.ab,
+                                    self.s, self.w_perm, self.dx_perm,
+                                    self.dw_gu, self.dw2, self.dp,
+                                    self.ws_bwd)
+        else:
+            # the same kernels in the same order as moe_grouped_mlp_bwd
+            tp = self.tk_pad
+            with timers.around("quant_bwd_operands"):
+                moe.moe_mxfp8_quantize(self.dout_perm, 0, None, self.doq,
+                                       self.dos)
+                moe.moe_mxfp8_quantize(w2.view(E * d, f), 1, None, self.w2tq,
+                                       self.w2ts, E * d)
+                moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 1, None,
+                                       self.wgutq, self.wguts, E * 2 * f)
+            with timers.around("down_swiglu_bwd"):
+                moe.moe_mx_down_swiglu_bwd(
+                    self.doq, self.dos, self.offsets, self.w2tq, self.w2ts,
+                    self.ab, self.w_perm, self.dab, self.dabq, self.dabs,
+                    self.dp_part)
+            with timers.around("dp_reduce"):
+                moe.moe_dp_reduce(self.dp_part, self.pos, self.dp)
+            with timers.around("gate_up_dgrad"):
+                moe.moe_mx_gate_up_dgrad(self.dabq, self.dabs, self.offsets,
+                                         self.wgutq, self.wguts, self.dx_perm)
+            with timers.around("quant_tokens"):
+                for src, cq, cs in ((self.dout_perm, self.dot, self.dots),
+                                    (self.s, self.st, self.sts),
+                                    (self.dab, self.dabt, self.dabts),
+                                    (self.x_perm, self.xpt, self.xpts)):
+                    moe.moe_mxfp8_quantize(src, 1, self.offsets, cq, cs, tp)
+            Tk = self.T * self.k
+            with timers.around("wgrad_down"):
+                moe.moe_mx_grouped_wgrad(self.dot, self.dots, self.st,
+                                         self.sts, self.offsets, Tk, self.dw2)
+            with timers.around("wgrad_gate_up"):
+                moe.moe_mx_grouped_wgrad(self.dabt, self.dabts, self.xpt,
+                                         self.xpts, self.offsets, Tk,
+                                         self.dw_gu)
         with _around(timers, "unpermute_dx"):
             moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
         return self.dx, self.dw_gu, self.dw2, self.dp

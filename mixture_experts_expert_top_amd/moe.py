@@ -28,7 +28,8 @@ EXPORTED = [
     "moe_mxfp8_padded_rows", "moe_workspace_bytes", "moe_dp_tiles",
     "moe_gate_up_swiglu_fwd", "moe_down_fwd", "moe_down_swiglu_bwd",
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
-    "moe_row_planes",
+    "moe_row_planes", "moe_mx_gate_up_swiglu_fwd", "moe_mx_down_fwd",
+    "moe_mx_down_swiglu_bwd", "moe_mx_gate_up_dgrad", "moe_mx_grouped_wgrad",
 ]
 
 
@@ -76,6 +77,15 @@ def _load():
         "moe_grouped_wgrad": (I32, [P, I64, P, I64, P, I32, I64, I64, I64, P,
                                     P]),
         "moe_dp_reduce": (I32, [P, I32, P, I64, I32, P, P]),
+        "moe_mx_gate_up_swiglu_fwd": (I32, [P, P, P, I32, I64, I64, I64, P,
+                                            P, P, P, P, P, P, P]),
+        "moe_mx_down_fwd": (I32, [P, P, P, I32, I64, I64, I64, P, P, P, P]),
+        "moe_mx_down_swiglu_bwd": (I32, [P, P, P, I32, I64, I64, I64, P, P,
+                                         P, P, P, P, P, P, P]),
+        "moe_mx_gate_up_dgrad": (I32, [P, P, P, I32, I64, I64, I64, P, P, P,
+                                       P]),
+        "moe_mx_grouped_wgrad": (I32, [P, P, P, P, I64, P, I32, I64, I64,
+                                       I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -366,3 +376,96 @@ def moe_dp_reduce(dp_part, pos, dp, stream=None):
     _check("moe_dp_reduce", lib.moe_dp_reduce(
         _p(dp_part), dp_part.shape[1], _p(pos), T, k, _p(dp),
         _stream(stream)))
+
+
+# ------------------------------------------------------------- MX stages
+# Codes are uint8 tensors, scales uint8 tensors with one byte per 32 codes
+# along the reduction axis (layouts in include/moe.h).
+
+def moe_mx_gate_up_swiglu_fwd(xq, xs, offsets, wq, ws, w_perm, ab_saved,
+                              s_saved, sq, ss, stream=None):
+    Tk, d = xq.shape
+    E, two_f, _ = wq.shape
+    f = two_f // 2
+    _want(xq, "xq", torch.uint8)
+    _want(xs, "xs", torch.uint8, (Tk, d // 32))
+    _want(wq, "wq", torch.uint8, (E, 2 * f, d))
+    _want(ws, "ws", torch.uint8, (E, 2 * f, d // 32))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
+    _want(sq, "sq", torch.uint8, (Tk, f))
+    _want(ss, "ss", torch.uint8, (Tk, f // 32))
+    _check("moe_mx_gate_up_swiglu_fwd", lib.moe_mx_gate_up_swiglu_fwd(
+        _p(xq), _p(xs), _p(offsets), E, Tk, d, f, _p(wq), _p(ws),
+        _p(w_perm), _p(ab_saved), _p(s_saved), _p(sq), _p(ss),
+        _stream(stream)))
+
+
+def moe_mx_down_fwd(sq, ss, offsets, wq, ws, out_perm, stream=None):
+    Tk, f = sq.shape
+    E, d, _ = wq.shape
+    _want(sq, "sq", torch.uint8)
+    _want(ss, "ss", torch.uint8, (Tk, f // 32))
+    _want(wq, "wq", torch.uint8, (E, d, f))
+    _want(ws, "ws", torch.uint8, (E, d, f // 32))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _check("moe_mx_down_fwd", lib.moe_mx_down_fwd(
+        _p(sq), _p(ss), _p(offsets), E, Tk, d, f, _p(wq), _p(ws),
+        _p(out_perm), _stream(stream)))
+
+
+def moe_mx_down_swiglu_bwd(doq, dos, offsets, w2tq, w2ts, ab_saved, w_perm,
+                           dab, dabq, dabs, dp_part, stream=None):
+    Tk, d = doq.shape
+    f, Ed = w2tq.shape
+    E = offsets.numel() - 1
+    _want(doq, "doq", torch.uint8)
+    _want(dos, "dos", torch.uint8, (Tk, d // 32))
+    _want(w2tq, "w2tq", torch.uint8, (f, E * d))
+    _want(w2ts, "w2ts", torch.uint8, (f, E * d // 32))
+    _want(offsets, "offsets", torch.int32)
+    _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
+    _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
+    _want(dab, "dab", torch.bfloat16, (Tk, 2 * f))
+    _want(dabq, "dabq", torch.uint8, (Tk, 2 * f))
+    _want(dabs, "dabs", torch.uint8, (Tk, 2 * f // 32))
+    _want(dp_part, "dp_part", torch.float32, (Tk, moe_dp_tiles(f)))
+    _check("moe_mx_down_swiglu_bwd", lib.moe_mx_down_swiglu_bwd(
+        _p(doq), _p(dos), _p(offsets), E, Tk, d, f, _p(w2tq), _p(w2ts),
+        _p(ab_saved), _p(w_perm), _p(dab), _p(dabq), _p(dabs), _p(dp_part),
+        _stream(stream)))
+
+
+def moe_mx_gate_up_dgrad(dabq, dabs, offsets, wgutq, wguts, dx_perm,
+                         stream=None):
+    Tk, two_f = dabq.shape
+    f = two_f // 2
+    d = wgutq.shape[0]
+    E = offsets.numel() - 1
+    _want(dabq, "dabq", torch.uint8)
+    _want(dabs, "dabs", torch.uint8, (Tk, two_f // 32))
+    _want(wgutq, "wgutq", torch.uint8, (d, E * two_f))
+    _want(wguts, "wguts", torch.uint8, (d, E * two_f // 32))
+    _want(offsets, "offsets", torch.int32)
+    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _check("moe_mx_gate_up_dgrad", lib.moe_mx_gate_up_dgrad(
+        _p(dabq), _p(dabs), _p(offsets), E, Tk, d, f, _p(wgutq), _p(wguts),
+        _p(dx_perm), _stream(stream)))
+
+
+def moe_mx_grouped_wgrad(aq, as_, bq, bs, offsets, Tk, c, stream=None):
+    M, ldt = aq.shape
+    N = bq.shape[0]
+    E = offsets.numel() - 1
+    _want(aq, "aq", torch.uint8)
+    _want(as_, "as", torch.uint8, (M, ldt // 32))
+    _want(bq, "bq", torch.uint8, (N, ldt))
+    _want(bs, "bs", torch.uint8, (N, ldt // 32))
+    _want(offsets, "offsets", torch.int32)
+    _want(c, "c", torch.bfloat16, (E, M, N))
+    _check("moe_mx_grouped_wgrad", lib.moe_mx_grouped_wgrad(
+        _p(aq), _p(as_), _p(bq), _p(bs), ldt, _p(offsets), E, Tk, M, N,
+        _p(c), _stream(stream)))

@@ -4,6 +4,8 @@ rejects bad calls before anything is launched (fake device pointers are
 safe here because validation fails first)."""
 
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -116,6 +118,41 @@ def test_mlp_bwd_validation():
     assert f(*bad, ws, None) == INVALID
 
 
+def test_mx_mlp_validation():
+    f = L.moe_grouped_mlp_fwd
+    ws = L.moe_workspace_bytes(1, MX, 64, 4, 2, 128, 128)
+    assert ws >= 128 * 128 + 128 * 4                  # S codes and scales
+    ok = [MX, A, A, A, 4, 128, 128, 128, A, A, A, A, A, A, A, A, A]
+    assert f(*ok, ws - 1, None) == WS
+    bad = list(ok)
+    bad[6] = 96                                       # d % 128 != 0
+    assert f(*bad, ws, None) == INVALID
+    assert b"128" in L.moe_last_error()
+    bad = list(ok)
+    bad[2] = None                                     # x_perm_scales
+    assert f(*bad, ws, None) == INVALID
+    b = L.moe_grouped_mlp_bwd
+    wsb = L.moe_workspace_bytes(2, MX, 64, 4, 2, 128, 128)
+    assert wsb > L.moe_workspace_bytes(2, BF16, 64, 4, 2, 128, 128)
+    args = [MX, A, A, A, A, 64, 2, 4, 128, 128, A, A, A, A, A, A, A, A, A, A]
+    assert b(*args, wsb - 1, None) == WS
+    args[9] = 160                                     # f % 128 != 0
+    assert b(*args, wsb, None) == INVALID
+
+
+def test_mx_stage_validation():
+    assert L.moe_mx_down_fwd(A, A, A, 4, 64, 128, 96, A, A, A,
+                             None) == INVALID
+    assert L.moe_mx_gate_up_dgrad(A, None, A, 4, 64, 128, 128, A, A, A,
+                                  None) == INVALID
+    # ldt must cover the padded token layout
+    tp = L.moe_mxfp8_padded_rows(128, 4)
+    assert L.moe_mx_grouped_wgrad(A, A, A, A, tp - 128, A, 4, 128, 64, 64,
+                                  A, None) == INVALID
+    assert L.moe_mx_grouped_wgrad(A, A, A, A, tp + 64, A, 4, 128, 64, 64,
+                                  A, None) == INVALID
+
+
 def test_unpermute_validation():
     assert L.moe_unpermute(A, 0, 1, A, None, 8, 0, 64, 0, A, None) == INVALID
     assert L.moe_unpermute(A, 1, 1, A, None, 8, 2, 60, 0, A, None) == INVALID
@@ -128,10 +165,20 @@ def test_unpermute_validation():
 
 
 def test_padded_rows():
-    assert L.moe_mxfp8_padded_rows(100, 1) == 256
-    assert L.moe_mxfp8_padded_rows(64, 4) == 640
-    assert L.moe_mxfp8_padded_rows(128, 1) == 256
+    assert L.moe_mxfp8_padded_rows(100, 1) == 128
+    assert L.moe_mxfp8_padded_rows(64, 4) == 512
+    assert L.moe_mxfp8_padded_rows(128, 1) == 128
     assert L.moe_mxfp8_padded_rows(-1, 1) == 0
+    # a bound on the padded layout of any split of the rows into segments,
+    # tight when every segment length is 1 mod 128
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        nseg = int(rng.integers(1, 20))
+        lens = rng.integers(0, 400, nseg)
+        need = int(sum((n + 127) // 128 * 128 for n in lens))
+        bound = L.moe_mxfp8_padded_rows(int(lens.sum()), nseg)
+        assert bound >= need and bound % 128 == 0
+    assert L.moe_mxfp8_padded_rows(3 * 129, 3) == 3 * 256
 
 
 def test_quantize_validation():
@@ -139,5 +186,6 @@ def test_quantize_validation():
     assert q(A, 8, 48, 0, None, 1, A, A, 0, None) == INVALID   # cols % 32
     assert q(A, 8, 64, 2, None, 1, A, A, 0, None) == INVALID   # axis
     assert q(A, 8, 64, 1, None, 2, A, A, 1024, None) == INVALID  # NULL segs
-    assert q(A, 100, 64, 1, None, 1, A, A, 128, None) == INVALID  # rows_pad
+    assert q(A, 200, 64, 1, None, 1, A, A, 128, None) == INVALID  # rows_pad
+    assert q(A, 100, 64, 1, None, 1, A, A, 192, None) == INVALID  # % 128
     assert q(None, 8, 64, 0, None, 1, A, A, 0, None) == INVALID

@@ -1,0 +1,429 @@
+"""GPU parity of the MXFP8 grouped GEMMs and of the MXFP8 layer.
+
+Stage tests: every MX stage entry point against the matching oracle step on
+the very same inputs.  Both sides quantize the same bf16 tensors, each with
+its own codec (the GPU's codes are checked bit-exact against the oracle's
+first), so the GEMM inputs are identical.  What is left is the arithmetic
+of gfx950's block-scaled MFMA, which does not sum its 64 exact products at
+fp32 precision: measured on random E4M3 operands over the whole exponent
+range, its result differs from the exact sum by up to 2^-11.5 of
+sum_k |a_k b_k| (exact for operands of a narrow exponent range).  The bars
+are therefore, element by element, with MFMA(i, j) = 2^-10 sum_k |a_ik b_jk|:
+  * fp32 outputs: |gpu - ref| <= MFMA + 1e-6 rms(ref);
+  * bf16 outputs: |gpu - ref| <= 2^-8 |ref| + MFMA (propagated through the
+    epilogue's SwiGLU or its gradient where there is one) + 1e-6 rms(ref);
+  * MX outputs of the epilogues (S along f, dAB along 2f) are quantized
+    from the kernel's fp32 values: each decoded GPU value lies within half
+    an E4M3 step at the GPU's block scale (or the saturation gap) plus the
+    propagated MFMA bound of the float64 value, and the block scales agree
+    with the oracle's on all but a few blocks.
+Layer tests: MoEPathMX forward and backward against the MX-emulating oracle
+(oracle/moe_mx.py).  Quantization is discontinuous, so the MFMA's rounding
+moves single codes by a whole E4M3 step (12.5%) wherever a value sits next
+to a rounding point; in a small layer one such step dominates the maximum
+error of an output that sums few terms (perturbing the float64 oracle's
+own AB and dAB by 2^-16 relative noise moves its max|err|/rms by 0.1-0.2
+at these sizes while its relative RMS error stays near 1e-3).  The small
+layers are therefore gated on the relative RMS error, at 1e-2, with
+max|err|/rms reported; the 6e-2 max|err|/rms bar is applied at the full
+16384-token Mixtral-shaped size (test_gpu_mx_full.py), where every output
+sums thousands of terms.  Stage entry points == fused entry points bitwise.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_expert_top_amd import inputs as I
+from oracle import moe_mx as X
+from oracle import moe_ref as R
+from oracle import mx_ref as M
+
+gpu = pytest.mark.gpu
+if torch.cuda.is_available():
+    from mixture_experts_expert_top_amd import moe
+    from mixture_experts_expert_top_amd.layer import MoEPathMX, StageTimers
+
+TOL_MX_RMS = 1e-2
+MFMA_REL = 2.0 ** -10        # block-scaled MFMA error bound / sum |a b|
+
+SHAPES = [
+    # name, T, d, f, E, k, router bias
+    ("small", 64, 128, 128, 4, 2, False),
+    ("ragged", 300, 256, 384, 5, 2, False),
+    ("skew", 1000, 256, 256, 16, 4, True),
+    ("one_token", 1, 128, 128, 4, 4, False),
+    ("deep", 700, 1024, 256, 3, 1, False),
+]
+IDS = [s[0] for s in SHAPES]
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def h64(t):
+    return t.double().cpu().numpy()
+
+
+def u8(t):
+    return t.cpu().numpy()
+
+
+def rms(v):
+    v = np.asarray(v, dtype=np.float64)
+    return float(np.sqrt(np.mean(v * v))) if v.size else 0.0
+
+
+def excess(got, ref, bound):
+    """max |got - ref| / bound (elementwise); <= 1 passes."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0
+    b = bound + 1e-6 * max(rms(ref), 1e-300)
+    return float(np.max(np.abs(got - ref) / b))
+
+
+def mfma_err(a, b):
+    """Elementwise MFMA bound of a @ b.T for dequantized operands."""
+    return MFMA_REL * (np.abs(a) @ np.abs(b).T)
+
+
+def rel(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    return float(np.max(np.abs(got - ref))) / max(rms(ref), 1e-300)
+
+
+def rel_rms(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    return rms(got - ref) / max(rms(ref), 1e-300)
+
+
+def mx_rounding_check(codes, scales, ref, slack):
+    """Decoded GPU MX values vs float64 values ``ref`` [rows, C]: within
+    half an E4M3 step at the GPU's block scale (or the saturation gap)
+    plus ``slack`` (the propagated arithmetic bound of the GPU's fp32
+    input).  Returns (worst ratio to the bound, fraction of blocks whose
+    scale differs from the oracle's scale of ref)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0, 0.0
+    dec = M.dequantize_rows(codes, scales)
+    e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    a = np.abs(ref) / np.ldexp(1.0, e)
+    _, ex = np.frexp(a)
+    binade = np.maximum(ex - 1, -6)
+    half = np.ldexp(1.0, binade - 4 + e)               # half an E4M3 step
+    sat = np.maximum(np.abs(ref) - 448.0 * np.ldexp(1.0, e), 0.0)
+    bound = np.maximum(half, sat) + 1.01 * slack + 1e-30
+    ratio = float(np.max(np.abs(dec - ref) / bound))
+    _, ref_scales = M.quantize_rows(ref)
+    return ratio, float(np.mean(ref_scales != scales))
+
+
+def sig(a):
+    return 1.0 / (1.0 + np.exp(-a))
+
+
+def _plan(T, E, k, bias, seed):
+    wl = I.Workload("s", T, 8, 8, E, k, router_bias=bias)
+    L = I.make_inputs(wl, seed=seed, with_weights=False,
+                      with_dy=False)["logits"].double().numpy()
+    idx, p = R.topk_route(L, k)
+    counts, offsets, pos, src = R.dispatch_plan(idx, E)
+    w_perm = R.permuted_weights(p, pos).astype(np.float32)
+    dev = _dev()
+    return dict(
+        idx=idx, counts=counts, offsets=offsets, pos=pos,
+        w_perm=w_perm.astype(np.float64),
+        offsets_d=torch.as_tensor(offsets.astype(np.int32), device=dev),
+        pos_d=torch.as_tensor(pos.astype(np.int32), device=dev),
+        w_perm_d=torch.as_tensor(w_perm, device=dev))
+
+
+def _segs(P, E):
+    for e in range(E):
+        yield e, int(P["offsets"][e]), int(P["offsets"][e + 1])
+
+
+def _quant_rows_both(t):
+    """GPU and oracle row quantization of a bf16 tensor [..., C] (viewed as
+    rows); asserts identical codes and returns (codes_d, scales_d,
+    dequantized float64 array with t's shape)."""
+    C = t.shape[-1]
+    flat = t.reshape(-1, C)
+    q = torch.empty(flat.shape, dtype=torch.uint8, device=t.device)
+    s = torch.empty(flat.shape[0], C // 32, dtype=torch.uint8,
+                    device=t.device)
+    moe.moe_mxfp8_quantize(flat, 0, None, q, s)
+    cq, cs = M.quantize_rows(h64(flat))
+    np.testing.assert_array_equal(u8(q), cq)
+    np.testing.assert_array_equal(u8(s), cs)
+    return (q.reshape(t.shape), s.reshape(*t.shape[:-1], C // 32),
+            M.dequantize_rows(cq, cs).reshape(t.shape))
+
+
+def _quant_cols_both(w):
+    """Column-wise (per expert, along the middle axis) quantization of
+    w [E, R, C] on both sides.  GPU: w viewed as [E*R, C], axis 1, one
+    segment, giving [C][E*R]; oracle: each w[e]^T along its rows.  Returns
+    (codes_d, scales_d, dequantized [E, R, C])."""
+    E, Rr, C = w.shape
+    q = torch.empty(C, E * Rr, dtype=torch.uint8, device=w.device)
+    s = torch.empty(C, E * Rr // 32, dtype=torch.uint8, device=w.device)
+    moe.moe_mxfp8_quantize(w.reshape(E * Rr, C), 1, None, q, s, E * Rr)
+    wh = h64(w)
+    deq = np.zeros(wh.shape)
+    for e in range(E):
+        cq, cs = M.quantize_rows(wh[e].T)                 # [C][R]
+        np.testing.assert_array_equal(u8(q[:, e * Rr:(e + 1) * Rr]), cq)
+        np.testing.assert_array_equal(
+            u8(s[:, e * Rr // 32:(e + 1) * Rr // 32]), cs)
+        deq[e] = M.dequantize_rows(cq, cs).T
+    return q, s, deq
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias", SHAPES, ids=IDS)
+def test_mx_gate_up_swiglu_stage(name, T, d, f, E, k, bias):
+    dev = _dev()
+    P = _plan(T, E, k, bias, seed=21)
+    Tk = T * k
+    xp = I.make_tensor((Tk, d), seed=1, device=dev)
+    xp[::7] *= 50.0                                    # block-scale spread
+    w_gu = I.make_tensor((E, 2 * f, d), seed=2, scale=0.1, device=dev)
+    xq, xs, xd = _quant_rows_both(xp)
+    wq, ws, wd = _quant_rows_both(w_gu)
+    ab = torch.empty(Tk, 2 * f, dtype=torch.bfloat16, device=dev)
+    s = torch.empty(Tk, f, dtype=torch.bfloat16, device=dev)
+    sq = torch.empty(Tk, f, dtype=torch.uint8, device=dev)
+    ss = torch.empty(Tk, f // 32, dtype=torch.uint8, device=dev)
+    moe.moe_mx_gate_up_swiglu_fwd(xq, xs, P["offsets_d"], wq, ws,
+                                  P["w_perm_d"], ab, s, sq, ss)
+    torch.cuda.synchronize()
+    ab_ref = np.zeros((Tk, 2 * f))
+    ab_err = np.zeros((Tk, 2 * f))
+    s_ref = np.zeros((Tk, f))
+    for e, r0, r1 in _segs(P, E):
+        ab_ref[r0:r1] = R.gate_up(xd[r0:r1], wd[e])
+        ab_err[r0:r1] = mfma_err(xd[r0:r1], wd[e])
+        s_ref[r0:r1] = R.scaled_swiglu(ab_ref[r0:r1], P["w_perm"][r0:r1])
+    g, u = ab_ref[:, :f], ab_ref[:, f:]
+    dg, du = ab_err[:, :f], ab_err[:, f:]
+    sg = sig(g)
+    s_err = np.abs(P["w_perm"])[:, None] * (
+        np.abs(sg * (1 + g * (1 - sg)) * u) * dg + np.abs(g * sg) * du)
+    ex = {"ab": excess(h64(ab), ab_ref, 2.0 ** -8 * np.abs(ab_ref) + ab_err),
+          "s": excess(h64(s), s_ref, 2.0 ** -8 * np.abs(s_ref) + s_err)}
+    ratio, sdiff = mx_rounding_check(u8(sq), u8(ss), s_ref, s_err)
+    print(name, ex, "S-mx bound ratio", ratio, "scale diff", sdiff)
+    assert max(ex.values()) <= 1.0, ex
+    assert ratio <= 1.0 and sdiff <= 1e-2
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias", SHAPES, ids=IDS)
+def test_mx_down_stage(name, T, d, f, E, k, bias):
+    dev = _dev()
+    P = _plan(T, E, k, bias, seed=22)
+    Tk = T * k
+    s = I.make_tensor((Tk, f), seed=3, device=dev)
+    w2 = I.make_tensor((E, d, f), seed=4, scale=0.1, device=dev)
+    sq, ss, sd = _quant_rows_both(s)
+    wq, ws, wd = _quant_rows_both(w2)
+    o = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    moe.moe_mx_down_fwd(sq, ss, P["offsets_d"], wq, ws, o)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((Tk, d))
+    o_err = np.zeros((Tk, d))
+    for e, r0, r1 in _segs(P, E):
+        o_ref[r0:r1] = R.down(sd[r0:r1], wd[e])
+        o_err[r0:r1] = mfma_err(sd[r0:r1], wd[e])
+    ex = excess(h64(o).sum(axis=0), o_ref, o_err)
+    print(name, "o", ex, "max|err|/rms", rel(h64(o).sum(axis=0), o_ref))
+    assert ex <= 1.0
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias", SHAPES, ids=IDS)
+def test_mx_down_swiglu_bwd_stage(name, T, d, f, E, k, bias):
+    dev = _dev()
+    P = _plan(T, E, k, bias, seed=23)
+    Tk = T * k
+    do = I.make_tensor((Tk, d), seed=5, device=dev)
+    ab = I.make_tensor((Tk, 2 * f), seed=6, scale=2.0, device=dev)
+    w2 = I.make_tensor((E, d, f), seed=7, scale=0.1, device=dev)
+    doq, dos, dod = _quant_rows_both(do)
+    w2tq, w2ts, w2c = _quant_cols_both(w2)
+    nt = moe.moe_dp_tiles(f)
+    dab = torch.empty(Tk, 2 * f, dtype=torch.bfloat16, device=dev)
+    dabq = torch.empty(Tk, 2 * f, dtype=torch.uint8, device=dev)
+    dabs = torch.empty(Tk, 2 * f // 32, dtype=torch.uint8, device=dev)
+    dp_part = torch.empty(Tk, nt, dtype=torch.float32, device=dev)
+    moe.moe_mx_down_swiglu_bwd(doq, dos, P["offsets_d"], w2tq, w2ts, ab,
+                               P["w_perm_d"], dab, dabq, dabs, dp_part)
+    torch.cuda.synchronize()
+    abh = h64(ab)
+    dab_ref = np.zeros((Tk, 2 * f))
+    dp_ref = np.zeros(Tk)
+    ds_err = np.zeros((Tk, f))
+    for e, r0, r1 in _segs(P, E):
+        dab_ref[r0:r1], dp_ref[r0:r1] = R.down_backward(
+            dod[r0:r1], abh[r0:r1], P["w_perm"][r0:r1], w2c[e])
+        ds_err[r0:r1] = mfma_err(dod[r0:r1], w2c[e].T)
+    g, u = abh[:, :f], abh[:, f:]
+    sg = sig(g)
+    w = np.abs(P["w_perm"])[:, None]
+    dab_err = np.concatenate([w * np.abs(u * sg * (1 + g * (1 - sg))) * ds_err,
+                              w * np.abs(g * sg) * ds_err], axis=1)
+    dp_err = np.sum(np.abs(g * sg * u) * ds_err, axis=1)
+    ex = excess(h64(dab), dab_ref, 2.0 ** -8 * np.abs(dab_ref) + dab_err)
+    dp_ex = excess(h64(dp_part).sum(axis=1), dp_ref, dp_err)
+    ratio, sdiff = mx_rounding_check(u8(dabq), u8(dabs), dab_ref, dab_err)
+    print(name, "dab", ex, "dp", dp_ex, "dAB-mx", ratio, sdiff)
+    assert ex <= 1.0 and dp_ex <= 1.0
+    assert ratio <= 1.0 and sdiff <= 1e-2
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias", SHAPES, ids=IDS)
+def test_mx_gate_up_dgrad_stage(name, T, d, f, E, k, bias):
+    dev = _dev()
+    P = _plan(T, E, k, bias, seed=24)
+    Tk = T * k
+    dab = I.make_tensor((Tk, 2 * f), seed=8, device=dev)
+    w_gu = I.make_tensor((E, 2 * f, d), seed=9, scale=0.1, device=dev)
+    dabq, dabs, dabd = _quant_rows_both(dab)
+    wq, ws, wc = _quant_cols_both(w_gu)
+    dx = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    moe.moe_mx_gate_up_dgrad(dabq, dabs, P["offsets_d"], wq, ws, dx)
+    torch.cuda.synchronize()
+    dx_ref = np.zeros((Tk, d))
+    dx_err = np.zeros((Tk, d))
+    for e, r0, r1 in _segs(P, E):
+        dx_ref[r0:r1] = R.gate_up_dgrad(dabd[r0:r1], wc[e])
+        dx_err[r0:r1] = mfma_err(dabd[r0:r1], wc[e].T)
+    ex = excess(h64(dx).sum(axis=0), dx_ref, dx_err)
+    print(name, "dx", ex, "max|err|/rms", rel(h64(dx).sum(axis=0), dx_ref))
+    assert ex <= 1.0
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias", SHAPES, ids=IDS)
+def test_mx_wgrad_stage(name, T, d, f, E, k, bias):
+    dev = _dev()
+    P = _plan(T, E, k, bias, seed=25)
+    Tk = T * k
+    a = I.make_tensor((Tk, d), seed=10, device=dev)
+    b = I.make_tensor((Tk, f), seed=11, device=dev)
+    a[::5] *= 30.0
+    tp = moe.moe_mxfp8_padded_rows(Tk, E)
+    qs = []
+    for t in (a, b):
+        C = t.shape[1]
+        q = torch.empty(C, tp, dtype=torch.uint8, device=dev)
+        s = torch.empty(C, tp // 32, dtype=torch.uint8, device=dev)
+        moe.moe_mxfp8_quantize(t, 1, P["offsets_d"], q, s, tp)
+        qs += [q, s]
+    c = torch.full((E, d, f), 7.0, dtype=torch.bfloat16, device=dev)
+    moe.moe_mx_grouped_wgrad(qs[0], qs[1], qs[2], qs[3], P["offsets_d"], Tk,
+                             c)
+    torch.cuda.synchronize()
+    ad = X.mx_tokens(h64(a), P["offsets"])
+    bd = X.mx_tokens(h64(b), P["offsets"])
+    c_ref = np.zeros((E, d, f))
+    c_err = np.zeros((E, d, f))
+    for e, r0, r1 in _segs(P, E):
+        if r1 > r0:
+            c_ref[e] = R.wgrad(ad[r0:r1], bd[r0:r1])
+            c_err[e] = mfma_err(ad[r0:r1].T, bd[r0:r1].T)
+    ex = excess(h64(c), c_ref, 2.0 ** -8 * np.abs(c_ref) + c_err)
+    print(name, "c", ex)
+    assert ex <= 1.0
+    for e in np.nonzero(P["counts"] == 0)[0]:
+        assert torch.count_nonzero(c[e]).item() == 0
+
+
+# ------------------------------------------------------------------ layer
+
+LAYER_SHAPES = [
+    ("small", 64, 128, 128, 4, 2, False, 0.0),
+    ("ragged", 300, 256, 384, 5, 2, False, 0.01),
+    ("skew", 600, 128, 256, 16, 4, True, 0.0),
+    ("outliers", 400, 256, 256, 8, 2, False, 0.05),
+]
+
+
+def _run_mx_layer(T, d, f, E, k, bias, outliers, seed, timers=None):
+    dev = _dev()
+    inp = I.make_custom(T, d, f, E, k, seed=seed, device=dev,
+                        router_bias=bias, outlier_frac=outliers)
+    path = MoEPathMX(T, d, f, E, k, device=dev)
+    path.forward(inp["x"], inp["w_gu"], inp["w2"], logits=inp["logits"],
+                 timers=timers)
+    path.backward(inp["dy"], inp["w_gu"], inp["w2"], timers=timers)
+    torch.cuda.synchronize()
+    return inp, path
+
+
+@gpu
+@pytest.mark.parametrize("name,T,d,f,E,k,bias,outliers", LAYER_SHAPES,
+                         ids=[s[0] for s in LAYER_SHAPES])
+def test_mx_layer_parity(name, T, d, f, E, k, bias, outliers):
+    inp, path = _run_mx_layer(T, d, f, E, k, bias, outliers, seed=len(name))
+    h = {n: (h64(v) if v is not None and v.is_floating_point() else v)
+         for n, v in inp.items()}
+    fwd = X.moe_forward_mx(h["x"], h["logits"], h["w_gu"], h["w2"], k)
+    bwd = X.moe_backward_mx(fwd, h["dy"], h["w_gu"], h["w2"])
+    np.testing.assert_array_equal(path.topk_idx.cpu().numpy(), fwd["idx"])
+    np.testing.assert_array_equal(path.pos.cpu().numpy(), fwd["pos"])
+    gpu_out = {"y": path.y, "dx": path.dx, "dw_gu": path.dw_gu,
+               "dw2": path.dw2, "dp": path.dp}
+    ref = {"y": fwd["y"], "dx": bwd["dx"], "dw_gu": bwd["dw_gu"],
+           "dw2": bwd["dw2"], "dp": bwd["dp"]}
+    bar = {n: rel_rms(h64(gpu_out[n]), ref[n]) for n in gpu_out}
+    mx_max = {n: rel(h64(gpu_out[n]), ref[n]) for n in gpu_out}
+    # distance from the unquantized layer: reported, not gated
+    efwd = R.moe_forward(h["x"], h["logits"], h["w_gu"], h["w2"], k)
+    ebwd = R.moe_backward(efwd, h["dy"], h["w_gu"], h["w2"])
+    exact = {"y": rel(h64(path.y), efwd["y"]),
+             "dx": rel(h64(path.dx), ebwd["dx"]),
+             "dw_gu": rel(h64(path.dw_gu), ebwd["dw_gu"]),
+             "dw2": rel(h64(path.dw2), ebwd["dw2"]),
+             "dp": rel(h64(path.dp), ebwd["dp"])}
+    print(name, "vs MX oracle: relative RMS",
+          {n: f"{v:.2e}" for n, v in bar.items()}, "max|err|/rms",
+          {n: f"{v:.2e}" for n, v in mx_max.items()},
+          "vs exact oracle max|err|/rms",
+          {n: f"{v:.2e}" for n, v in exact.items()})
+    bad = {n: v for n, v in bar.items() if not v <= TOL_MX_RMS}
+    assert not bad, bad
+    for e in np.nonzero(fwd["counts"] == 0)[0]:
+        assert torch.count_nonzero(path.dw_gu[e]).item() == 0
+        assert torch.count_nonzero(path.dw2[e]).item() == 0
+
+
+@gpu
+def test_mx_stage_entries_equal_fused_entries():
+    outs = []
+    for timers in (None, StageTimers()):
+        _, path = _run_mx_layer(500, 256, 256, 6, 2, False, 0.02, seed=9,
+                                timers=timers)
+        outs.append([t.clone() for t in (path.y, path.dx, path.dw_gu,
+                                         path.dw2, path.dp)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@gpu
+def test_mx_layer_deterministic():
+    outs = []
+    for _ in range(2):
+        _, path = _run_mx_layer(300, 256, 384, 5, 2, False, 0.01, seed=3)
+        outs.append([t.clone() for t in (path.y, path.dx, path.dw_gu,
+                                         path.dw2, path.dp)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
