@@ -10,7 +10,9 @@ of dX.  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer,
 forward+backward in bf16 (T=8192 tokens as 2 x 4096, d=4096, f=14336, E=8,
-top-2, renormalised), random weights and inputs.
+top-2, renormalised), random weights and inputs.  ``--workload mxfp8`` runs
+the same layer at T=16384 with MXFP8 GEMM operands (the quantization of x,
+of the weights, of dY and of every backward operand inside the step).
 """
 
 import argparse
@@ -26,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = ("MoE-layer fwd+bwd tokens/s & TFLOP/s (% MFMA peak), "
           "Mixtral shape, 1 MI355X")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (MX) MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
 GEMM_STAGES = ("gate_up_swiglu_fwd", "down_fwd", "down_swiglu_bwd",
@@ -45,17 +48,24 @@ def stage_flops(name, T, d, f, E, k):
     }.get(name, 0.0)
 
 
-def stage_bytes(name, T, d, f, E, k, planes=1):
+def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
     """Algorithmic HBM bytes of the memory-bound stages (each tensor read
     or written once; the fp32 rows the combines read come as `planes`
-    partial-sum planes)."""
+    partial-sum planes; an MX row of n codes is n * 33/32 bytes)."""
     Tk = T * k
+    xb = 33.0 / 32.0 if mx else 2.0            # bytes per permuted x value
+    q = 33.0 / 32.0                            # bytes per MX value
     return {
         "route": T * E * 4 + Tk * 8,
-        "permute": Tk * 8 + T * d * 2 + Tk * d * 2 + Tk * 12 + E * 8,
+        "permute": Tk * 8 + T * d * xb + Tk * d * xb + Tk * 12 + E * 8,
         "unpermute_y": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
         "permute_dy": Tk * 4 + T * d * 2 + Tk * d * 2,
+        "permute_x": Tk * 4 + T * d * 2 + Tk * d * 2,
         "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
+        "quant_x": T * d * (2 + q),
+        "quant_weights": 3 * E * d * f * (2 + q),
+        "quant_bwd_operands": (Tk * d + 3 * E * d * f) * (2 + q),
+        "quant_tokens": Tk * (2 * d + 3 * f) * (2 + q),
     }.get(name, 0)
 
 
@@ -95,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
-                    help="mixtral (default), finegrain, tiny")
+                    help="mixtral (default), mxfp8, finegrain, tiny")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -106,15 +116,16 @@ def main():
 
     import torch
     from mixture_experts_expert_top_amd import inputs, moe
-    from mixture_experts_expert_top_amd.layer import MoEPath, StageTimers
+    from mixture_experts_expert_top_amd.layer import (MoEPath, MoEPathMX,
+                                                      StageTimers)
 
     wl = inputs.WORKLOADS[args.workload]
-    if wl.prec != "bf16":
-        raise SystemExit("the bench drives the bf16 path")
+    mx = wl.prec == "mxfp8"
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
     dev = torch.device("cuda:0")
     inp = inputs.make_inputs(wl, seed=0, device=dev)
-    path = MoEPath(T, d, f, E, k, device=dev)
+    path = (MoEPathMX if mx else MoEPath)(T, d, f, E, k, device=dev)
 
     def step(timers=None):
         path.forward(inp["x"], inp["w_gu"], inp["w2"], w_g=inp["w_g"],
@@ -149,7 +160,7 @@ def main():
     for n, v in stage_ms.items():
         e = {"ms": round(v, 4)}
         fl = stage_flops(n, T, d, f, E, k)
-        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES)
+        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES, mx=mx)
         if fl:
             e["tflops"] = round(fl / (v / 1e3) / 1e12, 1)
         if by:
@@ -167,28 +178,28 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8-e4m3" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name} fwd+bwd", "T": T, "d": d, "f": f,
                    "E": E, "k": k, "renorm": wl.renorm,
                    "router_bias": wl.router_bias},
         "tflops": round(all_flops / (ms / 1e3) / 1e12, 1),
         "pct_mfma_peak": round(100.0 * all_flops / (ms / 1e3) / 1e12
-                               / PEAK_BF16_TFLOPS, 2),
+                               / peak, 2),
         "gemm_tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
             "achieved": round(dom_tflops, 1),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dom_tflops / peak, 4),
             "traffic": None,
         },
         "stages": stages,
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx:
         out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_tokens, T))
     print(json.dumps(out), flush=True)
 

@@ -19,7 +19,8 @@ Sources (cited by page title and section):
 Every function is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_mx_pins.py`` and ``tests/test_oracle_mx_layer_pins.py``
 (brute force, closed forms, library routines, finite differences,
-exhaustive codec sweeps, an independent formulation of the MXFP8 layer).  See each module header for what is and is not pinned.
+exhaustive codec sweeps, an independent formulation of the MXFP8 layer).
+See each module header for what is and is not pinned.
 """
 
 from . import moe_mx, moe_ref, mx_ref  # noqa: F401

@@ -34,8 +34,9 @@ Pinned by tests/test_oracle_mx_layer_pins.py: a dense masked formulation
 (every expert on every token, no dispatch plan) whose quantizer is torch's
 float8_e4m3fn cast with independently computed block scales; exactness on
 inputs that are MX-representable along the documented axis only; the
-reduction to the plain layer when no block loses precision; and the
-per-element MX error bound.
+reduction to the plain layer when no block loses precision; the size of
+the MX error against the exact layer; and the sampled single-output
+helpers against the full layer.
 """
 
 import numpy as np
@@ -160,3 +161,98 @@ def moe_backward_mx(fwd, dy, w_gu, w2):
     return dict(dx=dx, dw_gu=dw_gu, dw2=dw2, dp=dp, dab=dab, dab_q=dab_q,
                 do=do, do_q=do_q, do_t=do_t, s_t=s_t, xp_t=xp_t,
                 dab_t=dab_t, w2_c=w2_c, w_gu_c=w_gu_c, dxp=dxp)
+
+
+# --------------------------------------------------------------------------
+# Sampled evaluation for full-size parity checks: the same definition for
+# single outputs.  Row-wise blocks of a row depend on that row alone and
+# token-axis blocks on one column alone, so each helper quantizes only the
+# rows or columns it needs.
+# --------------------------------------------------------------------------
+
+def expert_weights_mx(w_gu_e=None, w2_e=None, backward=False):
+    """Dequantized MX forms of one expert's weights: forward w_gu along d
+    ("gu_q") and w2 along f ("w2_q"); with ``backward`` also w2 along d
+    ("w2_c") and w_gu along 2f ("gu_c")."""
+    out = {}
+    if w_gu_e is not None:
+        w_gu_e = np.asarray(w_gu_e, dtype=np.float64)
+        out["gu_q"] = mx_rows(w_gu_e)
+        if backward:
+            out["gu_c"] = mx_rows(w_gu_e.T).T
+    if w2_e is not None:
+        w2_e = np.asarray(w2_e, dtype=np.float64)
+        out["w2_q"] = mx_rows(w2_e)
+        if backward:
+            out["w2_c"] = mx_rows(w2_e.T).T
+    return out
+
+
+def token_forward_mx(x_t, idx_t, p_t, W):
+    """y[t] for one token: its experts' MX forward rows summed in ascending
+    expert id.  W[e] holds expert_weights_mx(...) of every chosen e."""
+    xq = mx_rows(np.asarray(x_t, dtype=np.float64)[None, :])
+    y = 0.0
+    for j in np.argsort(np.asarray(idx_t), kind="stable"):
+        e = int(idx_t[j])
+        ab = R.gate_up(xq, W[e]["gu_q"])
+        s = R.scaled_swiglu(ab, np.array([p_t[j]], dtype=np.float64))
+        y = y + R.down(mx_rows(s), W[e]["w2_q"])[0]
+    return y
+
+
+def row_backward_mx(x_t, dy_t, p_r, We):
+    """(dXp row, dp) of the permuted row of token t at one expert, whose
+    weights We come from expert_weights_mx(..., backward=True)."""
+    xq = mx_rows(np.asarray(x_t, dtype=np.float64)[None, :])
+    ab = R.bf16_round(R.gate_up(xq, We["gu_q"]))
+    do_q = mx_rows(np.asarray(dy_t, dtype=np.float64)[None, :])
+    dab, dp = R.down_backward(do_q, ab, np.array([p_r], dtype=np.float64),
+                              We["w2_c"])
+    return R.gate_up_dgrad(mx_rows(dab), We["gu_c"])[0], dp[0]
+
+
+def _gate_up_cols(x_e, w_gu_e, cols):
+    """Columns ``cols`` of the expert's AB (bf16 as kept), from x quantized
+    along d and the needed W_gu rows quantized along d."""
+    xq = mx_rows(np.asarray(x_e, dtype=np.float64))
+    wr = mx_rows(np.asarray(w_gu_e, dtype=np.float64)[cols])
+    return R.bf16_round(xq @ wr.T)
+
+
+def dw2_column_mx(x_e, dy_e, w_e, w_gu_e, j):
+    """Column j of the expert's dW2 (all d entries): dO (bf16 dY rows) and
+    S[:, j] (bf16 S from the MX forward) quantized along the expert's
+    tokens.  x_e, dy_e, w_e: the expert's rows in permuted order."""
+    f = np.asarray(w_gu_e).shape[0] // 2
+    xq = mx_rows(np.asarray(x_e, dtype=np.float64))
+    wr = mx_rows(np.asarray(w_gu_e, dtype=np.float64)[[j, f + j]])
+    ab = xq @ wr.T
+    s = R.bf16_round(np.asarray(w_e, dtype=np.float64) *
+                     R.silu(ab[:, 0]) * ab[:, 1])
+    n = s.shape[0]
+    s_t = mx_tokens(s[:, None], [0, n])[:, 0]
+    do_t = mx_tokens(np.asarray(dy_e, dtype=np.float64), [0, n])
+    return do_t.T @ s_t
+
+
+def dw_gu_row_mx(x_e, dy_e, w_e, w_gu_e, w2_e, i):
+    """Row i of the expert's dW_gu (gate row for i < f, up row f + i' for
+    i = f + i'): dAB[:, i] (bf16, from dS = dO quantized along d times W2
+    quantized along d) and Xp quantized along the expert's tokens."""
+    w_gu_e = np.asarray(w_gu_e, dtype=np.float64)
+    f = w_gu_e.shape[0] // 2
+    c = i % f
+    ab = _gate_up_cols(x_e, w_gu_e, [c, f + c])
+    g, u = ab[:, 0], ab[:, 1]
+    do_q = mx_rows(np.asarray(dy_e, dtype=np.float64))
+    w2col = mx_rows(np.asarray(w2_e, dtype=np.float64)[:, c][None, :])[0]
+    ds = do_q @ w2col
+    dh = np.asarray(w_e, dtype=np.float64) * ds
+    sg = R.sigmoid(g)
+    dab = dh * u * sg * (1.0 + g * (1.0 - sg)) if i < f else dh * R.silu(g)
+    dab = R.bf16_round(dab)
+    n = dab.shape[0]
+    dab_t = mx_tokens(dab[:, None], [0, n])[:, 0]
+    xp_t = mx_tokens(np.asarray(x_e, dtype=np.float64), [0, n])
+    return dab_t @ xp_t

@@ -218,3 +218,41 @@ def test_mx_layer_error_is_small_but_nonzero():
         # 2^-4/sqrt(3) relative RMS error, and the backward chains up to
         # three quantized GEMMs
         assert 1e-3 < rr(got, ref) < 0.3
+
+
+# ------------------------------------------------------------ 5. sampled
+
+def test_sampled_helpers_match_the_full_layer():
+    """The single-output helpers used at full size give the full layer's
+    values (same definition, evaluated for one token, row or column)."""
+    x, logits, w_gu, w2, dy = _problem(7)
+    fwd = X.moe_forward_mx(x, logits, w_gu, w2, K)
+    bwd = X.moe_backward_mx(fwd, dy, w_gu, w2)
+    W = {e: X.expert_weights_mx(w_gu[e], w2[e], backward=True)
+         for e in range(E)}
+    idx, p, pos = fwd["idx"], fwd["p"], fwd["pos"]
+    for t in (0, 5, 17, T - 1):
+        y_t = X.token_forward_mx(x[t], idx[t], p[t], W)
+        assert np.max(np.abs(y_t - fwd["y"][t])) <= 1e-12 * np.max(
+            np.abs(fwd["y"]))
+        for j in range(K):
+            dxp, dp = X.row_backward_mx(x[t], dy[t], p[t, j], W[idx[t, j]])
+            r = pos[t, j]
+            assert np.allclose(dxp, bwd["dxp"][r], rtol=1e-12, atol=1e-12)
+            assert abs(dp - bwd["dp"][t, j]) <= 1e-12 * max(
+                1.0, abs(bwd["dp"][t, j]))
+    off, src = fwd["offsets"], fwd["src"]
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 == r0:
+            continue
+        rows = src[r0:r1]
+        we = fwd["w_perm"][r0:r1]
+        for j in (0, F - 1):
+            col = X.dw2_column_mx(x[rows], dy[rows], we, w_gu[e], j)
+            assert np.allclose(col, bwd["dw2"][e][:, j], rtol=1e-12,
+                               atol=1e-12 * np.max(np.abs(bwd["dw2"])))
+        for i in (1, F + 2):
+            row = X.dw_gu_row_mx(x[rows], dy[rows], we, w_gu[e], w2[e], i)
+            assert np.allclose(row, bwd["dw_gu"][e][i], rtol=1e-12,
+                               atol=1e-12 * np.max(np.abs(bwd["dw_gu"])))
