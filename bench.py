@@ -16,6 +16,7 @@ of the weights, of dY and of every backward operand inside the step).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,13 @@ METRIC = ("MoE-layer fwd+bwd tokens/s & TFLOP/s (% MFMA peak), "
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (MX) MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+# Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE per dispatch, with the same counters' reading of a plain 1 GiB
+# device copy); valid only for the kernel source it was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc",
+                           "gemm.hip")
 
 GEMM_STAGES = ("gate_up_swiglu_fwd", "down_fwd", "down_swiglu_bwd",
                "wgrad_down", "gate_up_dgrad", "wgrad_gate_up")
@@ -69,6 +77,38 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
     }.get(name, 0)
 
 
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of ``stage`` from the recorded counter runs,
+    scaled by the copy calibration; None when there is no record for this
+    workload and stage or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(GEMM_SOURCE, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if (rec.get("workload") != workload or rec.get("stage") != stage
+            or rec.get("kernel_source_sha256") != sha):
+        return None
+    fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
+    write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
+    return round(fetch + write)
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, five times: the reference that scales
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 28                                   # fp32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(6):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "copies": 6}), flush=True)
+
+
 def cpu_baseline(inp, wl, n_tokens):
     """The float64 oracle, untuned, on the first n_tokens tokens of the same
     workload (router scores, routing, experts, combine and backward)."""
@@ -106,13 +146,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
                     help="mixtral (default), mxfp8, finegrain, tiny")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB device copy that calibrates "
+                         "the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
               "supported (this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from mixture_experts_expert_top_amd import inputs, moe
@@ -194,7 +241,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(dom_tflops / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, dom),
         },
         "stages": stages,
         "wall_s": round(wall, 3),

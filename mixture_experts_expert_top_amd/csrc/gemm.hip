@@ -65,6 +65,7 @@ constexpr int BK = 64;
 constexpr int kTileElems = BM * BK;       // one operand stage (A or B)
 constexpr int kStageElems = 2 * kTileElems;
 constexpr int kGroupN = 4;                // n-tiles per scheduling group
+constexpr int kGroupM = 8;                // m-tiles per block of a group
 constexpr int kEpiRows = 64;              // rows per epilogue pass of a wave
 
 enum Mode { kSegM = 0, kSegK = 1, kSegKT = 2 };
@@ -260,6 +261,24 @@ __device__ __forceinline__ void load_one(const M& mv, i32x4* v,
     mv.load(v, rs, ld, k0, kmax, colbase, part);
 }
 
+// Tile order inside one expert's mt x nt tile grid: groups of kGroupN
+// n-tiles; inside a group, blocks of kGroupM m-tiles (the last group and
+// block may be narrower), m fastest inside a block.  Consecutive tiles --
+// which run together on one XCD -- then share kGroupN B column blocks and
+// kGroupM A row blocks in its L2, in both short (forward: a few m-tiles an
+// expert) and tall (weight gradients: M = d or 2f) grids.
+__device__ __forceinline__ void tile_order(int local, int mtn, int ntn,
+                                           int* mt, int* nt) {
+  const int grp = local / (mtn * kGroupN);
+  const int ng = min(kGroupN, ntn - grp * kGroupN);
+  int rem = local - grp * mtn * kGroupN;
+  const int blk = rem / (kGroupM * ng);
+  const int mb = min(kGroupM, mtn - blk * kGroupM);
+  rem -= blk * kGroupM * ng;
+  *mt = blk * kGroupM + rem % mb;
+  *nt = grp * kGroupN + rem / mb;
+}
+
 __device__ __forceinline__ int find_segment(const int* pref, int E, int key) {
   // largest e in [0, E) with pref[e] <= key (pref non-decreasing)
   int lo = 0, hi = E - 1;
@@ -377,24 +396,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     const int total = s_pref[E] * P.ntn;
     if (bid >= total) return;
     e = find_segment(s_pref, E, bid / P.ntn);
-    // the expert's tiles: groups of kGroupN n-tiles, m fastest inside
     const int mte = s_pref[e + 1] - s_pref[e];
-    const int local = bid - s_pref[e] * P.ntn;
-    const int grp = local / (mte * kGroupN);
-    const int within = local - grp * mte * kGroupN;
-    mt = within % mte;
-    nt = grp * kGroupN + within / mte;
+    tile_order(bid - s_pref[e] * P.ntn, mte, P.ntn, &mt, &nt);
     seg0 = P.offsets[e];
     seg_len = P.offsets[e + 1] - P.offsets[e];
   } else {
     const int mtiles = (P.M + BM - 1) / BM;
     const int per_e = mtiles * P.ntn;
     e = bid / per_e;
-    const int local = bid - e * per_e;
-    const int grp = local / (mtiles * kGroupN);
-    const int within = local - grp * mtiles * kGroupN;
-    mt = within % mtiles;
-    nt = grp * kGroupN + within / mtiles;
+    tile_order(bid - e * per_e, mtiles, P.ntn, &mt, &nt);
     seg0 = P.offsets[e];
     seg_len = P.offsets[e + 1] - P.offsets[e];
   }
