@@ -569,16 +569,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   };
 
   // Software pipeline over k-steps of BK.  At iteration kt the mover
-  // registers hold stage kt+1 (loaded one iteration earlier); they are
-  // written to the other LDS buffer during k-slices 0 and 1, and stage
-  // kt+2 is loaded into them during k-slices 2 and 3.  MFMA fragments are
+  // registers hold stage kt+1 (loaded one iteration earlier) and go to the
+  // other LDS buffer in k-slices 0 and 1.  MFMA fragments are
   // double-buffered so the next slice's LDS reads overlap the current
-  // slice's MFMAs.  Loads past K return zeros and the one stray store of
-  // the last iteration lands in the buffer no one reads any more.
-  auto kloop = [&](auto&& gload, auto&& lstore) {
+  // slice's MFMAs.  Two schedules, by mover layout:
+  //   * K-contiguous movers (each half of a stage has its own registers):
+  //     right after half p of stage kt+1 is stored, the same registers are
+  //     refilled with half p of stage kt+2, so a load has a whole
+  //     iteration to land; the last slice's MFMAs are issued after the
+  //     barrier, behind the first LDS reads of the next stage.
+  //   * transposing movers (storing either half reads all registers):
+  //     stage kt+2 is loaded in slices 2 and 3, after both stores, and the
+  //     barrier follows the last MFMAs (measured faster for these).
+  // Loads past K return zeros and the one stray store of the last
+  // iteration lands in the buffer no one reads any more.
+  auto kloop = [&](auto&& gload, auto&& lstore, auto indep_halves) {
+    constexpr bool kIndep = decltype(indep_halves)::value;
     constexpr int kMf = BI * BJ;                   // MFMAs per k-slice
     constexpr int kRd = BI + BJ;                   // fragment reads per slice
-    constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per slice
+    constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per half stage
     bf16x8_v a0[BI], b0[BJ], a1[BI], b1[BJ];
     if (nk > 0) {
       gload(kbeg, 0);
@@ -593,50 +602,68 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     for (int kt = 0; kt < nk; ++kt) {
       const int cs = kt & 1, ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
-      // slice 0: MFMAs on (a0,b0); reads of slice 1; stores of stage kt+1
+      // slices 0 and 1: MFMAs; reads of the next slice; half p of stage
+      // kt+1 to LDS (and, K-contiguous, half p of stage kt+2 loaded)
       read_frags(cs, 1, a1, b1);
       lstore(ns, 0);
+      if constexpr (kIndep) gload(k2, 0);
       mfmas(a0, b0);
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
         if (i < kMv) sched_group(kSgDsWrite, 1);
+        if (kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // slice 1: MFMAs on (a1,b1); reads of slice 2; stores of stage kt+1
       read_frags(cs, 2, a0, b0);
       lstore(ns, 1);
+      if constexpr (kIndep) gload(k2, 1);
       mfmas(a1, b1);
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
         if (i < kMv) sched_group(kSgDsWrite, 1);
+        if (kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // slice 2: MFMAs on (a0,b0); reads of slice 3; loads of stage kt+2
+      // slice 2: MFMAs on (a0,b0); reads of slice 3
       read_frags(cs, 3, a1, b1);
-      gload(k2, 0);
+      if constexpr (!kIndep) gload(k2, 0);
       mfmas(a0, b0);
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
         if (i < kRd) sched_group(kSgDsRead, 1);
-        if (i < kMv) sched_group(kSgVmemRead, 1);
+        if (!kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // slice 3: MFMAs on (a1,b1); loads of stage kt+2
-      gload(k2, 1);
-      mfmas(a1, b1);
-#pragma unroll
-      for (int i = 0; i < kMf; ++i) {
-        sched_group(kSgMfma, 1);
-        if (i < kMv) sched_group(kSgVmemRead, 1);
+      if constexpr (kIndep) {
+        // slice 3 after the barrier: stage kt+1 is complete, its first
+        // fragments are read while slice 3's MFMAs run from registers
+        __syncthreads();
+        read_frags(ns, 0, a0, b0);
+        mfmas(a1, b1);
+  #pragma unroll
+        for (int i = 0; i < kMf; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < kRd) sched_group(kSgDsRead, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // slice 3: MFMAs on (a1,b1); second half of stage kt+2
+        gload(k2, 1);
+        mfmas(a1, b1);
+  #pragma unroll
+        for (int i = 0; i < kMf; ++i) {
+          sched_group(kSgMfma, 1);
+          if (i < kMv) sched_group(kSgVmemRead, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        read_frags(ns, 0, a0, b0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      read_frags(ns, 0, a0, b0);
     }
   };
 
@@ -802,10 +829,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   if constexpr (MX) {
     kloop_mx();
   } else if constexpr (C::kSplitLoad && AKC != BKC) {
-    if (mv_a) kloop(gload_a, lstore_a);
-    else kloop(gload_b, lstore_b);
+    if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<AKC>{});
+    else kloop(gload_b, lstore_b, std::bool_constant<BKC>{});
   } else {
-    kloop(gload, lstore);
+    kloop(gload, lstore, std::bool_constant<AKC && BKC>{});
   }
 
   // ---------------------------------------------------------- epilogue
