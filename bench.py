@@ -88,11 +88,12 @@ def measured_traffic(workload, stage):
             sha = hashlib.sha256(fh.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if (rec.get("workload") != workload or rec.get("stage") != stage
+    st = rec.get("stages", {}).get(stage)
+    if (rec.get("workload") != workload or st is None
             or rec.get("kernel_source_sha256") != sha):
         return None
-    fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
-    write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
+    fetch = st["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
+    write = st["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
     return round(fetch + write)
 
 
@@ -146,7 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
                     help="mixtral (default), mxfp8, finegrain, tiny")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
