@@ -94,65 +94,108 @@ __device__ void padded_prefix(const int32_t* seg, int nseg, int64_t rows,
   __syncthreads();
 }
 
-// Workgroup = one padded 32-row block x 256 columns; thread = column.
+// Workgroup = one 128-row tile of the padded layout x kTokTiles runs of 64
+// columns (a tile never straddles a segment: segments start on multiples
+// of 128), each run in three steps:
+//   1. 256 threads load the tile's source rows with 16-byte loads (8
+//      columns each; rows past the segment read as zero) into LDS;
+//   2. thread (block b = t/64, column c = t%64) quantizes its 32-row block
+//      of one column and writes the 32 codes to an LDS staging line;
+//   3. every column's 128 codes leave as one 128-byte line (8 lanes, 16
+//      bytes each) and its 4 scale bytes as one 4-byte word.
+constexpr int kTokRows = 128;
+constexpr int kTokCols = 64;
+constexpr int kTokLd = kTokCols + 8;       // bf16 row stride of the tile
+constexpr int kTokTiles = 4;               // column runs per workgroup
+
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ gather,
-    int64_t rows, int64_t cols,
-    const int32_t* __restrict__ seg, int nseg, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t rows_pad) {
+    int64_t rows, int64_t cols, const int32_t* __restrict__ seg, int nseg,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int64_t rows_pad) {
   __shared__ int s_pad[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[kTokRows * kTokLd];
+  __shared__ __attribute__((aligned(16))) uint8_t out[kTokCols][kTokRows];
+  __shared__ uint32_t sc_out[kTokCols];
   padded_prefix(seg, nseg, rows, s_pad);
-  const int64_t pb = blockIdx.x;                 // padded 32-row block
-  const int64_t c = static_cast<int64_t>(blockIdx.y) * blockDim.x +
-                    threadIdx.x;
-  const int64_t p0 = pb * kMxBlock;              // first padded row
-  // segment holding this block: largest s with s_pad[s] <= p0
+  const int t = threadIdx.x;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kTokRows;
+  // segment holding this tile: largest s with s_pad[s] <= p0
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_pad[mid] <= p0) lo = mid; else hi = mid - 1;
   }
-  const int s = lo;
   int64_t r0 = 0, r_end = 0;                     // source rows [r0, r_end)
   if (p0 < s_pad[nseg]) {
-    const int64_t sbeg = seg ? seg[s] : 0;
-    const int64_t send = seg ? seg[s + 1] : rows;
-    r0 = sbeg + (p0 - s_pad[s]);
-    r_end = r0 + kMxBlock < send ? r0 + kMxBlock : send;
+    const int64_t sbeg = seg ? seg[lo] : 0;
+    const int64_t send = seg ? seg[lo + 1] : rows;
+    r0 = sbeg + (p0 - s_pad[lo]);
+    r_end = r0 + kTokRows < send ? r0 + kTokRows : send;
   }
-  if (c >= cols) return;
-  float v[kMxBlock];
-  float amax = 0.0f;
+  for (int ct = 0; ct < kTokTiles; ++ct) {
+    const int64_t c0 =
+        (static_cast<int64_t>(blockIdx.y) * kTokTiles + ct) * kTokCols;
+    if (c0 >= cols) break;
+    if (ct > 0) __syncthreads();                   // LDS of the previous run
+    // 1. load: thread t covers columns 8 (t%8) .. +7 of rows t/8 + 32 i
+    {
+      const int cc = (t & 7) * 8;
+      const bool col_ok = c0 + cc < cols;          // cols % 8 == 0
 #pragma unroll
-  for (int i = 0; i < kMxBlock; ++i) {
-    const int64_t r = r0 + i;
-    float x = 0.0f;
-    if (r < r_end) {
-      const int64_t sr = gather ? static_cast<int64_t>(gather[r]) : r;
-      x = bf2f(src[sr * cols + c]);
+      for (int i = 0; i < kTokRows / 32; ++i) {
+        const int rr = (t >> 3) + 32 * i;
+        i32x4 v = {0, 0, 0, 0};
+        if (col_ok && r0 + rr < r_end) {
+          const int64_t r = r0 + rr;
+          const int64_t sr = gather ? static_cast<int64_t>(gather[r]) : r;
+          v = *reinterpret_cast<const i32x4*>(src + sr * cols + c0 + cc);
+        }
+        *reinterpret_cast<i32x4*>(tile + rr * kTokLd + cc) = v;
+      }
     }
-    v[i] = x;
-    amax = fmaxf(amax, fabsf(v[i]));
-  }
-  const int e = mx_scale_exp(amax);
-  const float inv = mx_inv_scale(e);
-  i32x4 out[2];
+    __syncthreads();
+    // 2. quantize one 32-row block of one column
+    {
+      const int c = t & (kTokCols - 1);
+      const int b = t / kTokCols;                  // block 0..3 of the tile
+      float v[kMxBlock];
+      float amax = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
+      for (int i = 0; i < kMxBlock; ++i) {
+        v[i] = bf2f(tile[(b * kMxBlock + i) * kTokLd + c]);
+        amax = fmaxf(amax, fabsf(v[i]));
+      }
+      const int e = mx_scale_exp(amax);           // all-zero block: byte 0
+      const float inv = mx_inv_scale(e);
+      i32x4 w[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = q * 4 + b;
-      const uint32_t cd = (r0 + i < r_end) ? e4m3_encode(v[i] * inv) : 0u;
-      word |= cd << (8 * b);
+      for (int q = 0; q < 8; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= e4m3_encode(v[q * 4 + k] * inv) << (8 * k);
+        w[q >> 2][q & 3] = static_cast<int>(word);
+      }
+      *reinterpret_cast<i32x4*>(&out[c][b * kMxBlock]) = w[0];
+      *reinterpret_cast<i32x4*>(&out[c][b * kMxBlock + 16]) = w[1];
+      reinterpret_cast<uint8_t*>(sc_out)[c * 4 + b] =
+          static_cast<uint8_t>(e + 127);
     }
-    out[q >> 2][q & 3] = static_cast<int>(word);
+    __syncthreads();
+    // 3. write: 64 columns x 128 code bytes, 8 lanes a line
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int id = t + 256 * j;
+      const int col = id >> 3, chunk = id & 7;
+      if (c0 + col < cols)
+        *reinterpret_cast<i32x4*>(codes + (c0 + col) * rows_pad + p0 +
+                                  chunk * 16) =
+            *reinterpret_cast<const i32x4*>(&out[col][chunk * 16]);
+    }
+    if (t < kTokCols && c0 + t < cols)
+      *reinterpret_cast<uint32_t*>(scales + (c0 + t) * (rows_pad / kMxBlock) +
+                                   p0 / kMxBlock) = sc_out[t];
   }
-  i32x4* o = reinterpret_cast<i32x4*>(codes + c * rows_pad + p0);
-  o[0] = out[0];
-  o[1] = out[1];
-  scales[c * (rows_pad / kMxBlock) + pb] =
-      static_cast<uint8_t>(r_end > r0 ? e + 127 : 0);
 }
 
 }  // namespace
@@ -173,8 +216,9 @@ hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
                                   const int32_t* seg, int nseg,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(rows_pad / kMxBlock),
-            static_cast<unsigned>((cols + 255) / 256));
+  dim3 grid(static_cast<unsigned>(rows_pad / kTokRows),
+            static_cast<unsigned>((cols + kTokCols * kTokTiles - 1) /
+                                  (kTokCols * kTokTiles)));
   hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, s, src, gather,
                      rows, cols, seg, nseg, codes, scales, rows_pad);
   return hipGetLastError();
