@@ -22,7 +22,9 @@ Pinned by tests/test_oracle_pins.py: routing against a pure-Python sort,
 softmax against scipy, dispatch against its invariants, the forward against
 a dense masked brute force and the E=1,k=1 plain SwiGLU MLP, hand-derived
 closed forms (tests/golden/closed_forms.json), the backward against torch
-autograd (float64) and central finite differences.
+autograd (float64) and central finite differences; the router backward and
+the balancing loss (tests/test_oracle_router_pins.py) against torch autograd
+of their forward definitions, finite differences and closed forms.
 """
 
 import numpy as np
@@ -390,3 +392,65 @@ def dw_gu_row(xp_e, do_e, w_e, w_gu_e, w2_e, i, bf16_act=False):
     else:
         col = dh * silu(g)
     return _keep(col, bf16_act) @ xp_e
+
+
+# --------------------------------------------------------------------------
+# Router backward and the load-balancing loss.  "How MoE Architecture Cuts
+# Costs ...", section "Engineering Challenges of Efficient Training": a
+# router that keeps favouring a few experts leaves the others idle, which
+# training counters with a balancing term.  The pages give no formula; the
+# reading here is the common one: alpha * E * sum_e f_e * P_e, with f_e the
+# fraction of routed slots that went to expert e (from the counts, a
+# constant) and P_e the mean over tokens of the full softmax probability of
+# e.  The selection itself is piecewise constant, so only the chosen
+# experts' scores receive the routing-weight gradient.
+# --------------------------------------------------------------------------
+
+def routing_weight_backward(logits, idx, p, dp, renorm=True):
+    """dL = d(sum_{t,j} dp[t,j] p[t,j]) / dL for fixed choices idx.
+
+    renorm: p is the softmax over the chosen scores, so
+      dL[t, idx_j] = p_j (dp_j - sum_i p_i dp_i), 0 for the other experts.
+    else:   p_j = P[idx_j] with P the softmax over all E scores, so
+      dL[t, e] = P_e (g_e - sum_i p_i dp_i), g_e = dp_j if e = idx_j else 0.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    idx = np.asarray(idx)
+    p = np.asarray(p, dtype=np.float64)
+    dp = np.asarray(dp, dtype=np.float64)
+    T, E = L.shape
+    s = np.sum(p * dp, axis=1, keepdims=True)
+    dL = np.zeros((T, E))
+    if renorm:
+        np.put_along_axis(dL, idx.astype(np.int64), p * (dp - s), axis=1)
+        return dL
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    g = np.zeros((T, E))
+    np.put_along_axis(g, idx.astype(np.int64), dp, axis=1)
+    return P * (g - s)
+
+
+def aux_loss(logits, counts, alpha):
+    """(loss, dL) of the balancing term alpha * E * sum_e f_e * mean_t P_e
+    with f_e = counts_e / sum(counts) held constant."""
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    f = np.asarray(counts, dtype=np.float64)
+    f = f / f.sum()
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    loss = alpha * E * np.sum(f * P.mean(axis=0))
+    # d/dL[t,i] of sum_e f_e P[t,e]  =  P[t,i] (f_i - sum_e f_e P[t,e])
+    dL = alpha * E / T * P * (f[None, :] - np.sum(f * P, axis=1,
+                                                  keepdims=True))
+    return loss, dL
+
+
+def router_backward(x, w_g, dlogits):
+    """Gradients through L = x . W_g^T (+ bias): dW_g = dL^T x [E, d],
+    db = sum_t dL [E], and the router's share of dx = dL . W_g [T, d]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_g = np.asarray(w_g, dtype=np.float64)
+    dL = np.asarray(dlogits, dtype=np.float64)
+    return dL.T @ x, dL.sum(axis=0), dL @ w_g
