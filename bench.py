@@ -5,8 +5,10 @@ backward: router scores (x . W_g), top-k routing, permutation, the grouped
 gate_up GEMM with the fused ScaledSwiGLU epilogue, the grouped down GEMM,
 the combine, the permutation of dY, the fused down-projection backward
 (dS, dSwiGLU, routing-weight gradient partials), their reduction, both
-variable-K weight-gradient GEMMs, the gate_up data gradient and the combine
-of dX.  Inputs are resident in HBM before timing starts.
+variable-K weight-gradient GEMMs, the gate_up data gradient, the combine
+of dX (fp32) and the router backward (score gradient with the balancing
+term, dW_g, db, and the router's share of dX added before its rounding).
+Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer,
 forward+backward in bf16 (T=8192 tokens as 2 x 4096, d=4096, f=14336, E=8,
@@ -47,6 +49,7 @@ def stage_flops(name, T, d, f, E, k):
     Tk = T * k
     return {
         "router_logits": 2.0 * T * d * E,
+        "router_backward": 4.0 * T * d * E,
         "gate_up_swiglu_fwd": 4.0 * Tk * d * f,
         "down_fwd": 2.0 * Tk * d * f,
         "down_swiglu_bwd": 2.0 * Tk * d * f,
@@ -69,7 +72,9 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
         "unpermute_y": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
         "permute_dy": Tk * 4 + T * d * 2 + Tk * d * 2,
         "permute_x": Tk * 4 + T * d * 2 + Tk * d * 2,
-        "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
+        "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 4,
+        "router_backward": (T * E * 4 * 3 + Tk * 12 + T * d * 2 + E * d * 2
+                            + T * d * 4 + T * d * 2 + E * d * 4),
         "quant_x": T * d * (2 + q),
         "quant_weights": 3 * E * d * f * (2 + q),
         "quant_bwd_operands": (Tk * d + 3 * E * d * f) * (2 + q),
@@ -131,7 +136,11 @@ def cpu_baseline(inp, wl, n_tokens):
     t0 = time.perf_counter()
     logits = moe_ref.router_logits(x, w_g, bias)
     fwd = moe_ref.moe_forward(x, logits, w_gu, w2, wl.k)
-    moe_ref.moe_backward(fwd, dy, w_gu, w2)
+    bwd = moe_ref.moe_backward(fwd, dy, w_gu, w2)
+    dl = moe_ref.routing_weight_backward(logits, fwd["idx"], fwd["p"],
+                                         bwd["dp"], wl.renorm)
+    dl = dl + moe_ref.aux_loss(logits, fwd["counts"], 0.01)[1]
+    moe_ref.router_backward(x, w_g, dl)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
@@ -199,7 +208,8 @@ def main():
 
     stage_ms = timers.mean_ms()
     gemm_flops = sum(stage_flops(n, T, d, f, E, k) for n in GEMM_STAGES)
-    all_flops = gemm_flops + stage_flops("router_logits", T, d, f, E, k)
+    all_flops = gemm_flops + sum(stage_flops(n, T, d, f, E, k)
+                                 for n in ("router_logits", "router_backward"))
     tokens_s = T / (ms / 1e3)
     dom = max(GEMM_STAGES, key=lambda n: stage_ms[n])
     dom_tflops = stage_flops(dom, T, d, f, E, k) / (stage_ms[dom] / 1e3) / 1e12

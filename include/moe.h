@@ -66,7 +66,8 @@ typedef enum moe_prec {
 typedef enum moe_entry {
   MOE_ENTRY_PERMUTE = 0,
   MOE_ENTRY_MLP_FWD = 1,
-  MOE_ENTRY_MLP_BWD = 2
+  MOE_ENTRY_MLP_BWD = 2,
+  MOE_ENTRY_ROUTER_BWD = 3
 } moe_entry;
 
 /* Short name of a status code (static string). */
@@ -103,6 +104,42 @@ moe_status moe_router_logits(const void* x, const void* w_g, const float* bias,
 moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
                      int32_t renorm, int32_t* topk_idx, float* topk_w,
                      hipStream_t stream);
+
+/*
+ * moe_router_backward -- gradient of the router, and the load-balancing
+ * term, [P4] "Engineering Challenges of Efficient Training" (a router that
+ * keeps favouring a few experts is counteracted by a balancing term; the
+ * pages give no formula, the one below is the common one).  With the
+ * choices topk_idx held fixed (the top-k selection is piecewise constant):
+ *   s = sum_j p_j dp_j over the token's k slots, and
+ *   renorm != 0: dlogits[t][idx_j] = p_j (dp_j - s), 0 at unchosen experts;
+ *   renorm == 0: dlogits[t][e] = P_e (g_e - s), P = softmax over all E,
+ *                g_e = dp_j where e = idx_j, else 0.
+ * With counts (the dispatch plan's [E]) the balancing term
+ *   aux = aux_coef * E * sum_e f_e * mean_t P[t][e],  f_e = counts[e]/(T k)
+ * (f held constant) adds aux_coef * E / T * P_e (f_e - sum_e' f_e' P_e')
+ * to dlogits and its value goes to aux_loss[0] (when not NULL).  Then
+ *   dw_g [E][d] fp32 = dlogits^T x,  db [E] fp32 = sum_t dlogits[t]
+ *   dx_out [T][d] bf16 = dx_in + dlogits . w_g   (fp32 sum, one rounding)
+ * topk_w are the forward's routing weights p; dp [T][k] fp32 comes from
+ * moe_grouped_mlp_bwd.  dw_g, db, dx_in, dx_out, aux_loss and counts may be
+ * NULL (the matching output is skipped; dx_in NULL means zero).  x (bf16
+ * [T][d]) is read only for dw_g, w_g (bf16 [E][d]) only for dx_out; d must
+ * then be a positive multiple of 8.  All sums run in a fixed order
+ * (deterministic).  Errors: MOE_ERR_INVALID_ARG for a missing pointer, bad
+ * T/E/k/d or aux_loss without counts; MOE_ERR_WORKSPACE for a short
+ * workspace.  All pointers are device memory owned by the caller.
+ * Workspace: MOE_ENTRY_ROUTER_BWD.
+ */
+moe_status moe_router_backward(const float* logits, const int32_t* topk_idx,
+                               const float* topk_w, const float* dp,
+                               const int32_t* counts, float aux_coef,
+                               int64_t T, int32_t E, int32_t k,
+                               int32_t renorm, const void* x, const void* w_g,
+                               int64_t d, float* dlogits, float* dw_g,
+                               float* db, const float* dx_in, void* dx_out,
+                               float* aux_loss, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_permute -- dispatch plan and token permutation, [P1] Challenge 1

@@ -210,6 +210,8 @@ size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
     case MOE_ENTRY_MLP_FWD:
       if (prec == MOE_BF16 || f < 1) return 0;
       return mx_fwd_layout(Tk, f).total;
+    case MOE_ENTRY_ROUTER_BWD:
+      return moe::router_backward_workspace(T, E, d < 1 ? 1 : d);
     case MOE_ENTRY_MLP_BWD:
       if (f < 1 || d < 1) return 0;
       if (prec == MOE_BF16) return bwd_layout(Tk, f).total;
@@ -248,6 +250,51 @@ moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
       moe::launch_route(logits, T, E, k, renorm ? 1 : 0, topk_idx, topk_w,
                         stream),
       "moe_route");
+}
+
+moe_status moe_router_backward(const float* logits, const int32_t* topk_idx,
+                               const float* topk_w, const float* dp,
+                               const int32_t* counts, float aux_coef,
+                               int64_t T, int32_t E, int32_t k,
+                               int32_t renorm, const void* x, const void* w_g,
+                               int64_t d, float* dlogits, float* dw_g,
+                               float* db, const float* dx_in, void* dx_out,
+                               float* aux_loss, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(dp);
+  REQUIRE_OPT_PTR(counts);
+  REQUIRE_PTR(dlogits);
+  REQUIRE_OPT_PTR(dw_g);
+  REQUIRE_OPT_PTR(db);
+  REQUIRE_OPT_PTR(dx_in);
+  REQUIRE_OPT_PTR(dx_out);
+  REQUIRE_OPT_PTR(aux_loss);
+  if (moe_status st = check_route_dims(T, E, k)) return st;
+  const bool need_x = dw_g != nullptr;
+  const bool need_w = dx_out != nullptr;
+  if (need_x) REQUIRE_PTR(x);
+  if (need_w) REQUIRE_PTR(w_g);
+  if (need_x || need_w) {
+    if (moe_status st = check_feature("d", d, MOE_BF16)) return st;
+    REQUIRE(T * d * 4 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+            "T x d too large");
+  }
+  REQUIRE(!(aux_loss && !counts), MOE_ERR_INVALID_ARG,
+          "aux_loss needs counts");
+  const size_t need = moe::router_backward_workspace(T, E, d > 0 ? d : 1);
+  REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+  return hip_status(
+      moe::launch_router_backward(
+          logits, topk_idx, topk_w, dp, counts, aux_coef, T, E, k, renorm,
+          static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_g), d,
+          dlogits, dw_g, db, dx_in, static_cast<bf16_t*>(dx_out), aux_loss,
+          workspace, stream),
+      "moe_router_backward");
 }
 
 moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,

@@ -62,6 +62,18 @@ hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s);
 
+// router backward (route.hip)
+size_t router_backward_workspace(int64_t T, int E, int64_t d);
+hipError_t launch_router_backward(const float* logits, const int32_t* idx,
+                                  const float* p, const float* dp,
+                                  const int32_t* counts, float alpha,
+                                  int64_t T, int E, int k, int renorm,
+                                  const bf16_t* x, const bf16_t* w_g,
+                                  int64_t d, float* dlogits, float* dw_g,
+                                  float* db, const float* dx_in,
+                                  bf16_t* dx_out, float* aux_loss, void* ws,
+                                  hipStream_t s);
+
 // grouped GEMMs (gemm.hip)
 int gemm_dp_tiles(int64_t f);
 hipError_t gemm_fc1_fwd(const bf16_t* xp, const bf16_t* w_gu,

@@ -8,6 +8,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -151,6 +153,200 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
 }
 
+// ---------------------------------------------------------------- backward
+// dlogits of one token (G lanes, as in route_kernel): the routing-weight
+// gradient of the chosen experts (renormalised: p_j (dp_j - s), s =
+// sum_j p_j dp_j; full softmax: P_e (g_e - s)) plus, with counts, the
+// balancing term's alpha E / T * P_e (f_e - sum_e' f_e' P_e').  Each token's
+// sum_e f_e P_e is kept per block (fixed order) for the loss value.
+template <int VPL>
+__global__ __launch_bounds__(256) void router_dlogits_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ p, const float* __restrict__ dp,
+    const int32_t* __restrict__ counts, float alpha, int T, int E, int k,
+    int renorm, int G, float* __restrict__ dlogits,
+    float* __restrict__ q_part) {
+  __shared__ float s_q[256];
+  const int lane = threadIdx.x & 63;
+  const int gwave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int tpw = 64 / G;
+  const int sub = lane / G, gl = lane % G;
+  const int t = gwave * tpw + sub;
+  const bool tok_ok = t < T;
+  const int64_t tk = static_cast<int64_t>(tok_ok ? t : 0) * k;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += tok_ok ? p[tk + j] * dp[tk + j] : 0.0f;
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = gl + i * G;
+    v[i] = (tok_ok && e < E) ? logits[static_cast<int64_t>(t) * E + e]
+                             : -INFINITY;
+  }
+  const bool need_p = !renorm || counts != nullptr;
+  float P[VPL];
+  float qf = 0.0f;
+  if (need_p) {
+    float top = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) top = fmaxf(top, v[i]);
+    for (int m = 1; m < G; m <<= 1) top = fmaxf(top, __shfl_xor(top, m, 64));
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      P[i] = (gl + i * G < E && tok_ok) ? expf(v[i] - top) : 0.0f;
+      z += P[i];
+    }
+    for (int m = 1; m < G; m <<= 1) z += __shfl_xor(z, m, 64);
+    const float inv = tok_ok ? 1.0f / z : 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) P[i] *= inv;
+    if (counts) {
+      const float rtk = 1.0f / (static_cast<float>(T) * k);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = gl + i * G;
+        if (e < E) qf += counts[e] * rtk * P[i];
+      }
+      for (int m = 1; m < G; m <<= 1) qf += __shfl_xor(qf, m, 64);
+    }
+  }
+  const float aux_scale = alpha * static_cast<float>(E) / static_cast<float>(T);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = gl + i * G;
+    if (!tok_ok || e >= E) continue;
+    float g = 0.0f, pj = 0.0f;
+    bool chosen = false;
+    for (int j = 0; j < k; ++j) {
+      if (idx[tk + j] == e) { g = dp[tk + j]; pj = p[tk + j]; chosen = true; }
+    }
+    float r;
+    if (renorm) r = chosen ? pj * (g - s) : 0.0f;
+    else r = P[i] * (g - s);
+    if (counts) {
+      const float fe = counts[e] / (static_cast<float>(T) * k);
+      r += aux_scale * P[i] * (fe - qf);
+    }
+    dlogits[static_cast<int64_t>(t) * E + e] = r;
+  }
+  // the block's tokens' sum_e f_e P_e, added in token order
+  const int tb = threadIdx.x / G;             // token slot in the block
+  if (gl == 0) s_q[tb] = tok_ok ? qf : 0.0f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float acc = 0.0f;
+    for (int i = 0; i < 256 / G; ++i) acc += s_q[i];
+    q_part[blockIdx.x] = acc;
+  }
+}
+
+// Partial dW_g over one chunk of 256 tokens, 256 columns and up to 32
+// experts: part[chunk][e][c] = sum over the chunk's tokens, in order, of
+// dlogits[t][e] * x[t][c]; the y == 0 blocks also sum dlogits over the
+// chunk (db).  With part == nullptr only the db sums are made (x unread).
+constexpr int kRbTok = 256;
+constexpr int kRbExp = 32;
+__global__ __launch_bounds__(256) void router_dwg_partial_kernel(
+    const float* __restrict__ dlogits, const bf16_t* __restrict__ x, int T,
+    int E, int d, float* __restrict__ part, float* __restrict__ db_part) {
+  __shared__ float s_dl[kRbTok][kRbExp];
+  const int tc = blockIdx.x, c = blockIdx.y * 256 + threadIdx.x;
+  const int e0 = blockIdx.z * kRbExp;
+  const int t0 = tc * kRbTok;
+  const int ne = min(kRbExp, E - e0), nt = min(kRbTok, T - t0);
+  for (int i = threadIdx.x; i < kRbTok * kRbExp; i += 256) {
+    const int tt = i / kRbExp, ee = i % kRbExp;
+    s_dl[tt][ee] = (tt < nt && ee < ne)
+        ? dlogits[static_cast<int64_t>(t0 + tt) * E + e0 + ee] : 0.0f;
+  }
+  __syncthreads();
+  if (blockIdx.y == 0 && threadIdx.x < ne) {
+    float acc = 0.0f;
+    for (int tt = 0; tt < nt; ++tt) acc += s_dl[tt][threadIdx.x];
+    db_part[static_cast<int64_t>(tc) * E + e0 + threadIdx.x] = acc;
+  }
+  if (part == nullptr || c >= d) return;
+  float acc[kRbExp];
+#pragma unroll
+  for (int ee = 0; ee < kRbExp; ++ee) acc[ee] = 0.0f;
+  for (int tt = 0; tt < nt; ++tt) {
+    const float xv = bf2f(x[static_cast<int64_t>(t0 + tt) * d + c]);
+#pragma unroll
+    for (int ee = 0; ee < kRbExp; ++ee) acc[ee] += s_dl[tt][ee] * xv;
+  }
+  for (int ee = 0; ee < ne; ++ee)
+    part[(static_cast<int64_t>(tc) * E + e0 + ee) * d + c] = acc[ee];
+}
+
+// dW_g[e][c] = sum over chunks, in order, of part[chunk][e][c]; db likewise.
+__global__ __launch_bounds__(256) void router_dwg_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ db_part,
+    int chunks, int E, int d, float* __restrict__ dw, float* __restrict__ db) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(E) * d;
+  if (dw && i < n) {
+    float acc = 0.0f;
+    for (int tc = 0; tc < chunks; ++tc) acc += part[tc * n + i];
+    dw[i] = acc;
+  }
+  if (db && i < E) {
+    float acc = 0.0f;
+    for (int tc = 0; tc < chunks; ++tc) acc += db_part[static_cast<int64_t>(tc) * E + i];
+    db[i] = acc;
+  }
+}
+
+// dx_out[t] = bf16(dx_in[t] + sum_e dlogits[t][e] w_g[e]): a block owns one
+// token and 2048 columns, a thread 8 of them; experts added in order.
+__global__ __launch_bounds__(256) void router_dx_kernel(
+    const float* __restrict__ dlogits, const bf16_t* __restrict__ wg,
+    const float* __restrict__ dx_in, int E, int d,
+    bf16_t* __restrict__ dx_out) {
+  __shared__ float s_dl[kMaxExperts];
+  const int64_t t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) s_dl[e] = dlogits[t * E + e];
+  __syncthreads();
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= d) return;
+  float acc[8];
+  if (dx_in) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(dx_in + t * d + c);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(dx_in + t * d + c + 4);
+    acc[0] = a[0]; acc[1] = a[1]; acc[2] = a[2]; acc[3] = a[3];
+    acc[4] = b[0]; acc[5] = b[1]; acc[6] = b[2]; acc[7] = b[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  }
+  for (int e = 0; e < E; ++e) {
+    const i32x4 w = *reinterpret_cast<const i32x4*>(wg + static_cast<int64_t>(e) * d + c);
+    const float g = s_dl[e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += g * bf_lo(static_cast<uint32_t>(w[q]));
+      acc[2 * q + 1] += g * bf_hi(static_cast<uint32_t>(w[q]));
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(dx_out + t * d + c) = o;
+}
+
+// aux_loss = alpha * E / T * sum over blocks, in order, of q_part.
+__global__ void router_aux_final_kernel(const float* __restrict__ q_part,
+                                        int blocks, float scale,
+                                        float* __restrict__ loss) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    float acc = 0.0f;
+    for (int b = 0; b < blocks; ++b) acc += q_part[b];
+    loss[0] = scale * acc;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
@@ -186,6 +382,87 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k,
   MOE_ROUTE_CASE(16)
 #undef MOE_ROUTE_CASE
   return hipErrorInvalidValue;
+}
+
+size_t router_backward_workspace(int64_t T, int E, int64_t d) {
+  const int64_t chunks = (T + kRbTok - 1) / kRbTok;
+  const size_t a = static_cast<size_t>(chunks * E * d * 4);
+  const size_t b = static_cast<size_t>(chunks * E * 4);
+  const size_t c = static_cast<size_t>(T * 4);
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  return up(a) + up(b) + up(c);
+}
+
+hipError_t launch_router_backward(const float* logits, const int32_t* idx,
+                                  const float* p, const float* dp,
+                                  const int32_t* counts, float alpha,
+                                  int64_t T, int E, int k, int renorm,
+                                  const bf16_t* x, const bf16_t* w_g,
+                                  int64_t d, float* dlogits, float* dw_g,
+                                  float* db, const float* dx_in,
+                                  bf16_t* dx_out, float* aux_loss, void* ws,
+                                  hipStream_t s) {
+  const int64_t chunks = (T + kRbTok - 1) / kRbTok;
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* part = reinterpret_cast<float*>(w);
+  w += up(static_cast<size_t>(chunks * E * d * 4));
+  float* db_part = reinterpret_cast<float*>(w);
+  w += up(static_cast<size_t>(chunks * E * 4));
+  float* q_part = reinterpret_cast<float*>(w);
+  int G = 1;
+  while (G < E && G < 64) G <<= 1;
+  const int vpl_needed = (E + G - 1) / G;
+  const int tokens_per_block = 256 / G;
+  const unsigned grid =
+      static_cast<unsigned>((T + tokens_per_block - 1) / tokens_per_block);
+  const int Ti = static_cast<int>(T);
+  hipError_t err = hipErrorInvalidValue;
+#define MOE_RB_CASE(V)                                                        \
+  if (err == hipErrorInvalidValue && vpl_needed <= V) {                       \
+    hipLaunchKernelGGL(router_dlogits_kernel<V>, dim3(grid), dim3(256), 0, s, \
+                       logits, idx, p, dp, counts, alpha, Ti, E, k, renorm,   \
+                       G, dlogits, q_part);                                   \
+    err = hipGetLastError();                                                  \
+  }
+  MOE_RB_CASE(1)
+  MOE_RB_CASE(2)
+  MOE_RB_CASE(4)
+  MOE_RB_CASE(8)
+  MOE_RB_CASE(16)
+#undef MOE_RB_CASE
+  if (err != hipSuccess) return err;
+  if (dw_g || db) {
+    // without dw_g only the db sums are wanted: one column block, x unread
+    const int64_t dd = dw_g ? d : 0;
+    dim3 g2(static_cast<unsigned>(chunks),
+            static_cast<unsigned>(dw_g ? (d + 255) / 256 : 1),
+            static_cast<unsigned>((E + kRbExp - 1) / kRbExp));
+    hipLaunchKernelGGL(router_dwg_partial_kernel, g2, dim3(256), 0, s, dlogits,
+                       x, Ti, E, static_cast<int>(dd), dw_g ? part : nullptr,
+                       db_part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t n = std::max<int64_t>(static_cast<int64_t>(E) * dd, E);
+    hipLaunchKernelGGL(router_dwg_reduce_kernel,
+                       dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, s, part, db_part, static_cast<int>(chunks), E,
+                       static_cast<int>(dd), dw_g, db);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (dx_out) {
+    dim3 g4(static_cast<unsigned>(T), static_cast<unsigned>((d + 2047) / 2048));
+    hipLaunchKernelGGL(router_dx_kernel, g4, dim3(256), 0, s, dlogits, w_g,
+                       dx_in, E, static_cast<int>(d), dx_out);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (aux_loss && counts) {
+    hipLaunchKernelGGL(router_aux_final_kernel, dim3(1), dim3(64), 0, s,
+                       q_part, static_cast<int>(grid),
+                       alpha * static_cast<float>(E) / static_cast<float>(T),
+                       aux_loss);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace moe

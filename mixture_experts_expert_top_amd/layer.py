@@ -6,6 +6,9 @@ with torch, reused every step) and issues the library calls in order:
   forward : moe_router_logits -> moe_route -> moe_permute
             -> moe_grouped_mlp_fwd -> moe_unpermute
   backward: moe_permute_rows (dY) -> moe_grouped_mlp_bwd -> moe_unpermute
+            -> moe_router_backward (when the forward computed the router
+               scores: dlogits with the balancing term, dW_g, db, and the
+               router's share added to dx before its one rounding)
 
 With a ``timers`` object (see ``StageTimers``) the GEMMs are issued
 through the per-GEMM stage entry points instead of the fused ones, with
@@ -26,7 +29,7 @@ import torch
 
 from . import moe
 from .moe import (MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_MLP_FWD,
-                  MOE_ENTRY_PERMUTE, MOE_MXFP8)
+                  MOE_ENTRY_PERMUTE, MOE_ENTRY_ROUTER_BWD, MOE_MXFP8)
 
 
 class StageTimers:
@@ -60,11 +63,13 @@ def _around(timers, name):
 
 class MoEPath:
     def __init__(self, T, d, f, E, k, renorm=True, prec=MOE_BF16,
-                 device="cuda", y_fp32=False):
+                 device="cuda", y_fp32=False, aux_coef=0.01):
         if prec != MOE_BF16:
             raise NotImplementedError("use MoEPathMX for the MXFP8 path")
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.renorm = renorm
+        self.aux_coef = aux_coef
+        self._router = None
         self.prec = prec
         Tk = T * k
         dev = torch.device(device)
@@ -106,6 +111,16 @@ class MoEPath:
                                        d, f)
         self.ws_bwd = torch.empty(max(ws_b, 16), dtype=torch.uint8,
                                   device=dev)
+        # router backward
+        self.dx_f32 = torch.empty(T, d, dtype=torch.float32, device=dev)
+        self.dlogits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        self.dw_g = torch.empty(E, d, dtype=torch.float32, device=dev)
+        self.db = torch.empty(E, dtype=torch.float32, device=dev)
+        self.aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
+        ws_r = moe.moe_workspace_bytes(MOE_ENTRY_ROUTER_BWD, MOE_BF16, T, E,
+                                       k, d, f)
+        self.ws_router = torch.empty(max(ws_r, 16), dtype=torch.uint8,
+                                     device=dev)
         self._bwd_ready = True
 
     # ------------------------------------------------------------------
@@ -114,6 +129,10 @@ class MoEPath:
             with _around(timers, "router_logits"):
                 moe.moe_router_logits(x, w_g, bias, self.logits)
             logits = self.logits
+            self._router = (x, w_g, bias)
+        else:
+            self._router = None
+        self._logits_used = logits
         with _around(timers, "route"):
             moe.moe_route(logits, self.k, self.renorm, self.topk_idx,
                           self.topk_w)
@@ -169,18 +188,33 @@ class MoEPath:
             with timers.around("wgrad_gate_up"):
                 moe.moe_grouped_wgrad(self.dab, self.x_perm, self.offsets,
                                       self.dw_gu)
-        with _around(timers, "unpermute_dx"):
-            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+        self._finish_dx(timers)
         return self.dx, self.dw_gu, self.dw2, self.dp
+
+    def _finish_dx(self, timers):
+        """Combine dX; with a router, add its share before the rounding."""
+        if self._router is None:
+            with _around(timers, "unpermute_dx"):
+                moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+            return
+        x, w_g, bias = self._router
+        with _around(timers, "unpermute_dx"):
+            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx_f32)
+        with _around(timers, "router_backward"):
+            moe.moe_router_backward(
+                self._logits_used, self.topk_idx, self.topk_w, self.dp,
+                self.counts, self.aux_coef, self.renorm, x, w_g,
+                self.dlogits, self.dw_g, self.db if bias is not None else None,
+                self.dx_f32, self.dx, self.aux_loss, self.ws_router)
 
 
 class MoEPathMX(MoEPath):
     """The layer with MXFP8 GEMM operands (see the module docstring)."""
 
     def __init__(self, T, d, f, E, k, renorm=True, device="cuda",
-                 y_fp32=False):
+                 y_fp32=False, aux_coef=0.01):
         super().__init__(T, d, f, E, k, renorm=renorm, prec=MOE_BF16,
-                         device=device, y_fp32=y_fp32)
+                         device=device, y_fp32=y_fp32, aux_coef=aux_coef)
         self.prec = MOE_MXFP8
         Tk = T * k
         dev = self.x_perm.device
@@ -307,6 +341,5 @@ class MoEPathMX(MoEPath):
                 moe.moe_mx_grouped_wgrad(self.dabt, self.dabts, self.xpt,
                                          self.xpts, self.offsets, Tk,
                                          self.dw_gu)
-        with _around(timers, "unpermute_dx"):
-            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
+        self._finish_dx(timers)
         return self.dx, self.dw_gu, self.dw2, self.dp

@@ -20,6 +20,7 @@ MOE_MXFP8 = 1
 MOE_ENTRY_PERMUTE = 0
 MOE_ENTRY_MLP_FWD = 1
 MOE_ENTRY_MLP_BWD = 2
+MOE_ENTRY_ROUTER_BWD = 3
 
 EXPORTED = [
     "moe_status_str", "moe_last_error", "moe_version", "moe_router_logits",
@@ -30,6 +31,7 @@ EXPORTED = [
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
     "moe_row_planes", "moe_mx_gate_up_swiglu_fwd", "moe_mx_down_fwd",
     "moe_mx_down_swiglu_bwd", "moe_mx_gate_up_dgrad", "moe_mx_grouped_wgrad",
+    "moe_router_backward",
 ]
 
 
@@ -86,6 +88,9 @@ def _load():
                                        P]),
         "moe_mx_grouped_wgrad": (I32, [P, P, P, P, I64, P, I32, I64, I64,
                                        I64, P, P]),
+        "moe_router_backward": (I32, [P, P, P, P, P, ctypes.c_float, I64,
+                                      I32, I32, I32, P, P, I64, P, P, P, P,
+                                      P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -159,6 +164,35 @@ def moe_route(logits, k, renorm, topk_idx, topk_w, stream=None):
     _check("moe_route", lib.moe_route(_p(logits), T, E, k, int(renorm),
                                       _p(topk_idx), _p(topk_w),
                                       _stream(stream)))
+
+
+def moe_router_backward(logits, topk_idx, topk_w, dp, counts, aux_coef,
+                        renorm, x, w_g, dlogits, dw_g, db, dx_in, dx_out,
+                        aux_loss, workspace, stream=None):
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    d = (x if x is not None else w_g).shape[1] if (
+        x is not None or w_g is not None) else 0
+    _want(logits, "logits", torch.float32)
+    _want(topk_idx, "topk_idx", torch.int32, (T, k))
+    _want(topk_w, "topk_w", torch.float32, (T, k))
+    _want(dp, "dp", torch.float32, (T, k))
+    _want(counts, "counts", torch.int32, (E,), allow_none=True)
+    _want(x, "x", torch.bfloat16, (T, d), allow_none=True)
+    _want(w_g, "w_g", torch.bfloat16, (E, d), allow_none=True)
+    _want(dlogits, "dlogits", torch.float32, (T, E))
+    _want(dw_g, "dw_g", torch.float32, (E, d), allow_none=True)
+    _want(db, "db", torch.float32, (E,), allow_none=True)
+    _want(dx_in, "dx_in", torch.float32, (T, d), allow_none=True)
+    _want(dx_out, "dx_out", torch.bfloat16, (T, d), allow_none=True)
+    _want(aux_loss, "aux_loss", torch.float32, (1,), allow_none=True)
+    nbytes = workspace.numel() * workspace.element_size() if workspace \
+        is not None else 0
+    _check("moe_router_backward", lib.moe_router_backward(
+        _p(logits), _p(topk_idx), _p(topk_w), _p(dp), _p(counts),
+        float(aux_coef), T, E, k, int(renorm), _p(x), _p(w_g), d,
+        _p(dlogits), _p(dw_g), _p(db), _p(dx_in), _p(dx_out), _p(aux_loss),
+        _p(workspace), nbytes, _stream(stream)))
 
 
 def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,

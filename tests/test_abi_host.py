@@ -189,3 +189,37 @@ def test_quantize_validation():
     assert q(A, 200, 64, 1, None, 1, A, A, 128, None) == INVALID  # rows_pad
     assert q(A, 100, 64, 1, None, 1, A, A, 192, None) == INVALID  # % 128
     assert q(None, 8, 64, 0, None, 1, A, A, 0, None) == INVALID
+
+
+def _router_bwd(T=300, E=8, k=2, d=64, x=A, w_g=A, dw_g=A, db=A, dx_out=A,
+                counts=A, aux=A, ws=A, ws_bytes=None, logits=A):
+    if ws_bytes is None:
+        ws_bytes = L.moe_workspace_bytes(3, BF16, T, E, k, d, 0)
+    return L.moe_router_backward(logits, A, A, A, counts, 0.01, T, E, k, 1,
+                                 x, w_g, d, A, dw_g, db, None, dx_out, aux,
+                                 ws, ws_bytes, None)
+
+
+def test_router_backward_validation():
+    assert _router_bwd(logits=None) == INVALID
+    assert b"logits" in L.moe_last_error()
+    assert _router_bwd(x=None) == INVALID          # dw_g needs x
+    assert _router_bwd(w_g=None) == INVALID        # dx_out needs w_g
+    assert _router_bwd(counts=None) == INVALID     # aux_loss needs counts
+    assert b"counts" in L.moe_last_error()
+    assert _router_bwd(d=12) == INVALID
+    assert _router_bwd(E=0) == INVALID
+    assert _router_bwd(k=9) == INVALID
+    assert _router_bwd(ws_bytes=0) == WS
+    assert _router_bwd(ws=None) == INVALID
+    assert _router_bwd(dx_out=MIS) == INVALID
+
+
+def test_router_backward_workspace_size():
+    # per-chunk (256 tokens) dW_g partials, db partials, one float per token
+    T, E, d = 300, 8, 64
+    got = L.moe_workspace_bytes(3, BF16, T, E, 2, d, 0)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert got == up(2 * E * d * 4) + up(2 * E * 4) + up(T * 4)
+    # without d (no dw_g / dx) the size query and the entry agree
+    assert L.moe_workspace_bytes(3, BF16, T, E, 2, 0, 0) > 0
