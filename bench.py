@@ -78,7 +78,7 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
         "quant_x": T * d * (2 + q),
         "quant_weights": 3 * E * d * f * (2 + q),
         "quant_bwd_operands": (Tk * d + 3 * E * d * f) * (2 + q),
-        "quant_tokens": Tk * (2 * d + 3 * f) * (2 + q),
+        "quant_tokens": Tk * 2 * d * (2 + q),      # dO and Xp
     }.get(name, 0)
 
 

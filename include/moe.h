@@ -16,7 +16,11 @@
  *  [P4] "How MoE Architecture Cuts Costs and Boosts Efficiency: Efficient
  *       Training of Biological Foundation Models", section "Why Biology Is
  *       Especially Well-Suited for MoE" (top-K router over per-expert
- *       scores).
+ *       scores) and "Engineering Challenges of Efficient Training" (load
+ *       balance).
+ *  [P5] the hgpu.org abstract of an MXFP4 MoE training recipe on Hopper
+ *       (block-quantized activations converted from row blocks to column
+ *       blocks with their scales, without a round trip through bf16).
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the
@@ -195,6 +199,16 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   inside the gate_up epilogue, from its fp32 value, for the down GEMM
  *   (held in the workspace); ab_saved/s_saved stay bf16, out_perm fp32.
  *   d and f must be multiples of 128.
+ *   With s_tok / s_tok_scales (MXFP8 only; [P5]'s conversion from row blocks
+ *   to column blocks, done inside the kernel that produces S) the same epilogue also
+ *   writes S quantized along each expert's tokens from its bf16 value --
+ *   bit for bit what moe_mxfp8_quantize axis 1 (seg_offsets = offsets,
+ *   rows_pad = ldt) makes of s_saved -- for the dW2 GEMM of the backward:
+ *   codes [f][ldt], scales [f][ldt/32], ldt a multiple of 128 and at
+ *   least moe_mxfp8_padded_rows(Tk, E).  Every expert's padded rows are
+ *   written (zero codes past its last row); columns past the last
+ *   expert's padded rows are not.  s_saved may then be NULL.  For bf16
+ *   s_tok must be NULL and s_saved is required.
  * w_perm may be NULL (weight 1).  Workspace: MOE_ENTRY_MLP_FWD (none for
  * bf16).
  */
@@ -205,8 +219,9 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
                                const uint8_t* w_gu_scales, const void* w2,
                                const uint8_t* w2_scales, const float* w_perm,
                                void* ab_saved, void* s_saved, void* out_perm,
-                               void* workspace, size_t workspace_bytes,
-                               hipStream_t stream);
+                               uint8_t* s_tok, uint8_t* s_tok_scales,
+                               int64_t ldt, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_grouped_mlp_bwd -- backward of moe_grouped_mlp_fwd ([P1] Challenge 3
@@ -229,7 +244,10 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   epilogue that produces it, from fp32), and for the weight gradients
  *   dO, s_saved, dAB (its bf16 value) and x_perm along the rows of each
  *   expert, blocks restarting at the expert's first row.  d and f must be
- *   multiples of 128.
+ *   multiples of 128.  dAB's token-axis codes come out of the epilogue
+ *   that produces dAB (no bf16 dAB is stored).  With s_tok/s_tok_scales
+ *   from the forward (ldt = moe_mxfp8_padded_rows(T*k, E)) S is not
+ *   quantized again and s_saved may be NULL; for bf16 s_tok must be NULL.
  * Workspace: MOE_ENTRY_MLP_BWD.
  */
 moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
@@ -238,6 +256,8 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                int32_t E, int64_t d, int64_t f,
                                const void* w_gu, const void* w2,
                                const void* ab_saved, const void* s_saved,
+                               const uint8_t* s_tok,
+                               const uint8_t* s_tok_scales, int64_t ldt,
                                const float* w_perm, void* dx_perm,
                                void* dw_gu, void* dw2, float* dp,
                                void* workspace, size_t workspace_bytes,
@@ -304,15 +324,20 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
  * be multiples of 128; outputs as in the bf16 stages.
  *
  * moe_mx_gate_up_swiglu_fwd: xq [T*k][d], xs [T*k][d/32]; wq [E][2f][d],
- *   ws [E][2f][d/32]; writes ab_saved, s_saved (bf16) and S quantized
- *   along f from its fp32 value: sq [T*k][f], ss [T*k][f/32].
+ *   ws [E][2f][d/32]; writes ab_saved, s_saved (bf16, may be NULL) and S
+ *   quantized along f from its fp32 value: sq [T*k][f], ss [T*k][f/32];
+ *   with s_tok/s_tok_scales also S along each expert's tokens (as in
+ *   moe_grouped_mlp_fwd; NULL to skip).
  * moe_mx_down_fwd: sq/ss as written above; wq [E][d][f], ws [E][d][f/32];
  *   out_perm [P][T*k][d] fp32.
  * moe_mx_down_swiglu_bwd: doq [T*k][d], dos [T*k][d/32] (dout_perm along
  *   d); w2tq [f][E*d], w2ts [f][E*d/32] (w2 viewed as [E*d][f] quantized
  *   with moe_mxfp8_quantize axis 1, one segment, rows_pad E*d: expert e
- *   in columns [e*d, (e+1)*d)); writes dab (bf16), dAB quantized along 2f
- *   from fp32 (dabq [T*k][2f], dabs [T*k][2f/32]) and dp_part.
+ *   in columns [e*d, (e+1)*d)); writes dab (bf16, may be NULL), dAB
+ *   quantized along 2f from fp32 (dabq [T*k][2f], dabs [T*k][2f/32]),
+ *   dp_part and, with dab_tok/dab_tok_scales, dAB along each expert's
+ *   tokens from its bf16 value (codes [2f][ldt], scales [2f][ldt/32],
+ *   bit for bit moe_mxfp8_quantize axis 1 of the bf16 dab; NULL to skip).
  * moe_mx_gate_up_dgrad: dabq/dabs as written above; wgutq [d][E*2f],
  *   wguts [d][E*2f/32] (w_gu viewed as [E*2f][d], axis 1, one segment,
  *   rows_pad E*2f); dx_perm [P][T*k][d] fp32.
@@ -327,7 +352,8 @@ moe_status moe_mx_gate_up_swiglu_fwd(
     const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
     int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
     const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
-    uint8_t* ss, hipStream_t stream);
+    uint8_t* ss, uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
+    hipStream_t stream);
 
 moe_status moe_mx_down_fwd(const uint8_t* sq, const uint8_t* ss,
                            const int32_t* offsets, int32_t E, int64_t Tk,
@@ -339,7 +365,8 @@ moe_status moe_mx_down_swiglu_bwd(
     const uint8_t* doq, const uint8_t* dos, const int32_t* offsets,
     int32_t E, int64_t Tk, int64_t d, int64_t f, const uint8_t* w2tq,
     const uint8_t* w2ts, const void* ab_saved, const float* w_perm,
-    void* dab, uint8_t* dabq, uint8_t* dabs, float* dp_part,
+    void* dab, uint8_t* dabq, uint8_t* dabs, uint8_t* dab_tok,
+    uint8_t* dab_tok_scales, int64_t ldt, float* dp_part,
     hipStream_t stream);
 
 moe_status moe_mx_gate_up_dgrad(const uint8_t* dabq, const uint8_t* dabs,

@@ -170,6 +170,32 @@ struct BwdWorkspace {
   size_t dab = 0, dp_part = 0, total = 0;
 };
 
+// The MX backward keeps no bf16 dAB (its epilogue writes both MX forms):
+// its workspace starts with dp_part alone.
+size_t mx_bwd_base(int64_t Tk, int64_t f) {
+  return align256(static_cast<size_t>(Tk * moe::gemm_dp_tiles(f) * 4));
+}
+
+// Optional token-axis MX output (codes [cols][ldt], scales [cols][ldt/32]):
+// both pointers or neither; ldt a multiple of 128 holding every expert's
+// padded rows.
+moe_status check_tok_out(const char* what, const void* codes,
+                         const void* scales, int64_t ldt, int64_t Tk,
+                         int32_t E, int64_t cols) {
+  if (!codes && !scales) return MOE_OK;
+  REQUIRE(codes && scales, MOE_ERR_INVALID_ARG,
+          "%s: token-axis codes and scales go together", what);
+  REQUIRE(aligned16(codes) && aligned16(scales), MOE_ERR_INVALID_ARG,
+          "%s: token-axis outputs must be 16-byte aligned", what);
+  REQUIRE(ldt % 128 == 0 && ldt >= padded_tokens(Tk, E), MOE_ERR_INVALID_ARG,
+          "%s: ldt must be a multiple of 128 and >= %lld (got %lld)", what,
+          static_cast<long long>(padded_tokens(Tk, E)),
+          static_cast<long long>(ldt));
+  REQUIRE(cols * ldt <= (int64_t{1} << 40), MOE_ERR_UNSUPPORTED,
+          "%s: token-axis output too large", what);
+  return MOE_OK;
+}
+
 BwdWorkspace bwd_layout(int64_t Tk, int64_t f) {
   BwdWorkspace w;
   w.dab = 0;
@@ -215,7 +241,7 @@ size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
     case MOE_ENTRY_MLP_BWD:
       if (f < 1 || d < 1) return 0;
       if (prec == MOE_BF16) return bwd_layout(Tk, f).total;
-      return mx_bwd_layout(Tk, E, d, f, bwd_layout(Tk, f).total).total;
+      return mx_bwd_layout(Tk, E, d, f, mx_bwd_base(Tk, f)).total;
   }
   return 0;
 }
@@ -372,8 +398,9 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
                                const uint8_t* w_gu_scales, const void* w2,
                                const uint8_t* w2_scales, const float* w_perm,
                                void* ab_saved, void* s_saved, void* out_perm,
-                               void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
+                               uint8_t* s_tok, uint8_t* s_tok_scales,
+                               int64_t ldt, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
   if (moe_status st = check_prec(prec)) return st;
   REQUIRE_PTR(x_perm);
   REQUIRE_PTR(offsets);
@@ -381,8 +408,12 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE_PTR(w2);
   REQUIRE_OPT_PTR(w_perm);
   REQUIRE_PTR(ab_saved);
-  REQUIRE_PTR(s_saved);
+  REQUIRE_OPT_PTR(s_saved);
   REQUIRE_PTR(out_perm);
+  REQUIRE(prec == MOE_MXFP8 || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
+          "token-axis S codes are an MXFP8 output");
+  REQUIRE(s_saved || (prec == MOE_MXFP8 && s_tok), MOE_ERR_INVALID_ARG,
+          "s_saved is NULL (it may be only with MXFP8 token-axis S codes)");
   REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
           "E must be in [1, %d]", moe::kMaxExperts);
   REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
@@ -396,6 +427,9 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
     REQUIRE_PTR(x_perm_scales);
     REQUIRE_PTR(w_gu_scales);
     REQUIRE_PTR(w2_scales);
+    if (moe_status st = check_tok_out("moe_grouped_mlp_fwd", s_tok,
+                                      s_tok_scales, ldt, Tk, E, f))
+      return st;
     const MxFwdWorkspace L = mx_fwd_layout(Tk, f);
     REQUIRE(workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
             "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
@@ -405,7 +439,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
         static_cast<const uint8_t*>(x_perm), x_perm_scales,
         static_cast<const uint8_t*>(w_gu), w_gu_scales, offsets, E, Tk, d, f,
         w_perm, static_cast<bf16_t*>(ab_saved), static_cast<bf16_t*>(s_saved),
-        ws + L.sq, ws + L.ss, stream);
+        ws + L.sq, ws + L.ss, s_tok, s_tok_scales, ldt, stream);
     if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_fwd/mx_fc1");
     e = moe::gemm_mx_fc2_fwd(ws + L.sq, ws + L.ss,
                              static_cast<const uint8_t*>(w2), w2_scales,
@@ -430,6 +464,8 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                int32_t E, int64_t d, int64_t f,
                                const void* w_gu, const void* w2,
                                const void* ab_saved, const void* s_saved,
+                               const uint8_t* s_tok,
+                               const uint8_t* s_tok_scales, int64_t ldt,
                                const float* w_perm, void* dx_perm,
                                void* dw_gu, void* dw2, float* dp,
                                void* workspace, size_t workspace_bytes,
@@ -442,9 +478,13 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   REQUIRE_PTR(w_gu);
   REQUIRE_PTR(w2);
   REQUIRE_PTR(ab_saved);
-  REQUIRE_PTR(s_saved);
+  REQUIRE_OPT_PTR(s_saved);
   REQUIRE_OPT_PTR(w_perm);
   REQUIRE_PTR(dx_perm);
+  REQUIRE(prec == MOE_MXFP8 || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
+          "token-axis S codes are an MXFP8 input");
+  REQUIRE(s_saved || (prec == MOE_MXFP8 && s_tok), MOE_ERR_INVALID_ARG,
+          "s_saved is NULL (it may be only with MXFP8 token-axis S codes)");
   REQUIRE_PTR(dw_gu);
   REQUIRE_PTR(dw2);
   REQUIRE_PTR(dp);
@@ -458,15 +498,21 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   const BwdWorkspace L = bwd_layout(Tk, f);
   if (prec == MOE_MXFP8) {
     if (moe_status st = check_mx_dims(d, f)) return st;
-    const MxBwdWorkspace X = mx_bwd_layout(Tk, E, d, f, L.total);
+    if (moe_status st = check_tok_out("moe_grouped_mlp_bwd", s_tok,
+                                      s_tok_scales, ldt, Tk, E, f))
+      return st;
+    REQUIRE(!s_tok || ldt == padded_tokens(Tk, E), MOE_ERR_INVALID_ARG,
+            "ldt must be moe_mxfp8_padded_rows(T*k, E) = %lld (got %lld)",
+            static_cast<long long>(padded_tokens(Tk, E)),
+            static_cast<long long>(ldt));
+    const MxBwdWorkspace X = mx_bwd_layout(Tk, E, d, f, mx_bwd_base(Tk, f));
     REQUIRE(2 * f * X.tk_pad <= kMaxBytes && E * 2 * f * d <= kMaxBytes,
             MOE_ERR_UNSUPPORTED, "MX operand larger than 2 GiB");
     REQUIRE(workspace_bytes >= X.total, MOE_ERR_WORKSPACE,
             "workspace too small: %zu < %zu bytes", workspace_bytes, X.total);
     REQUIRE_PTR(workspace);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    bf16_t* dab = reinterpret_cast<bf16_t*>(ws + L.dab);
-    float* dp_part = reinterpret_cast<float*>(ws + L.dp_part);
+    float* dp_part = reinterpret_cast<float*>(ws);
     const bf16_t* dO = static_cast<const bf16_t*>(dout_perm);
     const int64_t tp = X.tk_pad;
     hipError_t e;
@@ -487,8 +533,9 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
     MX_STEP(moe::gemm_mx_fc2_dgrad(ws + X.doq, ws + X.dos, ws + X.w2tq,
                                    ws + X.w2ts, E * d, offsets, E, Tk, d, f,
                                    static_cast<const bf16_t*>(ab_saved),
-                                   w_perm, dab, ws + X.dabq, ws + X.dabs,
-                                   dp_part, stream), "mx_fc2_dgrad");
+                                   w_perm, nullptr, ws + X.dabq, ws + X.dabs,
+                                   ws + X.dabt, ws + X.dabts, tp, dp_part,
+                                   stream), "mx_fc2_dgrad");
     MX_STEP(moe::launch_dp_reduce(dp_part, moe::gemm_dp_tiles(f), pos, T, k,
                                   dp, stream), "dp");
     MX_STEP(moe::gemm_mx_fc1_dgrad(ws + X.dabq, ws + X.dabs, ws + X.wgutq,
@@ -499,17 +546,20 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
     MX_STEP(moe::launch_mx_quant_tokens(dO, nullptr, Tk, d, offsets, E,
                                         ws + X.dot, ws + X.dots, tp, stream),
             "quant_dO_tokens");
-    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(s_saved),
-                                        nullptr, Tk, f, offsets, E,
-                                        ws + X.st, ws + X.sts, tp, stream),
-            "quant_S_tokens");
-    MX_STEP(moe::gemm_mx_wgrad(ws + X.dot, ws + X.dots, ws + X.st,
-                               ws + X.sts, tp, offsets, E, d, f,
-                               static_cast<bf16_t*>(dw2), stream),
+    const uint8_t* st_c = s_tok;
+    const uint8_t* st_s = s_tok_scales;
+    if (!s_tok) {
+      MX_STEP(moe::launch_mx_quant_tokens(
+                  static_cast<const bf16_t*>(s_saved), nullptr, Tk, f,
+                  offsets, E, ws + X.st, ws + X.sts, tp, stream),
+              "quant_S_tokens");
+      st_c = ws + X.st;
+      st_s = ws + X.sts;
+    }
+    MX_STEP(moe::gemm_mx_wgrad(ws + X.dot, ws + X.dots, st_c, st_s, tp,
+                               offsets, E, d, f, static_cast<bf16_t*>(dw2),
+                               stream),
             "mx_dw2");
-    MX_STEP(moe::launch_mx_quant_tokens(dab, nullptr, Tk, 2 * f, offsets, E,
-                                        ws + X.dabt, ws + X.dabts, tp,
-                                        stream), "quant_dAB_tokens");
     MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(x_perm),
                                         nullptr, Tk, d, offsets, E,
                                         ws + X.xpt, ws + X.xpts, tp, stream),
@@ -692,17 +742,22 @@ moe_status moe_mx_gate_up_swiglu_fwd(
     const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
     int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
     const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
-    uint8_t* ss, hipStream_t stream) {
+    uint8_t* ss, uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
+    hipStream_t stream) {
   REQUIRE_PTR(xq); REQUIRE_PTR(xs); REQUIRE_PTR(offsets);
   REQUIRE_PTR(wq); REQUIRE_PTR(ws); REQUIRE_OPT_PTR(w_perm);
-  REQUIRE_PTR(ab_saved); REQUIRE_PTR(s_saved); REQUIRE_PTR(sq);
+  REQUIRE_PTR(ab_saved); REQUIRE_OPT_PTR(s_saved); REQUIRE_PTR(sq);
   REQUIRE_PTR(ss);
   if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
   if (moe_status st = check_mx_dims(d, f)) return st;
+  if (moe_status st = check_tok_out("moe_mx_gate_up_swiglu_fwd", s_tok,
+                                    s_tok_scales, ldt, Tk, E, f))
+    return st;
   return hip_status(
       moe::gemm_mx_fc1_fwd(xq, xs, wq, ws, offsets, E, Tk, d, f, w_perm,
                            static_cast<bf16_t*>(ab_saved),
-                           static_cast<bf16_t*>(s_saved), sq, ss, stream),
+                           static_cast<bf16_t*>(s_saved), sq, ss, s_tok,
+                           s_tok_scales, ldt, stream),
       "moe_mx_gate_up_swiglu_fwd");
 }
 
@@ -724,19 +779,23 @@ moe_status moe_mx_down_swiglu_bwd(
     const uint8_t* doq, const uint8_t* dos, const int32_t* offsets,
     int32_t E, int64_t Tk, int64_t d, int64_t f, const uint8_t* w2tq,
     const uint8_t* w2ts, const void* ab_saved, const float* w_perm,
-    void* dab, uint8_t* dabq, uint8_t* dabs, float* dp_part,
+    void* dab, uint8_t* dabq, uint8_t* dabs, uint8_t* dab_tok,
+    uint8_t* dab_tok_scales, int64_t ldt, float* dp_part,
     hipStream_t stream) {
   REQUIRE_PTR(doq); REQUIRE_PTR(dos); REQUIRE_PTR(offsets);
   REQUIRE_PTR(w2tq); REQUIRE_PTR(w2ts); REQUIRE_PTR(ab_saved);
-  REQUIRE_OPT_PTR(w_perm); REQUIRE_PTR(dab); REQUIRE_PTR(dabq);
+  REQUIRE_OPT_PTR(w_perm); REQUIRE_OPT_PTR(dab); REQUIRE_PTR(dabq);
   REQUIRE_PTR(dabs); REQUIRE_PTR(dp_part);
   if (moe_status st = check_mlp_dims(E, Tk, d, f, MOE_MXFP8)) return st;
   if (moe_status st = check_mx_dims(d, f)) return st;
+  if (moe_status st = check_tok_out("moe_mx_down_swiglu_bwd", dab_tok,
+                                    dab_tok_scales, ldt, Tk, E, 2 * f))
+    return st;
   return hip_status(
       moe::gemm_mx_fc2_dgrad(doq, dos, w2tq, w2ts, E * d, offsets, E, Tk, d,
                              f, static_cast<const bf16_t*>(ab_saved), w_perm,
-                             static_cast<bf16_t*>(dab), dabq, dabs, dp_part,
-                             stream),
+                             static_cast<bf16_t*>(dab), dabq, dabs, dab_tok,
+                             dab_tok_scales, ldt, dp_part, stream),
       "moe_mx_down_swiglu_bwd");
 }
 

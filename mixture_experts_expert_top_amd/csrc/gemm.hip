@@ -131,6 +131,15 @@ struct Params {
   // S (kSwiglu, ldq = f) or dAB (kDSwiglu, ldq = 2f); null to skip
   uint8_t* Qc;
   uint8_t* Qs;
+  // MX token-axis epilogue outputs (kSwiglu: S, f columns; kDSwiglu: dAB,
+  // 2f columns), quantized from the bf16 values the epilogue rounds to, in
+  // blocks of 32 rows restarting at each expert's first row: codes
+  // [cols][ldt] and scales [cols][ldt / 32], expert e's rows starting at
+  // its padded start (the sum over e' < e of counts rounded up to 128);
+  // null to skip
+  uint8_t* Tc;
+  uint8_t* Ts;
+  int64_t ldt;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -301,9 +310,8 @@ __device__ __forceinline__ uint32_t mx_quant4(const float* v, bool valid,
   for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   const int e = mx_scale_exp(amax);
   const float inv = mx_inv_scale(e);
-  uint32_t word = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) word |= e4m3_encode(v[c] * inv) << (8 * c);
+  const uint32_t word =
+      e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
   *scale_byte = static_cast<uint32_t>(e + 127);
   return word;
 }
@@ -849,6 +857,26 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
                                                                 : nullptr;
   constexpr int kLanesPerRow = TN / 4;             // 4 columns a lane
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  // Token-axis MX output: each wave's TM = 128 rows are one 128-row unit
+  // of the padded layout (four 32-row blocks, two per pass), so a wave
+  // writes whole 128-byte code lines and one scale dword per column.
+  constexpr bool kTokEpi = MX && (EPI == kSwiglu || EPI == kDSwiglu) &&
+                           TM == kMxPad && TN == 64;
+  const bool tok = kTokEpi && P.Tc != nullptr;
+  int64_t pe = 0;                                  // padded start of e
+  const int pad_len = (seg_len + kMxPad - 1) / kMxPad * kMxPad;
+  const int wrow0 = m0 + wm * TM;                  // wave's first row in e
+  uint32_t tsc[2] = {0u, 0u};                      // scale bytes, 4 blocks
+  if (tok) {
+    int acc_p = 0;
+    for (int i = lane; i < e; i += 64) {
+      const int n = P.offsets[i + 1] - P.offsets[i];
+      acc_p += (n + kMxPad - 1) / kMxPad * kMxPad;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc_p += __shfl_xor(acc_p, m, 64);
+    pe = acc_p;
+  }
 #pragma unroll
   for (int h = 0; h < TM / kEpiRows; ++h) {
 #pragma unroll
@@ -912,14 +940,56 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
                   static_cast<uint8_t>(sbyte);
           }
         }
+        uint2 os;
+        os.x = pack_bf16x2(sv[0], sv[1]); os.y = pack_bf16x2(sv[2], sv[3]);
         if (ok) {
-          uint2 og, ou, os;
+          uint2 og, ou;
           og.x = pack_bf16x2(g[0], g[1]); og.y = pack_bf16x2(g[2], g[3]);
           ou.x = pack_bf16x2(u[0], u[1]); ou.y = pack_bf16x2(u[2], u[3]);
-          os.x = pack_bf16x2(sv[0], sv[1]); os.y = pack_bf16x2(sv[2], sv[3]);
           *reinterpret_cast<uint2*>(AB + ro * P.ldc + col) = og;
           *reinterpret_cast<uint2*>(AB + ro * P.ldc + f + col) = ou;
-          *reinterpret_cast<uint2*>(S + ro * f + col) = os;
+          if (P.S) *reinterpret_cast<uint2*>(S + ro * f + col) = os;
+        }
+        if constexpr (kTokEpi) {
+          // the bf16 S values go back over this row's gate slots for the
+          // token-axis pass (zero past the expert's rows)
+          if (tok) {
+            f32x4 sb;
+            sb[0] = ok ? bf_lo(os.x) : 0.0f; sb[1] = ok ? bf_hi(os.x) : 0.0f;
+            sb[2] = ok ? bf_lo(os.y) : 0.0f; sb[3] = ok ? bf_hi(os.y) : 0.0f;
+            *reinterpret_cast<f32x4*>(stage + r * LD + c4) = sb;
+          }
+        }
+      }
+      if constexpr (kTokEpi) {
+        if (tok) {
+          // lane = (32-row block cb of this pass, S column cc of the wave)
+          __syncthreads();
+          const int cb = lane >> 5, cc = lane & 31;
+          float v[kMxBlock];
+          float amax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < kMxBlock; ++i) {
+            v[i] = stage[(cb * kMxBlock + i) * LD + cc];
+            amax = fmaxf(amax, fabsf(v[i]));
+          }
+          const int ex = mx_scale_exp(amax);
+          const float inv = mx_inv_scale(ex);
+          i32x4 q[2];
+#pragma unroll
+          for (int k4 = 0; k4 < 8; ++k4)
+            q[k4 >> 2][k4 & 3] = static_cast<int>(
+                e4m3_pack4(v[k4 * 4] * inv, v[k4 * 4 + 1] * inv,
+                           v[k4 * 4 + 2] * inv, v[k4 * 4 + 3] * inv));
+          const int trow = wrow0 + h * kEpiRows + cb * kMxBlock;
+          if (trow < pad_len) {
+            uint8_t* dst = P.Tc +
+                static_cast<int64_t>(n0g + wn * (TN / 2) + cc) * P.ldt + pe +
+                trow;
+            *reinterpret_cast<i32x4*>(dst) = q[0];
+            *reinterpret_cast<i32x4*>(dst + 16) = q[1];
+          }
+          tsc[0] |= static_cast<uint32_t>(ex + 127) << (8 * (2 * h + cb));
         }
       }
     } else {  // kDSwiglu
@@ -953,11 +1023,24 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             dg[c] = dh * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
             du[c] = dh * sl;
           }
-          uint2 og, ou;
-          og.x = pack_bf16x2(dg[0], dg[1]); og.y = pack_bf16x2(dg[2], dg[3]);
-          ou.x = pack_bf16x2(du[0], du[1]); ou.y = pack_bf16x2(du[2], du[3]);
-          *reinterpret_cast<uint2*>(dAB + ro * P.ldc + col) = og;
-          *reinterpret_cast<uint2*>(dAB + ro * P.ldc + f + col) = ou;
+          if (P.C) {
+            uint2 og, ou;
+            og.x = pack_bf16x2(dg[0], dg[1]); og.y = pack_bf16x2(dg[2], dg[3]);
+            ou.x = pack_bf16x2(du[0], du[1]); ou.y = pack_bf16x2(du[2], du[3]);
+            *reinterpret_cast<uint2*>(dAB + ro * P.ldc + col) = og;
+            *reinterpret_cast<uint2*>(dAB + ro * P.ldc + f + col) = ou;
+          }
+        }
+        if constexpr (kTokEpi) {
+          // (bf16 dA_g, bf16 dA_u) pairs go back over this row's dS slots
+          // for the token-axis pass (zero past the expert's rows)
+          if (tok) {
+            i32x4 pk;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              pk[c] = static_cast<int>(pack_bf16x2(dg[c], du[c]));
+            *reinterpret_cast<i32x4*>(stage + r * LD + c4) = pk;
+          }
         }
         if constexpr (MX) {
           // dAB along 2f: gate and up blocks of 32 columns, 8 lanes each
@@ -982,8 +1065,75 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         if ((lane % kLanesPerRow) == 0)
           s_dp[wn * BM + wm * TM + h * kEpiRows + r] = part;
       }
+      if constexpr (kTokEpi) {
+        if (tok) {
+          // lane = dS column of the wave; both 32-row blocks of the pass,
+          // gate (low half) and up (high half) of the packed pairs
+          __syncthreads();
+          const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
+          const int col = n0 + wn * TN + lane;
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            uint32_t pk[kMxBlock];
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kMxBlock; ++i) {
+              pk[i] = st32[(cb * kMxBlock + i) * LD + lane];
+              ag = fmaxf(ag, fabsf(bf_lo(pk[i])));
+              au = fmaxf(au, fabsf(bf_hi(pk[i])));
+            }
+            const int eg = mx_scale_exp(ag), eu = mx_scale_exp(au);
+            const float ig = mx_inv_scale(eg), iu = mx_inv_scale(eu);
+            i32x4 qg[2], qu[2];
+#pragma unroll
+            for (int k4 = 0; k4 < 8; ++k4) {
+              const uint32_t* p4 = pk + k4 * 4;
+              qg[k4 >> 2][k4 & 3] = static_cast<int>(e4m3_pack4(
+                  bf_lo(p4[0]) * ig, bf_lo(p4[1]) * ig, bf_lo(p4[2]) * ig,
+                  bf_lo(p4[3]) * ig));
+              qu[k4 >> 2][k4 & 3] = static_cast<int>(e4m3_pack4(
+                  bf_hi(p4[0]) * iu, bf_hi(p4[1]) * iu, bf_hi(p4[2]) * iu,
+                  bf_hi(p4[3]) * iu));
+            }
+            const int trow = wrow0 + h * kEpiRows + cb * kMxBlock;
+            if (trow < pad_len && col < f) {
+              uint8_t* dg_dst = P.Tc + static_cast<int64_t>(col) * P.ldt + pe +
+                                trow;
+              uint8_t* du_dst = dg_dst + static_cast<int64_t>(f) * P.ldt;
+              *reinterpret_cast<i32x4*>(dg_dst) = qg[0];
+              *reinterpret_cast<i32x4*>(dg_dst + 16) = qg[1];
+              *reinterpret_cast<i32x4*>(du_dst) = qu[0];
+              *reinterpret_cast<i32x4*>(du_dst + 16) = qu[1];
+            }
+            tsc[0] |= static_cast<uint32_t>(eg + 127) << (8 * (2 * h + cb));
+            tsc[1] |= static_cast<uint32_t>(eu + 127) << (8 * (2 * h + cb));
+          }
+        }
+      }
     }
     __syncthreads();
+  }
+  if constexpr (kTokEpi) {
+    // one scale dword (the wave's four 32-row blocks) per column
+    if (tok && wrow0 < pad_len) {
+      const int64_t so = (pe + wrow0) / kMxBlock;
+      const int64_t lds_t = P.ldt / kMxBlock;
+      if (EPI == kSwiglu) {
+        // lanes 0-31 hold blocks 0 and 2, lanes 32-63 blocks 1 and 3
+        const uint32_t word = tsc[0] | __shfl(tsc[0], (lane & 31) + 32, 64);
+        if (lane < 32) {
+          const int col = n0g + wn * (TN / 2) + lane;
+          *reinterpret_cast<uint32_t*>(P.Ts + col * lds_t + so) = word;
+        }
+      } else {
+        const int col = n0 + wn * TN + lane;
+        if (col < f) {
+          *reinterpret_cast<uint32_t*>(P.Ts + col * lds_t + so) = tsc[0];
+          *reinterpret_cast<uint32_t*>(P.Ts + (f + col) * lds_t + so) =
+              tsc[1];
+        }
+      }
+    }
   }
   if (EPI == kDSwiglu) {
     // the tile's column groups, added in order (wn = 0, 1, ...)
@@ -1118,14 +1268,20 @@ hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
 // Operands are E4M3 codes with one E8M0 byte per 32 codes along K; the
 // kernel addresses codes in pairs, so leading dimensions and K are halved.
 
-// fc1 forward: AB = Xp . W_gu^T, S = w*silu(g)*u as bf16 and as MX codes
-// along f (the down GEMM's A)
+// The token-axis epilogue output needs waves of 128 rows x 64 columns.
+constexpr bool kMxTokEpi = CfgMx::TM == kMxPad && CfgMx::TN == 64;
+
+// fc1 forward: AB = Xp . W_gu^T, S = w*silu(g)*u as bf16 (s, optional),
+// as MX codes along f (the down GEMM's A) and, optionally, as MX codes
+// along each expert's tokens from its bf16 value (the dW2 GEMM's B)
 hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
                            const uint8_t* wq, const uint8_t* ws,
                            const int32_t* offsets, int E, int64_t Tk,
                            int64_t d, int64_t f, const float* w_perm,
                            bf16_t* ab, bf16_t* s, uint8_t* sq, uint8_t* ss,
+                           uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
                            hipStream_t st) {
+  if (s_tok && !kMxTokEpi) return hipErrorInvalidValue;
   Params P{};
   P.A = reinterpret_cast<const bf16_t*>(xq); P.lda = d / 2;
   P.sA = xs; P.lds_a = d / kMxBlock;
@@ -1137,6 +1293,7 @@ hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
   P.N = f; P.K = d / 2; P.f = f;
   P.ntn = static_cast<int>((f + BN / 2 - 1) / (BN / 2));
   P.w = w_perm; P.S = s; P.Qc = sq; P.Qs = ss;
+  P.Tc = s_tok; P.Ts = s_tok_scales; P.ldt = ldt;
   return launch<CfgMx, kSegM, true, true, kSwiglu, true>(
       P, segm_grid(Tk, E, P.ntn), st);
 }
@@ -1163,14 +1320,18 @@ hipError_t gemm_mx_fc2_fwd(const uint8_t* sq, const uint8_t* ss,
 
 // fc2 dgrad + dSwiGLU: dS = dO . W2 with W2 quantized along d and stored
 // transposed ([f][ldw] codes, expert e in columns [e d, (e+1) d)); dAB as
-// bf16 and as MX codes along 2f (the gate_up data gradient's A)
+// bf16 (dab, optional), as MX codes along 2f (the gate_up data gradient's
+// A) and, optionally, as MX codes along each expert's tokens from its bf16
+// value (the dW_gu GEMM's A)
 hipError_t gemm_mx_fc2_dgrad(const uint8_t* doq, const uint8_t* dos,
                              const uint8_t* wtq, const uint8_t* wts,
                              int64_t ldw, const int32_t* offsets, int E,
                              int64_t Tk, int64_t d, int64_t f,
                              const bf16_t* ab, const float* w_perm,
                              bf16_t* dab, uint8_t* dabq, uint8_t* dabs,
-                             float* dp_part, hipStream_t st) {
+                             uint8_t* dab_tok, uint8_t* dab_tok_scales,
+                             int64_t ldt, float* dp_part, hipStream_t st) {
+  if (dab_tok && !kMxTokEpi) return hipErrorInvalidValue;
   Params P{};
   P.A = reinterpret_cast<const bf16_t*>(doq); P.lda = d / 2;
   P.sA = dos; P.lds_a = d / kMxBlock;
@@ -1182,6 +1343,7 @@ hipError_t gemm_mx_fc2_dgrad(const uint8_t* doq, const uint8_t* dos,
   P.N = f; P.K = d / 2; P.f = f;
   P.ntn = gemm_dp_tiles(f);
   P.AB = ab; P.w = w_perm; P.dp_part = dp_part; P.Qc = dabq; P.Qs = dabs;
+  P.Tc = dab_tok; P.Ts = dab_tok_scales; P.ldt = ldt;
   return launch<CfgMx, kSegM, true, true, kDSwiglu, true>(
       P, segm_grid(Tk, E, P.ntn), st);
 }

@@ -101,6 +101,7 @@ hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
                            const int32_t* offsets, int E, int64_t Tk,
                            int64_t d, int64_t f, const float* w_perm,
                            bf16_t* ab, bf16_t* s, uint8_t* sq, uint8_t* ss,
+                           uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
                            hipStream_t st);
 hipError_t gemm_mx_fc2_fwd(const uint8_t* sq, const uint8_t* ss,
                            const uint8_t* wq, const uint8_t* ws,
@@ -112,7 +113,8 @@ hipError_t gemm_mx_fc2_dgrad(const uint8_t* doq, const uint8_t* dos,
                              int64_t Tk, int64_t d, int64_t f,
                              const bf16_t* ab, const float* w_perm,
                              bf16_t* dab, uint8_t* dabq, uint8_t* dabs,
-                             float* dp_part, hipStream_t st);
+                             uint8_t* dab_tok, uint8_t* dab_tok_scales,
+                             int64_t ldt, float* dp_part, hipStream_t st);
 hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
                              const uint8_t* wtq, const uint8_t* wts,
                              int64_t ldw, const int32_t* offsets, int E,

@@ -28,29 +28,24 @@ __device__ __forceinline__ float mx_inv_scale(int e) {
   return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
 }
 
-// E4M3 code of x (already divided by the block scale): round to nearest,
-// ties to even mantissa, saturate at +-448, keep the sign (also of zero).
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __uint_as_float(u & 0x7fffffffu);
-  uint32_t code;
-  if (!(a < 448.0f)) {
-    code = 0x7eu;                              // saturate (448 itself too)
-  } else if (a < 0.015625f) {                  // below 2^-6: subnormal step
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 0..8
-  } else {
-    const uint32_t b = u & 0x7fffffffu;
-    uint32_t exp = (b >> 23) - 127 + 7;        // biased E4M3 exponent 1..15
-    uint32_t man = (b >> 20) & 7u;
-    const uint32_t rem = b & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (man & 1u))) {
-      if (++man == 8u) { man = 0; ++exp; }
-    }
-    code = (exp << 3) | man;
-    if (code > 0x7eu) code = 0x7eu;
-  }
-  return code | sign;
+// E4M3 codes of four values (already divided by the block scale), packed
+// little-endian: round to nearest, ties to even mantissa, saturate at
+// +-448, keep the sign (also of zero).  gfx950's v_cvt_pk_fp8_f32 converts
+// two floats to OCP E4M3 with round-to-nearest-even; it returns NaN past
+// the largest finite value, so the inputs are clamped to +-448 first.
+// Checked against a software encoder of this rule on every float of
+// magnitude below 512, both signs (no difference), and against the
+// float64 codec on every finite bf16 value in the tests.
+__device__ __forceinline__ float e4m3_clamp(float x) {
+  return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
+                                               float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0,
+                                          false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+  return static_cast<uint32_t>(w);
 }
 
 }  // namespace moe

@@ -46,13 +46,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const float inv = mx_inv_scale(e);
   i32x4 out[2];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      word |= e4m3_encode(v[q * 4 + b] * inv) << (8 * b);
-    out[q >> 2][q & 3] = static_cast<int>(word);
-  }
+  for (int q = 0; q < 8; ++q)
+    out[q >> 2][q & 3] = static_cast<int>(
+        e4m3_pack4(v[q * 4] * inv, v[q * 4 + 1] * inv, v[q * 4 + 2] * inv,
+                   v[q * 4 + 3] * inv));
   i32x4* o = reinterpret_cast<i32x4*>(codes + blk * kMxBlock);
   o[0] = out[0];
   o[1] = out[1];
@@ -170,12 +167,10 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
       const float inv = mx_inv_scale(e);
       i32x4 w[2];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) word |= e4m3_encode(v[q * 4 + k] * inv) << (8 * k);
-        w[q >> 2][q & 3] = static_cast<int>(word);
-      }
+      for (int q = 0; q < 8; ++q)
+        w[q >> 2][q & 3] = static_cast<int>(
+            e4m3_pack4(v[q * 4] * inv, v[q * 4 + 1] * inv,
+                       v[q * 4 + 2] * inv, v[q * 4 + 3] * inv));
       *reinterpret_cast<i32x4*>(&out[c][b * kMxBlock]) = w[0];
       *reinterpret_cast<i32x4*>(&out[c][b * kMxBlock + 16]) = w[1];
       reinterpret_cast<uint8_t*>(sc_out)[c * 4 + b] =

@@ -17,8 +17,9 @@ HIP events recorded around each stage on the stream it runs on.
 ``MoEPathMX`` is the same layer with MXFP8 GEMM operands: x is quantized
 along d before the permutation, the weights along their rows once per step
 (forward) and along their columns inside the backward, S and dAB inside the
-GEMM epilogues that produce them, and the weight-gradient operands along
-the rows of each expert.
+GEMM epilogues that produce them (both along their GEMM axis and along each
+expert's tokens, the latter for the weight gradients), and dO and Xp along
+each expert's tokens in the backward.  No bf16 copy of S or dAB is kept.
 
 No arithmetic happens here: every step runs in the library's kernels.
 """
@@ -225,6 +226,12 @@ class MoEPathMX(MoEPath):
         self.wguq, self.wgus = z(E, 2 * f, d), z(E, 2 * f, d // 32)
         self.w2q, self.w2s = z(E, d, f), z(E, d, f // 32)
         self.sq, self.ss = z(Tk, f), z(Tk, f // 32)
+        # S along each expert's tokens, written by the gate_up epilogue and
+        # read by the dW2 GEMM of the backward
+        tp = moe.moe_mxfp8_padded_rows(Tk, E)
+        self.tk_pad = tp
+        self.st, self.sts = z(f, tp), z(f, tp // 32)
+        self.s = None
         ws_f = moe.moe_workspace_bytes(MOE_ENTRY_MLP_FWD, MOE_MXFP8, T, E, k,
                                        d, f)
         self.ws_fwd = z(max(ws_f, 16))
@@ -236,14 +243,13 @@ class MoEPathMX(MoEPath):
         dev = self.x_perm.device
         u8 = torch.uint8
         z = lambda *s: torch.empty(*s, dtype=u8, device=dev)  # noqa: E731
-        tp = moe.moe_mxfp8_padded_rows(Tk, E)
-        self.tk_pad = tp
+        tp = self.tk_pad
         self.doq, self.dos = z(Tk, d), z(Tk, d // 32)
         self.w2tq, self.w2ts = z(f, E * d), z(f, E * d // 32)
         self.wgutq, self.wguts = z(d, E * 2 * f), z(d, E * 2 * f // 32)
+        self.dab = None
         self.dabq, self.dabs = z(Tk, 2 * f), z(Tk, 2 * f // 32)
         self.dot, self.dots = z(d, tp), z(d, tp // 32)
-        self.st, self.sts = z(f, tp), z(f, tp // 32)
         self.dabt, self.dabts = z(2 * f, tp), z(2 * f, tp // 32)
         self.xpt, self.xpts = z(d, tp), z(d, tp // 32)
         ws_b = moe.moe_workspace_bytes(MOE_ENTRY_MLP_BWD, MOE_MXFP8, T, E, k,
@@ -277,12 +283,14 @@ class MoEPathMX(MoEPath):
             moe.moe_grouped_mlp_fwd(MOE_MXFP8, self.xpq, self.xps,
                                     self.offsets, self.wguq, self.wgus,
                                     self.w2q, self.w2s, self.w_perm, self.ab,
-                                    self.s, self.o, self.ws_fwd)
+                                    None, self.o, self.ws_fwd,
+                                    s_tok=self.st, s_tok_scales=self.sts)
         else:
             with timers.around("gate_up_swiglu_fwd"):
                 moe.moe_mx_gate_up_swiglu_fwd(
                     self.xpq, self.xps, self.offsets, self.wguq, self.wgus,
-                    self.w_perm, self.ab, self.s, self.sq, self.ss)
+                    self.w_perm, self.ab, None, self.sq, self.ss,
+                    s_tok=self.st, s_tok_scales=self.sts)
             with timers.around("down_fwd"):
                 moe.moe_mx_down_fwd(self.sq, self.ss, self.offsets, self.w2q,
                                     self.w2s, self.o)
@@ -304,9 +312,10 @@ class MoEPathMX(MoEPath):
         if timers is None:
             moe.moe_grouped_mlp_bwd(MOE_MXFP8, self.dout_perm, self.x_perm,
                                     self.offsets, self.pos, w_gu, w2, self.ab,
-                                    self.s, self.w_perm, self.dx_perm,
+                                    None, self.w_perm, self.dx_perm,
                                     self.dw_gu, self.dw2, self.dp,
-                                    self.ws_bwd)
+                                    self.ws_bwd, s_tok=self.st,
+                                    s_tok_scales=self.sts)
         else:
             # the same kernels in the same order as moe_grouped_mlp_bwd
             tp = self.tk_pad
@@ -320,8 +329,9 @@ class MoEPathMX(MoEPath):
             with timers.around("down_swiglu_bwd"):
                 moe.moe_mx_down_swiglu_bwd(
                     self.doq, self.dos, self.offsets, self.w2tq, self.w2ts,
-                    self.ab, self.w_perm, self.dab, self.dabq, self.dabs,
-                    self.dp_part)
+                    self.ab, self.w_perm, None, self.dabq, self.dabs,
+                    self.dp_part, dab_tok=self.dabt,
+                    dab_tok_scales=self.dabts)
             with timers.around("dp_reduce"):
                 moe.moe_dp_reduce(self.dp_part, self.pos, self.dp)
             with timers.around("gate_up_dgrad"):
@@ -329,8 +339,6 @@ class MoEPathMX(MoEPath):
                                          self.wgutq, self.wguts, self.dx_perm)
             with timers.around("quant_tokens"):
                 for src, cq, cs in ((self.dout_perm, self.dot, self.dots),
-                                    (self.s, self.st, self.sts),
-                                    (self.dab, self.dabt, self.dabts),
                                     (self.x_perm, self.xpt, self.xpts)):
                     moe.moe_mxfp8_quantize(src, 1, self.offsets, cq, cs, tp)
             Tk = self.T * self.k

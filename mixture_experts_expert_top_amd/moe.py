@@ -59,10 +59,11 @@ def _load():
                               P, P, P, P, P, SZ, P]),
         "moe_permute_rows": (I32, [I32, P, I64, I32, P, P, I64, P, P, P]),
         "moe_grouped_mlp_fwd": (I32, [I32, P, P, P, I32, I64, I64, I64, P, P,
-                                      P, P, P, P, P, P, P, SZ, P]),
-        "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
-                                      I64, P, P, P, P, P, P, P, P, P, P, SZ,
+                                      P, P, P, P, P, P, P, P, I64, P, SZ,
                                       P]),
+        "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
+                                      I64, P, P, P, P, P, P, I64, P, P, P,
+                                      P, P, P, SZ, P]),
         "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
                                 P]),
         "moe_row_planes": (I32, []),
@@ -80,10 +81,10 @@ def _load():
                                     P]),
         "moe_dp_reduce": (I32, [P, I32, P, I64, I32, P, P]),
         "moe_mx_gate_up_swiglu_fwd": (I32, [P, P, P, I32, I64, I64, I64, P,
-                                            P, P, P, P, P, P, P]),
+                                            P, P, P, P, P, P, P, P, I64, P]),
         "moe_mx_down_fwd": (I32, [P, P, P, I32, I64, I64, I64, P, P, P, P]),
         "moe_mx_down_swiglu_bwd": (I32, [P, P, P, I32, I64, I64, I64, P, P,
-                                         P, P, P, P, P, P, P]),
+                                         P, P, P, P, P, P, P, I64, P, P]),
         "moe_mx_gate_up_dgrad": (I32, [P, P, P, I32, I64, I64, I64, P, P, P,
                                        P]),
         "moe_mx_grouped_wgrad": (I32, [P, P, P, P, I64, P, I32, I64, I64,
@@ -232,9 +233,21 @@ def moe_permute_rows(prec, pos, x, x_scales, x_perm, x_perm_scales,
         _p(x_perm_scales), _stream(stream)))
 
 
+def _tok_out(name, codes, scales, cols):
+    """(ldt, codes, scales) of an optional token-axis MX tensor
+    ([cols][ldt] codes, [cols][ldt/32] scales)."""
+    if codes is None and scales is None:
+        return 0
+    ldt = codes.shape[1]
+    _want(codes, name, torch.uint8, (cols, ldt))
+    _want(scales, name + "_scales", torch.uint8, (cols, ldt // 32))
+    return ldt
+
+
 def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
                         w_gu_scales, w2, w2_scales, w_perm, ab_saved, s_saved,
-                        out_perm, workspace=None, stream=None):
+                        out_perm, workspace=None, stream=None, s_tok=None,
+                        s_tok_scales=None):
     Tk, d = x_perm.shape
     E, two_f, _ = w_gu.shape
     f = two_f // 2
@@ -245,20 +258,21 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
         _want(w2, "w2", torch.bfloat16, (E, d, f))
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
-    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f), allow_none=True)
     _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
+    ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
     _check("moe_grouped_mlp_fwd", lib.moe_grouped_mlp_fwd(
         prec, _p(x_perm), _p(x_perm_scales), _p(offsets), E, Tk, d, f,
         _p(w_gu), _p(w_gu_scales), _p(w2), _p(w2_scales), _p(w_perm),
-        _p(ab_saved), _p(s_saved), _p(out_perm), _p(workspace), nbytes,
-        _stream(stream)))
+        _p(ab_saved), _p(s_saved), _p(out_perm), _p(s_tok), _p(s_tok_scales),
+        ldt, _p(workspace), nbytes, _stream(stream)))
 
 
 def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                         ab_saved, s_saved, w_perm, dx_perm, dw_gu, dw2, dp,
-                        workspace, stream=None):
+                        workspace, stream=None, s_tok=None, s_tok_scales=None):
     Tk, d = x_perm.shape
     T, k = pos.shape
     E, two_f, _ = w_gu.shape
@@ -267,9 +281,10 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                       ("x_perm", x_perm, (Tk, d)),
                       ("w_gu", w_gu, (E, 2 * f, d)), ("w2", w2, (E, d, f)),
                       ("ab_saved", ab_saved, (Tk, 2 * f)),
-                      ("s_saved", s_saved, (Tk, f)),
                       ("dw_gu", dw_gu, (E, 2 * f, d)), ("dw2", dw2, (E, d, f))):
         _want(t, n, torch.bfloat16, shp)
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f), allow_none=True)
+    ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
     _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
     _want(pos, "pos", torch.int32)
@@ -279,9 +294,9 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
         is not None else 0
     _check("moe_grouped_mlp_bwd", lib.moe_grouped_mlp_bwd(
         prec, _p(dout_perm), _p(x_perm), _p(offsets), _p(pos), T, k, E, d, f,
-        _p(w_gu), _p(w2), _p(ab_saved), _p(s_saved), _p(w_perm),
-        _p(dx_perm), _p(dw_gu), _p(dw2), _p(dp), _p(workspace), nbytes,
-        _stream(stream)))
+        _p(w_gu), _p(w2), _p(ab_saved), _p(s_saved), _p(s_tok),
+        _p(s_tok_scales), ldt, _p(w_perm), _p(dx_perm), _p(dw_gu), _p(dw2),
+        _p(dp), _p(workspace), nbytes, _stream(stream)))
 
 
 def moe_unpermute(o_perm, pos, w, y, stream=None):
@@ -417,7 +432,8 @@ def moe_dp_reduce(dp_part, pos, dp, stream=None):
 # along the reduction axis (layouts in include/moe.h).
 
 def moe_mx_gate_up_swiglu_fwd(xq, xs, offsets, wq, ws, w_perm, ab_saved,
-                              s_saved, sq, ss, stream=None):
+                              s_saved, sq, ss, s_tok=None, s_tok_scales=None,
+                              stream=None):
     Tk, d = xq.shape
     E, two_f, _ = wq.shape
     f = two_f // 2
@@ -428,13 +444,14 @@ def moe_mx_gate_up_swiglu_fwd(xq, xs, offsets, wq, ws, w_perm, ab_saved,
     _want(offsets, "offsets", torch.int32, (E + 1,))
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
-    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f))
+    _want(s_saved, "s_saved", torch.bfloat16, (Tk, f), allow_none=True)
     _want(sq, "sq", torch.uint8, (Tk, f))
     _want(ss, "ss", torch.uint8, (Tk, f // 32))
+    ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
     _check("moe_mx_gate_up_swiglu_fwd", lib.moe_mx_gate_up_swiglu_fwd(
         _p(xq), _p(xs), _p(offsets), E, Tk, d, f, _p(wq), _p(ws),
-        _p(w_perm), _p(ab_saved), _p(s_saved), _p(sq), _p(ss),
-        _stream(stream)))
+        _p(w_perm), _p(ab_saved), _p(s_saved), _p(sq), _p(ss), _p(s_tok),
+        _p(s_tok_scales), ldt, _stream(stream)))
 
 
 def moe_mx_down_fwd(sq, ss, offsets, wq, ws, out_perm, stream=None):
@@ -452,7 +469,8 @@ def moe_mx_down_fwd(sq, ss, offsets, wq, ws, out_perm, stream=None):
 
 
 def moe_mx_down_swiglu_bwd(doq, dos, offsets, w2tq, w2ts, ab_saved, w_perm,
-                           dab, dabq, dabs, dp_part, stream=None):
+                           dab, dabq, dabs, dp_part, dab_tok=None,
+                           dab_tok_scales=None, stream=None):
     Tk, d = doq.shape
     f, Ed = w2tq.shape
     E = offsets.numel() - 1
@@ -463,14 +481,15 @@ def moe_mx_down_swiglu_bwd(doq, dos, offsets, w2tq, w2ts, ab_saved, w_perm,
     _want(offsets, "offsets", torch.int32)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
-    _want(dab, "dab", torch.bfloat16, (Tk, 2 * f))
+    _want(dab, "dab", torch.bfloat16, (Tk, 2 * f), allow_none=True)
     _want(dabq, "dabq", torch.uint8, (Tk, 2 * f))
     _want(dabs, "dabs", torch.uint8, (Tk, 2 * f // 32))
     _want(dp_part, "dp_part", torch.float32, (Tk, moe_dp_tiles(f)))
+    ldt = _tok_out("dab_tok", dab_tok, dab_tok_scales, 2 * f)
     _check("moe_mx_down_swiglu_bwd", lib.moe_mx_down_swiglu_bwd(
         _p(doq), _p(dos), _p(offsets), E, Tk, d, f, _p(w2tq), _p(w2ts),
-        _p(ab_saved), _p(w_perm), _p(dab), _p(dabq), _p(dabs), _p(dp_part),
-        _stream(stream)))
+        _p(ab_saved), _p(w_perm), _p(dab), _p(dabq), _p(dabs), _p(dab_tok),
+        _p(dab_tok_scales), ldt, _p(dp_part), _stream(stream)))
 
 
 def moe_mx_gate_up_dgrad(dabq, dabs, offsets, wgutq, wguts, dx_perm,

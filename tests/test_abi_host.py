@@ -96,33 +96,55 @@ def test_workspace_sizes():
     assert L.moe_workspace_bytes(0, BF16, 8, 8, 9, 64, 64) == 0
 
 
+def _fwd_args(prec=BF16, E=4, Tk=128, d=32, f=64, s=A, s_tok=None,
+              s_tok_scales=None, ldt=0, ws=None):
+    # prec, x_perm, x_perm_scales, offsets, E, Tk, d, f, w_gu, w_gu_scales,
+    # w2, w2_scales, w_perm, ab_saved, s_saved, out_perm, s_tok,
+    # s_tok_scales, ldt, workspace
+    sc = A if prec == MX else None
+    return [prec, A, sc, A, E, Tk, d, f, A, sc, A, sc, A, A, s, A, s_tok,
+            s_tok_scales, ldt, ws]
+
+
+def _bwd_args(prec=BF16, T=64, k=2, E=4, d=32, f=64, s=A, s_tok=None,
+              s_tok_scales=None, ldt=0):
+    # prec, dout_perm, x_perm, offsets, pos, T, k, E, d, f, w_gu, w2,
+    # ab_saved, s_saved, s_tok, s_tok_scales, ldt, w_perm, dx_perm, dw_gu,
+    # dw2, dp, workspace
+    return [prec, A, A, A, A, T, k, E, d, f, A, A, A, s, s_tok, s_tok_scales,
+            ldt, A, A, A, A, A, A]
+
+
 def test_mlp_fwd_validation():
     f = L.moe_grouped_mlp_fwd
     # f not a multiple of 8
-    assert f(BF16, A, None, A, 4, 128, 32, 60, A, None, A, None, A, A, A, A,
-             None, 0, None) == INVALID
+    assert f(*_fwd_args(f=60), 0, None) == INVALID
     # too large for 32-bit buffer offsets
-    assert f(BF16, A, None, A, 8, 1 << 20, 4096, 14336, A, None, A, None, A,
-             A, A, A, None, 0, None) == UNSUP
-    assert f(BF16, None, None, A, 4, 128, 32, 64, A, None, A, None, A, A, A,
-             A, None, 0, None) == INVALID
+    assert f(*_fwd_args(E=8, Tk=1 << 20, d=4096, f=14336), 0, None) == UNSUP
+    bad = _fwd_args()
+    bad[1] = None
+    assert f(*bad, 0, None) == INVALID
+    # bf16: S is required, token-axis codes are not allowed
+    assert f(*_fwd_args(s=None), 0, None) == INVALID
+    assert f(*_fwd_args(s_tok=A, s_tok_scales=A, ldt=256), 0,
+             None) == INVALID
 
 
 def test_mlp_bwd_validation():
     f = L.moe_grouped_mlp_bwd
     ws = L.moe_workspace_bytes(2, BF16, 64, 4, 2, 32, 64)
-    args = [BF16, A, A, A, A, 64, 2, 4, 32, 64, A, A, A, A, A, A, A, A, A, A]
-    assert f(*args, ws - 1, None) == WS
-    bad = list(args)
-    bad[7] = 1                          # E < k
-    assert f(*bad, ws, None) == INVALID
+    assert f(*_bwd_args(), ws - 1, None) == WS
+    assert f(*_bwd_args(E=1), ws, None) == INVALID          # E < k
+    assert f(*_bwd_args(s=None), ws, None) == INVALID
+    assert f(*_bwd_args(s_tok=A, s_tok_scales=A, ldt=640), ws,
+             None) == INVALID                               # bf16 + codes
 
 
 def test_mx_mlp_validation():
     f = L.moe_grouped_mlp_fwd
     ws = L.moe_workspace_bytes(1, MX, 64, 4, 2, 128, 128)
     assert ws >= 128 * 128 + 128 * 4                  # S codes and scales
-    ok = [MX, A, A, A, 4, 128, 128, 128, A, A, A, A, A, A, A, A, A]
+    ok = _fwd_args(MX, d=128, f=128, ws=A)
     assert f(*ok, ws - 1, None) == WS
     bad = list(ok)
     bad[6] = 96                                       # d % 128 != 0
@@ -133,11 +155,44 @@ def test_mx_mlp_validation():
     assert f(*bad, ws, None) == INVALID
     b = L.moe_grouped_mlp_bwd
     wsb = L.moe_workspace_bytes(2, MX, 64, 4, 2, 128, 128)
-    assert wsb > L.moe_workspace_bytes(2, BF16, 64, 4, 2, 128, 128)
-    args = [MX, A, A, A, A, 64, 2, 4, 128, 128, A, A, A, A, A, A, A, A, A, A]
+    args = _bwd_args(MX, d=128, f=128)
     assert b(*args, wsb - 1, None) == WS
     args[9] = 160                                     # f % 128 != 0
     assert b(*args, wsb, None) == INVALID
+
+
+def test_mx_token_axis_output_validation():
+    """The token-axis S / dAB outputs: codes and scales together, ldt a
+    multiple of 128 covering every expert's padded rows; the backward
+    takes exactly moe_mxfp8_padded_rows(T*k, E)."""
+    f = L.moe_grouped_mlp_fwd
+    Tk, E = 128, 4
+    tp = L.moe_mxfp8_padded_rows(Tk, E)
+    ws = L.moe_workspace_bytes(1, MX, 64, E, 2, 128, 128)
+    tok = dict(s_tok=A, s_tok_scales=A)
+    for kw, want in ((dict(s_tok=A, ldt=tp), INVALID),          # no scales
+                     (dict(tok, ldt=tp - 128), INVALID),        # too short
+                     (dict(tok, ldt=tp + 64), INVALID),         # % 128
+                     (dict(s=None), INVALID)):                  # no S at all
+        assert f(*_fwd_args(MX, E=E, Tk=Tk, d=128, f=128, ws=A, **kw), ws,
+                 None) == want, kw
+    assert f(*_fwd_args(MX, E=E, Tk=Tk, d=128, f=128, ws=A, s=None,
+                        s_tok=MIS, s_tok_scales=A, ldt=tp), ws,
+             None) == INVALID                                   # aligned
+    b = L.moe_grouped_mlp_bwd
+    wsb = L.moe_workspace_bytes(2, MX, 64, E, 2, 128, 128)
+    assert b(*_bwd_args(MX, E=E, d=128, f=128, s=None, s_tok=A,
+                        s_tok_scales=A, ldt=tp + 128), wsb, None) == INVALID
+    assert b"padded" in L.moe_last_error()
+    assert b(*_bwd_args(MX, E=E, d=128, f=128, s=None), wsb,
+             None) == INVALID
+    # stage entries
+    assert L.moe_mx_gate_up_swiglu_fwd(A, A, A, E, Tk, 128, 128, A, A, A, A,
+                                       None, A, A, A, None, tp,
+                                       None) == INVALID
+    assert L.moe_mx_down_swiglu_bwd(A, A, A, E, Tk, 128, 128, A, A, A, A,
+                                    None, A, A, A, A, tp - 128, A,
+                                    None) == INVALID
 
 
 def test_mx_stage_validation():

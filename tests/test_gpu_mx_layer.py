@@ -113,15 +113,74 @@ def mx_rounding_check(codes, scales, ref, slack):
         return 0.0, 0.0
     dec = M.dequantize_rows(codes, scales)
     e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    _, ref_scales = M.quantize_rows(ref)
+    return (mx_step_ratio(dec, e, ref, slack),
+            float(np.mean(ref_scales != scales)))
+
+
+def tok_rows(codes, scales, offsets):
+    """A token-axis MX tensor (codes [C][ldt], scales [C][ldt/32], expert
+    e's rows from its 128-padded start) as decoded values and block
+    exponents [T*k, C], plus the per-expert padded starts."""
+    dec = M.dequantize_rows(codes, scales)
+    ex = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    Tk, C = int(offsets[-1]), codes.shape[0]
+    v = np.zeros((Tk, C))
+    e = np.zeros((Tk, C), dtype=np.int64)
+    starts = []
+    pad = 0
+    for s0, s1 in zip(offsets[:-1], offsets[1:]):
+        s0, s1 = int(s0), int(s1)
+        starts.append(pad)
+        v[s0:s1] = dec[:, pad:pad + s1 - s0].T
+        e[s0:s1] = ex[:, pad:pad + s1 - s0].T
+        pad += (s1 - s0 + 127) // 128 * 128
+    return v, e, starts, pad
+
+
+def tok_check(codes, scales, offsets, ref, slack):
+    """mx_rounding_check for a token-axis MX tensor against float64 ref
+    [T*k, C]; the scale comparison uses the oracle's segment blocks."""
+    ref = np.asarray(ref, dtype=np.float64)
+    v, e, starts, _ = tok_rows(codes, scales, offsets)
+    ratio = mx_step_ratio(v, e, ref, slack)
+    _, blocks = M.quantize_segments(ref, offsets)
+    diff = n = 0
+    for b0, b1, sc in blocks:
+        s = int(np.searchsorted(offsets, b0, side="right")) - 1
+        col = (starts[s] + b0 - int(offsets[s])) // 32
+        diff += int(np.sum(scales[:, col] != sc))
+        n += sc.size
+    return ratio, diff / max(n, 1)
+
+
+def mx_step_ratio(dec, e, ref, slack):
+    """max |dec - ref| / (half an E4M3 step at block exponent e, or the
+    saturation gap, + slack)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0
     a = np.abs(ref) / np.ldexp(1.0, e)
     _, ex = np.frexp(a)
     binade = np.maximum(ex - 1, -6)
     half = np.ldexp(1.0, binade - 4 + e)               # half an E4M3 step
     sat = np.maximum(np.abs(ref) - 448.0 * np.ldexp(1.0, e), 0.0)
     bound = np.maximum(half, sat) + 1.01 * slack + 1e-30
-    ratio = float(np.max(np.abs(dec - ref) / bound))
-    _, ref_scales = M.quantize_rows(ref)
-    return ratio, float(np.mean(ref_scales != scales))
+    return float(np.max(np.abs(dec - ref) / bound))
+
+
+def tok_same_as_quantizer(src_bf16, codes, scales, offsets_d, npad):
+    """The epilogue's token-axis codes are, over every expert's padded
+    rows, bit for bit the token-axis quantizer's codes of the bf16 tensor
+    the same kernel stored (both are HIP; the quantizer itself is pinned
+    bit-exact to the oracle's codec in test_gpu_mx.py)."""
+    C, ldt = codes.shape
+    q = torch.empty(C, ldt, dtype=torch.uint8, device=codes.device)
+    s = torch.empty(C, ldt // 32, dtype=torch.uint8, device=codes.device)
+    moe.moe_mxfp8_quantize(src_bf16, 1, offsets_d, q, s, ldt)
+    torch.cuda.synchronize()
+    assert torch.equal(codes[:, :npad], q[:, :npad])
+    assert torch.equal(scales[:, :npad // 32], s[:, :npad // 32])
 
 
 def sig(a):
@@ -201,8 +260,12 @@ def test_mx_gate_up_swiglu_stage(name, T, d, f, E, k, bias):
     s = torch.empty(Tk, f, dtype=torch.bfloat16, device=dev)
     sq = torch.empty(Tk, f, dtype=torch.uint8, device=dev)
     ss = torch.empty(Tk, f // 32, dtype=torch.uint8, device=dev)
+    tp = moe.moe_mxfp8_padded_rows(Tk, E)
+    st = torch.full((f, tp), 0xA5, dtype=torch.uint8, device=dev)
+    sts = torch.full((f, tp // 32), 0xA5, dtype=torch.uint8, device=dev)
     moe.moe_mx_gate_up_swiglu_fwd(xq, xs, P["offsets_d"], wq, ws,
-                                  P["w_perm_d"], ab, s, sq, ss)
+                                  P["w_perm_d"], ab, s, sq, ss, s_tok=st,
+                                  s_tok_scales=sts)
     torch.cuda.synchronize()
     ab_ref = np.zeros((Tk, 2 * f))
     ab_err = np.zeros((Tk, 2 * f))
@@ -219,9 +282,16 @@ def test_mx_gate_up_swiglu_stage(name, T, d, f, E, k, bias):
     ex = {"ab": excess(h64(ab), ab_ref, 2.0 ** -8 * np.abs(ab_ref) + ab_err),
           "s": excess(h64(s), s_ref, 2.0 ** -8 * np.abs(s_ref) + s_err)}
     ratio, sdiff = mx_rounding_check(u8(sq), u8(ss), s_ref, s_err)
-    print(name, ex, "S-mx bound ratio", ratio, "scale diff", sdiff)
+    # S along the tokens is quantized from its bf16 value
+    tratio, tdiff = tok_check(u8(st), u8(sts), P["offsets"], s_ref,
+                              s_err + 2.0 ** -8 * np.abs(s_ref))
+    print(name, ex, "S-mx bound ratio", ratio, "scale diff", sdiff,
+          "S-tok", tratio, tdiff)
     assert max(ex.values()) <= 1.0, ex
     assert ratio <= 1.0 and sdiff <= 1e-2
+    assert tratio <= 1.0 and tdiff <= 1e-2
+    tok_same_as_quantizer(s, st, sts, P["offsets_d"],
+                          tok_rows(u8(st), u8(sts), P["offsets"])[3])
 
 
 @gpu
@@ -263,8 +333,13 @@ def test_mx_down_swiglu_bwd_stage(name, T, d, f, E, k, bias):
     dabq = torch.empty(Tk, 2 * f, dtype=torch.uint8, device=dev)
     dabs = torch.empty(Tk, 2 * f // 32, dtype=torch.uint8, device=dev)
     dp_part = torch.empty(Tk, nt, dtype=torch.float32, device=dev)
+    tp = moe.moe_mxfp8_padded_rows(Tk, E)
+    dabt = torch.full((2 * f, tp), 0xA5, dtype=torch.uint8, device=dev)
+    dabts = torch.full((2 * f, tp // 32), 0xA5, dtype=torch.uint8,
+                       device=dev)
     moe.moe_mx_down_swiglu_bwd(doq, dos, P["offsets_d"], w2tq, w2ts, ab,
-                               P["w_perm_d"], dab, dabq, dabs, dp_part)
+                               P["w_perm_d"], dab, dabq, dabs, dp_part,
+                               dab_tok=dabt, dab_tok_scales=dabts)
     torch.cuda.synchronize()
     abh = h64(ab)
     dab_ref = np.zeros((Tk, 2 * f))
@@ -283,9 +358,15 @@ def test_mx_down_swiglu_bwd_stage(name, T, d, f, E, k, bias):
     ex = excess(h64(dab), dab_ref, 2.0 ** -8 * np.abs(dab_ref) + dab_err)
     dp_ex = excess(h64(dp_part).sum(axis=1), dp_ref, dp_err)
     ratio, sdiff = mx_rounding_check(u8(dabq), u8(dabs), dab_ref, dab_err)
-    print(name, "dab", ex, "dp", dp_ex, "dAB-mx", ratio, sdiff)
+    tratio, tdiff = tok_check(u8(dabt), u8(dabts), P["offsets"], dab_ref,
+                              dab_err + 2.0 ** -8 * np.abs(dab_ref))
+    print(name, "dab", ex, "dp", dp_ex, "dAB-mx", ratio, sdiff, "dAB-tok",
+          tratio, tdiff)
     assert ex <= 1.0 and dp_ex <= 1.0
     assert ratio <= 1.0 and sdiff <= 1e-2
+    assert tratio <= 1.0 and tdiff <= 1e-2
+    tok_same_as_quantizer(dab, dabt, dabts, P["offsets_d"],
+                          tok_rows(u8(dabt), u8(dabts), P["offsets"])[3])
 
 
 @gpu
@@ -426,4 +507,38 @@ def test_mx_layer_deterministic():
         outs.append([t.clone() for t in (path.y, path.dx, path.dw_gu,
                                          path.dw2, path.dp)])
     for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@gpu
+def test_mx_fused_token_codes_equal_requantized():
+    """The fused MX forward/backward with S's token-axis codes made in the
+    gate_up epilogue give the same bits as the same calls with a bf16 S
+    that the backward quantizes along the tokens itself."""
+    T, d, f, E, k = 500, 256, 384, 6, 2
+    _, path = _run_mx_layer(T, d, f, E, k, False, 0.02, seed=11)
+    dev = _dev()
+    Tk = T * k
+    inp = I.make_custom(T, d, f, E, k, seed=11, device=dev,
+                        outlier_frac=0.02)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    ab = torch.empty(Tk, 2 * f, **bf)
+    s = torch.empty(Tk, f, **bf)
+    o = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    moe.moe_grouped_mlp_fwd(moe.MOE_MXFP8, path.xpq, path.xps, path.offsets,
+                            path.wguq, path.wgus, path.w2q, path.w2s,
+                            path.w_perm, ab, s, o, path.ws_fwd)
+    dx_perm = torch.empty_like(path.dx_perm)
+    dw_gu = torch.empty_like(path.dw_gu)
+    dw2 = torch.empty_like(path.dw2)
+    dp = torch.empty_like(path.dp)
+    moe.moe_grouped_mlp_bwd(moe.MOE_MXFP8, path.dout_perm, path.x_perm,
+                            path.offsets, path.pos, inp["w_gu"], inp["w2"],
+                            ab, s, path.w_perm, dx_perm, dw_gu, dw2, dp,
+                            path.ws_bwd)
+    torch.cuda.synchronize()
+    assert torch.equal(ab, path.ab)
+    assert torch.equal(o, path.o)
+    for a, b in ((dx_perm, path.dx_perm), (dw_gu, path.dw_gu),
+                 (dw2, path.dw2), (dp, path.dp)):
         assert torch.equal(a, b)
