@@ -14,13 +14,19 @@ Sources (cited by page title and section):
     ScaledSwiGLU -> GroupedLinear, the routing probabilities act as scales).
   * "How MoE Architecture Cuts Costs and Boosts Efficiency: Efficient
     Training of Biological Foundation Models" -- section "Why Biology Is
-    Especially Well-Suited for MoE" (top-K router over per-expert scores).
+    Especially Well-Suited for MoE" (top-K router over per-expert scores)
+    and "Engineering Challenges of Efficient Training" (load balance).
+  * the hgpu.org abstract of an MXFP4 MoE training recipe on Hopper (FP8
+    GEMMs, MXFP4 activations and payloads, FP4 row blocks converted to
+    column blocks with new scales).
 
 Every function is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_oracle_mx_pins.py`` and ``tests/test_oracle_mx_layer_pins.py``
-(brute force, closed forms, library routines, finite differences,
-exhaustive codec sweeps, an independent formulation of the MXFP8 layer).
+``tests/test_oracle_mx_pins.py``, ``tests/test_oracle_mx_layer_pins.py``,
+``tests/test_oracle_router_pins.py``, ``tests/test_oracle_mx4_pins.py`` and
+``tests/test_oracle_mx4_layer_pins.py`` (brute force, closed forms, library
+routines, finite differences, exhaustive codec sweeps, independent
+formulations of the MXFP8 and MXFP4-activation layers).
 See each module header for what is and is not pinned.
 """
 
-from . import moe_mx, moe_ref, mx_ref  # noqa: F401
+from . import moe_mx, moe_ref, mx4_ref, mx_ref  # noqa: F401

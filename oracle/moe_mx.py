@@ -25,7 +25,16 @@ bf16 path:
                                             first row; from the bf16 copies)
 
 Stored activations are bfloat16 as in the bf16 path (AB and S for the
-backward, dAB for the weight gradients).  Arithmetic between quantization
+backward, dAB for the weight gradients).
+
+The MXFP4-activation variant (``act4=True``; the hgpu.org abstract of the
+MXFP4 MoE training recipe: FP8 GEMMs, MXFP4 activations and expert-parallel
+payloads, FP4 row blocks converted to column blocks with new scales)
+changes two points and nothing else:
+
+  forward   x              MXFP4 along d   (the dispatched payload)
+  backward  Xp             MXFP4 along tokens, from the dequantized MXFP4
+                           payload (no bf16 copy of x is used)  Arithmetic between quantization
 points is float64.  Each function is the plain composition of the float64
 step functions of ``moe_ref`` and the codec of ``mx_ref``; nothing is
 blocked or fused.
@@ -42,6 +51,7 @@ helpers against the full layer.
 import numpy as np
 
 from . import moe_ref as R
+from . import mx4_ref as M4
 from . import mx_ref as M
 
 
@@ -67,7 +77,27 @@ def mx_tokens(a, offsets):
     return M.dequantize_segments(c, blocks)
 
 
-def experts_forward_mx(x, idx, p, w_gu, w2):
+def mx4_rows(a):
+    """MXFP4 quantize-dequantize along the last axis."""
+    a = np.asarray(a, dtype=np.float64)
+    shape = a.shape
+    c, s = M4.quantize_rows4(a.reshape(-1, shape[-1]))
+    return M4.dequantize_rows4(c, s).reshape(shape)
+
+
+def mx4_tokens(a, offsets):
+    """MXFP4 quantize-dequantize along the rows of a [Tk, C] permuted
+    tensor, blocks restarting at every expert segment start."""
+    c, blocks = M4.quantize_segments4(a, offsets)
+    return M4.dequantize_segments4(c, blocks)
+
+
+def _payload(x, act4):
+    """x as the fc1 GEMM reads it: MX along d, MXFP4 or MXFP8."""
+    return mx4_rows(x) if act4 else mx_rows(x)
+
+
+def experts_forward_mx(x, idx, p, w_gu, w2, act4=False):
     """Forward with routing given.  Returns the bf16 path's dict plus the
     dequantized GEMM operands (xq, w_gu_q, w2_q, s_q)."""
     x = np.asarray(x, dtype=np.float64)
@@ -77,7 +107,7 @@ def experts_forward_mx(x, idx, p, w_gu, w2):
     f = w_gu.shape[1] // 2
     d = x.shape[1]
     counts, offsets, pos, src = R.dispatch_plan(idx, E)
-    xq = mx_rows(x)
+    xq = _payload(x, act4)
     w_gu_q = mx_rows(w_gu)
     w2_q = mx_rows(w2)
     xp_q = R.permute_rows(xq, src)
@@ -102,13 +132,13 @@ def experts_forward_mx(x, idx, p, w_gu, w2):
                 counts=counts, offsets=offsets, pos=pos, src=src,
                 xp=R.permute_rows(x, src), xp_q=xp_q, xq=xq,
                 w_gu_q=w_gu_q, w2_q=w2_q, w_perm=w_perm,
-                ab=ab, s=s, s_q=s_q, o=o, y=y)
+                ab=ab, s=s, s_q=s_q, o=o, y=y, act4=act4)
 
 
-def moe_forward_mx(x, logits, w_gu, w2, k, renorm=True):
+def moe_forward_mx(x, logits, w_gu, w2, k, renorm=True, act4=False):
     """Route on the given scores, then the MX forward."""
     idx, p = R.topk_route(logits, k, renorm)
-    return experts_forward_mx(x, idx, p, w_gu, w2)
+    return experts_forward_mx(x, idx, p, w_gu, w2, act4)
 
 
 def moe_backward_mx(fwd, dy, w_gu, w2):
@@ -129,7 +159,10 @@ def moe_backward_mx(fwd, dy, w_gu, w2):
     w_gu_c = mx_cols(w_gu)                     # along 2f
     do_t = mx_tokens(do, offsets)
     s_t = mx_tokens(s, offsets)
-    xp_t = mx_tokens(xp, offsets)
+    # the weight gradient's Xp: MXFP8 along tokens from the bf16 rows, or
+    # (act4) MXFP4 along tokens from the dequantized MXFP4 payload
+    xp_t = (mx4_tokens(fwd["xp_q"], offsets) if fwd.get("act4")
+            else mx_tokens(xp, offsets))
     dab = np.zeros((Tk, two_f))
     dab_q = np.zeros((Tk, two_f))
     dxp = np.zeros((Tk, d))
@@ -188,10 +221,10 @@ def expert_weights_mx(w_gu_e=None, w2_e=None, backward=False):
     return out
 
 
-def token_forward_mx(x_t, idx_t, p_t, W):
+def token_forward_mx(x_t, idx_t, p_t, W, act4=False):
     """y[t] for one token: its experts' MX forward rows summed in ascending
     expert id.  W[e] holds expert_weights_mx(...) of every chosen e."""
-    xq = mx_rows(np.asarray(x_t, dtype=np.float64)[None, :])
+    xq = _payload(np.asarray(x_t, dtype=np.float64)[None, :], act4)
     y = 0.0
     for j in np.argsort(np.asarray(idx_t), kind="stable"):
         e = int(idx_t[j])
@@ -201,10 +234,10 @@ def token_forward_mx(x_t, idx_t, p_t, W):
     return y
 
 
-def row_backward_mx(x_t, dy_t, p_r, We):
+def row_backward_mx(x_t, dy_t, p_r, We, act4=False):
     """(dXp row, dp) of the permuted row of token t at one expert, whose
     weights We come from expert_weights_mx(..., backward=True)."""
-    xq = mx_rows(np.asarray(x_t, dtype=np.float64)[None, :])
+    xq = _payload(np.asarray(x_t, dtype=np.float64)[None, :], act4)
     ab = R.bf16_round(R.gate_up(xq, We["gu_q"]))
     do_q = mx_rows(np.asarray(dy_t, dtype=np.float64)[None, :])
     dab, dp = R.down_backward(do_q, ab, np.array([p_r], dtype=np.float64),
@@ -212,20 +245,20 @@ def row_backward_mx(x_t, dy_t, p_r, We):
     return R.gate_up_dgrad(mx_rows(dab), We["gu_c"])[0], dp[0]
 
 
-def _gate_up_cols(x_e, w_gu_e, cols):
+def _gate_up_cols(x_e, w_gu_e, cols, act4=False):
     """Columns ``cols`` of the expert's AB (bf16 as kept), from x quantized
     along d and the needed W_gu rows quantized along d."""
-    xq = mx_rows(np.asarray(x_e, dtype=np.float64))
+    xq = _payload(np.asarray(x_e, dtype=np.float64), act4)
     wr = mx_rows(np.asarray(w_gu_e, dtype=np.float64)[cols])
     return R.bf16_round(xq @ wr.T)
 
 
-def dw2_column_mx(x_e, dy_e, w_e, w_gu_e, j):
+def dw2_column_mx(x_e, dy_e, w_e, w_gu_e, j, act4=False):
     """Column j of the expert's dW2 (all d entries): dO (bf16 dY rows) and
     S[:, j] (bf16 S from the MX forward) quantized along the expert's
     tokens.  x_e, dy_e, w_e: the expert's rows in permuted order."""
     f = np.asarray(w_gu_e).shape[0] // 2
-    xq = mx_rows(np.asarray(x_e, dtype=np.float64))
+    xq = _payload(np.asarray(x_e, dtype=np.float64), act4)
     wr = mx_rows(np.asarray(w_gu_e, dtype=np.float64)[[j, f + j]])
     ab = xq @ wr.T
     s = R.bf16_round(np.asarray(w_e, dtype=np.float64) *
@@ -236,14 +269,14 @@ def dw2_column_mx(x_e, dy_e, w_e, w_gu_e, j):
     return do_t.T @ s_t
 
 
-def dw_gu_row_mx(x_e, dy_e, w_e, w_gu_e, w2_e, i):
+def dw_gu_row_mx(x_e, dy_e, w_e, w_gu_e, w2_e, i, act4=False):
     """Row i of the expert's dW_gu (gate row for i < f, up row f + i' for
     i = f + i'): dAB[:, i] (bf16, from dS = dO quantized along d times W2
     quantized along d) and Xp quantized along the expert's tokens."""
     w_gu_e = np.asarray(w_gu_e, dtype=np.float64)
     f = w_gu_e.shape[0] // 2
     c = i % f
-    ab = _gate_up_cols(x_e, w_gu_e, [c, f + c])
+    ab = _gate_up_cols(x_e, w_gu_e, [c, f + c], act4)
     g, u = ab[:, 0], ab[:, 1]
     do_q = mx_rows(np.asarray(dy_e, dtype=np.float64))
     w2col = mx_rows(np.asarray(w2_e, dtype=np.float64)[:, c][None, :])[0]
@@ -254,5 +287,7 @@ def dw_gu_row_mx(x_e, dy_e, w_e, w_gu_e, w2_e, i):
     dab = R.bf16_round(dab)
     n = dab.shape[0]
     dab_t = mx_tokens(dab[:, None], [0, n])[:, 0]
-    xp_t = mx_tokens(np.asarray(x_e, dtype=np.float64), [0, n])
+    x_e = np.asarray(x_e, dtype=np.float64)
+    xp_t = (mx4_tokens(mx4_rows(x_e), [0, n]) if act4
+            else mx_tokens(x_e, [0, n]))
     return dab_t @ xp_t
