@@ -427,6 +427,34 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                               int32_t nseg, uint8_t* codes, uint8_t* scales,
                               int64_t rows_pad, hipStream_t stream);
 
+/*
+ * moe_mxfp4_quantize -- MXFP4 block quantization ([P5]: MXFP4 activations
+ * and dispatch payloads under FP8 GEMMs; row-blocked FP4 turned into column
+ * blocks with new scales).  E2M1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ * negatives; sign in bit 3), two a byte with the lower index in the low
+ * nibble, and one E8M0 scale byte per 32 values: scale exponent
+ * e = clamp(floor(log2 amax) - 2, -127, 127) (-127 for an all-zero block),
+ * byte e + 127, codes rounded to nearest with ties to the even code and
+ * saturated at +-6.
+ *   src_fmt 0: src is bf16 [rows][cols].
+ *   src_fmt 1: src is MXFP4 rows, codes [rows][cols/2] with src_scales
+ *     [rows][cols/32]; every value is decoded exactly first (axis 1 only:
+ *     the row-to-column conversion).
+ *   axis 0: codes [rows][cols/2], scales [rows][cols/32] (src_fmt 0).
+ *   axis 1: blocks of 32 rows restarting at each segment start
+ *     (seg_offsets [nseg+1] on the device, or NULL for one segment),
+ *     transposed and 128-padded as moe_mxfp8_quantize axis 1: codes
+ *     [cols][rows_pad/2], scales [cols][rows_pad/32]; every byte up to
+ *     rows_pad is written (padding: code 0, scale byte 0).
+ * cols must be a multiple of 32.  Bit-exact and deterministic.
+ */
+moe_status moe_mxfp4_quantize(const void* src, int32_t src_fmt,
+                              const uint8_t* src_scales, int64_t rows,
+                              int64_t cols, int32_t axis,
+                              const int32_t* seg_offsets, int32_t nseg,
+                              uint8_t* codes, uint8_t* scales,
+                              int64_t rows_pad, hipStream_t stream);
+
 /* Host-side bound on rows_pad for axis == 1 quantization: the padded
  * segment lengths sum to a multiple of 128 that is at most rows + 127 *
  * nseg, so the bound is that number rounded down to a multiple of 128

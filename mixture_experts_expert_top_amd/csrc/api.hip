@@ -884,4 +884,51 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                     "moe_mxfp8_quantize/tokens");
 }
 
+moe_status moe_mxfp4_quantize(const void* src, int32_t src_fmt,
+                              const uint8_t* src_scales, int64_t rows,
+                              int64_t cols, int32_t axis,
+                              const int32_t* seg_offsets, int32_t nseg,
+                              uint8_t* codes, uint8_t* scales,
+                              int64_t rows_pad, hipStream_t stream) {
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE(src_fmt == 0 || src_fmt == 1, MOE_ERR_INVALID_ARG,
+          "src_fmt must be 0 (bf16) or 1 (MXFP4 rows)");
+  if (src_fmt == 1) REQUIRE_PTR(src_scales);
+  REQUIRE(rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG,
+          "rows and cols must be >= 1");
+  REQUIRE(cols % 32 == 0, MOE_ERR_INVALID_ARG,
+          "cols must be a multiple of 32 (got %lld)",
+          static_cast<long long>(cols));
+  REQUIRE(rows * cols * 2 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+          "source larger than 4 GiB");
+  if (axis == 0) {
+    REQUIRE(src_fmt == 0, MOE_ERR_INVALID_ARG,
+            "axis 0 quantizes bf16 rows (src_fmt 0)");
+    return hip_status(
+        moe::launch_mx4_quant_rows(static_cast<const bf16_t*>(src), rows,
+                                   cols, codes, scales, stream),
+        "moe_mxfp4_quantize/rows");
+  }
+  REQUIRE(axis == 1, MOE_ERR_INVALID_ARG, "axis must be 0 or 1");
+  REQUIRE(nseg >= 1 && nseg <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+          "nseg must be in [1, %d]", moe::kMaxExperts);
+  REQUIRE(seg_offsets != nullptr || nseg == 1, MOE_ERR_INVALID_ARG,
+          "seg_offsets may be NULL only for one segment");
+  REQUIRE_OPT_PTR(seg_offsets);
+  REQUIRE(rows_pad >= moe_mxfp8_padded_rows(rows, nseg) &&
+              rows_pad % moe::kMxPad == 0,
+          MOE_ERR_INVALID_ARG,
+          "rows_pad must be a multiple of %d and >= moe_mxfp8_padded_rows",
+          moe::kMxPad);
+  REQUIRE(cols * rows_pad <= kMaxBytes * 4, MOE_ERR_UNSUPPORTED,
+          "output larger than 4 GiB");
+  return hip_status(
+      moe::launch_mx4_quant_tokens(src, src_fmt == 1 ? src_scales : nullptr,
+                                   rows, cols, seg_offsets, nseg, codes,
+                                   scales, rows_pad, stream),
+      "moe_mxfp4_quantize/tokens");
+}
+
 }  // extern "C"

@@ -62,6 +62,19 @@ hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s);
 
+// MXFP4 (E2M1 codes two a byte, E8M0 scale per 32): rows of a bf16 tensor,
+// and blocks along the rows (token axis, 128-padded segments, transposed)
+// from bf16 (src_scales == nullptr) or from MXFP4 rows (codes [rows][cols/2]
+// with src_scales [rows][cols/32]).
+hipError_t launch_mx4_quant_rows(const bf16_t* src, int64_t rows,
+                                 int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+hipError_t launch_mx4_quant_tokens(const void* src,
+                                   const uint8_t* src_scales, int64_t rows,
+                                   int64_t cols, const int32_t* seg, int nseg,
+                                   uint8_t* codes, uint8_t* scales,
+                                   int64_t rows_pad, hipStream_t s);
+
 // router backward (route.hip)
 size_t router_backward_workspace(int64_t T, int E, int64_t d);
 hipError_t launch_router_backward(const float* logits, const int32_t* idx,

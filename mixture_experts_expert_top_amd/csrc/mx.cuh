@@ -6,6 +6,7 @@
 #pragma once
 
 #include "common.cuh"
+#include "internal.h"
 
 namespace moe {
 
@@ -46,6 +47,94 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
                                           false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
   return static_cast<uint32_t>(w);
+}
+
+// Exclusive prefix of the 128-padded segment lengths into s_pad[0..nseg]
+// (one wave), from device offsets seg[0..nseg] (or one segment of `rows`).
+__device__ inline void padded_prefix(const int32_t* seg, int nseg, int64_t rows,
+                              int* s_pad) {
+  const int lane = threadIdx.x;
+  if (lane < 64) {
+    constexpr int kPer = (kMaxExperts + 1 + 63) / 64;
+    int loc[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = lane * kPer + q;
+      int len = 0;
+      if (i < nseg)
+        len = seg ? seg[i + 1] - seg[i] : static_cast<int>(rows);
+      loc[q] = (len + kMxPad - 1) / kMxPad * kMxPad;
+      sum += loc[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(incl, m, 64);
+      if (lane >= m) incl += o;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = lane * kPer + q;
+      if (i <= nseg) s_pad[i] = run;
+      run += loc[q];
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- MXFP4
+// The hgpu.org abstract of the MXFP4 MoE training recipe keeps activations
+// and payloads as MXFP4: E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+// their negatives) with one E8M0 scale per 32 values, stored two codes a
+// byte (the lower index in the low nibble).
+
+// Block scale exponent: clamp(floor(log2 amax) - 2, -127, 127), 2 being
+// the exponent of E2M1's largest value (6 = 1.5 * 2^2); zero and subnormal
+// maxima give -127.
+__device__ __forceinline__ int mx4_scale_exp(float amax) {
+  const int ef = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+  if (ef == 0) return -127;
+  const int e = ef - 127 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E2M1 codes of v[0..7] (already divided by the block scale): round to
+// nearest, ties to the even code, saturate at +-6, keep the sign.  gfx950's
+// v_cvt_scalef32_pk_fp4_f32 (scale 1) rounds this way; it was checked
+// against a software encoder of the rule on every float of magnitude
+// below 16, both signs, and the inputs are clamped to +-6 first.
+__device__ __forceinline__ float e2m1_clamp(float x) {
+  return __builtin_amdgcn_fmed3f(x, -6.0f, 6.0f);
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_clamp(v[0]),
+                                               e2m1_clamp(v[1]), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_clamp(v[2]),
+                                               e2m1_clamp(v[3]), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_clamp(v[4]),
+                                               e2m1_clamp(v[5]), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_clamp(v[6]),
+                                               e2m1_clamp(v[7]), 1.0f, 3);
+  return w;
+}
+
+// Value of an E2M1 code (bits 0-3).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  // m < 2: 0 or 0.5; else (1 + (m & 1) / 2) * 2^((m >> 1) - 1)
+  const float v = (m < 2u) ? 0.5f * static_cast<float>(m)
+                           : __uint_as_float(((126u + (m >> 1)) << 23) |
+                                             ((m & 1u) << 22));
+  return (c & 8u) ? -v : v;
+}
+
+// 2^(byte - 127) for a scale byte (2^-127 is a subnormal float).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
 }
 
 }  // namespace moe

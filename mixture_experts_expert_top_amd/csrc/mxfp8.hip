@@ -56,40 +56,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   scales[blk] = static_cast<uint8_t>(e + 127);
 }
 
-// Exclusive prefix of the 128-padded segment lengths into s_pad[0..nseg]
-// (one wave), from device offsets seg[0..nseg] (or one segment of `rows`).
-__device__ void padded_prefix(const int32_t* seg, int nseg, int64_t rows,
-                              int* s_pad) {
-  const int lane = threadIdx.x;
-  if (lane < 64) {
-    constexpr int kPer = (kMaxExperts + 1 + 63) / 64;
-    int loc[kPer];
-    int sum = 0;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int i = lane * kPer + q;
-      int len = 0;
-      if (i < nseg)
-        len = seg ? seg[i + 1] - seg[i] : static_cast<int>(rows);
-      loc[q] = (len + kMxPad - 1) / kMxPad * kMxPad;
-      sum += loc[q];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int o = __shfl_up(incl, m, 64);
-      if (lane >= m) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int i = lane * kPer + q;
-      if (i <= nseg) s_pad[i] = run;
-      run += loc[q];
-    }
-  }
-  __syncthreads();
-}
 
 // Workgroup = one 128-row tile of the padded layout x kTokTiles runs of 64
 // columns (a tile never straddles a segment: segments start on multiples

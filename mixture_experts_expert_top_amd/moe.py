@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_BF16 = 0
 MOE_MXFP8 = 1
+MOE_MXFP4 = 2
 MOE_ENTRY_PERMUTE = 0
 MOE_ENTRY_MLP_FWD = 1
 MOE_ENTRY_MLP_BWD = 2
@@ -31,7 +32,7 @@ EXPORTED = [
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
     "moe_row_planes", "moe_mx_gate_up_swiglu_fwd", "moe_mx_down_fwd",
     "moe_mx_down_swiglu_bwd", "moe_mx_gate_up_dgrad", "moe_mx_grouped_wgrad",
-    "moe_router_backward",
+    "moe_router_backward", "moe_mxfp4_quantize",
 ]
 
 
@@ -69,6 +70,8 @@ def _load():
         "moe_row_planes": (I32, []),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
         "moe_mxfp8_padded_rows": (I64, [I64, I32]),
+        "moe_mxfp4_quantize": (I32, [P, I32, P, I64, I64, I32, P, I32, P, P,
+                                     I64, P]),
         "moe_workspace_bytes": (SZ, [I32, I32, I64, I32, I32, I64, I64]),
         "moe_dp_tiles": (I32, [I64]),
         "moe_gate_up_swiglu_fwd": (I32, [P, P, I32, I64, I64, I64, P, P, P,
@@ -335,6 +338,31 @@ def moe_mxfp8_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,
     _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(
         _p(src), rows, cols, axis, _p(seg_offsets), nseg, _p(codes),
         _p(scales), rows_pad, _stream(stream)))
+
+
+def moe_mxfp4_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,
+                       src_scales=None, cols=None, stream=None):
+    """src: bf16 [rows, cols], or (with src_scales) MXFP4 rows as uint8
+    codes [rows, cols/2] with scales [rows, cols/32].  Codes are two a
+    byte: axis 0 gives [rows, cols/2], axis 1 [cols, rows_pad/2]."""
+    rows = src.shape[0]
+    if src_scales is None:
+        _want(src, "src", torch.bfloat16)
+        cols = src.shape[1]
+        fmt = 0
+    else:
+        cols = 2 * src.shape[1]
+        _want(src, "src", torch.uint8)
+        _want(src_scales, "src_scales", torch.uint8, (rows, cols // 32))
+        fmt = 1
+    _want(codes, "codes", torch.uint8)
+    _want(scales, "scales", torch.uint8)
+    nseg = 1 if seg_offsets is None else seg_offsets.numel() - 1
+    if seg_offsets is not None:
+        _want(seg_offsets, "seg_offsets", torch.int32)
+    _check("moe_mxfp4_quantize", lib.moe_mxfp4_quantize(
+        _p(src), fmt, _p(src_scales), rows, cols, axis, _p(seg_offsets),
+        nseg, _p(codes), _p(scales), rows_pad, _stream(stream)))
 
 
 # ---------------------------------------------------------------- stages

@@ -278,3 +278,17 @@ def test_router_backward_workspace_size():
     assert got == up(2 * E * d * 4) + up(2 * E * 4) + up(T * 4)
     # without d (no dw_g / dx) the size query and the entry agree
     assert L.moe_workspace_bytes(3, BF16, T, E, 2, 0, 0) > 0
+
+
+def test_mxfp4_quantize_validation():
+    q = L.moe_mxfp4_quantize
+    # src, src_fmt, src_scales, rows, cols, axis, seg, nseg, codes, scales,
+    # rows_pad, stream
+    assert q(A, 0, None, 64, 48, 0, None, 1, A, A, 0, None) == INVALID
+    assert q(A, 1, A, 64, 64, 0, None, 1, A, A, 0, None) == INVALID
+    assert b"axis 0" in L.moe_last_error()
+    assert q(A, 1, None, 64, 64, 1, None, 1, A, A, 128, None) == INVALID
+    assert q(A, 2, None, 64, 64, 1, None, 1, A, A, 128, None) == INVALID
+    assert q(A, 0, None, 200, 64, 1, None, 1, A, A, 128, None) == INVALID
+    assert q(A, 0, None, 64, 64, 1, None, 2, A, A, 256, None) == INVALID
+    assert q(A, 0, None, 64, 64, 2, None, 1, A, A, 128, None) == INVALID
