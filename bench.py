@@ -59,13 +59,15 @@ def stage_flops(name, T, d, f, E, k):
     }.get(name, 0.0)
 
 
-def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
+def stage_bytes(name, T, d, f, E, k, planes=1, mx=False, act4=False):
     """Algorithmic HBM bytes of the memory-bound stages (each tensor read
     or written once; the fp32 rows the combines read come as `planes`
-    partial-sum planes; an MX row of n codes is n * 33/32 bytes)."""
+    partial-sum planes; an MXFP8 row of n codes is n * 33/32 bytes, an
+    MXFP4 row n * 17/32)."""
     Tk = T * k
-    xb = 33.0 / 32.0 if mx else 2.0            # bytes per permuted x value
-    q = 33.0 / 32.0                            # bytes per MX value
+    q4 = 17.0 / 32.0                           # bytes per MXFP4 value
+    q = 33.0 / 32.0                            # bytes per MXFP8 value
+    xb = (q4 if act4 else q) if mx else 2.0    # bytes per permuted x value
     return {
         "route": T * E * 4 + Tk * 8,
         "permute": Tk * 8 + T * d * xb + Tk * d * xb + Tk * 12 + E * 8,
@@ -75,10 +77,13 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False):
         "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 4,
         "router_backward": (T * E * 4 * 3 + Tk * 12 + T * d * 2 + E * d * 2
                             + T * d * 4 + T * d * 2 + E * d * 4),
-        "quant_x": T * d * (2 + q),
+        "quant_x": T * d * (2 + xb),
         "quant_weights": 3 * E * d * f * (2 + q),
         "quant_bwd_operands": (Tk * d + 3 * E * d * f) * (2 + q),
-        "quant_tokens": Tk * 2 * d * (2 + q),      # dO and Xp
+        # dO along tokens from bf16, and Xp from bf16 (MXFP8) or from the
+        # MXFP4 payload (MXFP4 activations)
+        "quant_tokens": Tk * d * (2 + q) + Tk * d * ((q4 + q4) if act4
+                                                    else (2 + q)),
     }.get(name, 0)
 
 
@@ -155,7 +160,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
-                    help="mixtral (default), mxfp8, finegrain, tiny")
+                    help="mixtral (default), mxfp8, mxfp4, finegrain, tiny")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -177,12 +182,16 @@ def main():
                                                       StageTimers)
 
     wl = inputs.WORKLOADS[args.workload]
-    mx = wl.prec == "mxfp8"
+    mx = wl.prec in ("mxfp8", "mxfp4")
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
     dev = torch.device("cuda:0")
     inp = inputs.make_inputs(wl, seed=0, device=dev)
-    path = (MoEPathMX if mx else MoEPath)(T, d, f, E, k, device=dev)
+    if mx:
+        path = MoEPathMX(T, d, f, E, k, device=dev,
+                         act_fp4=wl.prec == "mxfp4")
+    else:
+        path = MoEPath(T, d, f, E, k, device=dev)
 
     def step(timers=None):
         path.forward(inp["x"], inp["w_gu"], inp["w2"], w_g=inp["w_g"],
@@ -218,7 +227,8 @@ def main():
     for n, v in stage_ms.items():
         e = {"ms": round(v, 4)}
         fl = stage_flops(n, T, d, f, E, k)
-        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES, mx=mx)
+        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES, mx=mx,
+                         act4=wl.prec == "mxfp4")
         if fl:
             e["tflops"] = round(fl / (v / 1e3) / 1e12, 1)
         if by:
@@ -236,7 +246,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-e4m3" if mx else "bf16",
+        "dtype": {"mxfp8": "mxfp8-e4m3", "mxfp4": "mxfp8-e4m3+mxfp4-act",
+                  "bf16": "bf16"}[wl.prec],
         "data": "synthetic",
         "config": {"workload": f"{wl.name} fwd+bwd", "T": T, "d": d, "f": f,
                    "E": E, "k": k, "renorm": wl.renorm,

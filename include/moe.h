@@ -63,7 +63,10 @@ typedef enum moe_status {
 
 typedef enum moe_prec {
   MOE_BF16 = 0,   /* bf16 operands, fp32 accumulation                    */
-  MOE_MXFP8 = 1   /* E4M3 codes + one E8M0 scale byte per 32 values       */
+  MOE_MXFP8 = 1,  /* E4M3 codes + one E8M0 scale byte per 32 values       */
+  MOE_MXFP4 = 2   /* MXFP8 GEMMs with MXFP4 activations ([P5]): the       */
+                  /* dispatched x and the saved fc1 input are E2M1 codes  */
+                  /* (two a byte) + one E8M0 scale byte per 32 values     */
 } moe_prec;
 
 /* Entry ids for moe_workspace_bytes. */
@@ -209,6 +212,12 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   written (zero codes past its last row); columns past the last
  *   expert's padded rows are not.  s_saved may then be NULL.  For bf16
  *   s_tok must be NULL and s_saved is required.
+ * prec == MOE_MXFP4 ([P5]: FP8 GEMMs with MXFP4 activations): as
+ *   MOE_MXFP8 except that x_perm is the MXFP4 payload from moe_permute --
+ *   E2M1 codes [T*k][d/2] (two a byte, from moe_mxfp4_quantize axis 0)
+ *   with scales [T*k][d/32] -- which the gate_up GEMM widens to E4M3 codes
+ *   on their way to LDS (every E2M1 value is an E4M3 value; the scales are
+ *   kept), so the GEMM runs on the FP8 MFMA.
  * w_perm may be NULL (weight 1).  Workspace: MOE_ENTRY_MLP_FWD (none for
  * bf16).
  */
@@ -248,10 +257,18 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   that produces dAB (no bf16 dAB is stored).  With s_tok/s_tok_scales
  *   from the forward (ldt = moe_mxfp8_padded_rows(T*k, E)) S is not
  *   quantized again and s_saved may be NULL; for bf16 s_tok must be NULL.
+ *   x_perm_scales is unused (NULL) for bf16 and MXFP8.
+ * prec == MOE_MXFP4: as MOE_MXFP8 except that x_perm is the forward's
+ *   MXFP4 payload (codes [T*k][d/2], x_perm_scales [T*k][d/32]); the dW_gu
+ *   GEMM reads it converted to MXFP4 blocks along each expert's tokens
+ *   (moe_mxfp4_quantize axis 1 from MXFP4 rows), widened to E4M3 as
+ *   above, so no bf16 copy of x is needed.
  * Workspace: MOE_ENTRY_MLP_BWD.
  */
 moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
-                               const void* x_perm, const int32_t* offsets,
+                               const void* x_perm,
+                               const uint8_t* x_perm_scales,
+                               const int32_t* offsets,
                                const int32_t* pos, int64_t T, int32_t k,
                                int32_t E, int64_t d, int64_t f,
                                const void* w_gu, const void* w2,
@@ -323,7 +340,8 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
  * one E8M0 scale byte per 32 codes along the reduction axis.  d and f must
  * be multiples of 128; outputs as in the bf16 stages.
  *
- * moe_mx_gate_up_swiglu_fwd: xq [T*k][d], xs [T*k][d/32]; wq [E][2f][d],
+ * moe_mx_gate_up_swiglu_fwd: xq [T*k][d], xs [T*k][d/32] (x_fp4 != 0:
+ *   E2M1 codes xq [T*k][d/2], two a byte); wq [E][2f][d],
  *   ws [E][2f][d/32]; writes ab_saved, s_saved (bf16, may be NULL) and S
  *   quantized along f from its fp32 value: sq [T*k][f], ss [T*k][f/32];
  *   with s_tok/s_tok_scales also S along each expert's tokens (as in
@@ -346,10 +364,12 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
  *   bq [N][ldt], bs [N][ldt/32] come from moe_mxfp8_quantize axis 1 with
  *   seg_offsets = offsets (nseg = E) and rows_pad = ldt (a multiple of 128,
  *   at least moe_mxfp8_padded_rows(T*k, E)).  Experts without rows get
- *   exact zeros.
+ *   exact zeros.  b_fp4 != 0: b is E2M1, codes bq [N][ldt/2] (two a byte)
+ *   from moe_mxfp4_quantize axis 1.
  */
 moe_status moe_mx_gate_up_swiglu_fwd(
-    const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
+    const uint8_t* xq, const uint8_t* xs, int32_t x_fp4,
+    const int32_t* offsets, int32_t E,
     int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
     const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
     uint8_t* ss, uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
@@ -377,7 +397,8 @@ moe_status moe_mx_gate_up_dgrad(const uint8_t* dabq, const uint8_t* dabs,
 
 moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
                                 const uint8_t* bq, const uint8_t* bs,
-                                int64_t ldt, const int32_t* offsets,
+                                int32_t b_fp4, int64_t ldt,
+                                const int32_t* offsets,
                                 int32_t E, int64_t Tk, int64_t M, int64_t N,
                                 void* c, hipStream_t stream);
 

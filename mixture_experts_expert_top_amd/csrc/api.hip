@@ -72,13 +72,25 @@ moe_status check_route_dims(int64_t T, int32_t E, int32_t k) {
 }
 
 moe_status check_prec(moe_prec prec) {
-  REQUIRE(prec == MOE_BF16 || prec == MOE_MXFP8, MOE_ERR_INVALID_ARG,
-          "unknown precision %d", static_cast<int>(prec));
+  REQUIRE(prec == MOE_BF16 || prec == MOE_MXFP8 || prec == MOE_MXFP4,
+          MOE_ERR_INVALID_ARG, "unknown precision %d",
+          static_cast<int>(prec));
   return MOE_OK;
 }
 
+// MX GEMM operands (MXFP8, or MXFP8 with MXFP4 activations)
+bool is_mx(moe_prec prec) {
+  return prec == MOE_MXFP8 || prec == MOE_MXFP4;
+}
+
+// Bytes of one row of d activation values as moved by the permutations:
+// bf16, E4M3 codes, or E2M1 codes two a byte.
+int64_t act_row_bytes(moe_prec prec, int64_t d) {
+  return prec == MOE_BF16 ? d * 2 : (prec == MOE_MXFP8 ? d : d / 2);
+}
+
 moe_status check_feature(const char* name, int64_t v, moe_prec prec) {
-  const int64_t q = (prec == MOE_MXFP8) ? 32 : 8;
+  const int64_t q = is_mx(prec) ? 32 : 8;
   REQUIRE(v >= q && v % q == 0, MOE_ERR_INVALID_ARG,
           "%s must be a positive multiple of %lld (got %lld)", name,
           static_cast<long long>(q), static_cast<long long>(v));
@@ -228,7 +240,7 @@ const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
 size_t moe_workspace_bytes(moe_entry entry, moe_prec prec, int64_t T,
                            int32_t E, int32_t k, int64_t d, int64_t f) {
   if (T < 1 || E < 1 || E > moe::kMaxExperts || k < 1 || k > E) return 0;
-  if (prec != MOE_BF16 && prec != MOE_MXFP8) return 0;
+  if (prec != MOE_BF16 && !is_mx(prec)) return 0;
   const int64_t Tk = T * k;
   switch (entry) {
     case MOE_ENTRY_PERMUTE:
@@ -344,10 +356,10 @@ moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
           "w_perm given without topk_w");
   if (moe_status st = check_route_dims(T, E, k)) return st;
   if (moe_status st = check_feature("d", d, prec)) return st;
-  const int64_t row_bytes = (prec == MOE_BF16) ? d * 2 : d;
+  const int64_t row_bytes = act_row_bytes(prec, d);
   REQUIRE(T * k * row_bytes <= kMaxBytes * 4, MOE_ERR_UNSUPPORTED,
           "permuted tensor too large");
-  if (prec == MOE_MXFP8) {
+  if (is_mx(prec)) {
     REQUIRE_PTR(x_scales);
     REQUIRE_PTR(x_perm_scales);
   }
@@ -358,7 +370,7 @@ moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
   hipError_t e = moe::launch_plan(topk_idx, T, E, k, counts, offsets, pos,
                                   workspace, stream);
   if (e != hipSuccess) return hip_status(e, "moe_permute/plan");
-  const bool mx = prec == MOE_MXFP8;
+  const bool mx = is_mx(prec);
   e = moe::launch_scatter(topk_idx, topk_w, T, E, k, offsets, pos, src,
                           topk_w ? w_perm : nullptr, x, row_bytes, x_perm,
                           mx ? x_scales : nullptr, mx ? d / 32 : 0,
@@ -378,12 +390,12 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
   REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
           "k must be in [1, %d]", moe::kMaxTopK);
   if (moe_status st = check_feature("d", d, prec)) return st;
-  const bool mx = prec == MOE_MXFP8;
+  const bool mx = is_mx(prec);
   if (mx) {
     REQUIRE_PTR(x_scales);
     REQUIRE_PTR(x_perm_scales);
   }
-  const int64_t row_bytes = mx ? d : d * 2;
+  const int64_t row_bytes = act_row_bytes(prec, d);
   return hip_status(
       moe::launch_permute_rows(pos, T, k, x, row_bytes, x_perm,
                                mx ? x_scales : nullptr, mx ? d / 32 : 0,
@@ -410,10 +422,10 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE_PTR(ab_saved);
   REQUIRE_OPT_PTR(s_saved);
   REQUIRE_PTR(out_perm);
-  REQUIRE(prec == MOE_MXFP8 || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
-          "token-axis S codes are an MXFP8 output");
-  REQUIRE(s_saved || (prec == MOE_MXFP8 && s_tok), MOE_ERR_INVALID_ARG,
-          "s_saved is NULL (it may be only with MXFP8 token-axis S codes)");
+  REQUIRE(is_mx(prec) || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
+          "token-axis S codes are an MX output");
+  REQUIRE(s_saved || (is_mx(prec) && s_tok), MOE_ERR_INVALID_ARG,
+          "s_saved is NULL (it may be only with MX token-axis S codes)");
   REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
           "E must be in [1, %d]", moe::kMaxExperts);
   REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
@@ -422,7 +434,7 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
-  if (prec == MOE_MXFP8) {
+  if (is_mx(prec)) {
     if (moe_status st = check_mx_dims(d, f)) return st;
     REQUIRE_PTR(x_perm_scales);
     REQUIRE_PTR(w_gu_scales);
@@ -437,7 +449,8 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     hipError_t e = moe::gemm_mx_fc1_fwd(
         static_cast<const uint8_t*>(x_perm), x_perm_scales,
-        static_cast<const uint8_t*>(w_gu), w_gu_scales, offsets, E, Tk, d, f,
+        prec == MOE_MXFP4, static_cast<const uint8_t*>(w_gu), w_gu_scales,
+        offsets, E, Tk, d, f,
         w_perm, static_cast<bf16_t*>(ab_saved), static_cast<bf16_t*>(s_saved),
         ws + L.sq, ws + L.ss, s_tok, s_tok_scales, ldt, stream);
     if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_fwd/mx_fc1");
@@ -459,7 +472,9 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
 }
 
 moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
-                               const void* x_perm, const int32_t* offsets,
+                               const void* x_perm,
+                               const uint8_t* x_perm_scales,
+                               const int32_t* offsets,
                                const int32_t* pos, int64_t T, int32_t k,
                                int32_t E, int64_t d, int64_t f,
                                const void* w_gu, const void* w2,
@@ -481,10 +496,11 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   REQUIRE_OPT_PTR(s_saved);
   REQUIRE_OPT_PTR(w_perm);
   REQUIRE_PTR(dx_perm);
-  REQUIRE(prec == MOE_MXFP8 || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
-          "token-axis S codes are an MXFP8 input");
-  REQUIRE(s_saved || (prec == MOE_MXFP8 && s_tok), MOE_ERR_INVALID_ARG,
-          "s_saved is NULL (it may be only with MXFP8 token-axis S codes)");
+  REQUIRE(is_mx(prec) || (!s_tok && !s_tok_scales), MOE_ERR_INVALID_ARG,
+          "token-axis S codes are an MX input");
+  REQUIRE(s_saved || (is_mx(prec) && s_tok), MOE_ERR_INVALID_ARG,
+          "s_saved is NULL (it may be only with MX token-axis S codes)");
+  if (prec == MOE_MXFP4) REQUIRE_PTR(x_perm_scales);
   REQUIRE_PTR(dw_gu);
   REQUIRE_PTR(dw2);
   REQUIRE_PTR(dp);
@@ -496,7 +512,7 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
               2 * f * d * 2 <= kMaxBytes,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
   const BwdWorkspace L = bwd_layout(Tk, f);
-  if (prec == MOE_MXFP8) {
+  if (is_mx(prec)) {
     if (moe_status st = check_mx_dims(d, f)) return st;
     if (moe_status st = check_tok_out("moe_grouped_mlp_bwd", s_tok,
                                       s_tok_scales, ldt, Tk, E, f))
@@ -556,16 +572,27 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
       st_c = ws + X.st;
       st_s = ws + X.sts;
     }
-    MX_STEP(moe::gemm_mx_wgrad(ws + X.dot, ws + X.dots, st_c, st_s, tp,
-                               offsets, E, d, f, static_cast<bf16_t*>(dw2),
-                               stream),
+    MX_STEP(moe::gemm_mx_wgrad(ws + X.dot, ws + X.dots, st_c, st_s, false,
+                               tp, offsets, E, d, f,
+                               static_cast<bf16_t*>(dw2), stream),
             "mx_dw2");
-    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(x_perm),
-                                        nullptr, Tk, d, offsets, E,
-                                        ws + X.xpt, ws + X.xpts, tp, stream),
-            "quant_Xp_tokens");
+    // the dW_gu GEMM's Xp along tokens: E4M3 from the bf16 rows, or (MXFP4
+    // activations) E2M1 converted from the MXFP4 payload rows
+    const bool act4 = prec == MOE_MXFP4;
+    if (act4) {
+      MX_STEP(moe::launch_mx4_quant_tokens(x_perm, x_perm_scales, Tk, d,
+                                           offsets, E, ws + X.xpt,
+                                           ws + X.xpts, tp, stream),
+              "convert_Xp_tokens");
+    } else {
+      MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(x_perm),
+                                          nullptr, Tk, d, offsets, E,
+                                          ws + X.xpt, ws + X.xpts, tp,
+                                          stream),
+              "quant_Xp_tokens");
+    }
     MX_STEP(moe::gemm_mx_wgrad(ws + X.dabt, ws + X.dabts, ws + X.xpt,
-                               ws + X.xpts, tp, offsets, E, 2 * f, d,
+                               ws + X.xpts, act4, tp, offsets, E, 2 * f, d,
                                static_cast<bf16_t*>(dw_gu), stream),
             "mx_dw_gu");
 #undef MX_STEP
@@ -739,7 +766,8 @@ moe_status moe_dp_reduce(const float* dp_part, int32_t ntiles,
 // ------------------------------------------------------------ MX stages
 
 moe_status moe_mx_gate_up_swiglu_fwd(
-    const uint8_t* xq, const uint8_t* xs, const int32_t* offsets, int32_t E,
+    const uint8_t* xq, const uint8_t* xs, int32_t x_fp4,
+    const int32_t* offsets, int32_t E,
     int64_t Tk, int64_t d, int64_t f, const uint8_t* wq, const uint8_t* ws,
     const float* w_perm, void* ab_saved, void* s_saved, uint8_t* sq,
     uint8_t* ss, uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
@@ -754,7 +782,8 @@ moe_status moe_mx_gate_up_swiglu_fwd(
                                     s_tok_scales, ldt, Tk, E, f))
     return st;
   return hip_status(
-      moe::gemm_mx_fc1_fwd(xq, xs, wq, ws, offsets, E, Tk, d, f, w_perm,
+      moe::gemm_mx_fc1_fwd(xq, xs, x_fp4 != 0, wq, ws, offsets, E, Tk, d, f,
+                           w_perm,
                            static_cast<bf16_t*>(ab_saved),
                            static_cast<bf16_t*>(s_saved), sq, ss, s_tok,
                            s_tok_scales, ldt, stream),
@@ -816,7 +845,8 @@ moe_status moe_mx_gate_up_dgrad(const uint8_t* dabq, const uint8_t* dabs,
 
 moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
                                 const uint8_t* bq, const uint8_t* bs,
-                                int64_t ldt, const int32_t* offsets,
+                                int32_t b_fp4, int64_t ldt,
+                                const int32_t* offsets,
                                 int32_t E, int64_t Tk, int64_t M, int64_t N,
                                 void* c, hipStream_t stream) {
   REQUIRE_PTR(aq); REQUIRE_PTR(as); REQUIRE_PTR(bq); REQUIRE_PTR(bs);
@@ -833,7 +863,8 @@ moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
   REQUIRE(M * ldt <= kMaxBytes && N * ldt <= kMaxBytes &&
               M * N * 2 * static_cast<int64_t>(E) <= kMaxBytes * 8,
           MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
-  return hip_status(moe::gemm_mx_wgrad(aq, as, bq, bs, ldt, offsets, E, M, N,
+  return hip_status(moe::gemm_mx_wgrad(aq, as, bq, bs, b_fp4 != 0, ldt,
+                                       offsets, E, M, N,
                                        static_cast<bf16_t*>(c), stream),
                     "moe_mx_grouped_wgrad");
 }

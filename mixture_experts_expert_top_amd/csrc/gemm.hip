@@ -257,6 +257,75 @@ struct Mover<false> {
   }
 };
 
+// E2M1 codes two a byte -> E4M3 codes one a byte, exactly (every E2M1
+// value is an E4M3 value): through f16 with gfx950's scaled conversions at
+// scale 1 (checked against the code table on every 16-bit input).
+__device__ __forceinline__ i32x4 e2m1x16_to_e4m3(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((ext_vector_type(2))) short s2;
+  const s2 z = {0, 0};
+  s2 r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      z, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0), 1.0f, false);
+  r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      r0, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1), 1.0f, true);
+  s2 r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      z, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2), 1.0f, false);
+  r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      r1, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3), 1.0f, true);
+  s2 r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      z, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0), 1.0f, false);
+  r2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      r2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1), 1.0f, true);
+  s2 r3 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      z, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2), 1.0f, false);
+  r3 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+      r3, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3), 1.0f, true);
+  return i32x4{__builtin_bit_cast(int, r0), __builtin_bit_cast(int, r1),
+               __builtin_bit_cast(int, r2), __builtin_bit_cast(int, r3)};
+}
+
+// K-contiguous MXFP4 operand (two codes a byte), widened to E4M3 on its
+// way to LDS: the LDS tiles, fragments and MFMAs are then those of an E4M3
+// operand with the same block scales.  Piece i of thread t is Mover<true>'s
+// 16-code chunk (row t/8 + 32 i, chunk t%8), loaded as its 8 code bytes
+// (into the low half of the piece register) and widened at the LDS store.
+// k0 and kmax count code pairs, which are bytes here.
+struct Mover4 {
+  uint32_t tpart;   // (t/8) * row bytes + (t%8) * 8
+  uint32_t ldb;     // operand row stride in bytes
+  int koff;         // (t%8) * 8 code pairs
+  __device__ __forceinline__ void init(int t, int64_t ld_units) {
+    ldb = static_cast<uint32_t>(ld_units * 2);
+    tpart = static_cast<uint32_t>(t >> 3) * ldb +
+            static_cast<uint32_t>((t & 7) * 8);
+    koff = (t & 7) * 8;
+  }
+  template <typename Blk>
+  __device__ __forceinline__ void load(i32x4* v, __amdgpu_buffer_rsrc_t rs,
+                                       int k0, int kmax, Blk blk,
+                                       int part) const {
+    const bool kok = k0 + koff < kmax;
+#pragma unroll
+    for (int i = 4 * part; i < 4 * part + 4; ++i) {
+      const uint32_t off = tpart + static_cast<uint32_t>(blk(i)) * ldb +
+                           static_cast<uint32_t>(k0);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, kok ? off : kOob,
+                                                          0, 0);
+      v[i] = i32x4{static_cast<int>(w[0]), static_cast<int>(w[1]), 0, 0};
+    }
+  }
+  __device__ __forceinline__ static void store(const i32x4* v, bf16_t* lds,
+                                               int t, int part) {
+    const int chunk = t & 7;
+#pragma unroll
+    for (int i = 4 * part; i < 4 * part + 4; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      *reinterpret_cast<i32x4*>(lds + lds_off(row, chunk)) =
+          e2m1x16_to_e4m3(static_cast<uint32_t>(v[i][0]),
+                          static_cast<uint32_t>(v[i][1]));
+    }
+  }
+};
+
 // Load part `part` of one operand with the mover of its layout: K-contig
 // movers take the block map, MN-contig movers the first column.
 template <bool KC, typename M, typename Blk>
@@ -333,9 +402,13 @@ __device__ __forceinline__ void mx_mfmas(f32x16 (&acc)[BI][BJ],
           static_cast<int>(sa[I0 + i]), OPS, static_cast<int>(sb[j]));
 }
 
-template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX>
+template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX, int FMT>
 __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     Params P) {
+  // FMT bit 0 / bit 1: A / B holds MXFP4 (E2M1) codes, widened to E4M3 by
+  // its movers
+  static_assert(FMT == 0 || (MX && AKC && BKC && C::kSplitLoad),
+                "E2M1 operands: MX kernels, K-contiguous, 8 waves");
   constexpr int NT = C::kThreads;
   constexpr int BI = C::BI, BJ = C::BJ, TM = C::TM, TN = C::TN;
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmemBytes / 2];
@@ -687,7 +760,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   // read right before the MFMAs that use them; with 8 waves (two a SIMD)
   // only half of the wave's A fragments are held at a time, and each
   // wave's LDS waits are covered by the other wave of its SIMD.
-  auto kloop_mx = [&]() {
+  // role4: this wave moves an E2M1 operand (compile-time, so each role's
+  // copy of the loop carries only its own mover)
+  auto kloop_mx = [&](auto role4) {
+    constexpr bool kRole4 = decltype(role4)::value;
     constexpr int kHalves = (C::kWaves == 4) ? 1 : 2;
     constexpr int kAH = BI / kHalves;             // A fragments held at once
     constexpr int kMfH = kAH * BJ;                // MFMAs per half-slice
@@ -696,8 +772,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     const uint32_t srow_b =
         static_cast<uint32_t>((blk_b(lt >> 5) + (lt & 31)) * P.lds_b);
     uint32_t vsa = 0, vsb = 0;
+    // an E2M1 operand has its own mover (half the bytes a stage)
+    Mover4 m4;
+    if constexpr (kRole4) m4.init(lt, ld_own);
+    auto gload_ops = [&](int k0, int part) {
+      if constexpr (kRole4) {
+        auto blk = [&](int i) { return mv_a ? blk_a(i) : blk_b(i); };
+        m4.load(va, rs_own, k0, Kdim, blk, part);
+      } else {
+        gload(k0, part);
+      }
+    };
+    auto lstore_ops = [&](int st, int part) {
+      if constexpr (kRole4)
+        Mover4::store(va, mv_a ? atile(st) : btile(st), lt, part);
+      else
+        lstore(st, part);
+    };
     auto gload_mx = [&](int k0, int part) {
-      gload(k0, part);
+      gload_ops(k0, part);
       if (part == 0) {
         const bool ok = k0 < Kdim;
         const uint32_t kb = static_cast<uint32_t>(k0 >> 4);   // 32-blocks
@@ -711,7 +804,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
     };
     auto lstore_mx = [&](int st, int part) {
-      lstore(st, part);
+      lstore_ops(st, part);
       if (part == 0) {
         uint32_t* sc = s_scl + st * (2 * BM);
         if (C::kSplitLoad) {
@@ -835,7 +928,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   };
 
   if constexpr (MX) {
-    kloop_mx();
+    // with an E2M1 operand the waves that move it run their own loop copy
+    const bool own4 =
+        (FMT != 0) && (mv_a ? (FMT & 1) != 0 : (FMT & 2) != 0);
+    if constexpr (FMT != 0) {
+      if (own4) kloop_mx(std::true_type{});
+      else kloop_mx(std::false_type{});
+    } else {
+      kloop_mx(std::false_type{});
+    }
   } else if constexpr (C::kSplitLoad && AKC != BKC) {
     if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<AKC>{});
     else kloop(gload_b, lstore_b, std::bool_constant<BKC>{});
@@ -1166,12 +1267,13 @@ using CfgWgrad = Cfg8;
 #endif
 using CfgMx = std::conditional_t<MOE_MX_WAVES == 4, Cfg4, Cfg8>;
 
-template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX = false>
+template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX = false,
+          int FMT = 0>
 hipError_t launch(Params P, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (P.ksplit < 1) P.ksplit = 1;
   grid *= P.ksplit;
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI, MX>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI, MX, FMT>),
                      dim3(grid), dim3(C::kThreads), 0, s, P);
   return hipGetLastError();
 }
@@ -1274,7 +1376,7 @@ constexpr bool kMxTokEpi = CfgMx::TM == kMxPad && CfgMx::TN == 64;
 // fc1 forward: AB = Xp . W_gu^T, S = w*silu(g)*u as bf16 (s, optional),
 // as MX codes along f (the down GEMM's A) and, optionally, as MX codes
 // along each expert's tokens from its bf16 value (the dW2 GEMM's B)
-hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
+hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs, bool x_fp4,
                            const uint8_t* wq, const uint8_t* ws,
                            const int32_t* offsets, int E, int64_t Tk,
                            int64_t d, int64_t f, const float* w_perm,
@@ -1282,8 +1384,10 @@ hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
                            uint8_t* s_tok, uint8_t* s_tok_scales, int64_t ldt,
                            hipStream_t st) {
   if (s_tok && !kMxTokEpi) return hipErrorInvalidValue;
+  if (x_fp4 && !CfgMx::kSplitLoad) return hipErrorInvalidValue;
   Params P{};
-  P.A = reinterpret_cast<const bf16_t*>(xq); P.lda = d / 2;
+  // lda in 2-byte units: E4M3 rows of d codes, or E2M1 rows of d/2 bytes
+  P.A = reinterpret_cast<const bf16_t*>(xq); P.lda = x_fp4 ? d / 4 : d / 2;
   P.sA = xs; P.lds_a = d / kMxBlock;
   P.B = reinterpret_cast<const bf16_t*>(wq); P.ldb = d / 2;
   P.b_stride = f * d; P.b_rows = 2 * f;
@@ -1294,6 +1398,9 @@ hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
   P.ntn = static_cast<int>((f + BN / 2 - 1) / (BN / 2));
   P.w = w_perm; P.S = s; P.Qc = sq; P.Qs = ss;
   P.Tc = s_tok; P.Ts = s_tok_scales; P.ldt = ldt;
+  if (x_fp4)
+    return launch<CfgMx, kSegM, true, true, kSwiglu, true, 1>(
+        P, segm_grid(Tk, E, P.ntn), st);
   return launch<CfgMx, kSegM, true, true, kSwiglu, true>(
       P, segm_grid(Tk, E, P.ntn), st);
 }
@@ -1374,13 +1481,15 @@ hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
 // A[m][t] B[n][t], both operands quantized along tokens and transposed
 // ([rows][ldt] codes, [rows][ldt / 32] scales)
 hipError_t gemm_mx_wgrad(const uint8_t* aq, const uint8_t* as,
-                         const uint8_t* bq, const uint8_t* bs, int64_t ldt,
-                         const int32_t* offsets, int E, int64_t M, int64_t N,
-                         bf16_t* c, hipStream_t st) {
+                         const uint8_t* bq, const uint8_t* bs, bool b_fp4,
+                         int64_t ldt, const int32_t* offsets, int E,
+                         int64_t M, int64_t N, bf16_t* c, hipStream_t st) {
+  if (b_fp4 && !CfgMx::kSplitLoad) return hipErrorInvalidValue;
   Params P{};
   P.A = reinterpret_cast<const bf16_t*>(aq); P.lda = ldt / 2;
   P.sA = as; P.lds_a = ldt / kMxBlock;
-  P.B = reinterpret_cast<const bf16_t*>(bq); P.ldb = ldt / 2;
+  // B: E4M3 rows of ldt codes, or E2M1 rows of ldt/2 bytes (2-byte units)
+  P.B = reinterpret_cast<const bf16_t*>(bq); P.ldb = b_fp4 ? ldt / 4 : ldt / 2;
   P.sB = bs; P.lds_b = ldt / kMxBlock;
   P.C = c; P.ldc = N; P.c_stride = M * N;
   P.offsets = offsets; P.E = E;
@@ -1388,6 +1497,8 @@ hipError_t gemm_mx_wgrad(const uint8_t* aq, const uint8_t* as,
   P.ntn = static_cast<int>((N + BN - 1) / BN);
   const int64_t mtiles = (M + BM - 1) / BM;
   const int grid = static_cast<int>(E * mtiles * P.ntn);
+  if (b_fp4)
+    return launch<CfgMx, kSegKT, true, true, kStore, true, 2>(P, grid, st);
   return launch<CfgMx, kSegKT, true, true, kStore, true>(P, grid, st);
 }
 

@@ -109,7 +109,7 @@ hipError_t gemm_wgrad(const bf16_t* a, int64_t lda, const bf16_t* b,
                       int64_t M, int64_t N, bf16_t* c, hipStream_t st);
 
 // MXFP8 grouped GEMMs (gemm.hip): codes + scale bytes, see the definitions
-hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs,
+hipError_t gemm_mx_fc1_fwd(const uint8_t* xq, const uint8_t* xs, bool x_fp4,
                            const uint8_t* wq, const uint8_t* ws,
                            const int32_t* offsets, int E, int64_t Tk,
                            int64_t d, int64_t f, const float* w_perm,
@@ -134,8 +134,8 @@ hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
                              int64_t Tk, int64_t d, int64_t f, float* dxp,
                              hipStream_t st);
 hipError_t gemm_mx_wgrad(const uint8_t* aq, const uint8_t* as,
-                         const uint8_t* bq, const uint8_t* bs, int64_t ldt,
-                         const int32_t* offsets, int E, int64_t M, int64_t N,
-                         bf16_t* c, hipStream_t st);
+                         const uint8_t* bq, const uint8_t* bs, bool b_fp4,
+                         int64_t ldt, const int32_t* offsets, int E,
+                         int64_t M, int64_t N, bf16_t* c, hipStream_t st);
 
 }  // namespace moe

@@ -40,7 +40,8 @@ class Workload:
     router_bias: bool = False
     outlier_frac: float = 0.0
     outlier_scale: float = 100.0
-    prec: str = "bf16"          # "bf16" or "mxfp8"
+    prec: str = "bf16"          # "bf16", "mxfp8" or "mxfp4" (MXFP8 GEMMs
+                                # with MXFP4 activations)
     backward: bool = True
 
     @property
@@ -57,6 +58,8 @@ WORKLOADS = {
                           router_bias=True),
     "mxfp8": Workload("mxfp8", 16384, 4096, 14336, 8, 2, outlier_frac=0.01,
                       prec="mxfp8"),
+    "mxfp4": Workload("mxfp4", 16384, 4096, 14336, 8, 2, outlier_frac=0.01,
+                      prec="mxfp4"),
 }
 
 

@@ -20,6 +20,11 @@ along d before the permutation, the weights along their rows once per step
 GEMM epilogues that produce them (both along their GEMM axis and along each
 expert's tokens, the latter for the weight gradients), and dO and Xp along
 each expert's tokens in the backward.  No bf16 copy of S or dAB is kept.
+With ``act_fp4`` the GEMMs stay MXFP8 but x is quantized to MXFP4 along d
+(the dispatched payload, half the bytes), the gate_up GEMM widens it to
+E4M3 on its way to LDS, and the backward converts that payload to MXFP4
+blocks along each expert's tokens for the dW_gu GEMM (widened the same way)
+instead of re-permuting bf16 x.
 
 No arithmetic happens here: every step runs in the library's kernels.
 """
@@ -30,7 +35,8 @@ import torch
 
 from . import moe
 from .moe import (MOE_BF16, MOE_ENTRY_MLP_BWD, MOE_ENTRY_MLP_FWD,
-                  MOE_ENTRY_PERMUTE, MOE_ENTRY_ROUTER_BWD, MOE_MXFP8)
+                  MOE_ENTRY_PERMUTE, MOE_ENTRY_ROUTER_BWD, MOE_MXFP4,
+                  MOE_MXFP8)
 
 
 class StageTimers:
@@ -213,16 +219,18 @@ class MoEPathMX(MoEPath):
     """The layer with MXFP8 GEMM operands (see the module docstring)."""
 
     def __init__(self, T, d, f, E, k, renorm=True, device="cuda",
-                 y_fp32=False, aux_coef=0.01):
+                 y_fp32=False, aux_coef=0.01, act_fp4=False):
         super().__init__(T, d, f, E, k, renorm=renorm, prec=MOE_BF16,
                          device=device, y_fp32=y_fp32, aux_coef=aux_coef)
-        self.prec = MOE_MXFP8
+        self.act_fp4 = act_fp4
+        self.prec = MOE_MXFP4 if act_fp4 else MOE_MXFP8
         Tk = T * k
         dev = self.x_perm.device
         u8 = torch.uint8
         z = lambda *s: torch.empty(*s, dtype=u8, device=dev)  # noqa: E731
-        self.xq, self.xs = z(T, d), z(T, d // 32)
-        self.xpq, self.xps = z(Tk, d), z(Tk, d // 32)
+        dx = d // 2 if act_fp4 else d          # payload bytes a row
+        self.xq, self.xs = z(T, dx), z(T, d // 32)
+        self.xpq, self.xps = z(Tk, dx), z(Tk, d // 32)
         self.wguq, self.wgus = z(E, 2 * f, d), z(E, 2 * f, d // 32)
         self.w2q, self.w2s = z(E, d, f), z(E, d, f // 32)
         self.sq, self.ss = z(Tk, f), z(Tk, f // 32)
@@ -251,7 +259,8 @@ class MoEPathMX(MoEPath):
         self.dabq, self.dabs = z(Tk, 2 * f), z(Tk, 2 * f // 32)
         self.dot, self.dots = z(d, tp), z(d, tp // 32)
         self.dabt, self.dabts = z(2 * f, tp), z(2 * f, tp // 32)
-        self.xpt, self.xpts = z(d, tp), z(d, tp // 32)
+        self.xpt = z(d, tp // 2 if self.act_fp4 else tp)
+        self.xpts = z(d, tp // 32)
         ws_b = moe.moe_workspace_bytes(MOE_ENTRY_MLP_BWD, MOE_MXFP8, T, E, k,
                                        d, f)
         self.ws_bwd = z(max(ws_b, 16))
@@ -272,15 +281,18 @@ class MoEPathMX(MoEPath):
                 timers=None):
         self.route(x, w_g, bias, logits, timers)
         with _around(timers, "quant_x"):
-            moe.moe_mxfp8_quantize(x, 0, None, self.xq, self.xs)
+            if self.act_fp4:
+                moe.moe_mxfp4_quantize(x, 0, None, self.xq, self.xs)
+            else:
+                moe.moe_mxfp8_quantize(x, 0, None, self.xq, self.xs)
         with _around(timers, "permute"):
-            moe.moe_permute(MOE_MXFP8, self.topk_idx, self.topk_w, self.E,
+            moe.moe_permute(self.prec, self.topk_idx, self.topk_w, self.E,
                             self.xq, self.xs, self.counts, self.offsets,
                             self.pos, self.src, self.w_perm, self.xpq,
                             self.xps, self.ws_permute)
         self.quantize_weights(w_gu, w2, timers)
         if timers is None:
-            moe.moe_grouped_mlp_fwd(MOE_MXFP8, self.xpq, self.xps,
+            moe.moe_grouped_mlp_fwd(self.prec, self.xpq, self.xps,
                                     self.offsets, self.wguq, self.wgus,
                                     self.w2q, self.w2s, self.w_perm, self.ab,
                                     None, self.o, self.ws_fwd,
@@ -290,7 +302,8 @@ class MoEPathMX(MoEPath):
                 moe.moe_mx_gate_up_swiglu_fwd(
                     self.xpq, self.xps, self.offsets, self.wguq, self.wgus,
                     self.w_perm, self.ab, None, self.sq, self.ss,
-                    s_tok=self.st, s_tok_scales=self.sts)
+                    s_tok=self.st, s_tok_scales=self.sts,
+                    x_fp4=self.act_fp4)
             with timers.around("down_fwd"):
                 moe.moe_mx_down_fwd(self.sq, self.ss, self.offsets, self.w2q,
                                     self.w2s, self.o)
@@ -306,16 +319,21 @@ class MoEPathMX(MoEPath):
         with _around(timers, "permute_dy"):
             moe.moe_permute_rows(MOE_BF16, self.pos, dy, None,
                                  self.dout_perm, None)
-        with _around(timers, "permute_x"):
-            moe.moe_permute_rows(MOE_BF16, self.pos, self._x, None,
-                                 self.x_perm, None)
+        if not self.act_fp4:
+            # the MXFP4 variant reads the forward's payload instead
+            with _around(timers, "permute_x"):
+                moe.moe_permute_rows(MOE_BF16, self.pos, self._x, None,
+                                     self.x_perm, None)
+        xp, xps = ((self.xpq, self.xps) if self.act_fp4
+                   else (self.x_perm, None))
         if timers is None:
-            moe.moe_grouped_mlp_bwd(MOE_MXFP8, self.dout_perm, self.x_perm,
+            moe.moe_grouped_mlp_bwd(self.prec, self.dout_perm, xp,
                                     self.offsets, self.pos, w_gu, w2, self.ab,
                                     None, self.w_perm, self.dx_perm,
                                     self.dw_gu, self.dw2, self.dp,
                                     self.ws_bwd, s_tok=self.st,
-                                    s_tok_scales=self.sts)
+                                    s_tok_scales=self.sts,
+                                    x_perm_scales=xps)
         else:
             # the same kernels in the same order as moe_grouped_mlp_bwd
             tp = self.tk_pad
@@ -338,9 +356,15 @@ class MoEPathMX(MoEPath):
                 moe.moe_mx_gate_up_dgrad(self.dabq, self.dabs, self.offsets,
                                          self.wgutq, self.wguts, self.dx_perm)
             with timers.around("quant_tokens"):
-                for src, cq, cs in ((self.dout_perm, self.dot, self.dots),
-                                    (self.x_perm, self.xpt, self.xpts)):
-                    moe.moe_mxfp8_quantize(src, 1, self.offsets, cq, cs, tp)
+                moe.moe_mxfp8_quantize(self.dout_perm, 1, self.offsets,
+                                       self.dot, self.dots, tp)
+                if self.act_fp4:
+                    moe.moe_mxfp4_quantize(self.xpq, 1, self.offsets,
+                                           self.xpt, self.xpts, tp,
+                                           src_scales=self.xps)
+                else:
+                    moe.moe_mxfp8_quantize(self.x_perm, 1, self.offsets,
+                                           self.xpt, self.xpts, tp)
             Tk = self.T * self.k
             with timers.around("wgrad_down"):
                 moe.moe_mx_grouped_wgrad(self.dot, self.dots, self.st,
@@ -348,6 +372,6 @@ class MoEPathMX(MoEPath):
             with timers.around("wgrad_gate_up"):
                 moe.moe_mx_grouped_wgrad(self.dabt, self.dabts, self.xpt,
                                          self.xpts, self.offsets, Tk,
-                                         self.dw_gu)
+                                         self.dw_gu, b_fp4=self.act_fp4)
         self._finish_dx(timers)
         return self.dx, self.dw_gu, self.dw2, self.dp

@@ -62,9 +62,9 @@ def _load():
         "moe_grouped_mlp_fwd": (I32, [I32, P, P, P, I32, I64, I64, I64, P, P,
                                       P, P, P, P, P, P, P, P, I64, P, SZ,
                                       P]),
-        "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, I64, I32, I32, I64,
-                                      I64, P, P, P, P, P, P, I64, P, P, P,
-                                      P, P, P, SZ, P]),
+        "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, P, I64, I32, I32,
+                                      I64, I64, P, P, P, P, P, P, I64, P, P,
+                                      P, P, P, P, SZ, P]),
         "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
                                 P]),
         "moe_row_planes": (I32, []),
@@ -83,15 +83,16 @@ def _load():
         "moe_grouped_wgrad": (I32, [P, I64, P, I64, P, I32, I64, I64, I64, P,
                                     P]),
         "moe_dp_reduce": (I32, [P, I32, P, I64, I32, P, P]),
-        "moe_mx_gate_up_swiglu_fwd": (I32, [P, P, P, I32, I64, I64, I64, P,
-                                            P, P, P, P, P, P, P, P, I64, P]),
+        "moe_mx_gate_up_swiglu_fwd": (I32, [P, P, I32, P, I32, I64, I64, I64,
+                                            P, P, P, P, P, P, P, P, P, I64,
+                                            P]),
         "moe_mx_down_fwd": (I32, [P, P, P, I32, I64, I64, I64, P, P, P, P]),
         "moe_mx_down_swiglu_bwd": (I32, [P, P, P, I32, I64, I64, I64, P, P,
                                          P, P, P, P, P, P, P, I64, P, P]),
         "moe_mx_gate_up_dgrad": (I32, [P, P, P, I32, I64, I64, I64, P, P, P,
                                        P]),
-        "moe_mx_grouped_wgrad": (I32, [P, P, P, P, I64, P, I32, I64, I64,
-                                       I64, P, P]),
+        "moe_mx_grouped_wgrad": (I32, [P, P, P, P, I32, I64, P, I32, I64,
+                                       I64, I64, P, P]),
         "moe_router_backward": (I32, [P, P, P, P, P, ctypes.c_float, I64,
                                       I32, I32, I32, P, P, I64, P, P, P, P,
                                       P, P, P, SZ, P]),
@@ -202,13 +203,14 @@ def moe_router_backward(logits, topk_idx, topk_w, dp, counts, aux_coef,
 def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
                 src, w_perm, x_perm, x_perm_scales, workspace, stream=None):
     T, k = topk_idx.shape
-    d = x.shape[1]
+    xdt, per = _act(prec, x, "x")
+    w = x.shape[1]
+    d = w * per
     _want(topk_idx, "topk_idx", torch.int32)
     _want(topk_w, "topk_w", torch.float32, (T, k), allow_none=True)
-    xdt = torch.bfloat16 if prec == MOE_BF16 else torch.uint8
-    _want(x, "x", xdt, (T, d))
-    _want(x_perm, "x_perm", xdt, (T * k, d))
-    if prec == MOE_MXFP8:
+    _want(x, "x", xdt, (T, w))
+    _want(x_perm, "x_perm", xdt, (T * k, w))
+    if prec != MOE_BF16:
         _want(x_scales, "x_scales", torch.uint8, (T, d // 32))
         _want(x_perm_scales, "x_perm_scales", torch.uint8, (T * k, d // 32))
     for n, t, shp in (("counts", counts, (E,)), ("offsets", offsets, (E + 1,)),
@@ -226,14 +228,23 @@ def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
 def moe_permute_rows(prec, pos, x, x_scales, x_perm, x_perm_scales,
                      stream=None):
     T, k = pos.shape
-    d = x.shape[1]
+    xdt, per = _act(prec, x, "x")
+    w = x.shape[1]
+    d = w * per
     _want(pos, "pos", torch.int32)
-    xdt = torch.bfloat16 if prec == MOE_BF16 else torch.uint8
-    _want(x, "x", xdt, (T, d))
-    _want(x_perm, "x_perm", xdt, (T * k, d))
+    _want(x, "x", xdt, (T, w))
+    _want(x_perm, "x_perm", xdt, (T * k, w))
     _check("moe_permute_rows", lib.moe_permute_rows(
         prec, _p(pos), T, k, _p(x), _p(x_scales), d, _p(x_perm),
         _p(x_perm_scales), _stream(stream)))
+
+
+def _act(prec, x, what):
+    """(dtype, values per stored element) of an activation tensor: bf16,
+    E4M3 codes, or E2M1 codes two a byte."""
+    if prec == MOE_BF16:
+        return torch.bfloat16, 1
+    return torch.uint8, (2 if prec == MOE_MXFP4 else 1)
 
 
 def _tok_out(name, codes, scales, cols):
@@ -251,10 +262,12 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
                         w_gu_scales, w2, w2_scales, w_perm, ab_saved, s_saved,
                         out_perm, workspace=None, stream=None, s_tok=None,
                         s_tok_scales=None):
-    Tk, d = x_perm.shape
-    E, two_f, _ = w_gu.shape
+    Tk = x_perm.shape[0]
+    E, two_f, d = w_gu.shape
     f = two_f // 2
     _want(offsets, "offsets", torch.int32, (E + 1,))
+    xdt, per = _act(prec, x_perm, "x_perm")
+    _want(x_perm, "x_perm", xdt, (Tk, d // per))
     if prec == MOE_BF16:
         _want(x_perm, "x_perm", torch.bfloat16)
         _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
@@ -275,13 +288,20 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
 
 def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                         ab_saved, s_saved, w_perm, dx_perm, dw_gu, dw2, dp,
-                        workspace, stream=None, s_tok=None, s_tok_scales=None):
-    Tk, d = x_perm.shape
+                        workspace, stream=None, s_tok=None, s_tok_scales=None,
+                        x_perm_scales=None):
+    """x_perm: bf16 rows (bf16 and MXFP8), or for MXFP4 the forward's
+    payload, E2M1 codes [T*k, d/2] with x_perm_scales [T*k, d/32]."""
+    Tk, d = dout_perm.shape
     T, k = pos.shape
     E, two_f, _ = w_gu.shape
     f = two_f // 2
+    if prec == MOE_MXFP4:
+        _want(x_perm, "x_perm", torch.uint8, (Tk, d // 2))
+        _want(x_perm_scales, "x_perm_scales", torch.uint8, (Tk, d // 32))
+    else:
+        _want(x_perm, "x_perm", torch.bfloat16, (Tk, d))
     for n, t, shp in (("dout_perm", dout_perm, (Tk, d)),
-                      ("x_perm", x_perm, (Tk, d)),
                       ("w_gu", w_gu, (E, 2 * f, d)), ("w2", w2, (E, d, f)),
                       ("ab_saved", ab_saved, (Tk, 2 * f)),
                       ("dw_gu", dw_gu, (E, 2 * f, d)), ("dw2", dw2, (E, d, f))):
@@ -296,7 +316,8 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
     _check("moe_grouped_mlp_bwd", lib.moe_grouped_mlp_bwd(
-        prec, _p(dout_perm), _p(x_perm), _p(offsets), _p(pos), T, k, E, d, f,
+        prec, _p(dout_perm), _p(x_perm), _p(x_perm_scales), _p(offsets),
+        _p(pos), T, k, E, d, f,
         _p(w_gu), _p(w2), _p(ab_saved), _p(s_saved), _p(s_tok),
         _p(s_tok_scales), ldt, _p(w_perm), _p(dx_perm), _p(dw_gu), _p(dw2),
         _p(dp), _p(workspace), nbytes, _stream(stream)))
@@ -461,11 +482,12 @@ def moe_dp_reduce(dp_part, pos, dp, stream=None):
 
 def moe_mx_gate_up_swiglu_fwd(xq, xs, offsets, wq, ws, w_perm, ab_saved,
                               s_saved, sq, ss, s_tok=None, s_tok_scales=None,
-                              stream=None):
-    Tk, d = xq.shape
-    E, two_f, _ = wq.shape
+                              stream=None, x_fp4=False):
+    """xq: E4M3 codes [T*k, d], or (x_fp4) E2M1 codes [T*k, d/2]."""
+    Tk = xq.shape[0]
+    E, two_f, d = wq.shape
     f = two_f // 2
-    _want(xq, "xq", torch.uint8)
+    _want(xq, "xq", torch.uint8, (Tk, d // 2 if x_fp4 else d))
     _want(xs, "xs", torch.uint8, (Tk, d // 32))
     _want(wq, "wq", torch.uint8, (E, 2 * f, d))
     _want(ws, "ws", torch.uint8, (E, 2 * f, d // 32))
@@ -477,7 +499,8 @@ def moe_mx_gate_up_swiglu_fwd(xq, xs, offsets, wq, ws, w_perm, ab_saved,
     _want(ss, "ss", torch.uint8, (Tk, f // 32))
     ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
     _check("moe_mx_gate_up_swiglu_fwd", lib.moe_mx_gate_up_swiglu_fwd(
-        _p(xq), _p(xs), _p(offsets), E, Tk, d, f, _p(wq), _p(ws),
+        _p(xq), _p(xs), int(bool(x_fp4)), _p(offsets), E, Tk, d, f, _p(wq),
+        _p(ws),
         _p(w_perm), _p(ab_saved), _p(s_saved), _p(sq), _p(ss), _p(s_tok),
         _p(s_tok_scales), ldt, _stream(stream)))
 
@@ -537,16 +560,19 @@ def moe_mx_gate_up_dgrad(dabq, dabs, offsets, wgutq, wguts, dx_perm,
         _p(dx_perm), _stream(stream)))
 
 
-def moe_mx_grouped_wgrad(aq, as_, bq, bs, offsets, Tk, c, stream=None):
+def moe_mx_grouped_wgrad(aq, as_, bq, bs, offsets, Tk, c, stream=None,
+                         b_fp4=False):
+    """aq [M, ldt] E4M3 codes; bq [N, ldt] E4M3, or (b_fp4) E2M1 codes
+    [N, ldt/2]."""
     M, ldt = aq.shape
     N = bq.shape[0]
     E = offsets.numel() - 1
     _want(aq, "aq", torch.uint8)
     _want(as_, "as", torch.uint8, (M, ldt // 32))
-    _want(bq, "bq", torch.uint8, (N, ldt))
+    _want(bq, "bq", torch.uint8, (N, ldt // 2 if b_fp4 else ldt))
     _want(bs, "bs", torch.uint8, (N, ldt // 32))
     _want(offsets, "offsets", torch.int32)
     _want(c, "c", torch.bfloat16, (E, M, N))
     _check("moe_mx_grouped_wgrad", lib.moe_mx_grouped_wgrad(
-        _p(aq), _p(as_), _p(bq), _p(bs), ldt, _p(offsets), E, Tk, M, N,
-        _p(c), _stream(stream)))
+        _p(aq), _p(as_), _p(bq), _p(bs), int(bool(b_fp4)), ldt,
+        _p(offsets), E, Tk, M, N, _p(c), _stream(stream)))

@@ -107,12 +107,12 @@ def _fwd_args(prec=BF16, E=4, Tk=128, d=32, f=64, s=A, s_tok=None,
 
 
 def _bwd_args(prec=BF16, T=64, k=2, E=4, d=32, f=64, s=A, s_tok=None,
-              s_tok_scales=None, ldt=0):
-    # prec, dout_perm, x_perm, offsets, pos, T, k, E, d, f, w_gu, w2,
-    # ab_saved, s_saved, s_tok, s_tok_scales, ldt, w_perm, dx_perm, dw_gu,
-    # dw2, dp, workspace
-    return [prec, A, A, A, A, T, k, E, d, f, A, A, A, s, s_tok, s_tok_scales,
-            ldt, A, A, A, A, A, A]
+              s_tok_scales=None, ldt=0, xs=None):
+    # prec, dout_perm, x_perm, x_perm_scales, offsets, pos, T, k, E, d, f,
+    # w_gu, w2, ab_saved, s_saved, s_tok, s_tok_scales, ldt, w_perm,
+    # dx_perm, dw_gu, dw2, dp, workspace
+    return [prec, A, A, xs, A, A, T, k, E, d, f, A, A, A, s, s_tok,
+            s_tok_scales, ldt, A, A, A, A, A, A]
 
 
 def test_mlp_fwd_validation():
@@ -187,8 +187,8 @@ def test_mx_token_axis_output_validation():
     assert b(*_bwd_args(MX, E=E, d=128, f=128, s=None), wsb,
              None) == INVALID
     # stage entries
-    assert L.moe_mx_gate_up_swiglu_fwd(A, A, A, E, Tk, 128, 128, A, A, A, A,
-                                       None, A, A, A, None, tp,
+    assert L.moe_mx_gate_up_swiglu_fwd(A, A, 0, A, E, Tk, 128, 128, A, A, A,
+                                       A, None, A, A, A, None, tp,
                                        None) == INVALID
     assert L.moe_mx_down_swiglu_bwd(A, A, A, E, Tk, 128, 128, A, A, A, A,
                                     None, A, A, A, A, tp - 128, A,
@@ -202,10 +202,10 @@ def test_mx_stage_validation():
                                   None) == INVALID
     # ldt must cover the padded token layout
     tp = L.moe_mxfp8_padded_rows(128, 4)
-    assert L.moe_mx_grouped_wgrad(A, A, A, A, tp - 128, A, 4, 128, 64, 64,
-                                  A, None) == INVALID
-    assert L.moe_mx_grouped_wgrad(A, A, A, A, tp + 64, A, 4, 128, 64, 64,
-                                  A, None) == INVALID
+    assert L.moe_mx_grouped_wgrad(A, A, A, A, 0, tp - 128, A, 4, 128, 64,
+                                  64, A, None) == INVALID
+    assert L.moe_mx_grouped_wgrad(A, A, A, A, 1, tp + 64, A, 4, 128, 64,
+                                  64, A, None) == INVALID
 
 
 def test_unpermute_validation():
@@ -292,3 +292,19 @@ def test_mxfp4_quantize_validation():
     assert q(A, 0, None, 200, 64, 1, None, 1, A, A, 128, None) == INVALID
     assert q(A, 0, None, 64, 64, 1, None, 2, A, A, 256, None) == INVALID
     assert q(A, 0, None, 64, 64, 2, None, 1, A, A, 128, None) == INVALID
+
+
+def test_mxfp4_precision_validation():
+    """MOE_MXFP4 (MXFP8 GEMMs with MXFP4 activations): the backward needs
+    the payload's scales; precision 3 does not exist."""
+    MX4 = 2
+    b = L.moe_grouped_mlp_bwd
+    wsb = L.moe_workspace_bytes(2, MX4, 64, 4, 2, 128, 128)
+    assert wsb == L.moe_workspace_bytes(2, MX, 64, 4, 2, 128, 128)
+    assert b(*_bwd_args(MX4, d=128, f=128), wsb, None) == INVALID
+    assert b"x_perm_scales" in L.moe_last_error()
+    assert L.moe_workspace_bytes(2, 3, 64, 4, 2, 128, 128) == 0
+    f = L.moe_grouped_mlp_fwd
+    assert f(*_fwd_args(3, d=128, f=128, ws=A), 1 << 20, None) == INVALID
+    # permute moves d/2 code bytes a row: d must still be a multiple of 32
+    assert _permute(prec=MX4, d=48, x_scales=A, xp_scales=A) == INVALID

@@ -1,4 +1,6 @@
-"""MXFP8 layer at its full size: 16384 tokens, the Mixtral expert shape
+"""MXFP8 layer at its full size, and its MXFP4-activation variant (the
+dispatched x and the saved fc1 input in MXFP4, MXFP8 GEMMs): 16384 tokens,
+the Mixtral expert shape
 (d=4096, f=14336, E=8, top-2, renormalised), 1% of the token rows scaled by
 100 (their router scores too).  GPU forward and backward through MoEPathMX
 against the MX-emulating oracle (oracle/moe_mx.py) evaluated for sampled
@@ -40,12 +42,13 @@ def rel(got, ref):
 
 @gpu
 @pytest.mark.timeout(900)
-def test_mx_full_size_sampled():
-    wl = I.WORKLOADS["mxfp8"]
+@pytest.mark.parametrize("act4", [False, True], ids=["mxfp8", "mxfp4_act"])
+def test_mx_full_size_sampled(act4):
+    wl = I.WORKLOADS["mxfp4" if act4 else "mxfp8"]
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
     dev = torch.device("cuda:0")
     inp = I.make_inputs(wl, seed=0, device=dev)
-    path = MoEPathMX(T, d, f, E, k, device=dev)
+    path = MoEPathMX(T, d, f, E, k, device=dev, act_fp4=act4)
     path.forward(inp["x"], inp["w_gu"], inp["w2"], logits=inp["logits"])
     path.backward(inp["dy"], inp["w_gu"], inp["w2"])
     torch.cuda.synchronize()
@@ -73,12 +76,12 @@ def test_mx_full_size_sampled():
     dxp_gpu = h64(path.dx_perm.sum(dim=0)[pos[tokens, :][idx[tokens] == 0]])
     dp_gpu = path.dp.cpu().numpy()
     results = {}
-    y_ref = np.stack([X.token_forward_mx(xt[i], idx[t], p[t], W)
+    y_ref = np.stack([X.token_forward_mx(xt[i], idx[t], p[t], W, act4)
                       for i, t in enumerate(tokens)])
     dxp_ref, dp_ref, dp_got = [], [], []
     for i, t in enumerate(tokens):
         j = int(np.nonzero(idx[t] == 0)[0][0])
-        g, dpv = X.row_backward_mx(xt[i], dyt[i], p[t, j], W[0])
+        g, dpv = X.row_backward_mx(xt[i], dyt[i], p[t, j], W[0], act4)
         dxp_ref.append(g)
         dp_ref.append(dpv)
         dp_got.append(dp_gpu[t, j])
@@ -102,10 +105,10 @@ def test_mx_full_size_sampled():
         wgu_e = h64(inp["w_gu"][e])
         w2_e = h64(inp["w2"][e])
         for j in cols:
-            ref = X.dw2_column_mx(xe, dye, we, wgu_e, j)
+            ref = X.dw2_column_mx(xe, dye, we, wgu_e, j, act4)
             results[f"dw2[{e}][:,{j}]"] = rel(h64(path.dw2[e][:, j]), ref)
         for i in rows:
-            ref = X.dw_gu_row_mx(xe, dye, we, wgu_e, w2_e, i)
+            ref = X.dw_gu_row_mx(xe, dye, we, wgu_e, w2_e, i, act4)
             results[f"dw_gu[{e}][{i}]"] = rel(h64(path.dw_gu[e][i]), ref)
     print("max|err|/rms per sampled group:",
           {n: f"{v:.2e}" for n, v in results.items()})
