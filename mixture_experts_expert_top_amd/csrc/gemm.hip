@@ -59,6 +59,22 @@
 namespace moe {
 namespace {
 
+// Streaming (non-temporal) stores of epilogue outputs.  Used for the fc1
+// outputs (AB, S and their MX codes) and the plain bf16 tile stores: on
+// MI355X they made the MX fc1 GEMM 9% and the MX weight gradient 9%
+// faster, with no change to the bf16 GEMMs.  The dSwiGLU outputs keep
+// ordinary stores (streaming made that GEMM 20% slower).
+__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
+  __builtin_nontemporal_store((static_cast<uint64_t>(v.y) << 32) | v.x,
+                              reinterpret_cast<uint64_t*>(p));
+}
+__device__ __forceinline__ void st_stream(i32x4* p, i32x4 v) {
+  __builtin_nontemporal_store(v, p);
+}
+__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
@@ -375,8 +391,7 @@ __device__ __forceinline__ uint32_t mx_quant4(const float* v, bool valid,
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) amax = fmaxf(amax, valid ? fabsf(v[c]) : 0.0f);
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  amax = dpp_group_max<8>(amax);
   const int e = mx_scale_exp(amax);
   const float inv = mx_inv_scale(e);
   const uint32_t word =
@@ -978,8 +993,31 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     for (int m = 1; m < 64; m <<= 1) acc_p += __shfl_xor(acc_p, m, 64);
     pe = acc_p;
   }
+  // kDSwiglu: a lane's rows of a pass are r0 + it * kRowsPerPass.  Every
+  // AB read and routing weight of the pass is issued before the
+  // accumulators are staged, so the reads overlap the staging and each
+  // other instead of waiting one row at a time between dAB stores.
+  constexpr int kDsIt = kEpiRows / kRowsPerPass;
+  constexpr int kPre = EPI == kDSwiglu ? kDsIt : 1;
 #pragma unroll
   for (int h = 0; h < TM / kEpiRows; ++h) {
+    const int row_base = m0 + wm * TM + h * kEpiRows;   // absolute row
+    uint2 pre_g[kPre], pre_u[kPre];
+    if constexpr (EPI == kDSwiglu) {
+      const bf16_t* AB = P.AB + seg0 * static_cast<int64_t>(2 * f);
+      const int col = n0 + wn * TN + (lane % kLanesPerRow) * 4;
+#pragma unroll
+      for (int it = 0; it < kDsIt; ++it) {
+        const int row = row_base + lane / kLanesPerRow + it * kRowsPerPass;
+        pre_g[it] = make_uint2(0u, 0u);
+        pre_u[it] = make_uint2(0u, 0u);
+        if (row < Mvalid && col < f) {
+          const bf16_t* src = AB + static_cast<int64_t>(row) * 2 * f + col;
+          pre_g[it] = *reinterpret_cast<const uint2*>(src);
+          pre_u[it] = *reinterpret_cast<const uint2*>(src + f);
+        }
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < kEpiRows / 32; ++ii)
 #pragma unroll
@@ -990,7 +1028,6 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           stage[r * LD + j * 32 + fr] = acc[h * (kEpiRows / 32) + ii][j][v];
         }
     __syncthreads();
-    const int row_base = m0 + wm * TM + h * kEpiRows;   // absolute row
     if (EPI == kStore || EPI == kStoreF32) {
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
@@ -1005,7 +1042,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             uint2 u;
             u.x = pack_bf16x2(x[0], x[1]);
             u.y = pack_bf16x2(x[2], x[3]);
-            *reinterpret_cast<uint2*>(P.C + o) = u;
+            st_stream(reinterpret_cast<uint2*>(P.C + o), u);
           }
         }
       }
@@ -1035,7 +1072,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const uint32_t q = mx_quant4(sv, ok, &sbyte);
           if (ok) {
             const int64_t qr = (seg0 + ro) * f;
-            *reinterpret_cast<uint32_t*>(P.Qc + qr + col) = q;
+            st_stream(reinterpret_cast<uint32_t*>(P.Qc + qr + col), q);
             if ((lane & 7) == 0)
               P.Qs[qr / kMxBlock + col / kMxBlock] =
                   static_cast<uint8_t>(sbyte);
@@ -1047,9 +1084,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           uint2 og, ou;
           og.x = pack_bf16x2(g[0], g[1]); og.y = pack_bf16x2(g[2], g[3]);
           ou.x = pack_bf16x2(u[0], u[1]); ou.y = pack_bf16x2(u[2], u[3]);
-          *reinterpret_cast<uint2*>(AB + ro * P.ldc + col) = og;
-          *reinterpret_cast<uint2*>(AB + ro * P.ldc + f + col) = ou;
-          if (P.S) *reinterpret_cast<uint2*>(S + ro * f + col) = os;
+          st_stream(reinterpret_cast<uint2*>(AB + ro * P.ldc + col), og);
+          st_stream(reinterpret_cast<uint2*>(AB + ro * P.ldc + f + col), ou);
+          if (P.S) st_stream(reinterpret_cast<uint2*>(S + ro * f + col), os);
         }
         if constexpr (kTokEpi) {
           // the bf16 S values go back over this row's gate slots for the
@@ -1087,18 +1124,19 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             uint8_t* dst = P.Tc +
                 static_cast<int64_t>(n0g + wn * (TN / 2) + cc) * P.ldt + pe +
                 trow;
-            *reinterpret_cast<i32x4*>(dst) = q[0];
-            *reinterpret_cast<i32x4*>(dst + 16) = q[1];
+            st_stream(reinterpret_cast<i32x4*>(dst), q[0]);
+            st_stream(reinterpret_cast<i32x4*>(dst + 16), q[1]);
           }
           tsc[0] |= static_cast<uint32_t>(ex + 127) << (8 * (2 * h + cb));
         }
       }
     } else {  // kDSwiglu
-      const bf16_t* AB = P.AB + seg0 * static_cast<int64_t>(2 * f);
       bf16_t* dAB = P.C + cbase;
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
-      for (int r = lane / kLanesPerRow; r < kEpiRows; r += kRowsPerPass) {
+#pragma unroll
+      for (int it = 0; it < kDsIt; ++it) {
+        const int r = lane / kLanesPerRow + it * kRowsPerPass;
         const int row = row_base + r;
         float part = 0.0f;
         const bool ok = row < Mvalid && col < f;
@@ -1107,9 +1145,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         float du[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (ok) {
           const f32x4 ds = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
-          const uint2 gb = *reinterpret_cast<const uint2*>(AB + ro * 2 * f + col);
-          const uint2 ub =
-              *reinterpret_cast<const uint2*>(AB + ro * 2 * f + f + col);
+          const uint2 gb = pre_g[it], ub = pre_u[it];
           const float g[4] = {bf_lo(gb.x), bf_hi(gb.x), bf_lo(gb.y),
                               bf_hi(gb.y)};
           const float u[4] = {bf_lo(ub.x), bf_hi(ub.x), bf_lo(ub.y),
@@ -1159,10 +1195,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             }
           }
         }
-        // row sum over the lanes of this row, fixed butterfly order
+        // row sum over the lanes of this row, fixed order
+        if constexpr (kLanesPerRow <= 16) {
+          part = dpp_group_sum<kLanesPerRow>(part);
+        } else {
+          part = dpp_group_sum<16>(part);
 #pragma unroll
-        for (int m = 1; m < kLanesPerRow; m <<= 1)
-          part += __shfl_xor(part, m, 64);
+          for (int m = 16; m < kLanesPerRow; m <<= 1)
+            part += __shfl_xor(part, m, 64);
+        }
         if ((lane % kLanesPerRow) == 0)
           s_dp[wn * BM + wm * TM + h * kEpiRows + r] = part;
       }
