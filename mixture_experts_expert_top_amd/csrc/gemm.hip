@@ -428,6 +428,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   constexpr int BI = C::BI, BJ = C::BJ, TM = C::TM, TN = C::TN;
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmemBytes / 2];
   __shared__ int s_pref[kMaxExperts + 1];
+  // weight gradients: expert sizes and their descending order
+  __shared__ int s_cnt[MODE == kSegM ? 1 : kMaxExperts];
+  __shared__ int s_ord[MODE == kSegM ? 1 : kMaxExperts];
+  __shared__ int s_stat[2];
   __shared__ float s_dp[C::WN * BM];
   // MX: scale dwords of the tile rows, [stage][A rows, B rows]
   __shared__ uint32_t s_scl[MX ? 2 * 2 * BM : 1];
@@ -497,10 +501,55 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     seg0 = P.offsets[e];
     seg_len = P.offsets[e + 1] - P.offsets[e];
   } else {
+    // A weight-gradient tile's depth is its expert's size (rows, or padded
+    // token units), so with skewed routing the contiguous per-XCD tile
+    // ranges would hand one XCD most of the work.  When the largest expert
+    // is above twice the mean, experts are taken largest first (ties by
+    // index) and tiles are dealt round-robin over the XCDs, in the order
+    // the hardware hands out block ids; otherwise the L2-friendly
+    // contiguous ranges stay.  Every workgroup reaches the same decision.
     const int mtiles = (P.M + BM - 1) / BM;
     const int per_e = mtiles * P.ntn;
-    e = bid / per_e;
-    tile_order(bid - e * per_e, mtiles, P.ntn, &mt, &nt);
+    for (int i = tid; i < E; i += NT)
+      s_cnt[i] = (MODE == kSegKT) ? s_pref[i + 1] - s_pref[i]
+                                  : P.offsets[i + 1] - P.offsets[i];
+    __syncthreads();
+    if (tid < 64) {
+      int mx = 0, sm = 0;
+      for (int i = tid; i < E; i += 64) {
+        mx = max(mx, s_cnt[i]);
+        sm += s_cnt[i];
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        mx = max(mx, __shfl_xor(mx, m, 64));
+        sm += __shfl_xor(sm, m, 64);
+      }
+      if (tid == 0) { s_stat[0] = mx; s_stat[1] = sm; }
+    }
+    __syncthreads();
+    const bool skew = static_cast<int64_t>(s_stat[0]) * E >
+                      2 * static_cast<int64_t>(s_stat[1]);
+    if (skew) {
+      for (int i = tid; i < E; i += NT) {
+        const int ci = s_cnt[i];
+        int r = 0;
+        for (int j = 0; j < E; ++j) {
+          const int cj = s_cnt[j];
+          r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
+        }
+        s_ord[r] = i;
+      }
+      __syncthreads();
+      const int t = blockIdx.x;
+      e = s_ord[t / per_e];
+      const int local = t - (t / per_e) * per_e;
+      mt = local % mtiles;
+      nt = local / mtiles;
+    } else {
+      e = bid / per_e;
+      tile_order(bid - e * per_e, mtiles, P.ntn, &mt, &nt);
+    }
     seg0 = P.offsets[e];
     seg_len = P.offsets[e + 1] - P.offsets[e];
   }
@@ -1031,10 +1080,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     if (EPI == kStore || EPI == kStoreF32) {
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
-      for (int r = lane / kLanesPerRow; r < kEpiRows; r += kRowsPerPass) {
+      // unrolled, so the stage reads of all rows are in flight together
+#pragma unroll
+      for (int it = 0; it < kEpiRows / kRowsPerPass; ++it) {
+        const int r = lane / kLanesPerRow + it * kRowsPerPass;
         const int row = row_base + r;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
         if (row < Mvalid && col < P.N) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
           const int64_t o = cbase + static_cast<int64_t>(row) * P.ldc + col;
           if (EPI == kStoreF32) {
             *reinterpret_cast<f32x4*>(P.Cf + split * P.plane + o) = x;
@@ -1054,14 +1106,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       constexpr int kRowsG = 64 / kLanesG;
       const int c4 = (lane % kLanesG) * 4;
       const int col = n0g + wn * (TN / 2) + c4;       // gate column
-      for (int r = lane / kLanesG; r < kEpiRows; r += kRowsG) {
+      // routing weights of the pass read up front; rows unrolled so the
+      // stage reads overlap
+      constexpr int kItG = kEpiRows / kRowsG;
+      float pre_wr[kItG];
+#pragma unroll
+      for (int it = 0; it < kItG; ++it) {
+        const int row = row_base + lane / kLanesG + it * kRowsG;
+        pre_wr[it] = (w && row < Mvalid && col < f) ? w[row] : 1.0f;
+      }
+#pragma unroll
+      for (int it = 0; it < kItG; ++it) {
+        const int r = lane / kLanesG + it * kRowsG;
         const int row = row_base + r;
         const bool ok = row < Mvalid && col < f;
         const int64_t ro = static_cast<int64_t>(row);
         const f32x4 g = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
         const f32x4 u =
             *reinterpret_cast<const f32x4*>(stage + r * LD + TN / 2 + c4);
-        const float wr = (w && ok) ? w[row] : 1.0f;
+        const float wr = pre_wr[it];
         float sv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
