@@ -241,17 +241,19 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
   }
 }
 
-// Partial dW_g over one chunk of 256 tokens, 256 columns and up to 32
+// Partial dW_g over one chunk of 256 tokens, 512 columns and up to 32
 // experts: part[chunk][e][c] = sum over the chunk's tokens, in order, of
 // dlogits[t][e] * x[t][c]; the y == 0 blocks also sum dlogits over the
 // chunk (db).  With part == nullptr only the db sums are made (x unread).
 constexpr int kRbTok = 256;
 constexpr int kRbExp = 32;
+constexpr int kRbCols = 512;          // columns of a block, two a thread
 __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     const float* __restrict__ dlogits, const bf16_t* __restrict__ x, int T,
     int E, int d, float* __restrict__ part, float* __restrict__ db_part) {
-  __shared__ float s_dl[kRbTok][kRbExp];
-  const int tc = blockIdx.x, c = blockIdx.y * 256 + threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float s_dl[kRbTok][kRbExp];
+  const int tc = blockIdx.x;
+  const int c = blockIdx.y * kRbCols + threadIdx.x * 2;
   const int e0 = blockIdx.z * kRbExp;
   const int t0 = tc * kRbTok;
   const int ne = min(kRbExp, E - e0), nt = min(kRbTok, T - t0);
@@ -267,16 +269,31 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     db_part[static_cast<int64_t>(tc) * E + e0 + threadIdx.x] = acc;
   }
   if (part == nullptr || c >= d) return;
-  float acc[kRbExp];
+  // columns c and c+1 (d is a multiple of 8), tokens added in order
+  float acc0[kRbExp], acc1[kRbExp];
 #pragma unroll
-  for (int ee = 0; ee < kRbExp; ++ee) acc[ee] = 0.0f;
+  for (int ee = 0; ee < kRbExp; ++ee) { acc0[ee] = 0.0f; acc1[ee] = 0.0f; }
+  const bf16_t* xc = x + static_cast<int64_t>(t0) * d + c;
   for (int tt = 0; tt < nt; ++tt) {
-    const float xv = bf2f(x[static_cast<int64_t>(t0 + tt) * d + c]);
+    const uint32_t xv =
+        *reinterpret_cast<const uint32_t*>(xc + static_cast<int64_t>(tt) * d);
+    const float x0 = bf_lo(xv), x1 = bf_hi(xv);
 #pragma unroll
-    for (int ee = 0; ee < kRbExp; ++ee) acc[ee] += s_dl[tt][ee] * xv;
+    for (int q = 0; q < kRbExp / 4; ++q) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&s_dl[tt][4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc0[4 * q + r] += g[r] * x0;
+        acc1[4 * q + r] += g[r] * x1;
+      }
+    }
   }
-  for (int ee = 0; ee < ne; ++ee)
-    part[(static_cast<int64_t>(tc) * E + e0 + ee) * d + c] = acc[ee];
+  for (int ee = 0; ee < ne; ++ee) {
+    float2 o;
+    o.x = acc0[ee];
+    o.y = acc1[ee];
+    *reinterpret_cast<float2*>(part + (static_cast<int64_t>(tc) * E + e0 + ee) * d + c) = o;
+  }
 }
 
 // dW_g[e][c] = sum over chunks, in order, of part[chunk][e][c]; db likewise.
@@ -297,54 +314,88 @@ __global__ __launch_bounds__(256) void router_dwg_reduce_kernel(
   }
 }
 
-// dx_out[t] = bf16(dx_in[t] + sum_e dlogits[t][e] w_g[e]): a block owns one
-// token and 2048 columns, a thread 8 of them; experts added in order.
+// dx_out[t] = bf16(dx_in[t] + sum_e dlogits[t][e] w_g[e]), experts added
+// in order: a block owns kDxTok tokens and 2048 columns, a thread 8
+// columns of each of the tokens, so every w_g chunk it loads serves
+// kDxTok tokens.
+constexpr int kDxTok = 8;
 __global__ __launch_bounds__(256) void router_dx_kernel(
     const float* __restrict__ dlogits, const bf16_t* __restrict__ wg,
-    const float* __restrict__ dx_in, int E, int d,
+    const float* __restrict__ dx_in, int T, int E, int d,
     bf16_t* __restrict__ dx_out) {
-  __shared__ float s_dl[kMaxExperts];
-  const int64_t t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) s_dl[e] = dlogits[t * E + e];
+  __shared__ __attribute__((aligned(16))) float s_dl[kMaxExperts * kDxTok];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kDxTok;
+  const int nt = min(kDxTok, static_cast<int>(T - t0));
+  // s_dl[e][tt]: the block's dlogits, expert-major
+  for (int i = threadIdx.x; i < kDxTok * E; i += 256) {
+    const int tt = i / E, e = i - (i / E) * E;
+    s_dl[e * kDxTok + tt] = tt < nt ? dlogits[(t0 + tt) * E + e] : 0.0f;
+  }
   __syncthreads();
   const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (c >= d) return;
-  float acc[8];
-  if (dx_in) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(dx_in + t * d + c);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(dx_in + t * d + c + 4);
-    acc[0] = a[0]; acc[1] = a[1]; acc[2] = a[2]; acc[3] = a[3];
-    acc[4] = b[0]; acc[5] = b[1]; acc[6] = b[2]; acc[7] = b[3];
-  } else {
+  float acc[kDxTok][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  }
-  for (int e = 0; e < E; ++e) {
-    const i32x4 w = *reinterpret_cast<const i32x4*>(wg + static_cast<int64_t>(e) * d + c);
-    const float g = s_dl[e];
+  for (int tt = 0; tt < kDxTok; ++tt) {
+    if (dx_in && tt < nt) {
+      const float* src = dx_in + (t0 + tt) * d + c;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      acc[tt][0] = a[0]; acc[tt][1] = a[1]; acc[tt][2] = a[2]; acc[tt][3] = a[3];
+      acc[tt][4] = b[0]; acc[tt][5] = b[1]; acc[tt][6] = b[2]; acc[tt][7] = b[3];
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += g * bf_lo(static_cast<uint32_t>(w[q]));
-      acc[2 * q + 1] += g * bf_hi(static_cast<uint32_t>(w[q]));
+      for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
     }
   }
-  uint4 o;
-  o.x = pack_bf16x2(acc[0], acc[1]);
-  o.y = pack_bf16x2(acc[2], acc[3]);
-  o.z = pack_bf16x2(acc[4], acc[5]);
-  o.w = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<uint4*>(dx_out + t * d + c) = o;
+  for (int e = 0; e < E; ++e) {
+    const i32x4 w =
+        *reinterpret_cast<const i32x4*>(wg + static_cast<int64_t>(e) * d + c);
+    float wv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wv[2 * q] = bf_lo(static_cast<uint32_t>(w[q]));
+      wv[2 * q + 1] = bf_hi(static_cast<uint32_t>(w[q]));
+    }
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok + 4);
+    const float g[kDxTok] = {g0[0], g0[1], g0[2], g0[3],
+                             g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+    for (int tt = 0; tt < kDxTok; ++tt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[tt][i] += g[tt] * wv[i];
+  }
+#pragma unroll
+  for (int tt = 0; tt < kDxTok; ++tt) {
+    if (tt < nt) {
+      uint4 o;
+      o.x = pack_bf16x2(acc[tt][0], acc[tt][1]);
+      o.y = pack_bf16x2(acc[tt][2], acc[tt][3]);
+      o.z = pack_bf16x2(acc[tt][4], acc[tt][5]);
+      o.w = pack_bf16x2(acc[tt][6], acc[tt][7]);
+      *reinterpret_cast<uint4*>(dx_out + (t0 + tt) * d + c) = o;
+    }
+  }
 }
 
-// aux_loss = alpha * E / T * sum over blocks, in order, of q_part.
-__global__ void router_aux_final_kernel(const float* __restrict__ q_part,
-                                        int blocks, float scale,
-                                        float* __restrict__ loss) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    float acc = 0.0f;
-    for (int b = 0; b < blocks; ++b) acc += q_part[b];
-    loss[0] = scale * acc;
+// aux_loss = alpha * E / T * sum of q_part: thread j adds blocks j, j+256,
+// ... in order, then the 256 partial sums are added pairwise in a fixed
+// tree (deterministic).
+__global__ __launch_bounds__(256) void router_aux_final_kernel(
+    const float* __restrict__ q_part, int blocks, float scale,
+    float* __restrict__ loss) {
+  __shared__ float s_sum[256];
+  float acc = 0.0f;
+  for (int b = threadIdx.x; b < blocks; b += 256) acc += q_part[b];
+  s_sum[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w)
+      s_sum[threadIdx.x] += s_sum[threadIdx.x + w];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) loss[0] = scale * s_sum[0];
 }
 
 }  // namespace
@@ -436,7 +487,7 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
     // without dw_g only the db sums are wanted: one column block, x unread
     const int64_t dd = dw_g ? d : 0;
     dim3 g2(static_cast<unsigned>(chunks),
-            static_cast<unsigned>(dw_g ? (d + 255) / 256 : 1),
+            static_cast<unsigned>(dw_g ? (d + kRbCols - 1) / kRbCols : 1),
             static_cast<unsigned>((E + kRbExp - 1) / kRbExp));
     hipLaunchKernelGGL(router_dwg_partial_kernel, g2, dim3(256), 0, s, dlogits,
                        x, Ti, E, static_cast<int>(dd), dw_g ? part : nullptr,
@@ -450,13 +501,14 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (dx_out) {
-    dim3 g4(static_cast<unsigned>(T), static_cast<unsigned>((d + 2047) / 2048));
+    dim3 g4(static_cast<unsigned>((T + kDxTok - 1) / kDxTok),
+            static_cast<unsigned>((d + 2047) / 2048));
     hipLaunchKernelGGL(router_dx_kernel, g4, dim3(256), 0, s, dlogits, w_g,
-                       dx_in, E, static_cast<int>(d), dx_out);
+                       dx_in, Ti, E, static_cast<int>(d), dx_out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (aux_loss && counts) {
-    hipLaunchKernelGGL(router_aux_final_kernel, dim3(1), dim3(64), 0, s,
+    hipLaunchKernelGGL(router_aux_final_kernel, dim3(1), dim3(256), 0, s,
                        q_part, static_cast<int>(grid),
                        alpha * static_cast<float>(E) / static_cast<float>(T),
                        aux_loss);
