@@ -141,17 +141,18 @@ def cpu_baseline(inp, wl, n_tokens):
     t0 = time.perf_counter()
     logits = moe_ref.router_logits(x, w_g, bias)
     fwd = moe_ref.moe_forward(x, logits, w_gu, w2, wl.k)
-    bwd = moe_ref.moe_backward(fwd, dy, w_gu, w2)
-    dl = moe_ref.routing_weight_backward(logits, fwd["idx"], fwd["p"],
-                                         bwd["dp"], wl.renorm)
-    dl = dl + moe_ref.aux_loss(logits, fwd["counts"], 0.01)[1]
-    moe_ref.router_backward(x, w_g, dl)
+    if wl.backward:
+        bwd = moe_ref.moe_backward(fwd, dy, w_gu, w2)
+        dl = moe_ref.routing_weight_backward(logits, fwd["idx"], fwd["p"],
+                                             bwd["dp"], wl.renorm)
+        dl = dl + moe_ref.aux_loss(logits, fwd["counts"], 0.01)[1]
+        moe_ref.router_backward(x, w_g, dl)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"first {n_tokens} tokens of the {wl.name} workload, "
-                       "fwd+bwd, float64 numpy per-expert loop with the full "
-                       f"weights ({dt:.1f} s)")}
+                       f"{'fwd+bwd' if wl.backward else 'fwd'}, float64 numpy "
+                       f"per-expert loop with the full weights ({dt:.1f} s)")}
 
 
 def main():
@@ -196,7 +197,8 @@ def main():
     def step(timers=None):
         path.forward(inp["x"], inp["w_gu"], inp["w2"], w_g=inp["w_g"],
                      bias=inp["bias"], timers=timers)
-        path.backward(inp["dy"], inp["w_gu"], inp["w2"], timers=timers)
+        if wl.backward:
+            path.backward(inp["dy"], inp["w_gu"], inp["w2"], timers=timers)
 
     for _ in range(args.warmup):
         step()
@@ -216,13 +218,15 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     stage_ms = timers.mean_ms()
-    gemm_flops = sum(stage_flops(n, T, d, f, E, k) for n in GEMM_STAGES)
+    gemm_stages = [n for n in GEMM_STAGES if n in stage_ms]
+    gemm_flops = sum(stage_flops(n, T, d, f, E, k) for n in gemm_stages)
     all_flops = gemm_flops + sum(stage_flops(n, T, d, f, E, k)
-                                 for n in ("router_logits", "router_backward"))
+                                 for n in ("router_logits", "router_backward")
+                                 if n in stage_ms)
     tokens_s = T / (ms / 1e3)
-    dom = max(GEMM_STAGES, key=lambda n: stage_ms[n])
+    dom = max(gemm_stages, key=lambda n: stage_ms[n])
     dom_tflops = stage_flops(dom, T, d, f, E, k) / (stage_ms[dom] / 1e3) / 1e12
-    gemm_ms = sum(stage_ms[n] for n in GEMM_STAGES)
+    gemm_ms = sum(stage_ms[n] for n in gemm_stages)
     stages = {}
     for n, v in stage_ms.items():
         e = {"ms": round(v, 4)}
@@ -249,7 +253,8 @@ def main():
         "dtype": {"mxfp8": "mxfp8-e4m3", "mxfp4": "mxfp8-e4m3+mxfp4-act",
                   "bf16": "bf16"}[wl.prec],
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} fwd+bwd", "T": T, "d": d, "f": f,
+        "config": {"workload": f"{wl.name} {'fwd+bwd' if wl.backward else 'fwd'}",
+                   "T": T, "d": d, "f": f,
                    "E": E, "k": k, "renorm": wl.renorm,
                    "router_bias": wl.router_bias},
         "tflops": round(all_flops / (ms / 1e3) / 1e12, 1),

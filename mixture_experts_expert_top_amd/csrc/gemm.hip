@@ -59,20 +59,30 @@
 namespace moe {
 namespace {
 
-// Streaming (non-temporal) stores of epilogue outputs.  Used for the fc1
-// outputs (AB, S and their MX codes) and the plain bf16 tile stores: on
-// MI355X they made the MX fc1 GEMM 9% and the MX weight gradient 9%
-// faster, with no change to the bf16 GEMMs.  The dSwiGLU outputs keep
-// ordinary stores (streaming made that GEMM 20% slower).
-__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
-  __builtin_nontemporal_store((static_cast<uint64_t>(v.y) << 32) | v.x,
-                              reinterpret_cast<uint64_t*>(p));
+// Epilogue output stores of the MX kernels' fc1 outputs (AB, S codes) and
+// plain tile stores are streaming (non-temporal): on MI355X that made the
+// MX fc1 GEMM 9% and the MX weight gradient 9% faster.  The bf16 kernels
+// keep ordinary stores: streaming left their time unchanged but raised
+// fc1's HBM reads from 3.6x to 4.1x the algorithmic bytes.  The dSwiGLU
+// outputs keep ordinary stores everywhere (streaming made that GEMM 20%
+// slower).
+template <bool kStream>
+__device__ __forceinline__ void st_epi(uint2* p, uint2 v) {
+  if constexpr (kStream)
+    __builtin_nontemporal_store((static_cast<uint64_t>(v.y) << 32) | v.x,
+                                reinterpret_cast<uint64_t*>(p));
+  else
+    *p = v;
 }
-__device__ __forceinline__ void st_stream(i32x4* p, i32x4 v) {
-  __builtin_nontemporal_store(v, p);
+template <bool kStream>
+__device__ __forceinline__ void st_epi(i32x4* p, i32x4 v) {
+  if constexpr (kStream) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
-__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
-  __builtin_nontemporal_store(v, p);
+template <bool kStream>
+__device__ __forceinline__ void st_epi(uint32_t* p, uint32_t v) {
+  if constexpr (kStream) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 
 constexpr int BM = 256;
@@ -1094,7 +1104,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             uint2 u;
             u.x = pack_bf16x2(x[0], x[1]);
             u.y = pack_bf16x2(x[2], x[3]);
-            st_stream(reinterpret_cast<uint2*>(P.C + o), u);
+            st_epi<MX>(reinterpret_cast<uint2*>(P.C + o), u);
           }
         }
       }
@@ -1135,7 +1145,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const uint32_t q = mx_quant4(sv, ok, &sbyte);
           if (ok) {
             const int64_t qr = (seg0 + ro) * f;
-            st_stream(reinterpret_cast<uint32_t*>(P.Qc + qr + col), q);
+            st_epi<MX>(reinterpret_cast<uint32_t*>(P.Qc + qr + col), q);
             if ((lane & 7) == 0)
               P.Qs[qr / kMxBlock + col / kMxBlock] =
                   static_cast<uint8_t>(sbyte);
@@ -1147,9 +1157,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           uint2 og, ou;
           og.x = pack_bf16x2(g[0], g[1]); og.y = pack_bf16x2(g[2], g[3]);
           ou.x = pack_bf16x2(u[0], u[1]); ou.y = pack_bf16x2(u[2], u[3]);
-          st_stream(reinterpret_cast<uint2*>(AB + ro * P.ldc + col), og);
-          st_stream(reinterpret_cast<uint2*>(AB + ro * P.ldc + f + col), ou);
-          if (P.S) st_stream(reinterpret_cast<uint2*>(S + ro * f + col), os);
+          st_epi<MX>(reinterpret_cast<uint2*>(AB + ro * P.ldc + col), og);
+          st_epi<MX>(reinterpret_cast<uint2*>(AB + ro * P.ldc + f + col), ou);
+          if (P.S) st_epi<MX>(reinterpret_cast<uint2*>(S + ro * f + col), os);
         }
         if constexpr (kTokEpi) {
           // the bf16 S values go back over this row's gate slots for the
@@ -1187,8 +1197,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             uint8_t* dst = P.Tc +
                 static_cast<int64_t>(n0g + wn * (TN / 2) + cc) * P.ldt + pe +
                 trow;
-            st_stream(reinterpret_cast<i32x4*>(dst), q[0]);
-            st_stream(reinterpret_cast<i32x4*>(dst + 16), q[1]);
+            st_epi<MX>(reinterpret_cast<i32x4*>(dst), q[0]);
+            st_epi<MX>(reinterpret_cast<i32x4*>(dst + 16), q[1]);
           }
           tsc[0] |= static_cast<uint32_t>(ex + 127) << (8 * (2 * h + cb));
         }

@@ -57,45 +57,68 @@ __global__ __launch_bounds__(64) void plan_rank_kernel(
     chunk_counts[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
-// Pass 2: one workgroup.  Thread e turns its column of chunk counts into
-// exclusive chunk bases (in place) and the expert total; then an exclusive
-// scan over experts gives the offsets.
+// Pass 2: one workgroup.  Each expert's column of chunk counts is turned
+// into exclusive chunk bases (in place) and the expert total by a group of
+// G lanes (G = 64 halved until G * E <= 1024): lane g sums its contiguous
+// range of chunks, the group scans those sums, and each lane rewrites its
+// range from its base.  An exclusive scan over experts then gives the
+// offsets.  Integer sums, so the result does not depend on the split.
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ chunk_counts, int nchunks, int E,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int s_cnt[kMaxExperts];
   __shared__ int wsum[16];
-  const int e = threadIdx.x;
-  int run = 0;
+  int G = 64;
+  while (G > 1 && G * E > 1024) G >>= 1;
+  const int t = threadIdx.x;
+  const int e = t / G, g = t - (t / G) * G;
+  const int per = (nchunks + G - 1) / G;
+  const int c0 = min(nchunks, g * per), c1 = min(nchunks, c0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c)
+      sum += chunk_counts[static_cast<int64_t>(c) * E + e];
+  int gincl = sum;
+  for (int m = 1; m < G; m <<= 1) {
+    const int o = __shfl_up(gincl, m, G);
+    if (g >= m) gincl += o;
+  }
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
+    int run = gincl - sum;
+    for (int c = c0; c < c1; ++c) {
       int32_t* p = chunk_counts + static_cast<int64_t>(c) * E + e;
       const int v = *p;
       *p = run;
       run += v;
     }
-    counts[e] = run;
+    if (g == G - 1) {
+      s_cnt[e] = gincl;
+      counts[e] = gincl;
+    }
   }
-  // block-wide exclusive scan of run over e
-  const int lane = e & 63, w = e >> 6;
-  int incl = run;
+  __syncthreads();
+  // block-wide exclusive scan over experts: thread t holds expert t
+  const int tot = t < E ? s_cnt[t] : 0;
+  const int lane = t & 63, w = t >> 6;
+  int incl = tot;
   for (int m = 1; m < 64; m <<= 1) {
     const int o = __shfl_up(incl, m, 64);
     if (lane >= m) incl += o;
   }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  if (e == 0) {
+  if (t == 0) {
     int acc = 0;
     for (int i = 0; i < 16; ++i) {
-      const int t = wsum[i];
+      const int v = wsum[i];
       wsum[i] = acc;
-      acc += t;
+      acc += v;
     }
   }
   __syncthreads();
-  const int excl = wsum[w] + incl - run;
-  if (e < E) offsets[e] = excl;
-  if (e == E - 1) offsets[E] = excl + run;
+  const int excl = wsum[w] + incl - tot;
+  if (t < E) offsets[t] = excl;
+  if (t == E - 1) offsets[E] = excl + tot;
 }
 
 // ---------------------------------------------------------------- rows
