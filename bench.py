@@ -231,7 +231,7 @@ def main():
     for n, v in stage_ms.items():
         e = {"ms": round(v, 4)}
         fl = stage_flops(n, T, d, f, E, k)
-        by = stage_bytes(n, T, d, f, E, k, planes=moe.ROW_PLANES, mx=mx,
+        by = stage_bytes(n, T, d, f, E, k, planes=moe.row_planes(f), mx=mx,
                          act4=wl.prec == "mxfp4")
         if fl:
             e["tflops"] = round(fl / (v / 1e3) / 1e12, 1)

@@ -192,7 +192,7 @@ moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,
  *   O[r]   = S[r] . w2[e]^T
  *   w_gu [E][2f][d], w2 [E][d][f]; ab_saved [T*k][2f] bf16 out,
  *   s_saved [T*k][f] bf16 out; out_perm [P][T*k][d] fp32 out, P =
- *   moe_row_planes(): O as P partial sums over consecutive ranges of the
+ *   moe_row_planes(f): O as P partial sums over consecutive ranges of the
  *   reduction (kept in fp32 and summed, in plane order, by moe_unpermute,
  *   so that each output is rounded once).
  * prec == MOE_MXFP8 ([P1] Challenge 2: blocks of 32 along each GEMM's
@@ -416,9 +416,10 @@ moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
                          int64_t T, int32_t k, int64_t d, int32_t y_fp32,
                          void* y, hipStream_t stream);
 
-/* Number of partial-sum planes in out_perm and dx_perm (fixed by the
- * library build). */
-int32_t moe_row_planes(void);
+/* Number of partial-sum planes P in out_perm and dx_perm for intermediate
+ * width f: 2 when f >= 4096 (fc2's reduction over f and fc1's data-gradient
+ * reduction over 2f are each cut in two), else 1; 0 when f < 1. */
+int32_t moe_row_planes(int64_t f);
 
 /*
  * moe_mxfp8_quantize -- MX block quantization, [P1] Challenge 2 (8-bit

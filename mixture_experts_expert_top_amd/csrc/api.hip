@@ -624,7 +624,7 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   return hip_status(e, "moe_grouped_mlp_bwd/dw_gu");
 }
 
-int32_t moe_row_planes(void) { return moe::kOutPlanes; }
+int32_t moe_row_planes(int64_t f) { return f >= 1 ? moe::out_planes(f) : 0; }
 
 moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
                          int32_t o_planes, const int32_t* pos, const float* w,

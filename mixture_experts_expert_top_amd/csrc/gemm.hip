@@ -1427,7 +1427,7 @@ hipError_t gemm_fc2_fwd(const bf16_t* s, const bf16_t* w2,
   P.Cf = o; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = f; P.f = f;
-  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ksplit = out_planes(f); P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgFwd, kSegM, true, true, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }
@@ -1459,7 +1459,7 @@ hipError_t gemm_fc1_dgrad(const bf16_t* dab, const bf16_t* w_gu,
   P.Cf = dxp; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = 2 * f; P.f = f;
-  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ksplit = out_planes(f); P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgDgrad, kSegM, true, false, kStoreF32>(P, segm_grid(Tk, E, P.ntn), st);
 }
@@ -1533,7 +1533,7 @@ hipError_t gemm_mx_fc2_fwd(const uint8_t* sq, const uint8_t* ss,
   P.Cf = o; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = f / 2; P.f = f;
-  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ksplit = out_planes(f); P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgMx, kSegM, true, true, kStoreF32, true>(
       P, segm_grid(Tk, E, P.ntn), st);
@@ -1585,7 +1585,7 @@ hipError_t gemm_mx_fc1_dgrad(const uint8_t* dabq, const uint8_t* dabs,
   P.Cf = dxp; P.ldc = d;
   P.offsets = offsets; P.E = E; P.Tk = Tk;
   P.N = d; P.K = f; P.f = f;
-  P.ksplit = kOutPlanes; P.plane = Tk * d;
+  P.ksplit = out_planes(f); P.plane = Tk * d;
   P.ntn = static_cast<int>((d + BN - 1) / BN);
   return launch<CfgMx, kSegM, true, true, kStoreF32, true>(
       P, segm_grid(Tk, E, P.ntn), st);

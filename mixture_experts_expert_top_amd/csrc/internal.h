@@ -15,7 +15,13 @@ constexpr int kPlanChunk = 512;   // slots per block of the counting pass
 // fp32 row outputs of the down projection and of the gate_up data
 // gradient are written as this many partial-sum planes [planes][T*k][d]
 // (split reduction); the combine adds them in plane order.
-constexpr int kOutPlanes = 2;
+// Partial-sum planes of the fp32 row outputs (fc2's O and fc1's data
+// gradient dXp).  Their reductions (over f and 2f) are cut in two when f is
+// at least kSplitF, which pays while each half still spans many k-steps
+// (measured at f = 14336).  With a narrower f one plane keeps the tiles
+// long and halves the combine's reads (measured at f = 1408).
+constexpr int64_t kSplitF = 4096;
+inline int out_planes(int64_t f) { return f >= kSplitF ? 2 : 1; }
 // MXFP8 along tokens: every expert segment is padded to a multiple of this
 // many rows so that each starts on a whole k-step of the MX GEMMs.
 constexpr int kMxPad = 128;

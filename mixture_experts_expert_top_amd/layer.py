@@ -93,7 +93,7 @@ class MoEPath:
         self.x_perm = z(Tk, d, dt=bf)
         self.ab = z(Tk, 2 * f, dt=bf)
         self.s = z(Tk, f, dt=bf)
-        self.o = z(moe.ROW_PLANES, Tk, d, dt=f32)
+        self.o = z(moe.row_planes(f), Tk, d, dt=f32)
         self.y = z(T, d, dt=f32 if y_fp32 else bf)
         ws_p = moe.moe_workspace_bytes(MOE_ENTRY_PERMUTE, prec, T, E, k, d, f)
         self.ws_permute = z(max(ws_p, 16), dt=torch.uint8)
@@ -105,7 +105,7 @@ class MoEPath:
         dev = self.x_perm.device
         bf = torch.bfloat16
         self.dout_perm = torch.empty(Tk, d, dtype=bf, device=dev)
-        self.dx_perm = torch.empty(moe.ROW_PLANES, Tk, d,
+        self.dx_perm = torch.empty(moe.row_planes(f), Tk, d,
                                    dtype=torch.float32, device=dev)
         self.dw_gu = torch.empty(E, 2 * f, d, dtype=bf, device=dev)
         self.dw2 = torch.empty(E, d, f, dtype=bf, device=dev)

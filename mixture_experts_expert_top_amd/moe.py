@@ -67,7 +67,7 @@ def _load():
                                       P, P, P, P, SZ, P]),
         "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
                                 P]),
-        "moe_row_planes": (I32, []),
+        "moe_row_planes": (I32, [I64]),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
         "moe_mxfp8_padded_rows": (I64, [I64, I32]),
         "moe_mxfp4_quantize": (I32, [P, I32, P, I64, I64, I32, P, I32, P, P,
@@ -143,7 +143,11 @@ def version():
     return lib.moe_version().decode()
 
 
-ROW_PLANES = int(lib.moe_row_planes())
+
+
+def row_planes(f):
+    """Partial-sum planes of out_perm / dx_perm for intermediate width f."""
+    return int(lib.moe_row_planes(int(f)))
 
 
 def moe_workspace_bytes(entry, prec, T, E, k, d, f):
@@ -275,7 +279,7 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(ab_saved, "ab_saved", torch.bfloat16, (Tk, 2 * f))
     _want(s_saved, "s_saved", torch.bfloat16, (Tk, f), allow_none=True)
-    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (row_planes(f), Tk, d))
     ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
@@ -308,7 +312,7 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
         _want(t, n, torch.bfloat16, shp)
     _want(s_saved, "s_saved", torch.bfloat16, (Tk, f), allow_none=True)
     ldt = _tok_out("s_tok", s_tok, s_tok_scales, f)
-    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(dx_perm, "dx_perm", torch.float32, (row_planes(f), Tk, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
     _want(pos, "pos", torch.int32)
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
@@ -418,7 +422,7 @@ def moe_down_fwd(s_saved, offsets, w2, out_perm, stream=None):
     _want(s_saved, "s_saved", torch.bfloat16)
     _want(w2, "w2", torch.bfloat16, (E, d, f))
     _want(offsets, "offsets", torch.int32, (E + 1,))
-    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (row_planes(f), Tk, d))
     _check("moe_down_fwd", lib.moe_down_fwd(
         _p(s_saved), _p(offsets), E, Tk, d, f, _p(w2), _p(out_perm),
         _stream(stream)))
@@ -447,7 +451,7 @@ def moe_gate_up_dgrad(dab, offsets, w_gu, dx_perm, stream=None):
     _want(dab, "dab", torch.bfloat16)
     _want(w_gu, "w_gu", torch.bfloat16, (E, 2 * f, d))
     _want(offsets, "offsets", torch.int32, (E + 1,))
-    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(dx_perm, "dx_perm", torch.float32, (row_planes(f), Tk, d))
     _check("moe_gate_up_dgrad", lib.moe_gate_up_dgrad(
         _p(dab), _p(offsets), E, Tk, d, f, _p(w_gu), _p(dx_perm),
         _stream(stream)))
@@ -513,7 +517,7 @@ def moe_mx_down_fwd(sq, ss, offsets, wq, ws, out_perm, stream=None):
     _want(wq, "wq", torch.uint8, (E, d, f))
     _want(ws, "ws", torch.uint8, (E, d, f // 32))
     _want(offsets, "offsets", torch.int32, (E + 1,))
-    _want(out_perm, "out_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(out_perm, "out_perm", torch.float32, (row_planes(f), Tk, d))
     _check("moe_mx_down_fwd", lib.moe_mx_down_fwd(
         _p(sq), _p(ss), _p(offsets), E, Tk, d, f, _p(wq), _p(ws),
         _p(out_perm), _stream(stream)))
@@ -554,7 +558,7 @@ def moe_mx_gate_up_dgrad(dabq, dabs, offsets, wgutq, wguts, dx_perm,
     _want(wgutq, "wgutq", torch.uint8, (d, E * two_f))
     _want(wguts, "wguts", torch.uint8, (d, E * two_f // 32))
     _want(offsets, "offsets", torch.int32)
-    _want(dx_perm, "dx_perm", torch.float32, (ROW_PLANES, Tk, d))
+    _want(dx_perm, "dx_perm", torch.float32, (row_planes(f), Tk, d))
     _check("moe_mx_gate_up_dgrad", lib.moe_mx_gate_up_dgrad(
         _p(dabq), _p(dabs), _p(offsets), E, Tk, d, f, _p(wgutq), _p(wguts),
         _p(dx_perm), _stream(stream)))

@@ -216,7 +216,12 @@ def test_unpermute_validation():
     # bf16 rows come as one plane; planes must be in [1, 8]
     assert L.moe_unpermute(A, 0, 2, A, None, 8, 2, 64, 0, A, None) == INVALID
     assert L.moe_unpermute(A, 1, 0, A, None, 8, 2, 64, 0, A, None) == INVALID
-    assert L.moe_row_planes() >= 1
+    # two fp32 partial planes for a wide intermediate width, one otherwise
+    assert L.moe_row_planes(14336) == 2
+    assert L.moe_row_planes(4096) == 2
+    assert L.moe_row_planes(1408) == 1
+    assert L.moe_row_planes(64) == 1
+    assert L.moe_row_planes(0) == 0
 
 
 def test_padded_rows():

@@ -304,7 +304,7 @@ def test_mx_down_stage(name, T, d, f, E, k, bias):
     w2 = I.make_tensor((E, d, f), seed=4, scale=0.1, device=dev)
     sq, ss, sd = _quant_rows_both(s)
     wq, ws, wd = _quant_rows_both(w2)
-    o = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    o = torch.empty(moe.row_planes(f), Tk, d, dtype=torch.float32, device=dev)
     moe.moe_mx_down_fwd(sq, ss, P["offsets_d"], wq, ws, o)
     torch.cuda.synchronize()
     o_ref = np.zeros((Tk, d))
@@ -379,7 +379,7 @@ def test_mx_gate_up_dgrad_stage(name, T, d, f, E, k, bias):
     w_gu = I.make_tensor((E, 2 * f, d), seed=9, scale=0.1, device=dev)
     dabq, dabs, dabd = _quant_rows_both(dab)
     wq, ws, wc = _quant_cols_both(w_gu)
-    dx = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    dx = torch.empty(moe.row_planes(f), Tk, d, dtype=torch.float32, device=dev)
     moe.moe_mx_gate_up_dgrad(dabq, dabs, P["offsets_d"], wq, ws, dx)
     torch.cuda.synchronize()
     dx_ref = np.zeros((Tk, d))
@@ -524,7 +524,7 @@ def test_mx_fused_token_codes_equal_requantized():
     bf = dict(dtype=torch.bfloat16, device=dev)
     ab = torch.empty(Tk, 2 * f, **bf)
     s = torch.empty(Tk, f, **bf)
-    o = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    o = torch.empty(moe.row_planes(f), Tk, d, dtype=torch.float32, device=dev)
     moe.moe_grouped_mlp_fwd(moe.MOE_MXFP8, path.xpq, path.xps, path.offsets,
                             path.wguq, path.wgus, path.w2q, path.w2s,
                             path.w_perm, ab, s, o, path.ws_fwd)

@@ -108,7 +108,7 @@ def test_down_stage(name, T, d, f, E, k, bias):
     Tk = T * k
     s = I.make_tensor((Tk, f), seed=3, device=dev)
     w2 = I.make_tensor((E, d, f), seed=4, scale=0.1, device=dev)
-    o = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    o = torch.empty(moe.row_planes(f), Tk, d, dtype=torch.float32, device=dev)
     moe.moe_down_fwd(s, P["offsets_d"], w2, o)
     torch.cuda.synchronize()
     o = o.double().sum(dim=0)        # a row is the sum of its planes
@@ -159,7 +159,7 @@ def test_gate_up_dgrad_stage(name, T, d, f, E, k, bias):
     Tk = T * k
     dab = I.make_tensor((Tk, 2 * f), seed=8, device=dev)
     w_gu = I.make_tensor((E, 2 * f, d), seed=9, scale=0.1, device=dev)
-    dxp = torch.empty(moe.ROW_PLANES, Tk, d, dtype=torch.float32, device=dev)
+    dxp = torch.empty(moe.row_planes(f), Tk, d, dtype=torch.float32, device=dev)
     moe.moe_gate_up_dgrad(dab, P["offsets_d"], w_gu, dxp)
     torch.cuda.synchronize()
     dxp = dxp.double().sum(dim=0)
