@@ -78,8 +78,9 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False, act4=False):
         "router_backward": (T * E * 4 * 3 + Tk * 12 + T * d * 2 + E * d * 2
                             + T * d * 4 + T * d * 2 + E * d * 4),
         "quant_x": T * d * (2 + xb),
-        "quant_weights": 3 * E * d * f * (2 + q),
-        "quant_bwd_operands": (Tk * d + 3 * E * d * f) * (2 + q),
+        # training: both MX layouts of each weight from one bf16 read
+        "quant_weights": 3 * E * d * f * (2 + 2 * q),
+        "quant_bwd_operands": Tk * d * (2 + q),
         # dO along tokens from bf16, and Xp from bf16 (MXFP8) or from the
         # MXFP4 payload (MXFP4 activations)
         "quant_tokens": Tk * d * (2 + q) + Tk * d * ((q4 + q4) if act4

@@ -450,6 +450,25 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                               int64_t rows_pad, hipStream_t stream);
 
 /*
+ * moe_mxfp8_quantize_weight -- both MX layouts of one weight matrix from a
+ * single read of it ([P1] Challenge 3: the weights are quantized for the
+ * forward GEMM, along their rows, and for the data-gradient GEMM, along
+ * their columns).  src [rows][cols] bf16; writes
+ *   row_codes [rows][cols], row_scales [rows][cols/32]: bit for bit
+ *     moe_mxfp8_quantize axis 0;
+ *   col_codes [cols][rows], col_scales [cols][rows/32]: bit for bit
+ *     moe_mxfp8_quantize axis 1 with one segment and rows_pad = rows.
+ * rows a multiple of 128, cols a multiple of 64.  Errors:
+ * MOE_ERR_INVALID_ARG for a missing pointer or bad sizes.  All pointers are
+ * device memory owned by the caller.  No workspace.
+ */
+moe_status moe_mxfp8_quantize_weight(const void* src, int64_t rows,
+                                     int64_t cols, uint8_t* row_codes,
+                                     uint8_t* row_scales, uint8_t* col_codes,
+                                     uint8_t* col_scales,
+                                     hipStream_t stream);
+
+/*
  * moe_mxfp4_quantize -- MXFP4 block quantization ([P5]: MXFP4 activations
  * and dispatch payloads under FP8 GEMMs; row-blocked FP4 turned into column
  * blocks with new scales).  E2M1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and

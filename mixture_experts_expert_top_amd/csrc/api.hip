@@ -915,6 +915,31 @@ moe_status moe_mxfp8_quantize(const void* src, int64_t rows, int64_t cols,
                     "moe_mxfp8_quantize/tokens");
 }
 
+moe_status moe_mxfp8_quantize_weight(const void* src, int64_t rows,
+                                     int64_t cols, uint8_t* row_codes,
+                                     uint8_t* row_scales, uint8_t* col_codes,
+                                     uint8_t* col_scales,
+                                     hipStream_t stream) {
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(row_codes);
+  REQUIRE_PTR(row_scales);
+  REQUIRE_PTR(col_codes);
+  REQUIRE_PTR(col_scales);
+  REQUIRE(rows >= 1 && cols >= 1, MOE_ERR_INVALID_ARG,
+          "rows and cols must be >= 1");
+  REQUIRE(rows % moe::kMxPad == 0 && cols % 64 == 0, MOE_ERR_INVALID_ARG,
+          "rows must be a multiple of %d and cols of 64 (got %lld, %lld)",
+          moe::kMxPad, static_cast<long long>(rows),
+          static_cast<long long>(cols));
+  REQUIRE(rows * cols * 2 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
+          "source larger than 4 GiB");
+  return hip_status(
+      moe::launch_mx_quant_both(static_cast<const bf16_t*>(src), rows, cols,
+                                row_codes, row_scales, col_codes, col_scales,
+                                stream),
+      "moe_mxfp8_quantize_weight");
+}
+
 moe_status moe_mxfp4_quantize(const void* src, int32_t src_fmt,
                               const uint8_t* src_scales, int64_t rows,
                               int64_t cols, int32_t axis,

@@ -67,6 +67,12 @@ hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
                                   const int32_t* seg, int nseg,
                                   uint8_t* codes, uint8_t* scales,
                                   int64_t rows_pad, hipStream_t s);
+// Both layouts of one bf16 matrix from a single read: quant_rows' codes and
+// the one-segment token-axis (transposed) codes; rows % 128 == 0.
+hipError_t launch_mx_quant_both(const bf16_t* src, int64_t rows,
+                                int64_t cols, uint8_t* row_codes,
+                                uint8_t* row_scales, uint8_t* col_codes,
+                                uint8_t* col_scales, hipStream_t s);
 
 // MXFP4 (E2M1 codes two a byte, E8M0 scale per 32): rows of a bf16 tensor,
 // and blocks along the rows (token axis, 128-padded segments, transposed)

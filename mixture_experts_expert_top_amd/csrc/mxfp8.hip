@@ -66,16 +66,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 //      of one column and writes the 32 codes to an LDS staging line;
 //   3. every column's 128 codes leave as one 128-byte line (8 lanes, 16
 //      bytes each) and its 4 scale bytes as one 4-byte word.
+// With kRows (one segment, no gather: a weight quantized for both of its
+// GEMMs from one read) thread (row t/2, half t%2) also quantizes its 32
+// columns of the tile along the row, as quant_rows_kernel does, into
+// row_codes [rows][cols] and row_scales [rows][cols/32].
 constexpr int kTokRows = 128;
 constexpr int kTokCols = 64;
 constexpr int kTokLd = kTokCols + 8;       // bf16 row stride of the tile
 constexpr int kTokTiles = 4;               // column runs per workgroup
 
+template <bool kRows>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ gather,
     int64_t rows, int64_t cols, const int32_t* __restrict__ seg, int nseg,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    int64_t rows_pad) {
+    int64_t rows_pad, uint8_t* __restrict__ row_codes,
+    uint8_t* __restrict__ row_scales) {
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) bf16_t tile[kTokRows * kTokLd];
   __shared__ __attribute__((aligned(16))) uint8_t out[kTokCols][kTokRows];
@@ -118,6 +124,41 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
       }
     }
     __syncthreads();
+    if constexpr (kRows) {
+      // along the row: 32 columns of row t/2 (c0 is a multiple of 64)
+      const int rr = t >> 1, half = t & 1;
+      const int64_t r = r0 + rr;
+      if (r < r_end && c0 + 32 * half < cols) {
+        float v[kMxBlock];
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x4 w = *reinterpret_cast<const i32x4*>(
+              tile + rr * kTokLd + 32 * half + 8 * q);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[q * 8 + 2 * c] = bf_lo(static_cast<uint32_t>(w[c]));
+            v[q * 8 + 2 * c + 1] = bf_hi(static_cast<uint32_t>(w[c]));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kMxBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const int e = mx_scale_exp(amax);
+        const float inv = mx_inv_scale(e);
+        i32x4 w[2];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q >> 2][q & 3] = static_cast<int>(
+              e4m3_pack4(v[q * 4] * inv, v[q * 4 + 1] * inv,
+                         v[q * 4 + 2] * inv, v[q * 4 + 3] * inv));
+        const int64_t cb = c0 + 32 * half;
+        i32x4* o = reinterpret_cast<i32x4*>(row_codes + r * cols + cb);
+        o[0] = w[0];
+        o[1] = w[1];
+        row_scales[r * (cols / kMxBlock) + cb / kMxBlock] =
+            static_cast<uint8_t>(e + 127);
+      }
+    }
     // 2. quantize one 32-row block of one column
     {
       const int c = t & (kTokCols - 1);
@@ -180,8 +221,22 @@ hipError_t launch_mx_quant_tokens(const bf16_t* src, const int32_t* gather,
   dim3 grid(static_cast<unsigned>(rows_pad / kTokRows),
             static_cast<unsigned>((cols + kTokCols * kTokTiles - 1) /
                                   (kTokCols * kTokTiles)));
-  hipLaunchKernelGGL(quant_tokens_kernel, grid, dim3(256), 0, s, src, gather,
-                     rows, cols, seg, nseg, codes, scales, rows_pad);
+  hipLaunchKernelGGL(quant_tokens_kernel<false>, grid, dim3(256), 0, s, src,
+                     gather, rows, cols, seg, nseg, codes, scales, rows_pad,
+                     nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_both(const bf16_t* src, int64_t rows,
+                                int64_t cols, uint8_t* row_codes,
+                                uint8_t* row_scales, uint8_t* col_codes,
+                                uint8_t* col_scales, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(rows / kTokRows),
+            static_cast<unsigned>((cols + kTokCols * kTokTiles - 1) /
+                                  (kTokCols * kTokTiles)));
+  hipLaunchKernelGGL(quant_tokens_kernel<true>, grid, dim3(256), 0, s, src,
+                     nullptr, rows, cols, nullptr, 1, col_codes, col_scales,
+                     rows, row_codes, row_scales);
   return hipGetLastError();
 }
 

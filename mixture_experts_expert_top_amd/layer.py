@@ -219,9 +219,14 @@ class MoEPathMX(MoEPath):
     """The layer with MXFP8 GEMM operands (see the module docstring)."""
 
     def __init__(self, T, d, f, E, k, renorm=True, device="cuda",
-                 y_fp32=False, aux_coef=0.01, act_fp4=False):
+                 y_fp32=False, aux_coef=0.01, act_fp4=False, training=True):
         super().__init__(T, d, f, E, k, renorm=renorm, prec=MOE_BF16,
                          device=device, y_fp32=y_fp32, aux_coef=aux_coef)
+        # training: the forward quantizes each weight for both of its GEMMs
+        # from one read (moe_mxfp8_quantize_weight) and the backward uses
+        # those column-wise codes; otherwise only the forward's codes are
+        # made and the backward quantizes the weights it is given
+        self.training = training
         self.act_fp4 = act_fp4
         self.prec = MOE_MXFP4 if act_fp4 else MOE_MXFP8
         Tk = T * k
@@ -240,6 +245,9 @@ class MoEPathMX(MoEPath):
         self.tk_pad = tp
         self.st, self.sts = z(f, tp), z(f, tp // 32)
         self.s = None
+        if training:
+            self.w2tq, self.w2ts = z(f, E * d), z(f, E * d // 32)
+            self.wgutq, self.wguts = z(d, E * 2 * f), z(d, E * 2 * f // 32)
         ws_f = moe.moe_workspace_bytes(MOE_ENTRY_MLP_FWD, MOE_MXFP8, T, E, k,
                                        d, f)
         self.ws_fwd = z(max(ws_f, 16))
@@ -253,8 +261,9 @@ class MoEPathMX(MoEPath):
         z = lambda *s: torch.empty(*s, dtype=u8, device=dev)  # noqa: E731
         tp = self.tk_pad
         self.doq, self.dos = z(Tk, d), z(Tk, d // 32)
-        self.w2tq, self.w2ts = z(f, E * d), z(f, E * d // 32)
-        self.wgutq, self.wguts = z(d, E * 2 * f), z(d, E * 2 * f // 32)
+        if not self.training:
+            self.w2tq, self.w2ts = z(f, E * d), z(f, E * d // 32)
+            self.wgutq, self.wguts = z(d, E * 2 * f), z(d, E * 2 * f // 32)
         self.dab = None
         self.dabq, self.dabs = z(Tk, 2 * f), z(Tk, 2 * f // 32)
         self.dot, self.dots = z(d, tp), z(d, tp // 32)
@@ -266,16 +275,26 @@ class MoEPathMX(MoEPath):
         self.ws_bwd = z(max(ws_b, 16))
 
     def quantize_weights(self, w_gu, w2, timers=None):
-        """Row-wise MX codes of the weights for the forward GEMMs (done once
-        per optimizer step)."""
+        """MX codes of the weights (once per optimizer step): along their
+        rows for the forward GEMMs and, when training, along their columns
+        for the data-gradient GEMMs, from the same read."""
         E, d, f = self.E, self.d, self.f
         with _around(timers, "quant_weights"):
-            moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 0, None,
-                                   self.wguq.view(E * 2 * f, d),
-                                   self.wgus.view(E * 2 * f, d // 32))
-            moe.moe_mxfp8_quantize(w2.view(E * d, f), 0, None,
-                                   self.w2q.view(E * d, f),
-                                   self.w2s.view(E * d, f // 32))
+            if self.training:
+                moe.moe_mxfp8_quantize_weight(
+                    w_gu.view(E * 2 * f, d), self.wguq.view(E * 2 * f, d),
+                    self.wgus.view(E * 2 * f, d // 32), self.wgutq,
+                    self.wguts)
+                moe.moe_mxfp8_quantize_weight(
+                    w2.view(E * d, f), self.w2q.view(E * d, f),
+                    self.w2s.view(E * d, f // 32), self.w2tq, self.w2ts)
+            else:
+                moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 0, None,
+                                       self.wguq.view(E * 2 * f, d),
+                                       self.wgus.view(E * 2 * f, d // 32))
+                moe.moe_mxfp8_quantize(w2.view(E * d, f), 0, None,
+                                       self.w2q.view(E * d, f),
+                                       self.w2s.view(E * d, f // 32))
 
     def forward(self, x, w_gu, w2, w_g=None, bias=None, logits=None,
                 timers=None):
@@ -335,15 +354,18 @@ class MoEPathMX(MoEPath):
                                     s_tok_scales=self.sts,
                                     x_perm_scales=xps)
         else:
-            # the same kernels in the same order as moe_grouped_mlp_bwd
+            # the kernels of moe_grouped_mlp_bwd in its order, except that
+            # when training the column-wise weight codes come from the
+            # forward's quantize_weights
             tp = self.tk_pad
             with timers.around("quant_bwd_operands"):
                 moe.moe_mxfp8_quantize(self.dout_perm, 0, None, self.doq,
                                        self.dos)
-                moe.moe_mxfp8_quantize(w2.view(E * d, f), 1, None, self.w2tq,
-                                       self.w2ts, E * d)
-                moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 1, None,
-                                       self.wgutq, self.wguts, E * 2 * f)
+                if not self.training:
+                    moe.moe_mxfp8_quantize(w2.view(E * d, f), 1, None,
+                                           self.w2tq, self.w2ts, E * d)
+                    moe.moe_mxfp8_quantize(w_gu.view(E * 2 * f, d), 1, None,
+                                           self.wgutq, self.wguts, E * 2 * f)
             with timers.around("down_swiglu_bwd"):
                 moe.moe_mx_down_swiglu_bwd(
                     self.doq, self.dos, self.offsets, self.w2tq, self.w2ts,

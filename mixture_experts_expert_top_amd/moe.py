@@ -27,6 +27,7 @@ EXPORTED = [
     "moe_status_str", "moe_last_error", "moe_version", "moe_router_logits",
     "moe_route", "moe_permute", "moe_permute_rows", "moe_grouped_mlp_fwd",
     "moe_grouped_mlp_bwd", "moe_unpermute", "moe_mxfp8_quantize",
+    "moe_mxfp8_quantize_weight",
     "moe_mxfp8_padded_rows", "moe_workspace_bytes", "moe_dp_tiles",
     "moe_gate_up_swiglu_fwd", "moe_down_fwd", "moe_down_swiglu_bwd",
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
@@ -69,6 +70,7 @@ def _load():
                                 P]),
         "moe_row_planes": (I32, [I64]),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
+        "moe_mxfp8_quantize_weight": (I32, [P, I64, I64, P, P, P, P, P]),
         "moe_mxfp8_padded_rows": (I64, [I64, I32]),
         "moe_mxfp4_quantize": (I32, [P, I32, P, I64, I64, I32, P, I32, P, P,
                                      I64, P]),
@@ -363,6 +365,23 @@ def moe_mxfp8_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,
     _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(
         _p(src), rows, cols, axis, _p(seg_offsets), nseg, _p(codes),
         _p(scales), rows_pad, _stream(stream)))
+
+
+def moe_mxfp8_quantize_weight(src, row_codes, row_scales, col_codes,
+                              col_scales, stream=None):
+    """Both MX layouts of a bf16 [rows, cols] weight from one read:
+    row_codes [rows, cols] / row_scales [rows, cols/32] (axis 0) and
+    col_codes [cols, rows] / col_scales [cols, rows/32] (axis 1, one
+    segment)."""
+    rows, cols = src.shape
+    _want(src, "src", torch.bfloat16)
+    _want(row_codes, "row_codes", torch.uint8, (rows, cols))
+    _want(row_scales, "row_scales", torch.uint8, (rows, cols // 32))
+    _want(col_codes, "col_codes", torch.uint8, (cols, rows))
+    _want(col_scales, "col_scales", torch.uint8, (cols, rows // 32))
+    _check("moe_mxfp8_quantize_weight", lib.moe_mxfp8_quantize_weight(
+        _p(src), rows, cols, _p(row_codes), _p(row_scales), _p(col_codes),
+        _p(col_scales), _stream(stream)))
 
 
 def moe_mxfp4_quantize(src, axis, seg_offsets, codes, scales, rows_pad=0,

@@ -251,6 +251,16 @@ def test_quantize_validation():
     assert q(None, 8, 64, 0, None, 1, A, A, 0, None) == INVALID
 
 
+def test_quantize_weight_validation():
+    q = L.moe_mxfp8_quantize_weight
+    assert q(A, 200, 128, A, A, A, A, None) == INVALID   # rows % 128
+    assert q(A, 256, 96, A, A, A, A, None) == INVALID    # cols % 64
+    assert q(A, 0, 128, A, A, A, A, None) == INVALID
+    assert q(None, 256, 128, A, A, A, A, None) == INVALID
+    assert q(A, 256, 128, A, A, None, A, None) == INVALID
+    assert b"col_codes" in L.moe_last_error()
+
+
 def _router_bwd(T=300, E=8, k=2, d=64, x=A, w_g=A, dw_g=A, db=A, dx_out=A,
                 counts=A, aux=A, ws=A, ws_bytes=None, logits=A):
     if ws_bytes is None:

@@ -132,3 +132,37 @@ def test_quantize_tokens_segments(offs):
     exp_codes, exp_scales = _expected_tokens(a64, offs, rows_pad)
     np.testing.assert_array_equal(scales.cpu().numpy(), exp_scales)
     np.testing.assert_array_equal(codes.cpu().numpy(), exp_codes)
+
+
+@gpu
+@pytest.mark.parametrize("R,C", [(128, 64), (256, 320), (384, 1024)])
+def test_quantize_weight_both_layouts(R, C):
+    """moe_mxfp8_quantize_weight: the row-wise codes equal the oracle's row
+    blocks and the column-wise (transposed) codes its one-segment blocks
+    along the rows, and both equal the two separate moe_mxfp8_quantize
+    calls bit for bit."""
+    rng = np.random.default_rng(R + C)
+    a = (rng.standard_normal((R, C)) *
+         2.0 ** rng.integers(-30, 30, (R, 1))).astype(np.float32)
+    a[:, ::13] *= 500.0
+    a[5] = 0.0                              # an all-zero row block
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    a64 = _as_f64(bits)
+    src = _to_gpu_bf16(bits.reshape(-1)).reshape(R, C)
+    u8 = dict(dtype=torch.uint8, device=_dev())
+    rc, rs = torch.full((R, C), 0x5A, **u8), torch.full((R, C // 32), 0x5A, **u8)
+    cc, cs = torch.full((C, R), 0x5A, **u8), torch.full((C, R // 32), 0x5A, **u8)
+    moe.moe_mxfp8_quantize_weight(src, rc, rs, cc, cs)
+    sep_rc, sep_rs = torch.empty_like(rc), torch.empty_like(rs)
+    sep_cc, sep_cs = torch.empty_like(cc), torch.empty_like(cs)
+    moe.moe_mxfp8_quantize(src, 0, None, sep_rc, sep_rs)
+    moe.moe_mxfp8_quantize(src, 1, None, sep_cc, sep_cs, R)
+    torch.cuda.synchronize()
+    codes_ref, scales_ref = M.quantize_rows(a64)
+    np.testing.assert_array_equal(rc.cpu().numpy(), codes_ref)
+    np.testing.assert_array_equal(rs.cpu().numpy(), scales_ref)
+    exp_codes, exp_scales = _expected_tokens(a64, [0, R], R)
+    np.testing.assert_array_equal(cc.cpu().numpy(), exp_codes)
+    np.testing.assert_array_equal(cs.cpu().numpy(), exp_scales)
+    for got, sep in ((rc, sep_rc), (rs, sep_rs), (cc, sep_cc), (cs, sep_cs)):
+        assert torch.equal(got, sep)
