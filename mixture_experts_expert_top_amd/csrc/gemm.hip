@@ -187,6 +187,15 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo,
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Orders a wave's LDS writes before its own later LDS reads of other
+// lanes' data.  The epilogue needs no more: each wave stages through its
+// own LDS region.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Workgroup id -> logical tile id so that the blocks one XCD receives
 // (hardware hands out ids round-robin over the 8 XCDs) form a contiguous
 // range of tiles that share operands in that XCD's L2.
@@ -1086,7 +1095,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const int r = ii * 32 + (v >> 2) * 8 + fk * 4 + (v & 3);
           stage[r * LD + j * 32 + fr] = acc[h * (kEpiRows / 32) + ii][j][v];
         }
-    __syncthreads();
+    wave_lds_sync();
     if (EPI == kStore || EPI == kStoreF32) {
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
@@ -1175,7 +1184,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       if constexpr (kTokEpi) {
         if (tok) {
           // lane = (32-row block cb of this pass, S column cc of the wave)
-          __syncthreads();
+          wave_lds_sync();
           const int cb = lane >> 5, cc = lane & 31;
           float v[kMxBlock];
           float amax = 0.0f;
@@ -1284,7 +1293,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         if (tok) {
           // lane = dS column of the wave; both 32-row blocks of the pass,
           // gate (low half) and up (high half) of the packed pairs
-          __syncthreads();
+          wave_lds_sync();
           const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
           const int col = n0 + wn * TN + lane;
 #pragma unroll
@@ -1326,7 +1335,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
   if constexpr (kTokEpi) {
     // one scale dword (the wave's four 32-row blocks) per column
@@ -1351,7 +1360,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     }
   }
   if (EPI == kDSwiglu) {
-    // the tile's column groups, added in order (wn = 0, 1, ...)
+    // the tile's column groups, added in order (wn = 0, 1, ...): the one
+    // read of other waves' LDS in the epilogue
+    __syncthreads();
     for (int lr = tid; lr < BM; lr += NT) {
       const int row = m0 + lr;
       if (row < Mvalid) {

@@ -100,7 +100,10 @@ def test_route_bitexact(T, E, k, renorm, kind):
 @pytest.mark.parametrize("T,E,k,d,kind", [
     (64, 4, 2, 32, "randn"), (8192, 8, 2, 4096, "randn"),
     (16384, 64, 8, 2048, "bias"), (3000, 16, 4, 136, "tied"),
-    (1, 4, 4, 64, "randn"), (513, 1024, 32, 8, "randn")])
+    (1, 4, 4, 64, "randn"), (513, 1024, 32, 8, "randn"),
+    # the plan's column scan splits each expert over 64 / 16 / 4 / 2 / 1
+    # lanes by E; E = 130 and 300 take the 4- and 2-lane groups
+    (700, 130, 7, 64, "randn"), (400, 300, 9, 32, "randn")])
 def test_permute_bitexact(T, E, k, d, kind):
     dev = _dev()
     L = _logits(kind, T, E, seed=7 * T + E)
