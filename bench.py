@@ -41,6 +41,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc",
                            "gemm.hip")
 
+# the five named configurations and the workloads that implement them
+CONFIGS = {"C1": "tiny_fwd", "C2": "mixtral_fwd", "C3": "mixtral",
+           "C4": "finegrain", "C5": "mxfp8"}
+
 GEMM_STAGES = ("gate_up_swiglu_fwd", "down_fwd", "down_swiglu_bwd",
                "wgrad_down", "gate_up_dgrad", "wgrad_gate_up")
 
@@ -126,10 +130,13 @@ def cpu_baseline(inp, wl, n_tokens):
     workload (router scores, routing, experts, combine and backward)."""
     import numpy as np
     from oracle import moe_ref
+    blas = "blas"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
+        if infos:
+            blas = infos[0].get("internal_api", "blas")
     except Exception:  # pragma: no cover - informational only
         threads = len(os.sched_getaffinity(0))
     h = lambda t: t.double().cpu().numpy()  # noqa: E731
@@ -153,7 +160,8 @@ def cpu_baseline(inp, wl, n_tokens):
             "kind": "oracle",
             "sample": (f"first {n_tokens} tokens of the {wl.name} workload, "
                        f"{'fwd+bwd' if wl.backward else 'fwd'}, float64 numpy "
-                       f"per-expert loop with the full weights ({dt:.1f} s)")}
+                       f"per-expert loop with the full weights ({dt:.1f} s, "
+                       f"{blas}, {threads} threads)")}
 
 
 def main():
@@ -162,13 +170,19 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral",
-                    help="mixtral (default), mxfp8, mxfp4, finegrain, tiny")
+                    help="mixtral (default), mixtral_fwd, mxfp8, mxfp4, "
+                         "finegrain, tiny, tiny_fwd")
+    ap.add_argument("--config", choices=sorted(CONFIGS),
+                    help="C1..C5: the tiny, Mixtral forward, Mixtral "
+                         "fwd+bwd, fine-grained and MXFP8 workloads")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
                          "the HBM traffic counters")
     args = ap.parse_args()
+    if args.config:
+        args.workload = CONFIGS[args.config]
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
               "supported (this build has no multi-GPU path).", file=sys.stderr)

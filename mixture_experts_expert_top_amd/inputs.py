@@ -51,6 +51,7 @@ class Workload:
 
 WORKLOADS = {
     "tiny": Workload("tiny", 64, 32, 64, 4, 2, backward=True),
+    "tiny_fwd": Workload("tiny_fwd", 64, 32, 64, 4, 2, backward=False),
     "mixtral_fwd": Workload("mixtral_fwd", 8192, 4096, 14336, 8, 2,
                             backward=False),
     "mixtral": Workload("mixtral", 8192, 4096, 14336, 8, 2),
