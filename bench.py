@@ -177,6 +177,9 @@ def main():
                          "fwd+bwd, fine-grained and MXFP8 workloads")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as a HIP graph and "
+                         "replayed (reported under 'graph')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
                          "the HBM traffic counters")
@@ -195,7 +198,7 @@ def main():
     import torch
     from mixture_experts_expert_top_amd import inputs, moe
     from mixture_experts_expert_top_amd.layer import (MoEPath, MoEPathMX,
-                                                      StageTimers)
+                                                      StageTimers, StepGraph)
 
     wl = inputs.WORKLOADS[args.workload]
     mx = wl.prec in ("mxfp8", "mxfp4")
@@ -288,6 +291,21 @@ def main():
         "stages": stages,
         "wall_s": round(wall, 3),
     }
+    if args.graph:
+        g = StepGraph(step)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.Event(enable_timing=True)
+        ge = torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(args.steps):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        gms = gs.elapsed_time(ge) / args.steps
+        out["graph"] = {"ms_per_step": round(gms, 4),
+                        "tokens_per_s": round(T / (gms / 1e3), 1)}
     if not args.no_cpu_baseline and not mx:
         out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_tokens, T))
     print(json.dumps(out), flush=True)

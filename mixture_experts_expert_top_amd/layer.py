@@ -215,6 +215,32 @@ class MoEPath:
                 self.dx_f32, self.dx, self.aux_loss, self.ws_router)
 
 
+class StepGraph:
+    """A step (e.g. one forward and backward of a path) captured once as a
+    HIP graph and replayed.  Every buffer and workspace belongs to the path
+    and no entry point allocates, clears with a memset, synchronizes or
+    reads back to the host, so the captured launches are the whole step.
+    The step runs eagerly twice first: once to allocate what the path
+    allocates lazily, once on the capture's side stream."""
+
+    def __init__(self, step):
+        step()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            step()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+
+
 class MoEPathMX(MoEPath):
     """The layer with MXFP8 GEMM operands (see the module docstring)."""
 
