@@ -668,18 +668,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   auto atile = [&](int st) { return smem + st * kTileElems; };
   auto btile = [&](int st) { return smem + (2 + st) * kTileElems; };
 
-  // bf16 fragments of k-slice kk (16 wide) of one LDS stage: the first NB
-  // 32-row A blocks of the wave (the others hold no rows of the expert and
-  // are neither read nor multiplied) and, when NB > 0, all B blocks.
-  auto read_frags = [&](auto nb_tag, int st, int kk, bf16x8_v* af,
-                        bf16x8_v* bf) {
-    constexpr int NB = decltype(nb_tag)::value;
-    if constexpr (NB == 0) return;
+  // bf16 fragments of k-slice kk (16 wide) of one LDS stage.
+  auto read_frags = [&](int st, int kk, bf16x8_v* af, bf16x8_v* bf) {
     const bf16_t* sa = atile(st);
     const bf16_t* sb = btile(st);
     const int chunk = kk * 2 + fk;
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < BI; ++i)
       af[i] = __builtin_bit_cast(
           bf16x8_v, *reinterpret_cast<const i32x4*>(
                         sa + lds_off(wm * TM + i * 32 + fr, chunk)));
@@ -689,10 +684,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           bf16x8_v, *reinterpret_cast<const i32x4*>(
                         sb + lds_off(wn * TN + j * 32 + fr, chunk)));
   };
-  auto mfmas = [&](auto nb_tag, const bf16x8_v* af, const bf16x8_v* bf) {
-    constexpr int NB = decltype(nb_tag)::value;
+  auto mfmas = [&](const bf16x8_v* af, const bf16x8_v* bf) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
       for (int j = 0; j < BJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j],
@@ -753,12 +747,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   //     barrier follows the last MFMAs (measured faster for these).
   // Loads past K return zeros and the one stray store of the last
   // iteration lands in the buffer no one reads any more.
-  auto kloop = [&](auto&& gload, auto&& lstore, auto indep_halves,
-                   auto nb_tag) {
+  auto kloop = [&](auto&& gload, auto&& lstore, auto indep_halves) {
     constexpr bool kIndep = decltype(indep_halves)::value;
-    constexpr int NB = decltype(nb_tag)::value;    // live A blocks
-    constexpr int kMf = NB * BJ;                   // MFMAs per k-slice
-    constexpr int kRd = NB > 0 ? NB + BJ : 0;      // fragment reads per slice
+    constexpr int kMf = BI * BJ;                   // MFMAs per k-slice
+    constexpr int kRd = BI + BJ;                   // fragment reads per slice
     constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per half stage
     bf16x8_v a0[BI], b0[BJ], a1[BI], b1[BJ];
     if (nk > 0) {
@@ -769,17 +761,17 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       gload(kbeg + BK, 0);
       gload(kbeg + BK, 1);
       __syncthreads();
-      read_frags(nb_tag, 0, 0, a0, b0);
+      read_frags(0, 0, a0, b0);
     }
     for (int kt = 0; kt < nk; ++kt) {
       const int cs = kt & 1, ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
       // slices 0 and 1: MFMAs; reads of the next slice; half p of stage
       // kt+1 to LDS (and, K-contiguous, half p of stage kt+2 loaded)
-      read_frags(nb_tag, cs, 1, a1, b1);
+      read_frags(cs, 1, a1, b1);
       lstore(ns, 0);
       if constexpr (kIndep) gload(k2, 0);
-      mfmas(nb_tag, a0, b0);
+      mfmas(a0, b0);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
@@ -788,10 +780,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         if (kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(nb_tag, cs, 2, a0, b0);
+      read_frags(cs, 2, a0, b0);
       lstore(ns, 1);
       if constexpr (kIndep) gload(k2, 1);
-      mfmas(nb_tag, a1, b1);
+      mfmas(a1, b1);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
@@ -801,9 +793,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
       // slice 2: MFMAs on (a0,b0); reads of slice 3
-      read_frags(nb_tag, cs, 3, a1, b1);
+      read_frags(cs, 3, a1, b1);
       if constexpr (!kIndep) gload(k2, 0);
-      mfmas(nb_tag, a0, b0);
+      mfmas(a0, b0);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
@@ -815,8 +807,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         // slice 3 after the barrier: stage kt+1 is complete, its first
         // fragments are read while slice 3's MFMAs run from registers
         __syncthreads();
-        read_frags(nb_tag, ns, 0, a0, b0);
-        mfmas(nb_tag, a1, b1);
+        read_frags(ns, 0, a0, b0);
+        mfmas(a1, b1);
   #pragma unroll
         for (int i = 0; i < kMf; ++i) {
           sched_group(kSgMfma, 1);
@@ -826,7 +818,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       } else {
         // slice 3: MFMAs on (a1,b1); second half of stage kt+2
         gload(k2, 1);
-        mfmas(nb_tag, a1, b1);
+        mfmas(a1, b1);
   #pragma unroll
         for (int i = 0; i < kMf; ++i) {
           sched_group(kSgMfma, 1);
@@ -834,7 +826,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        read_frags(nb_tag, ns, 0, a0, b0);
+        read_frags(ns, 0, a0, b0);
       }
     }
   };
@@ -1028,25 +1020,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     } else {
       kloop_mx(std::false_type{});
     }
+  } else if constexpr (C::kSplitLoad && AKC != BKC) {
+    if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<AKC>{});
+    else kloop(gload_b, lstore_b, std::bool_constant<BKC>{});
   } else {
-    // Row-segmented tiles: the 32-row blocks of a wave that lie past the
-    // expert's rows (the ragged tail of its last m-tile) take no MFMAs.
-    // The loop copy is picked per wave: all BI blocks, the first half, or
-    // none (loads, stores and barriers only).
-    const int live = (MODE == kSegM)
-        ? __builtin_amdgcn_readfirstlane(Mvalid - (m0 + wm * TM))
-        : TM;
-    auto run = [&](auto nb_tag) {
-      if constexpr (C::kSplitLoad && AKC != BKC) {
-        if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<AKC>{}, nb_tag);
-        else kloop(gload_b, lstore_b, std::bool_constant<BKC>{}, nb_tag);
-      } else {
-        kloop(gload, lstore, std::bool_constant<AKC && BKC>{}, nb_tag);
-      }
-    };
-    if (MODE != kSegM || live > TM / 2) run(std::integral_constant<int, BI>{});
-    else if (live > 0) run(std::integral_constant<int, BI / 2>{});
-    else run(std::integral_constant<int, 0>{});
+    kloop(gload, lstore, std::bool_constant<AKC && BKC>{});
   }
 
   // ---------------------------------------------------------- epilogue
