@@ -38,6 +38,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # WRITE_SIZE per dispatch, with the same counters' reading of a plain 1 GiB
 # device copy); valid only for the kernel source it was taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Measured whole-chip MFMA ceiling with random operands (power-limited
+# clock), written from the output of `bench.py --mfma-ceiling`.
+CEILING_FILE = os.path.join(ROOT, "profiles", "mfma_ceiling.json")
+PROBE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "probe",
+                     "mfma_ceiling")
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc",
                            "gemm.hip")
 
@@ -112,6 +117,38 @@ def measured_traffic(workload, stage):
     return round(fetch + write)
 
 
+def measured_ceiling(prec):
+    """TFLOP/s that MFMAs alone sustain on the whole chip with random
+    operands of the path's GEMM type; None when not recorded."""
+    key = "bf16" if prec == "bf16" else "fp8"
+    try:
+        with open(CEILING_FILE) as fh:
+            rec = json.load(fh)
+        return float(rec[key]["random"]["tflops"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def mfma_ceiling():
+    """Runs the ceiling probe (built by build()) and prints its cases as one
+    JSON line: {dtype: {operands: {ms, tflops, ghz}}}."""
+    import subprocess
+    if not os.path.exists(PROBE):
+        raise SystemExit(f"{PROBE} is missing: run __graft_entry__.build()")
+    res = subprocess.run([PROBE], capture_output=True, text=True, timeout=120)
+    if res.returncode != 0:
+        raise SystemExit(f"mfma_ceiling failed ({res.returncode}):\n"
+                         f"{res.stdout}\n{res.stderr}")
+    out = {}
+    for line in res.stdout.split("\n"):
+        f = line.split()
+        if len(f) == 6:
+            out.setdefault(f[0], {})[f[1]] = {
+                "iters": int(f[2]), "ms": float(f[3]), "tflops": float(f[4]),
+                "ghz": float(f[5])}
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB, five times: the reference that scales
     the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -180,6 +217,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured as a HIP graph and "
                          "replayed (reported under 'graph')")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the MFMA ceiling probe (constant and "
+                         "random operands, bf16 and fp8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
                          "the HBM traffic counters")
@@ -194,6 +234,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.mfma_ceiling:
+        mfma_ceiling()
+        return
 
     import torch
     from mixture_experts_expert_top_amd import inputs, moe
@@ -203,6 +246,7 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     mx = wl.prec in ("mxfp8", "mxfp4")
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    ceiling = measured_ceiling(wl.prec)
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
     dev = torch.device("cuda:0")
     inp = inputs.make_inputs(wl, seed=0, device=dev)
@@ -287,6 +331,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(dom_tflops / peak, 4),
             "traffic": measured_traffic(wl.name, dom),
+            "ceiling_random_operands": ceiling,
+            "frac_of_ceiling": (round(dom_tflops / ceiling, 4)
+                                if ceiling else None),
         },
         "stages": stages,
         "wall_s": round(wall, 3),

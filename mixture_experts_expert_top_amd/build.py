@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+# the roofline's ceiling probe: a standalone program, not part of the library
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_ceiling.hip")
+PROBE = os.path.join(PKG, "probe", "mfma_ceiling")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -58,7 +61,18 @@ def build(verbose=False):
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe():
+    tmp = PROBE + ".tmp"
+    cmd = [HIPCC, *FLAGS, PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":
