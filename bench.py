@@ -43,8 +43,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CEILING_FILE = os.path.join(ROOT, "profiles", "mfma_ceiling.json")
 PROBE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "probe",
                      "mfma_ceiling")
-GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc",
-                           "gemm.hip")
+# the grouped GEMM kernel's sources: the recorded traffic is valid only
+# for the sources it was measured on
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc", n)
+                for n in ("gemm.hip", "common.cuh", "internal.h", "mx.cuh")]
+
+
+def gemm_source_sha256():
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 # the five named configurations and the workloads that implement them
 CONFIGS = {"C1": "tiny_fwd", "C2": "mixtral_fwd", "C3": "mixtral",
@@ -104,8 +114,7 @@ def measured_traffic(workload, stage):
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
-        with open(GEMM_SOURCE, "rb") as fh:
-            sha = hashlib.sha256(fh.read()).hexdigest()
+        sha = gemm_source_sha256()
     except (OSError, ValueError):
         return None
     st = rec.get("stages", {}).get(stage)
