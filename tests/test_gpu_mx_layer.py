@@ -435,6 +435,7 @@ LAYER_SHAPES = [
     ("ragged", 300, 256, 384, 5, 2, False, 0.01),
     ("skew", 600, 128, 256, 16, 4, True, 0.0),
     ("outliers", 400, 256, 256, 8, 2, False, 0.05),
+    ("max_experts", 96, 128, 128, 1024, 4, False, 0.0),
 ]
 
 

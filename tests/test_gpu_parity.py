@@ -217,6 +217,11 @@ SHAPES = [
     ("k1", 200, 96, 104, 3, 1, False),
     ("wide_f", 130, 64, 520, 2, 2, False),
     ("two_tiles", 700, 320, 288, 2, 1, False),
+    # the expert limit: most of the 1024 experts are empty, the rest hold a
+    # token or two (tile decode, prefix scans and the wgrad expert ranking
+    # at E above the workgroup's thread count)
+    ("max_experts", 96, 64, 64, 1024, 4, False),
+    ("many_experts_bias", 200, 64, 96, 300, 8, True),
 ]
 
 
