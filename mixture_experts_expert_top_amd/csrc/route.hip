@@ -241,16 +241,21 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
   }
 }
 
-// Partial dW_g over one chunk of 256 tokens, 512 columns and up to 32
-// experts: part[chunk][e][c] = sum over the chunk's tokens, in order, of
-// dlogits[t][e] * x[t][c]; the y == 0 blocks also sum dlogits over the
-// chunk (db).  With part == nullptr only the db sums are made (x unread).
+// Partial dW_g over one chunk of 256 tokens, 512 columns and up to kExp
+// experts (8 when E <= 8, else 32 a block): part[chunk][e][c] = sum over
+// the chunk's tokens, in order, of dlogits[t][e] * x[t][c]; the y == 0
+// blocks also sum dlogits over the chunk (db).  With part == nullptr only
+// the db sums are made (x unread).  The x values of kAhead tokens are
+// loaded before any of them is used, so the loads overlap; the sums still
+// take the tokens one by one in order.
 constexpr int kRbTok = 256;
 constexpr int kRbExp = 32;
 constexpr int kRbCols = 512;          // columns of a block, two a thread
+template <int kExp>
 __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     const float* __restrict__ dlogits, const bf16_t* __restrict__ x, int T,
     int E, int d, float* __restrict__ part, float* __restrict__ db_part) {
+  constexpr int kRbExp = kExp;
   __shared__ __attribute__((aligned(16))) float s_dl[kRbTok][kRbExp];
   const int tc = blockIdx.x;
   const int c = blockIdx.y * kRbCols + threadIdx.x * 2;
@@ -274,17 +279,27 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
 #pragma unroll
   for (int ee = 0; ee < kRbExp; ++ee) { acc0[ee] = 0.0f; acc1[ee] = 0.0f; }
   const bf16_t* xc = x + static_cast<int64_t>(t0) * d + c;
-  for (int tt = 0; tt < nt; ++tt) {
-    const uint32_t xv =
-        *reinterpret_cast<const uint32_t*>(xc + static_cast<int64_t>(tt) * d);
-    const float x0 = bf_lo(xv), x1 = bf_hi(xv);
+  constexpr int kAhead = 8;
+  for (int tb = 0; tb < nt; tb += kAhead) {
+    uint32_t xv[kAhead];
 #pragma unroll
-    for (int q = 0; q < kRbExp / 4; ++q) {
-      const f32x4 g = *reinterpret_cast<const f32x4*>(&s_dl[tt][4 * q]);
+    for (int u = 0; u < kAhead; ++u)
+      xv[u] = (tb + u < nt) ? *reinterpret_cast<const uint32_t*>(
+                                  xc + static_cast<int64_t>(tb + u) * d)
+                            : 0u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc0[4 * q + r] += g[r] * x0;
-        acc1[4 * q + r] += g[r] * x1;
+    for (int u = 0; u < kAhead; ++u) {
+      if (tb + u >= nt) break;
+      const int tt = tb + u;
+      const float x0 = bf_lo(xv[u]), x1 = bf_hi(xv[u]);
+#pragma unroll
+      for (int q = 0; q < kRbExp / 4; ++q) {
+        const f32x4 g = *reinterpret_cast<const f32x4*>(&s_dl[tt][4 * q]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc0[4 * q + r] += g[r] * x0;
+          acc1[4 * q + r] += g[r] * x1;
+        }
       }
     }
   }
@@ -486,12 +501,19 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
   if (dw_g || db) {
     // without dw_g only the db sums are wanted: one column block, x unread
     const int64_t dd = dw_g ? d : 0;
+    // experts a block: 8 when they all fit, else 32 (grid.z covers E)
+    const int eb = E <= 8 ? 8 : kRbExp;
     dim3 g2(static_cast<unsigned>(chunks),
             static_cast<unsigned>(dw_g ? (d + kRbCols - 1) / kRbCols : 1),
-            static_cast<unsigned>((E + kRbExp - 1) / kRbExp));
-    hipLaunchKernelGGL(router_dwg_partial_kernel, g2, dim3(256), 0, s, dlogits,
-                       x, Ti, E, static_cast<int>(dd), dw_g ? part : nullptr,
-                       db_part);
+            static_cast<unsigned>((E + eb - 1) / eb));
+    if (eb == 8)
+      hipLaunchKernelGGL(router_dwg_partial_kernel<8>, g2, dim3(256), 0, s,
+                         dlogits, x, Ti, E, static_cast<int>(dd),
+                         dw_g ? part : nullptr, db_part);
+    else
+      hipLaunchKernelGGL(router_dwg_partial_kernel<kRbExp>, g2, dim3(256), 0,
+                         s, dlogits, x, Ti, E, static_cast<int>(dd),
+                         dw_g ? part : nullptr, db_part);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t n = std::max<int64_t>(static_cast<int64_t>(E) * dd, E);
     hipLaunchKernelGGL(router_dwg_reduce_kernel,
