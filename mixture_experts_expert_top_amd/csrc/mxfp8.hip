@@ -102,28 +102,38 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     r0 = sbeg + (p0 - s_pad[lo]);
     r_end = r0 + kTokRows < send ? r0 + kTokRows : send;
   }
+  // 1. load: thread t covers columns 8 (t%8) .. +7 of rows t/8 + 32 i of
+  // column run ct; the next run's loads are issued as soon as this run is
+  // in LDS, so they land while this run is quantized and written
+  const int cc = (t & 7) * 8;
+  i32x4 nxt[kTokRows / 32];
+  auto load_run = [&](int ct) {
+    const int64_t c0 =
+        (static_cast<int64_t>(blockIdx.y) * kTokTiles + ct) * kTokCols;
+    const bool col_ok = c0 + cc < cols;            // cols % 8 == 0
+#pragma unroll
+    for (int i = 0; i < kTokRows / 32; ++i) {
+      const int rr = (t >> 3) + 32 * i;
+      nxt[i] = i32x4{0, 0, 0, 0};
+      if (col_ok && r0 + rr < r_end) {
+        const int64_t r = r0 + rr;
+        const int64_t sr = gather ? static_cast<int64_t>(gather[r]) : r;
+        nxt[i] = *reinterpret_cast<const i32x4*>(src + sr * cols + c0 + cc);
+      }
+    }
+  };
+  load_run(0);
   for (int ct = 0; ct < kTokTiles; ++ct) {
     const int64_t c0 =
         (static_cast<int64_t>(blockIdx.y) * kTokTiles + ct) * kTokCols;
     if (c0 >= cols) break;
     if (ct > 0) __syncthreads();                   // LDS of the previous run
-    // 1. load: thread t covers columns 8 (t%8) .. +7 of rows t/8 + 32 i
-    {
-      const int cc = (t & 7) * 8;
-      const bool col_ok = c0 + cc < cols;          // cols % 8 == 0
 #pragma unroll
-      for (int i = 0; i < kTokRows / 32; ++i) {
-        const int rr = (t >> 3) + 32 * i;
-        i32x4 v = {0, 0, 0, 0};
-        if (col_ok && r0 + rr < r_end) {
-          const int64_t r = r0 + rr;
-          const int64_t sr = gather ? static_cast<int64_t>(gather[r]) : r;
-          v = *reinterpret_cast<const i32x4*>(src + sr * cols + c0 + cc);
-        }
-        *reinterpret_cast<i32x4*>(tile + rr * kTokLd + cc) = v;
-      }
-    }
+    for (int i = 0; i < kTokRows / 32; ++i)
+      *reinterpret_cast<i32x4*>(tile + ((t >> 3) + 32 * i) * kTokLd + cc) =
+          nxt[i];
     __syncthreads();
+    if (ct + 1 < kTokTiles) load_run(ct + 1);
     if constexpr (kRows) {
       // along the row: 32 columns of row t/2 (c0 is a multiple of 64)
       const int rr = t >> 1, half = t & 1;
