@@ -4,21 +4,30 @@ the same seeded inputs.
 The reference is the oracle at the pages' precision: arithmetic in float64,
 with the activations the path stores in bf16 (AB, S, dAB) rounded to bf16
 where they are stored (BF16 training keeps every activation in 16 bits).
-Bars:
+Bars, on every layer shape and on the full-size workloads:
   * routing indices, counts, offsets, positions and permuted rows:
     bit-exact;
-  * outputs and gradients (y, dx, dW_gu, dW2, dp): max|gpu - ref| /
-    rms(ref) <= 2e-2 per tensor on the tiny workload and on the full
-    Mixtral-sized and fine-grained workloads;
+  * outputs and gradients (y, dx, dW_gu, dW2, dp): the error beyond the
+    output format's own rounding,
+        max over elements of max(|gpu - ref| - h(ref), 0) / rms(ref),
+    is at most 2e-2, where h(ref) is half the bf16 spacing at ref for the
+    bf16 outputs (y, dx, dW) and 0 for the fp32 dp.  No bf16 tensor can
+    be nearer the exact values than its own rounding: with max|ref| / rms
+    near 12 (rank-one gradients of one-token experts) that rounding alone
+    is up to 12 * 2^-8 = 4.7e-2 of the rms, above the bar whatever
+    computed it.  Each expert's weight gradient is its own parameter
+    tensor (one weight per expert), so the rms of dW is taken per expert
+    over the experts that received rows; experts with none must be exact
+    zeros;
   * every floating tensor on every shape, element by element:
     |gpu - ref| <= 2 * (2^-7 |ref| + 2e-3 rms(ref)), i.e. within two bf16
     ulps (one for the output's own rounding, one for a stored activation
     rounded the other way by the two sides) plus accumulation noise.
-The distance to the exact float64 definition (no bf16 storage) is printed
-for every case.  Small shapes are compared element by element; the
-full-size layers on sampled outputs the oracle computes one by one.  The
-per-stage tests (test_gpu_stages.py) hold each kernel to its rounding
-bound on identical inputs."""
+The plain max|gpu - ref| / rms(ref) and the distance to the exact float64
+definition (no bf16 storage) are printed for every case.  Small shapes are
+compared element by element; the full-size layers on sampled outputs the
+oracle computes one by one.  The per-stage tests (test_gpu_stages.py) hold
+each kernel to its rounding bound on identical inputs."""
 
 import numpy as np
 import pytest
@@ -48,6 +57,32 @@ def rel(got, ref):
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
+
+
+def half_ulp_bf16(ref):
+    """Half the bf16 spacing at each value of ref (0 at zero): the most that
+    rounding the exact value to bf16 moves it."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    _, ex = np.frexp(a)                   # a = m 2^ex, m in [0.5, 1)
+    binade = np.maximum(ex - 1, -126)
+    return np.where(a > 0, np.ldexp(1.0, binade - 8), 0.0)
+
+
+def bar_err(got, ref, bf16_out=True):
+    """max(|got - ref| - h(ref), 0) / rms(ref): the error beyond the output
+    format's own rounding (h = half a bf16 spacing, or 0 for fp32)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    if bf16_out:
+        err = np.maximum(err - half_ulp_bf16(ref), 0.0)
+    return float(np.max(err)) / max(rms, 1e-300)
+
+
+def per_expert(metric, got, ref, experts):
+    """The worst of metric(got[e], ref[e]) over the given experts."""
+    return max((metric(got[e], ref[e]) for e in experts), default=0.0)
 
 
 ULP_REL = 2.0 ** -7
@@ -141,6 +176,83 @@ def test_permute_bitexact(T, E, k, d, kind):
     moe.moe_permute_rows(0, pos, x, None, xp2, None)
     torch.cuda.synchronize()
     assert torch.equal(xp2, xp)
+
+
+def _plan_on_gpu(idx, w, E, x):
+    dev = _dev()
+    T, k = idx.shape
+    d = x.shape[1]
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty(T, k, dtype=torch.int32, device=dev)
+    src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    w_perm = torch.empty(T * k, dtype=torch.float32, device=dev)
+    xp = torch.empty(T * k, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.moe_workspace_bytes(0, 0, T, E, k, d, 8),
+                     dtype=torch.uint8, device=dev)
+    moe.moe_permute(0, idx, w, E, x, None, counts, offsets, pos, src,
+                    w_perm if w is not None else None, xp, None, ws)
+    torch.cuda.synchronize()
+    return counts, offsets, pos, src, xp
+
+
+@gpu
+@pytest.mark.parametrize("E,k", [(8, 2), (5, 5), (64, 8), (3, 3)])
+def test_route_nan_and_inf_scores(E, k):
+    """Scores holding NaN or infinities still route every slot to a real
+    expert: NaN ranks below every number (ties by id), as in the oracle's
+    sort; the weights of such tokens may be NaN.  The plan built on those
+    ids is the oracle's."""
+    dev = _dev()
+    T = 300
+    L = _logits("randn", T, E, seed=E + k)
+    L[0, :] = float("nan")                       # every score NaN
+    L[1, E // 2] = float("nan")                  # one NaN
+    L[2, 0] = float("inf")
+    L[3, :] = float("-inf")
+    L[4, 1 % E] = float("-inf")
+    L[4, 0] = float("nan")
+    L[5::7, (E - 1)] = float("nan")
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    moe.moe_route(L, k, True, idx, w)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert got.min() >= 0 and got.max() < E
+    ref_idx, ref_p = R.topk_route(h64(L), k)
+    np.testing.assert_array_equal(got, ref_idx)
+    fin = np.isfinite(ref_p)
+    assert np.max(np.abs(h64(w)[fin] - ref_p[fin]), initial=0.0) <= 2e-6
+    x = I.make_custom(T, 64, 8, E, k, seed=1, device=dev)["x"]
+    counts, offsets, pos, _, _ = _plan_on_gpu(idx, w, E, x)
+    c, o, p, _ = R.dispatch_plan(ref_idx, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    np.testing.assert_array_equal(pos.cpu().numpy(), p)
+
+
+@gpu
+def test_permute_clamps_out_of_range_ids():
+    """Expert ids a caller passes outside [0, E) are taken as the nearest
+    valid id: the plan is the oracle's plan of the clamped ids and every
+    row lands inside the permuted buffer."""
+    dev = _dev()
+    T, E, k = 700, 6, 2
+    g = torch.Generator(device="cpu")
+    g.manual_seed(11)
+    raw = torch.randint(-3, E + 3, (T, k), generator=g, dtype=torch.int32)
+    raw[0, 0] = -2 ** 31
+    raw[1, 1] = 2 ** 31 - 1
+    x = I.make_custom(T, 32, 8, E, k, seed=2, device=dev)["x"]
+    counts, offsets, pos, src, xp = _plan_on_gpu(raw.to(dev), None, E, x)
+    ref = np.clip(raw.numpy(), 0, E - 1)
+    c, o, p, s_ = R.dispatch_plan(ref, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    np.testing.assert_array_equal(pos.cpu().numpy(), p)
+    np.testing.assert_array_equal(src.cpu().numpy(), s_)
+    np.testing.assert_array_equal(xp.view(torch.int16).cpu().numpy(),
+                                  x.view(torch.int16).cpu().numpy()[s_])
 
 
 @gpu
@@ -258,26 +370,32 @@ def test_layer_parity(name, T, d, f, E, k, bias):
            "dx": bwd["dx"], "dw_gu": bwd["dw_gu"], "dw2": bwd["dw2"],
            "dp": bwd["dp"]}
     ulp = {n: ulp_excess(h64(gpu[n]), ref[n]) for n in gpu}
-    # the spec bar against the exact oracle (reported for every
-    # shape, gated on the tiny workload's shape)
+    live = np.nonzero(fwd["counts"] > 0)[0]
+    G = {n: h64(gpu[n]) for n in ("y", "dx", "dw_gu", "dw2", "dp")}
+
+    def metric(fn, n, **kw):
+        if n in ("dw_gu", "dw2"):
+            return per_expert(lambda g, r: fn(g, r, **kw), G[n], ref[n], live)
+        return fn(G[n], ref[n], **kw)
+
+    bar = {n: metric(bar_err, n, bf16_out=(n != "dp")) for n in G}
+    plain = {n: metric(rel, n) for n in G}
+    # distance to the exact definition (no bf16 storage), reported
     efwd = R.moe_forward(h["x"], h["logits"], h["w_gu"], h["w2"], k)
     ebwd = R.moe_backward(efwd, h["dy"], h["w_gu"], h["w2"])
-    exact = {"y": rel(h64(path.y), efwd["y"]),
-             "dx": rel(h64(path.dx), ebwd["dx"]),
-             "dw_gu": rel(h64(path.dw_gu), ebwd["dw_gu"]),
-             "dw2": rel(h64(path.dw2), ebwd["dw2"]),
-             "dp": rel(h64(path.dp), ebwd["dp"])}
-    bar = {n: rel(h64(gpu[n]), ref[n])
-           for n in ("y", "dx", "dw_gu", "dw2", "dp")}
-    print(name, "ulp-excess", {n: f"{v:.2f}" for n, v in ulp.items()},
-          "max|err|/rms", {n: f"{v:.2e}" for n, v in bar.items()},
+    exact = {"y": rel(G["y"], efwd["y"]), "dx": rel(G["dx"], ebwd["dx"]),
+             "dw_gu": per_expert(rel, G["dw_gu"], ebwd["dw_gu"], live),
+             "dw2": per_expert(rel, G["dw2"], ebwd["dw2"], live),
+             "dp": rel(G["dp"], ebwd["dp"])}
+    print(name, "bar (beyond output rounding; dW per expert)",
+          {n: f"{v:.2e}" for n, v in bar.items()},
+          "plain max|err|/rms", {n: f"{v:.2e}" for n, v in plain.items()},
+          "ulp-excess", {n: f"{v:.2f}" for n, v in ulp.items()},
           "exact-fp64 max|err|/rms",
           {n: f"{v:.2e}" for n, v in exact.items()})
     bad = {n: v for n, v in ulp.items() if not v <= 2.0}
+    bad.update({"bar:" + n: v for n, v in bar.items() if not v <= TOL_BF16})
     assert not bad, bad
-    if name == "tiny":
-        bad = {n: v for n, v in bar.items() if not v <= TOL_BF16}
-        assert not bad, bad
     # experts with no rows: weight gradients exactly zero
     for e in np.nonzero(fwd["counts"] == 0)[0]:
         assert torch.count_nonzero(path.dw_gu[e]).item() == 0
@@ -392,39 +510,65 @@ def _full_size(name, seed, backward, n_tok=6, n_col=3):
                 D["dp"].append(dps)
         G["ab"] = np.stack(Gs["ab"])
         G["s"] = np.stack(Gs["s"])
-        # sampled weight-gradient columns / rows of two experts
+        # sampled weight-gradient columns / rows of the three busiest
+        # experts and of the least busy one that received rows (skew puts
+        # the largest values there); the metric is taken per expert
         w_perm = R.permuted_weights(ref_p, pos)
-        G["dw2"], G["dw_gu"] = [], []
-        busy = np.argsort(-counts)
-        for e in (busy[0], busy[len(busy) // 2]):
+        busy = np.argsort(-counts, kind="stable")
+        live = [int(e) for e in busy if counts[e] > 0]
+        sample_e = list(dict.fromkeys(live[:3] + live[-1:]))
+        for n in ("dw2", "dw_gu"):
+            G[n] = {}
+            X[n] = {}
+            B[n] = {}
+        for e in sample_e:
             r0, r1 = int(offsets[e]), int(offsets[e + 1])
             sl = torch.as_tensor(src[r0:r1], device=dev)
             xp_e = h64(inp["x"][sl])
             do_e = h64(inp["dy"][sl])
+            for n in ("dw2", "dw_gu"):
+                G[n][e], X[n][e], B[n][e] = [], [], []
             for j in rng.integers(0, f, n_col):
-                G["dw2"].append(h64(path.dw2[e][:, int(j)]))
+                G["dw2"][e].append(h64(path.dw2[e][:, int(j)]))
                 for mode, D in ((False, X), (True, B)):
-                    D["dw2"].append(R.dw2_column(
+                    D["dw2"][e].append(R.dw2_column(
                         xp_e, do_e, w_perm[r0:r1], wgu[e], int(j),
                         bf16_act=mode))
             for i in list(rng.integers(0, f, n_col)) + \
                     list(f + rng.integers(0, f, n_col)):
-                G["dw_gu"].append(h64(path.dw_gu[e][int(i)]))
+                G["dw_gu"][e].append(h64(path.dw_gu[e][int(i)]))
                 for mode, D in ((False, X), (True, B)):
-                    D["dw_gu"].append(R.dw_gu_row(
+                    D["dw_gu"][e].append(R.dw_gu_row(
                         xp_e, do_e, w_perm[r0:r1], wgu[e], w2[e], int(i),
                         bf16_act=mode))
-        G["dw2"] = np.stack(G["dw2"])
-        G["dw_gu"] = np.stack(G["dw_gu"])
+        for n in ("dw2", "dw_gu"):
+            for D in (G, X, B):
+                D[n] = {e: np.stack(v) for e, v in D[n].items()}
         for e in np.nonzero(counts == 0)[0]:
             assert torch.count_nonzero(path.dw_gu[e]).item() == 0
             assert torch.count_nonzero(path.dw2[e]).item() == 0
-    exact = {n: rel(G[n], np.array(v)) for n, v in X.items() if v}
-    bar = {n: rel(G[n], np.array(B[n])) for n in X if B[n]}
-    ulp = {n: ulp_excess(G[n], np.array(v)) for n, v in B.items() if v}
-    print(name, "counts", counts.tolist()[:16], "max|err|/rms",
-          {n: f"{v:.2e}" for n, v in bar.items()}, "ulp-excess",
-          {n: f"{v:.2f}" for n, v in ulp.items()}, "exact-fp64 max|err|/rms",
+
+    def metric(fn, n, D, **kw):
+        if isinstance(G[n], dict):
+            return per_expert(lambda g, r: fn(g, r, **kw), G[n], D[n],
+                              list(G[n]))
+        return fn(G[n], np.array(D[n]), **kw)
+
+    names = [n for n in X if len(X[n])]
+    exact = {n: metric(rel, n, X) for n in names}
+    plain = {n: metric(rel, n, B) for n in names}
+    bar = {n: metric(bar_err, n, B, bf16_out=(n != "dp")) for n in names}
+    ulp = {n: ulp_excess(G[n], np.array(v)) for n, v in B.items()
+           if len(v) and not isinstance(v, dict)}
+    for n in ("dw2", "dw_gu"):
+        if isinstance(B[n], dict):
+            ulp[n] = max(ulp_excess(G[n][e], B[n][e]) for e in B[n])
+    print(name, "counts", counts.tolist()[:16],
+          "bar (beyond output rounding; dW per expert)",
+          {n: f"{v:.2e}" for n, v in bar.items()},
+          "plain max|err|/rms", {n: f"{v:.2e}" for n, v in plain.items()},
+          "ulp-excess", {n: f"{v:.2f}" for n, v in ulp.items()},
+          "exact-fp64 max|err|/rms",
           {n: f"{v:.2e}" for n, v in exact.items()})
     bad = {n: v for n, v in bar.items() if not v <= TOL_BF16}
     bad.update({"ulp:" + n: v for n, v in ulp.items() if not v <= 2.0})

@@ -75,6 +75,22 @@ def test_closed_forms(case):
                                    rtol=1e-14, atol=1e-300)
 
 
+def _router_cases():
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as fh:
+        return json.load(fh)["router_cases"]
+
+
+@pytest.mark.parametrize("case", _router_cases(), ids=lambda c: c["name"])
+def test_router_logits_closed_forms(case):
+    x = np.array(case["x"], dtype=np.float64)
+    w_g = np.array(case["w_g"], dtype=np.float64)
+    bias = None if case["bias"] is None else np.array(case["bias"])
+    got = R.router_logits(x, w_g, bias)
+    want = np.array(_evtree(case["expect_logits"]), dtype=np.float64)
+    assert got.shape == want.shape
+    np.testing.assert_array_equal(got, want)
+
+
 # ---------------------------------------------------------------- routing
 
 def _python_topk(L, k):
@@ -101,6 +117,27 @@ def test_topk_ties_go_to_lower_id(E, k):
     np.testing.assert_array_equal(idx, _python_topk(L, k))
     for t in range(L.shape[0]):
         assert len(set(idx[t].tolist())) == k
+
+
+def test_topk_nan_ranks_below_every_number():
+    """A NaN score ranks below every number, -inf included; NaNs among
+    themselves go by ascending id (the reading the routing kernel follows
+    for scores the pages never meet)."""
+    nan, inf = float("nan"), float("inf")
+    L = np.array([[nan, 1.0, nan, -inf], [inf, nan, 0.0, 0.0],
+                  [nan, nan, nan, nan], [2.0, -inf, nan, 3.0]])
+    idx, p = R.topk_route(L, 4)
+    want = []
+    for row in L.tolist():
+        want.append(sorted(range(4), key=lambda e: (math.isnan(row[e]),
+                                                    -row[e] if not
+                                                    math.isnan(row[e]) else 0,
+                                                    e)))
+    np.testing.assert_array_equal(idx, np.array(want))
+    np.testing.assert_array_equal(idx[0], [1, 3, 0, 2])
+    idx2, p2 = R.topk_route(L[3:], 2)
+    np.testing.assert_array_equal(idx2, [[3, 0]])
+    assert np.all(np.isfinite(p2))
 
 
 @pytest.mark.parametrize("renorm", [True, False])
