@@ -15,6 +15,13 @@
 namespace moe {
 namespace {
 
+// An expert id outside [0, E) (the routing kernel never writes one; a
+// caller's own idx might) is taken as the nearest valid id, so that no
+// count, offset or row index leaves its buffer.
+__device__ __forceinline__ int clamp_expert(int e, int E) {
+  return min(max(e, 0), E - 1);
+}
+
 // ---------------------------------------------------------------- plan
 // Pass 1: one wavefront per chunk of kPlanChunk slots walks its chunk in
 // 64-slot steps.  For each step the lanes that share an expert id are
@@ -34,7 +41,7 @@ __global__ __launch_bounds__(64) void plan_rank_kernel(
   for (int64_t s0 = c0; s0 < c1; s0 += 64) {
     const int64_t s = s0 + lane;
     const bool valid = s < c1;
-    const int e = valid ? idx[s] : -1;
+    const int e = valid ? clamp_expert(idx[s], E) : -1;
     uint64_t active = __ballot(valid);
     int rank = 0, grp = 0;
     while (active) {
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   if (threadIdx.x < k) {
     const int j = threadIdx.x;
     const int64_t s = t * k + j;
-    const int e = idx[s];
+    const int e = clamp_expert(idx[s], E);
     const int64_t c = s / kPlanChunk;
     const int p = offsets[e] + chunk_base[c * E + e] + pos[s];
     pos[s] = p;

@@ -79,7 +79,15 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
 // experts g, g+G, ..., (VPL of them).  k rounds of a butterfly arg-max over
 // the G lanes pick the experts in order; the comparison is "larger score,
 // or equal score and smaller id", so ties go to the lower id and +0 == -0.
+// A NaN score ranks below every number (NaNs among themselves by id), so
+// every round picks a real expert whatever the scores hold; kNoExpert marks
+// a lane with nothing left and loses to any expert.
+constexpr int kNoExpert = 0x7fffffff;
 __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+  if (ea == kNoExpert) return false;
+  if (eb == kNoExpert) return true;
+  const bool na = va != va, nb = vb != vb;
+  if (na || nb) return na && nb ? ea < eb : nb;
   return (va > vb) || (va == vb && ea < eb);
 }
 
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     if (j >= k) break;
     // local best among live values
     float bv = -INFINITY;
-    int be = 0x7fffffff;
+    int be = kNoExpert;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = gl + i * G;

@@ -54,7 +54,9 @@ def topk_route(logits, k, renorm=True):
 
     Selection compares the given score values exactly (float32 scores are
     exact in float64): experts are ordered by descending score, equal scores
-    by ascending expert id, and the first k are kept.  Weights are the
+    by ascending expert id, and the first k are kept.  A NaN score ranks
+    below every number (NaNs by ascending id), which is where numpy's sort
+    places NaN.  Weights are the
     softmax of the scores; with ``renorm`` they are renormalised over the k
     chosen experts, which equals a softmax over the chosen scores alone.
     Returns idx [T, k] int32 and p [T, k] float64.
