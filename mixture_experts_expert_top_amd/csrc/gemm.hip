@@ -462,12 +462,6 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int E = P.E;
 
   // ---------------------------------------------------------- tile decode
-  // SegM grids hold ksplit copies of an upper bound on the tile count;
-  // copy s (the slowest index) computes reduction range s.
-  const int lbid = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_split = gridDim.x / P.ksplit;
-  const int split = lbid / per_split;
-  const int bid = lbid - split * per_split;
   int e, mt, nt;
   int64_t seg0;      // first permuted row of the expert
   int seg_len;       // rows of the expert
@@ -511,9 +505,19 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     }
     __syncthreads();
   }
+  int split = 0;
   if (MODE == kSegM) {
+    // The grid holds ksplit copies of an upper bound on the tile count and
+    // only the first ksplit * total ids carry a tile (copy s, the slowest
+    // index, computes reduction range s).  The XCD-aware remap runs over
+    // those ids alone, so each XCD receives an equal share of real tiles;
+    // the surplus ids, dealt round-robin over the XCDs, exit at once.
     const int total = s_pref[E] * P.ntn;
-    if (bid >= total) return;
+    const int nreal = total * P.ksplit;
+    if (static_cast<int>(blockIdx.x) >= nreal) return;
+    const int lbid = xcd_remap(blockIdx.x, nreal);
+    split = lbid / total;
+    const int bid = lbid - split * total;
     e = find_segment(s_pref, E, bid / P.ntn);
     const int mte = s_pref[e + 1] - s_pref[e];
     tile_order(bid - s_pref[e] * P.ntn, mte, P.ntn, &mt, &nt);
@@ -566,6 +570,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       mt = local % mtiles;
       nt = local / mtiles;
     } else {
+      const int bid = xcd_remap(blockIdx.x, gridDim.x);
       e = bid / per_e;
       tile_order(bid - e * per_e, mtiles, P.ntn, &mt, &nt);
     }
