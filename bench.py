@@ -38,11 +38,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 # WRITE_SIZE per dispatch, with the same counters' reading of a plain 1 GiB
 # device copy); valid only for the kernel source it was taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# Measured whole-chip MFMA ceiling with random operands (power-limited
-# clock), written from the output of `bench.py --mfma-ceiling`.
+# Recorded whole-chip MFMA ceiling with random operands (power-limited
+# clock): a measured figure, read as data.
 CEILING_FILE = os.path.join(ROOT, "profiles", "mfma_ceiling.json")
-PROBE = os.path.join(ROOT, "mixture_experts_expert_top_amd", "probe",
-                     "mfma_ceiling")
 # the grouped GEMM kernel's sources: the recorded traffic is valid only
 # for the sources it was measured on
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_expert_top_amd", "csrc", n)
@@ -138,26 +136,6 @@ def measured_ceiling(prec):
         return None
 
 
-def mfma_ceiling():
-    """Runs the ceiling probe (built by build()) and prints its cases as one
-    JSON line: {dtype: {operands: {ms, tflops, ghz}}}."""
-    import subprocess
-    if not os.path.exists(PROBE):
-        raise SystemExit(f"{PROBE} is missing: run __graft_entry__.build()")
-    res = subprocess.run([PROBE], capture_output=True, text=True, timeout=120)
-    if res.returncode != 0:
-        raise SystemExit(f"mfma_ceiling failed ({res.returncode}):\n"
-                         f"{res.stdout}\n{res.stderr}")
-    out = {}
-    for line in res.stdout.split("\n"):
-        f = line.split()
-        if len(f) == 6:
-            out.setdefault(f[0], {})[f[1]] = {
-                "iters": int(f[2]), "ms": float(f[3]), "tflops": float(f[4]),
-                "ghz": float(f[5])}
-    print(json.dumps(out), flush=True)
-
-
 def copy_calibration():
     """A plain device copy of 1 GiB, five times: the reference that scales
     the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -226,9 +204,6 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured as a HIP graph and "
                          "replayed (reported under 'graph')")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="only run the MFMA ceiling probe (constant and "
-                         "random operands, bf16 and fp8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
                          "the HBM traffic counters")
@@ -242,9 +217,6 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
-        return
-    if args.mfma_ceiling:
-        mfma_ceiling()
         return
 
     import torch
