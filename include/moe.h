@@ -24,9 +24,10 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the
- *    library never allocates or frees memory and keeps no mutable global
- *    state.  Scratch memory is the caller's `workspace` (size from
- *    moe_workspace_bytes); it need not be zeroed.
+ *    library never allocates or frees memory.  Scratch memory is the
+ *    caller's `workspace` (size from moe_workspace_bytes); it need not be
+ *    zeroed.  The one exception, moe_permute_noalloc, uses a fixed
+ *    per-GPU scratch array of the library instead (see there).
  *  - Row-major layouts.  bf16 tensors are passed as `void*` holding IEEE
  *    bfloat16 bit patterns.  Every tensor pointer must be 16-byte aligned.
  *  - Work is enqueued on `stream` and the call returns without waiting.
@@ -171,6 +172,31 @@ moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
                        int32_t* src, float* w_perm, void* x_perm,
                        uint8_t* x_perm_scales, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments (minus workspace), outputs and errors as moe_permute.  Its
+ * scratch (the plan's per-chunk counts) is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in device memory, one copy per GPU, held until
+ * the process ends; the call allocates and frees nothing.  A plan that
+ * needs more than that (moe_workspace_bytes(MOE_ENTRY_PERMUTE, ...) above
+ * the limit) is rejected with MOE_ERR_UNSUPPORTED before any launch.  The
+ * kernels write every scratch word they read, so nothing is cleared
+ * between calls.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (concurrent streams, or threads) race and give
+ * undefined results; calls ordered on one stream are safe.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_permute_noalloc(moe_prec prec, const int32_t* topk_idx,
+                               const float* topk_w, int64_t T, int32_t E,
+                               int32_t k, const void* x,
+                               const uint8_t* x_scales, int64_t d,
+                               int32_t* counts, int32_t* offsets,
+                               int32_t* pos, int32_t* src, float* w_perm,
+                               void* x_perm, uint8_t* x_perm_scales,
+                               hipStream_t stream);
 
 /*
  * moe_permute_rows -- row permutation with an existing plan (used for the

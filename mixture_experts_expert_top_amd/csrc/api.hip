@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "internal.h"
 
@@ -220,6 +222,99 @@ BwdWorkspace bwd_layout(int64_t Tk, int64_t f) {
 
 }  // namespace
 
+namespace {
+
+// Validation shared by the two permutation entries (everything but the
+// workspace); the launch order of both.
+moe_status permute_check(moe_prec prec, const int32_t* topk_idx,
+                         const float* topk_w, int64_t T, int32_t E, int32_t k,
+                         const void* x, const uint8_t* x_scales, int64_t d,
+                         int32_t* counts, int32_t* offsets, int32_t* pos,
+                         int32_t* src, float* w_perm, void* x_perm,
+                         uint8_t* x_perm_scales) {
+  if (moe_status st = check_prec(prec)) return st;
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_OPT_PTR(topk_w);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(pos);
+  REQUIRE_PTR(src);
+  REQUIRE_OPT_PTR(w_perm);
+  REQUIRE_PTR(x_perm);
+  REQUIRE(!(w_perm && !topk_w), MOE_ERR_INVALID_ARG,
+          "w_perm given without topk_w");
+  if (moe_status st = check_route_dims(T, E, k)) return st;
+  if (moe_status st = check_feature("d", d, prec)) return st;
+  const int64_t row_bytes = act_row_bytes(prec, d);
+  REQUIRE(T * k * row_bytes <= kMaxBytes * 4, MOE_ERR_UNSUPPORTED,
+          "permuted tensor too large");
+  if (is_mx(prec)) {
+    REQUIRE_PTR(x_scales);
+    REQUIRE_PTR(x_perm_scales);
+  }
+  return MOE_OK;
+}
+
+moe_status permute_launch(moe_prec prec, const int32_t* topk_idx,
+                          const float* topk_w, int64_t T, int32_t E,
+                          int32_t k, const void* x, const uint8_t* x_scales,
+                          int64_t d, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* src, float* w_perm,
+                          void* x_perm, uint8_t* x_perm_scales, void* ws,
+                          hipStream_t stream) {
+  const int64_t row_bytes = act_row_bytes(prec, d);
+  hipError_t e = moe::launch_plan(topk_idx, T, E, k, counts, offsets, pos,
+                                  ws, stream);
+  if (e != hipSuccess) return hip_status(e, "moe_permute/plan");
+  const bool mx = is_mx(prec);
+  e = moe::launch_scatter(topk_idx, topk_w, T, E, k, offsets, pos, src,
+                          topk_w ? w_perm : nullptr, x, row_bytes, x_perm,
+                          mx ? x_scales : nullptr, mx ? d / 32 : 0,
+                          mx ? x_perm_scales : nullptr, ws, stream);
+  return hip_status(e, "moe_permute/scatter");
+}
+
+}  // namespace
+
+// ------------------------------------------------------- allocation-free
+// Scratch of moe_permute_noalloc: a fixed array in device memory, one copy
+// on every GPU the library runs on, held until the process ends.  On the
+// host the array's name is only a stand-in; kernels get the device address
+// that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch (looked up on its first use,
+// with that device current).
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc/hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED,
+          "device index %d is beyond the %d the library tracks", dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+      return hip_status(e, "moe_permute_noalloc/hipGetSymbolAddress");
+    REQUIRE(p != nullptr, MOE_ERR_HIP,
+            "moe_permute_noalloc: no device address for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_status_str(moe_status s) {
@@ -342,40 +437,43 @@ moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
                        int32_t* src, float* w_perm, void* x_perm,
                        uint8_t* x_perm_scales, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  if (moe_status st = check_prec(prec)) return st;
-  REQUIRE_PTR(topk_idx);
-  REQUIRE_OPT_PTR(topk_w);
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(counts);
-  REQUIRE_PTR(offsets);
-  REQUIRE_PTR(pos);
-  REQUIRE_PTR(src);
-  REQUIRE_OPT_PTR(w_perm);
-  REQUIRE_PTR(x_perm);
-  REQUIRE(!(w_perm && !topk_w), MOE_ERR_INVALID_ARG,
-          "w_perm given without topk_w");
-  if (moe_status st = check_route_dims(T, E, k)) return st;
-  if (moe_status st = check_feature("d", d, prec)) return st;
-  const int64_t row_bytes = act_row_bytes(prec, d);
-  REQUIRE(T * k * row_bytes <= kMaxBytes * 4, MOE_ERR_UNSUPPORTED,
-          "permuted tensor too large");
-  if (is_mx(prec)) {
-    REQUIRE_PTR(x_scales);
-    REQUIRE_PTR(x_perm_scales);
-  }
+  if (moe_status st = permute_check(prec, topk_idx, topk_w, T, E, k, x,
+                                    x_scales, d, counts, offsets, pos, src,
+                                    w_perm, x_perm, x_perm_scales))
+    return st;
   const size_t need = moe::plan_workspace_bytes(T * k, E);
   REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "workspace too small: %zu < %zu bytes", workspace_bytes, need);
   REQUIRE_PTR(workspace);
-  hipError_t e = moe::launch_plan(topk_idx, T, E, k, counts, offsets, pos,
-                                  workspace, stream);
-  if (e != hipSuccess) return hip_status(e, "moe_permute/plan");
-  const bool mx = is_mx(prec);
-  e = moe::launch_scatter(topk_idx, topk_w, T, E, k, offsets, pos, src,
-                          topk_w ? w_perm : nullptr, x, row_bytes, x_perm,
-                          mx ? x_scales : nullptr, mx ? d / 32 : 0,
-                          mx ? x_perm_scales : nullptr, workspace, stream);
-  return hip_status(e, "moe_permute/scatter");
+  return permute_launch(prec, topk_idx, topk_w, T, E, k, x, x_scales, d,
+                        counts, offsets, pos, src, w_perm, x_perm,
+                        x_perm_scales, workspace, stream);
+}
+
+moe_status moe_permute_noalloc(moe_prec prec, const int32_t* topk_idx,
+                               const float* topk_w, int64_t T, int32_t E,
+                               int32_t k, const void* x,
+                               const uint8_t* x_scales, int64_t d,
+                               int32_t* counts, int32_t* offsets,
+                               int32_t* pos, int32_t* src, float* w_perm,
+                               void* x_perm, uint8_t* x_perm_scales,
+                               hipStream_t stream) {
+  if (moe_status st = permute_check(prec, topk_idx, topk_w, T, E, k, x,
+                                    x_scales, d, counts, offsets, pos, src,
+                                    w_perm, x_perm, x_perm_scales))
+    return st;
+  const size_t need = moe::plan_workspace_bytes(T * k, E);
+  REQUIRE(need <= MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+          "moe_permute_noalloc: the plan of T*k = %lld slots over E = %d "
+          "experts needs %zu bytes of scratch, above its %zu-byte limit "
+          "(use moe_permute with a workspace)",
+          static_cast<long long>(T) * k, E, need,
+          static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (moe_status st = scratch_of_current_device(&ws)) return st;
+  return permute_launch(prec, topk_idx, topk_w, T, E, k, x, x_scales, d,
+                        counts, offsets, pos, src, w_perm, x_perm,
+                        x_perm_scales, ws, stream);
 }
 
 moe_status moe_permute_rows(moe_prec prec, const int32_t* pos, int64_t T,

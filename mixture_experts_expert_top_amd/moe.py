@@ -33,8 +33,10 @@ EXPORTED = [
     "moe_gate_up_dgrad", "moe_grouped_wgrad", "moe_dp_reduce",
     "moe_row_planes", "moe_mx_gate_up_swiglu_fwd", "moe_mx_down_fwd",
     "moe_mx_down_swiglu_bwd", "moe_mx_gate_up_dgrad", "moe_mx_grouped_wgrad",
-    "moe_router_backward", "moe_mxfp4_quantize",
+    "moe_router_backward", "moe_mxfp4_quantize", "moe_permute_noalloc",
 ]
+# fixed per-GPU scratch of moe_permute_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class MoeError(RuntimeError):
@@ -59,6 +61,8 @@ def _load():
         "moe_route": (I32, [P, I64, I32, I32, I32, P, P, P]),
         "moe_permute": (I32, [I32, P, P, I64, I32, I32, P, P, I64, P, P, P,
                               P, P, P, P, P, SZ, P]),
+        "moe_permute_noalloc": (I32, [I32, P, P, I64, I32, I32, P, P, I64,
+                                      P, P, P, P, P, P, P, P]),
         "moe_permute_rows": (I32, [I32, P, I64, I32, P, P, I64, P, P, P]),
         "moe_grouped_mlp_fwd": (I32, [I32, P, P, P, I32, I64, I64, I64, P, P,
                                       P, P, P, P, P, P, P, P, I64, P, SZ,
@@ -206,8 +210,8 @@ def moe_router_backward(logits, topk_idx, topk_w, dp, counts, aux_coef,
         _p(workspace), nbytes, _stream(stream)))
 
 
-def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
-                src, w_perm, x_perm, x_perm_scales, workspace, stream=None):
+def _permute_args(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets,
+                  pos, src, w_perm, x_perm, x_perm_scales):
     T, k = topk_idx.shape
     xdt, per = _act(prec, x, "x")
     w = x.shape[1]
@@ -223,12 +227,28 @@ def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
                       ("pos", pos, (T, k)), ("src", src, (T * k,))):
         _want(t, n, torch.int32, shp)
     _want(w_perm, "w_perm", torch.float32, (T * k,), allow_none=True)
+    return (prec, _p(topk_idx), _p(topk_w), T, E, k, _p(x), _p(x_scales), d,
+            _p(counts), _p(offsets), _p(pos), _p(src), _p(w_perm), _p(x_perm),
+            _p(x_perm_scales))
+
+
+def moe_permute(prec, topk_idx, topk_w, E, x, x_scales, counts, offsets, pos,
+                src, w_perm, x_perm, x_perm_scales, workspace, stream=None):
+    args = _permute_args(prec, topk_idx, topk_w, E, x, x_scales, counts,
+                         offsets, pos, src, w_perm, x_perm, x_perm_scales)
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
-    _check("moe_permute", lib.moe_permute(
-        prec, _p(topk_idx), _p(topk_w), T, E, k, _p(x), _p(x_scales), d,
-        _p(counts), _p(offsets), _p(pos), _p(src), _p(w_perm), _p(x_perm),
-        _p(x_perm_scales), _p(workspace), nbytes, _stream(stream)))
+    _check("moe_permute", lib.moe_permute(*args, _p(workspace), nbytes,
+                                          _stream(stream)))
+
+
+def moe_permute_noalloc(prec, topk_idx, topk_w, E, x, x_scales, counts,
+                        offsets, pos, src, w_perm, x_perm, x_perm_scales,
+                        stream=None):
+    args = _permute_args(prec, topk_idx, topk_w, E, x, x_scales, counts,
+                         offsets, pos, src, w_perm, x_perm, x_perm_scales)
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(*args,
+                                                          _stream(stream)))
 
 
 def moe_permute_rows(prec, pos, x, x_scales, x_perm, x_perm_scales,

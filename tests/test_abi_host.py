@@ -87,6 +87,23 @@ def test_permute_validation():
     assert _permute(ws=None) == INVALID
 
 
+def test_permute_noalloc_validation():
+    # prec, topk_idx, topk_w, T, E, k, x, x_scales, d, counts, offsets, pos,
+    # src, w_perm, x_perm, x_perm_scales, stream
+    def call(T=64, E=4, k=2, d=32, prec=BF16, w=A):
+        return L.moe_permute_noalloc(prec, A, w, T, E, k, A, None, d, A, A,
+                                     A, A, w, A, None, None)
+    assert call(d=12) == INVALID
+    assert call(T=0) == INVALID
+    # a plan whose per-chunk counts exceed the fixed scratch is refused on
+    # the host, before any launch, with a message naming the limit
+    need = L.moe_workspace_bytes(0, BF16, 1 << 20, 1024, 8, 32, 32)
+    assert need > moe.NOALLOC_SCRATCH_BYTES
+    assert call(T=1 << 20, E=1024, k=8) == UNSUP
+    msg = L.moe_last_error()
+    assert b"scratch" in msg and str(moe.NOALLOC_SCRATCH_BYTES).encode() in msg
+
+
 def test_workspace_sizes():
     assert L.moe_workspace_bytes(0, BF16, 8192, 8, 2, 4096, 14336) > 0
     assert L.moe_workspace_bytes(1, BF16, 8192, 8, 2, 4096, 14336) == 0
