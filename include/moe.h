@@ -37,9 +37,13 @@
  *    moe_status, launches nothing and leaves every output untouched;
  *    moe_last_error() then describes the failure (thread-local).  A failed
  *    kernel launch returns MOE_ERR_HIP.  No exception crosses the ABI.
- *  - Limits: 1 <= k <= E <= 1024, k <= 32, T >= 1, d and f >= 8 and
- *    multiples of 8 (bf16) or of 32 (MXFP8); every tensor smaller than
- *    2 GiB.
+ *  - Limits: 1 <= k <= E <= 1024, k <= 32, T >= 1, T*k < 2^31, d and
+ *    f >= 8 and multiples of 8 (bf16) or of 32 (MXFP8).  Sizes are bound
+ *    per buffer resource, not per tensor: one expert's weight, and for the
+ *    weight gradients T*k rows of 2f (bf16) values, or a token-axis MX
+ *    operand, must each stay within 4 GiB; x and the router weight within
+ *    2 GiB.  (The Mixtral shape, d = 4096 and f = 14336, runs up to about
+ *    T*k = 74,000 rows a call.)
  *  - Deterministic: identical inputs give bitwise identical outputs (no
  *    floating-point atomics; all reductions run in a fixed order).
  */
@@ -180,15 +184,16 @@ moe_status moe_permute(moe_prec prec, const int32_t* topk_idx,
  * arguments (minus workspace), outputs and errors as moe_permute.  Its
  * scratch (the plan's per-chunk counts) is a fixed array of
  * MOE_NOALLOC_SCRATCH_BYTES in device memory, one copy per GPU, held until
- * the process ends; the call allocates and frees nothing.  A plan that
- * needs more than that (moe_workspace_bytes(MOE_ENTRY_PERMUTE, ...) above
- * the limit) is rejected with MOE_ERR_UNSUPPORTED before any launch.  The
+ * the process ends; the call allocates and frees nothing.  The plan uses
+ * at most 512 chunks, so every valid (T*k, E) fits (at most 512 * E * 4
+ * bytes); a plan needing more than the limit would be rejected with
+ * MOE_ERR_UNSUPPORTED before any launch.  The
  * kernels write every scratch word they read, so nothing is cleared
  * between calls.  Every call on one GPU shares that GPU's scratch: calls
  * that overlap on one GPU (concurrent streams, or threads) race and give
  * undefined results; calls ordered on one stream are safe.
  */
-#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES (2u << 20)
 moe_status moe_permute_noalloc(moe_prec prec, const int32_t* topk_idx,
                                const float* topk_w, int64_t T, int32_t E,
                                int32_t k, const void* x,

@@ -11,7 +11,6 @@ typedef uint16_t bf16_t;
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
-constexpr int kPlanChunk = 512;   // slots per block of the counting pass
 // fp32 row outputs of the down projection and of the gate_up data
 // gradient are written as this many partial-sum planes [planes][T*k][d]
 // (split reduction); the combine adds them in plane order.

@@ -23,20 +23,35 @@ __device__ __forceinline__ int clamp_expert(int e, int E) {
 }
 
 // ---------------------------------------------------------------- plan
-// Pass 1: one wavefront per chunk of kPlanChunk slots walks its chunk in
-// 64-slot steps.  For each step the lanes that share an expert id are
-// grouped with ballots; a lane's rank is the number of lower lanes in its
-// group plus the chunk's running count of that expert (LDS).  The rank
-// within the chunk is stashed in pos; the chunk's counts go to ws.
-__global__ __launch_bounds__(64) void plan_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t TK, int E,
-    int32_t* __restrict__ rank_out, int32_t* __restrict__ chunk_counts) {
-  __shared__ int cnt[kMaxExperts];
-  const int lane = threadIdx.x;
+// Pass 1: every wavefront ranks one chunk of `chunk` slots (a multiple of
+// 64, see plan_chunk) in 64-slot steps.  For each step the lanes that share
+// an expert id are grouped with ballots; a lane's rank is the number of
+// lower lanes in its group plus the chunk's running count of that expert
+// (the wave's own LDS row).  The rank within the chunk is stashed in pos;
+// the chunk's counts go to ws.  Four waves a workgroup, each on its own
+// chunk and LDS row, so only wave-level ordering is needed.
+constexpr int kRankWaves = 4;
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(64 * kRankWaves) void plan_rank_kernel(
+    const int32_t* __restrict__ idx, int64_t TK, int E, int chunk,
+    int nchunks, int32_t* __restrict__ rank_out,
+    int32_t* __restrict__ chunk_counts) {
+  __shared__ int cnt_all[kRankWaves][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int c = blockIdx.x * kRankWaves + w;
+  if (c >= nchunks) return;                     // whole wave
+  int* cnt = cnt_all[w];
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  __syncthreads();
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kPlanChunk;
-  const int64_t c1 = min(TK, c0 + kPlanChunk);
+  wave_sync_lds();
+  const int64_t c0 = static_cast<int64_t>(c) * chunk;
+  const int64_t c1 = min(TK, c0 + chunk);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t s0 = c0; s0 < c1; s0 += 64) {
     const int64_t s = s0 + lane;
@@ -55,13 +70,13 @@ __global__ __launch_bounds__(64) void plan_rank_kernel(
       active &= ~mask;
     }
     const int base = valid ? cnt[e] : 0;
-    __syncthreads();
+    wave_sync_lds();
     if (valid && rank == grp - 1) cnt[e] = base + grp;
     if (valid) rank_out[s] = base + rank;
-    __syncthreads();
+    wave_sync_lds();
   }
   for (int e = lane; e < E; e += 64)
-    chunk_counts[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+    chunk_counts[static_cast<int64_t>(c) * E + e] = cnt[e];
 }
 
 // Pass 2: one workgroup.  Each expert's column of chunk counts is turned
@@ -159,7 +174,7 @@ __device__ __forceinline__ void copy_row1(const uint8_t* __restrict__ src,
 // token's row (and side bytes) copied to its k permuted rows.
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int k,
-    int E, const int32_t* __restrict__ offsets,
+    int E, int chunk, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ chunk_base, int32_t* __restrict__ pos,
     int32_t* __restrict__ src, float* __restrict__ w_perm,
     const uint8_t* __restrict__ x, int64_t row_bytes, uint8_t* __restrict__ xp,
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     const int j = threadIdx.x;
     const int64_t s = t * k + j;
     const int e = clamp_expert(idx[s], E);
-    const int64_t c = s / kPlanChunk;
+    const int64_t c = s / chunk;
     const int p = offsets[e] + chunk_base[c * E + e] + pos[s];
     pos[s] = p;
     src[p] = static_cast<int32_t>(t);
@@ -295,8 +310,19 @@ __global__ __launch_bounds__(256) void dp_reduce_kernel(
 
 }  // namespace
 
+// Slots per chunk of the counting pass: a power of two at least 64, E and
+// Tk / 512.  So there are at most 512 chunks (their counts fill at most
+// 512 * E * 4 bytes, 2 MiB at E = 1024), and each wave ranks few 64-slot
+// steps while the small problems still spread over many waves.
+int plan_chunk(int64_t Tk, int E) {
+  int64_t c = 64;
+  while (c < E || c * 512 < Tk) c <<= 1;
+  return static_cast<int>(c);
+}
+
 size_t plan_workspace_bytes(int64_t Tk, int E) {
-  const int64_t nchunks = (Tk + kPlanChunk - 1) / kPlanChunk;
+  const int64_t chunk = plan_chunk(Tk, E);
+  const int64_t nchunks = (Tk + chunk - 1) / chunk;
   return static_cast<size_t>(nchunks * E * sizeof(int32_t));
 }
 
@@ -304,14 +330,17 @@ hipError_t launch_plan(const int32_t* idx, int64_t T, int E, int k,
                        int32_t* counts, int32_t* offsets, int32_t* pos,
                        void* ws, hipStream_t s) {
   const int64_t TK = T * k;
-  const int nchunks = static_cast<int>((TK + kPlanChunk - 1) / kPlanChunk);
-  int32_t* chunk = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(plan_rank_kernel, dim3(nchunks), dim3(64), 0, s, idx, TK,
-                     E, pos, chunk);
+  const int chunk = plan_chunk(TK, E);
+  const int nchunks = static_cast<int>((TK + chunk - 1) / chunk);
+  int32_t* chunk_counts = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(plan_rank_kernel,
+                     dim3((nchunks + kRankWaves - 1) / kRankWaves),
+                     dim3(64 * kRankWaves), 0, s, idx, TK, E, chunk, nchunks,
+                     pos, chunk_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, chunk,
-                     nchunks, E, counts, offsets);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s,
+                     chunk_counts, nchunks, E, counts, offsets);
   return hipGetLastError();
 }
 
@@ -322,7 +351,7 @@ hipError_t launch_scatter(const int32_t* idx, const float* topk_w, int64_t T,
                           int64_t side_bytes, void* side_perm, const void* ws,
                           hipStream_t s) {
   hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>(T)), dim3(256),
-                     0, s, idx, topk_w, k, E, offsets,
+                     0, s, idx, topk_w, k, E, plan_chunk(T * k, E), offsets,
                      static_cast<const int32_t*>(ws), pos, src, w_perm,
                      static_cast<const uint8_t*>(x), row_bytes,
                      static_cast<uint8_t*>(x_perm),

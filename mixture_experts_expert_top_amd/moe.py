@@ -36,7 +36,7 @@ EXPORTED = [
     "moe_router_backward", "moe_mxfp4_quantize", "moe_permute_noalloc",
 ]
 # fixed per-GPU scratch of moe_permute_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
-NOALLOC_SCRATCH_BYTES = 8 << 20
+NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
 class MoeError(RuntimeError):

@@ -95,13 +95,13 @@ def test_permute_noalloc_validation():
                                      A, A, w, A, None, None)
     assert call(d=12) == INVALID
     assert call(T=0) == INVALID
-    # a plan whose per-chunk counts exceed the fixed scratch is refused on
-    # the host, before any launch, with a message naming the limit
-    need = L.moe_workspace_bytes(0, BF16, 1 << 20, 1024, 8, 32, 32)
-    assert need > moe.NOALLOC_SCRATCH_BYTES
-    assert call(T=1 << 20, E=1024, k=8) == UNSUP
-    msg = L.moe_last_error()
-    assert b"scratch" in msg and str(moe.NOALLOC_SCRATCH_BYTES).encode() in msg
+    # the plan never needs more scratch than the fixed array holds: at most
+    # 512 chunks of E counts, for every valid T*k and E
+    for tk, E in ((1, 1), (16384, 8), (131072, 64), ((1 << 31) - 1, 1024),
+                  (1 << 20, 1024), (1 << 30, 3)):
+        need = L.moe_workspace_bytes(0, BF16, tk, E, 1, 32, 32)
+        assert 0 < need <= moe.NOALLOC_SCRATCH_BYTES
+        assert need <= 512 * E * 4
 
 
 def test_workspace_sizes():
@@ -136,8 +136,9 @@ def test_mlp_fwd_validation():
     f = L.moe_grouped_mlp_fwd
     # f not a multiple of 8
     assert f(*_fwd_args(f=60), 0, None) == INVALID
-    # too large for 32-bit buffer offsets
-    assert f(*_fwd_args(E=8, Tk=1 << 20, d=4096, f=14336), 0, None) == UNSUP
+    # one expert's weight beyond one buffer resource's 4 GiB range
+    assert f(*_fwd_args(E=1, Tk=64, d=1 << 16, f=1 << 16), 0, None) == UNSUP
+    assert b"4 GiB" in L.moe_last_error()
     bad = _fwd_args()
     bad[1] = None
     assert f(*bad, 0, None) == INVALID
@@ -155,6 +156,14 @@ def test_mlp_bwd_validation():
     assert f(*_bwd_args(s=None), ws, None) == INVALID
     assert f(*_bwd_args(s_tok=A, s_tok_scales=A, ldt=640), ws,
              None) == INVALID                               # bf16 + codes
+    # the weight gradients read up to T*k rows of 2f values through one
+    # resource: the Mixtral shape is accepted at T = 32768 and refused at
+    # T = 2^17 (before the workspace is looked at)
+    big = L.moe_workspace_bytes(2, BF16, 1 << 17, 8, 2, 4096, 14336)
+    assert f(*_bwd_args(T=1 << 17, k=2, E=8, d=4096, f=14336), big,
+             None) == UNSUP
+    assert f(*_bwd_args(T=1 << 15, k=2, E=8, d=4096, f=14336), 0,
+             None) == WS
 
 
 def test_mx_mlp_validation():

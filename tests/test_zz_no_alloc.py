@@ -74,19 +74,3 @@ def test_noalloc_permute_matches_workspace_permute(prec):
             b = got[n].view(torch.uint8).cpu().numpy()
             np.testing.assert_array_equal(b, a, err_msg=f"{n} T={T} E={E}")
         assert int(got["offsets"][-1]) == T * k
-
-
-@gpu
-def test_noalloc_permute_rejects_plans_beyond_its_scratch():
-    dev = torch.device("cuda:0")
-    T, E, k, d = 1 << 20, 1024, 8, 32
-    need = moe.moe_workspace_bytes(0, 0, T, E, k, d, 64)
-    assert need > moe.NOALLOC_SCRATCH_BYTES
-    # the size check happens on the host before anything is launched
-    idx = torch.zeros(T, k, dtype=torch.int32, device=dev)
-    x = torch.zeros(T, d, dtype=torch.bfloat16, device=dev)
-    o = _outputs(T, E, k, d, x, 0, dev)
-    with pytest.raises(moe.MoeError, match="scratch"):
-        moe.moe_permute_noalloc(0, idx, None, E, x, None, o["counts"],
-                                o["offsets"], o["pos"], o["src"], None,
-                                o["x_perm"], None)
