@@ -35,6 +35,11 @@ moe_status hip_status(hipError_t e, const char* where) {
 }
 
 constexpr int64_t kMaxBytes = (int64_t{1} << 31) - 1;
+// Largest byte range of one buffer resource (32-bit offsets).  The grouped
+// GEMMs bound each resource by what one workgroup touches: the rows of one
+// tile (row-segmented GEMMs), one expert's weight, one expert's rows of a
+// weight-gradient operand, or one token-axis MX operand.
+constexpr int64_t kMaxRange = (int64_t{1} << 32) - 1;
 
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -106,9 +111,8 @@ moe_status check_mlp_dims(int32_t E, int64_t Tk, int64_t d, int64_t f,
   REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
   if (moe_status st = check_feature("d", d, prec)) return st;
   if (moe_status st = check_feature("f", f, prec)) return st;
-  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
-              2 * f * d * 2 <= kMaxBytes,
-          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  REQUIRE(2 * f * d * 2 <= kMaxRange, MOE_ERR_UNSUPPORTED,
+          "one expert's weight is larger than 4 GiB");
   return MOE_OK;
 }
 
@@ -529,9 +533,8 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
   REQUIRE(Tk >= 1, MOE_ERR_INVALID_ARG, "Tk must be >= 1");
   if (moe_status st = check_feature("d", d, prec)) return st;
   if (moe_status st = check_feature("f", f, prec)) return st;
-  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
-              2 * f * d * 2 <= kMaxBytes,
-          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  REQUIRE(2 * f * d * 2 <= kMaxRange, MOE_ERR_UNSUPPORTED,
+          "one expert's weight is larger than 4 GiB");
   if (is_mx(prec)) {
     if (moe_status st = check_mx_dims(d, f)) return st;
     REQUIRE_PTR(x_perm_scales);
@@ -606,9 +609,13 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
   if (moe_status st = check_feature("d", d, prec)) return st;
   if (moe_status st = check_feature("f", f, prec)) return st;
   const int64_t Tk = T * k;
-  REQUIRE(Tk * 2 * f * 2 <= kMaxBytes && Tk * d * 4 <= kMaxBytes &&
-              2 * f * d * 2 <= kMaxBytes,
-          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+  // the weight gradients read each expert's rows of dAB (2f wide) and of
+  // the permuted x / dO (d wide) through one resource; an expert may hold
+  // every row
+  REQUIRE(2 * f * d * 2 <= kMaxRange && Tk * 2 * f * 2 <= kMaxRange &&
+              Tk * d * 2 <= kMaxRange,
+          MOE_ERR_UNSUPPORTED,
+          "T*k rows of 2f bf16 values, or one expert's weight, exceed 4 GiB");
   const BwdWorkspace L = bwd_layout(Tk, f);
   if (is_mx(prec)) {
     if (moe_status st = check_mx_dims(d, f)) return st;
@@ -620,8 +627,8 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
             static_cast<long long>(padded_tokens(Tk, E)),
             static_cast<long long>(ldt));
     const MxBwdWorkspace X = mx_bwd_layout(Tk, E, d, f, mx_bwd_base(Tk, f));
-    REQUIRE(2 * f * X.tk_pad <= kMaxBytes && E * 2 * f * d <= kMaxBytes,
-            MOE_ERR_UNSUPPORTED, "MX operand larger than 2 GiB");
+    REQUIRE(2 * f * X.tk_pad <= kMaxRange && E * 2 * f * d <= kMaxRange,
+            MOE_ERR_UNSUPPORTED, "MX operand larger than 4 GiB");
     REQUIRE(workspace_bytes >= X.total, MOE_ERR_WORKSPACE,
             "workspace too small: %zu < %zu bytes", workspace_bytes, X.total);
     REQUIRE_PTR(workspace);
@@ -838,9 +845,9 @@ moe_status moe_grouped_wgrad(const void* a, int64_t lda, const void* b,
   if (moe_status st = check_feature("N", N, MOE_BF16)) return st;
   REQUIRE(lda >= M && lda % 8 == 0 && ldb >= N && ldb % 8 == 0,
           MOE_ERR_INVALID_ARG, "need lda >= M, ldb >= N, both multiples of 8");
-  REQUIRE(Tk * lda * 2 <= kMaxBytes && Tk * ldb * 2 <= kMaxBytes &&
+  REQUIRE(Tk * lda * 2 <= kMaxRange && Tk * ldb * 2 <= kMaxRange &&
               M * N * 2 * static_cast<int64_t>(E) <= kMaxBytes * 8,
-          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+          MOE_ERR_UNSUPPORTED, "operand rows of one expert exceed 4 GiB");
   return hip_status(
       moe::gemm_wgrad(static_cast<const bf16_t*>(a), lda,
                       static_cast<const bf16_t*>(b), ldb, offsets, E, Tk, M, N,
@@ -958,9 +965,9 @@ moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
           MOE_ERR_INVALID_ARG,
           "ldt must be a multiple of %d and >= moe_mxfp8_padded_rows(Tk, E)",
           moe::kMxPad);
-  REQUIRE(M * ldt <= kMaxBytes && N * ldt <= kMaxBytes &&
+  REQUIRE(M * ldt <= kMaxRange && N * ldt <= kMaxRange &&
               M * N * 2 * static_cast<int64_t>(E) <= kMaxBytes * 8,
-          MOE_ERR_UNSUPPORTED, "tensor larger than 2 GiB");
+          MOE_ERR_UNSUPPORTED, "token-axis operand larger than 4 GiB");
   return hip_status(moe::gemm_mx_wgrad(aq, as, bq, bs, b_fp4 != 0, ldt,
                                        offsets, E, M, N,
                                        static_cast<bf16_t*>(c), stream),

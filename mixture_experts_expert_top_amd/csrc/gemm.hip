@@ -93,6 +93,10 @@ constexpr int kStageElems = 2 * kTileElems;
 constexpr int kGroupN = 4;                // n-tiles per scheduling group
 constexpr int kGroupM = 8;                // m-tiles per block of a group
 constexpr int kEpiRows = 64;              // rows per epilogue pass of a wave
+#ifndef MOE_INDEP_LOOP
+#define MOE_INDEP_LOOP 1
+#endif
+constexpr bool kIndepLoop = MOE_INDEP_LOOP != 0;
 
 enum Mode { kSegM = 0, kSegK = 1, kSegKT = 2 };
 enum Epi { kStore = 0, kSwiglu = 1, kDSwiglu = 2, kStoreF32 = 3 };
@@ -251,11 +255,14 @@ struct Mover<true> {
   }
 };
 
-// MN-contiguous operand: 64 k-rows x 256 columns as 256 blocks of 8x8;
-// thread t loads block t (k = kr*8 + i, i = 0..7 is piece i; columns
-// colbase + mc*8 .. +7) and transposes it so that each column's 8 k-values
-// become one LDS chunk (part 0 writes columns 0-3 of the block, part 1
-// columns 4-7).
+// MN-contiguous operand: 64 k-rows x 256 columns, kept in LDS as it lies
+// in memory ([k][mn], 512-byte rows) and transposed by the fragment reads
+// (ds_read_b64_tr_b16, see frag_tr).  Thread t moves the 16-byte column
+// chunk t % 32 of k-rows 8 (t / 32) + i, i = 0..7 (piece i); part 0 holds
+// pieces 0-3, part 1 pieces 4-7.  Chunk c of k-row r sits at chunk
+// c ^ ((r & 3) << 2) of its row: the 64 lanes of a store write two rows'
+// 32 chunks and the 64 lanes of a transposed read touch 8 rows x 4 chunks,
+// both spread evenly over the LDS banks.
 template <>
 struct Mover<false> {
   uint32_t tpart;   // (kr*8 * ld + mc*8) * 2
@@ -276,21 +283,40 @@ struct Mover<false> {
   }
   __device__ __forceinline__ static void store(const i32x4* v, bf16_t* lds,
                                                int t, int part) {
-    const int kr = t >> 5, mc = t & 31;
-    // v[i] holds k = kr*8+i, columns mc*8+0..7 (dword q: columns 2q, 2q+1)
+    const int kr0 = (t >> 5) * 8, cc = t & 31;
 #pragma unroll
-    for (int m = 4 * part; m < 4 * part + 4; ++m) {
-      const int q = m >> 1;
-      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-      i32x4 o;
-      o[0] = perm_b32(v[1][q], v[0][q], sel);
-      o[1] = perm_b32(v[3][q], v[2][q], sel);
-      o[2] = perm_b32(v[5][q], v[4][q], sel);
-      o[3] = perm_b32(v[7][q], v[6][q], sel);
-      *reinterpret_cast<i32x4*>(lds + lds_off(mc * 8 + m, kr)) = o;
+    for (int i = 4 * part; i < 4 * part + 4; ++i) {
+      const int kr = kr0 + i;
+      *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(lds) + kr * 512 +
+                                ((cc ^ ((kr & 3) << 2)) << 4)) = v[i];
     }
   }
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA 32x32x16 fragment (lane l: column l % 32, k = 8 (l / 32) + 0..7 of
+// k-slice kk) of a [k][mn] LDS tile laid out by Mover<false>, for the 32
+// columns starting at 32 * blk.  ds_read_b64_tr_b16 works on groups of 16
+// lanes: lane 4R + m of a group gives the address of 4 consecutive
+// elements, which become columns 4m..4m+3 of row R of a 4 x 16 block, and
+// lane j receives column j (rows 0..3).  Group g = l / 16 of the fragment
+// covers k-rows 8 (g / 2) + 0..3 (first read) and + 4..7 (second read,
+// 2048 bytes on) and columns 16 (g % 2) + 0..15.  lane_base holds the
+// lane's part of the address (its row and chunk inside the block).
+__device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
+                                            int R, int blk, int kk) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(tile) + lane_base +
+                     ((blk ^ R) << 6) + kk * 8192;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(p + 2048));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_v, v);
+}
 
 // E2M1 codes two a byte -> E4M3 codes one a byte, exactly (every E2M1
 // value is an E4M3 value): through f16 with gfx950's scaled conversions at
@@ -594,9 +620,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   __amdgpu_buffer_rsrc_t rsA, rsB;
   // MX scale bytes (empty resources in the bf16 kernels)
   __amdgpu_buffer_rsrc_t rsSA = make_rsrc(P.sA, 0), rsSB = make_rsrc(P.sB, 0);
+  // SegM: the A resource starts at the tile's first row and spans only the
+  // expert's rows inside the tile (at most BM rows), so no tensor size
+  // limits its 32-bit offsets; rows past the expert read as zero.
+  const int a_row0 = (MODE == kSegM) ? 0 : m0;
   if (MODE == kSegM) {
-    const bf16_t* a = P.A + seg0 * P.lda;
-    const int64_t bytes = (P.Tk - seg0) * P.lda * 2;
+    const int tile_rows = min(BM, seg_len - m0);
+    const bf16_t* a = P.A + (seg0 + m0) * P.lda;
+    const int64_t bytes = static_cast<int64_t>(tile_rows) * P.lda * 2;
     rsA = make_rsrc(a, static_cast<uint32_t>(bytes));
     const bf16_t* b = P.B + static_cast<int64_t>(e) * P.b_stride;
     // MX B may be a column range of a transposed weight: bound it by the
@@ -606,8 +637,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
            : static_cast<int64_t>(P.b_rows) * P.ldb * 2;
     rsB = make_rsrc(b, static_cast<uint32_t>(bbytes));
     if (MX) {
-      rsSA = make_rsrc(P.sA + seg0 * P.lds_a,
-                       static_cast<uint32_t>((P.Tk - seg0) * P.lds_a));
+      rsSA = make_rsrc(P.sA + (seg0 + m0) * P.lds_a,
+                       static_cast<uint32_t>(tile_rows * P.lds_a));
       rsSB = make_rsrc(
           P.sB + static_cast<int64_t>(e) * P.bs_stride,
           static_cast<uint32_t>((static_cast<int64_t>(P.b_rows) - 1) *
@@ -631,7 +662,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   // indices.
   const int f = P.f;
   const int n0g = nt * (BN / 2);
-  auto blk_a = [&](int i) -> int64_t { return m0 + 32 * i; };
+  auto blk_a = [&](int i) -> int64_t { return a_row0 + 32 * i; };
   auto blk_b = [&](int i) -> int64_t {
     if (EPI == kSwiglu) {
       constexpr int half = BJ / 2;
@@ -673,21 +704,35 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   auto atile = [&](int st) { return smem + st * kTileElems; };
   auto btile = [&](int st) { return smem + (2 + st) * kTileElems; };
 
+  // Transposed fragment reads (MN-contiguous operands): the lane's fixed
+  // part of the address, see frag_tr.
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int tr_R = tr_j >> 2, tr_m = tr_j & 3;
+  const int tr_base = ((tr_g >> 1) * 8 + tr_R) * 512 +
+                      (2 * (tr_g & 1) + (tr_m >> 1)) * 16 + (tr_m & 1) * 8;
   // bf16 fragments of k-slice kk (16 wide) of one LDS stage.
   auto read_frags = [&](int st, int kk, bf16x8_v* af, bf16x8_v* bf) {
     const bf16_t* sa = atile(st);
     const bf16_t* sb = btile(st);
     const int chunk = kk * 2 + fk;
 #pragma unroll
-    for (int i = 0; i < BI; ++i)
-      af[i] = __builtin_bit_cast(
-          bf16x8_v, *reinterpret_cast<const i32x4*>(
-                        sa + lds_off(wm * TM + i * 32 + fr, chunk)));
+    for (int i = 0; i < BI; ++i) {
+      if constexpr (AKC)
+        af[i] = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const i32x4*>(
+                          sa + lds_off(wm * TM + i * 32 + fr, chunk)));
+      else
+        af[i] = frag_tr(sa, tr_base, tr_R, wm * (TM / 32) + i, kk);
+    }
 #pragma unroll
-    for (int j = 0; j < BJ; ++j)
-      bf[j] = __builtin_bit_cast(
-          bf16x8_v, *reinterpret_cast<const i32x4*>(
-                        sb + lds_off(wn * TN + j * 32 + fr, chunk)));
+    for (int j = 0; j < BJ; ++j) {
+      if constexpr (BKC)
+        bf[j] = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const i32x4*>(
+                          sb + lds_off(wn * TN + j * 32 + fr, chunk)));
+      else
+        bf[j] = frag_tr(sb, tr_base, tr_R, wn * (TN / 32) + j, kk);
+    }
   };
   auto mfmas = [&](const bf16x8_v* af, const bf16x8_v* bf) {
 #pragma unroll
@@ -747,15 +792,21 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   //     refilled with half p of stage kt+2, so a load has a whole
   //     iteration to land; the last slice's MFMAs are issued after the
   //     barrier, behind the first LDS reads of the next stage.
-  //   * transposing movers (storing either half reads all registers):
-  //     stage kt+2 is loaded in slices 2 and 3, after both stores, and the
-  //     barrier follows the last MFMAs (measured faster for these).
+  //   * the other schedule (kept selectable): stage kt+2 is loaded in
+  //     slices 2 and 3, after both stores, and the barrier follows the
+  //     last MFMAs.
+  // Both movers keep the halves of a stage in separate registers, so the
+  // first schedule serves every layout.
   // Loads past K return zeros and the one stray store of the last
   // iteration lands in the buffer no one reads any more.
   auto kloop = [&](auto&& gload, auto&& lstore, auto indep_halves) {
     constexpr bool kIndep = decltype(indep_halves)::value;
     constexpr int kMf = BI * BJ;                   // MFMAs per k-slice
-    constexpr int kRd = BI + BJ;                   // fragment reads per slice
+    // fragment reads per slice (a transposed fragment takes two)
+    constexpr int kRd = BI * (AKC ? 1 : 2) + BJ * (BKC ? 1 : 2);
+    // LDS reads placed after MFMA i of a slice: kRd spread evenly (one
+    // more after each of the first kRd % kMf)
+    constexpr int kRdLo = kRd / kMf, kRdHi = kRdLo + 1, kRdN = kRd % kMf;
     constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per half stage
     bf16x8_v a0[BI], b0[BJ], a1[BI], b1[BJ];
     if (nk > 0) {
@@ -780,7 +831,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
-        if (i < kRd) sched_group(kSgDsRead, 1);
+        if (i < kRdN) sched_group(kSgDsRead, kRdHi);
+        else if (kRdLo > 0) sched_group(kSgDsRead, kRdLo);
         if (i < kMv) sched_group(kSgDsWrite, 1);
         if (kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
@@ -792,7 +844,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
-        if (i < kRd) sched_group(kSgDsRead, 1);
+        if (i < kRdN) sched_group(kSgDsRead, kRdHi);
+        else if (kRdLo > 0) sched_group(kSgDsRead, kRdLo);
         if (i < kMv) sched_group(kSgDsWrite, 1);
         if (kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
@@ -804,7 +857,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
         sched_group(kSgMfma, 1);
-        if (i < kRd) sched_group(kSgDsRead, 1);
+        if (i < kRdN) sched_group(kSgDsRead, kRdHi);
+        else if (kRdLo > 0) sched_group(kSgDsRead, kRdLo);
         if (!kIndep && i < kMv) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -817,7 +871,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   #pragma unroll
         for (int i = 0; i < kMf; ++i) {
           sched_group(kSgMfma, 1);
-          if (i < kRd) sched_group(kSgDsRead, 1);
+          if (i < kRdN) sched_group(kSgDsRead, kRdHi);
+        else if (kRdLo > 0) sched_group(kSgDsRead, kRdLo);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
@@ -856,7 +911,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     constexpr int kAH = BI / kHalves;             // A fragments held at once
     constexpr int kMfH = kAH * BJ;                // MFMAs per half-slice
     constexpr int kMv = C::kSplitLoad ? 4 : 8;    // moves per part
-    const uint32_t srow_a = static_cast<uint32_t>((m0 + lt) * P.lds_a);
+    const uint32_t srow_a = static_cast<uint32_t>((a_row0 + lt) * P.lds_a);
     const uint32_t srow_b =
         static_cast<uint32_t>((blk_b(lt >> 5) + (lt & 31)) * P.lds_b);
     uint32_t vsa = 0, vsb = 0;
@@ -1026,10 +1081,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       kloop_mx(std::false_type{});
     }
   } else if constexpr (C::kSplitLoad && AKC != BKC) {
-    if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<AKC>{});
-    else kloop(gload_b, lstore_b, std::bool_constant<BKC>{});
+    if (mv_a) kloop(gload_a, lstore_a, std::bool_constant<kIndepLoop>{});
+    else kloop(gload_b, lstore_b, std::bool_constant<kIndepLoop>{});
   } else {
-    kloop(gload, lstore, std::bool_constant<AKC && BKC>{});
+    kloop(gload, lstore, std::bool_constant<kIndepLoop>{});
   }
 
   // ---------------------------------------------------------- epilogue

@@ -12,6 +12,7 @@ skewed variant; all values synthetic, no dataset or trained weight):
 
   tiny      T=64    d=32   f=64    E=4  k=2
   mixtral   T=8192  d=4096 f=14336 E=8  k=2           (forward / fwd+bwd)
+  mixtral_long T=32768, otherwise the same (fwd+bwd)
   finegrain T=16384 d=2048 f=1408  E=64 k=8  router bias -2*ln(rank)
   mxfp8     T=16384 d=4096 f=14336 E=8  k=2  1% of token rows scaled x100
 
@@ -55,6 +56,10 @@ WORKLOADS = {
     "mixtral_fwd": Workload("mixtral_fwd", 8192, 4096, 14336, 8, 2,
                             backward=False),
     "mixtral": Workload("mixtral", 8192, 4096, 14336, 8, 2),
+    # long-sequence variant (4 x 8192 tokens): past the size at which any
+    # single activation tensor of the layer exceeds 2 GiB (AB and dAB are
+    # 3.8 GB)
+    "mixtral_long": Workload("mixtral_long", 32768, 4096, 14336, 8, 2),
     "finegrain": Workload("finegrain", 16384, 2048, 1408, 64, 8,
                           router_bias=True),
     "mxfp8": Workload("mxfp8", 16384, 4096, 14336, 8, 2, outlier_frac=0.01,

@@ -588,3 +588,11 @@ def test_full_mixtral_fwd_bwd_sampled():
 @gpu
 def test_full_finegrain_fwd_bwd_sampled():
     _full_size("finegrain", seed=3, backward=True)
+
+
+@gpu
+def test_full_mixtral_long_fwd_bwd_sampled():
+    """T = 32768 tokens at the Mixtral shape: AB and dAB (3.8 GB each) are
+    beyond 2 GiB, so every buffer resource must be bounded by what one
+    workgroup touches."""
+    _full_size("mixtral_long", seed=5, backward=True)
