@@ -188,6 +188,59 @@ def cpu_baseline(inp, wl, n_tokens):
                        f"{blas}, {threads} threads)")}
 
 
+def cpu_baseline_mx(inp, wl, d_slice=384, f_slice=1344):
+    """The float64 MX oracle, untuned, on every token of the workload but a
+    slice of the layer's features (the first d_slice hidden and f_slice
+    intermediate features of every expert), forward and backward with every
+    quantization inside the timed region, scaled by d*f / (d_slice*f_slice):
+    the oracle's GEMMs and its codec work are proportional to d*f.  Its
+    routing, dispatch plan and per-token loops are not, and are scaled too,
+    so the value is a lower bound on the oracle's full-layer rate.  The full
+    layer is out of reach for a bounded run: the oracle's codec spends about
+    15 s on one 28672 x 4096 weight matrix, and a step quantizes 24."""
+    from oracle import moe_mx, moe_ref
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
+        blas = infos[0].get("internal_api", "blas") if infos else "blas"
+    except Exception:  # pragma: no cover - informational only
+        threads, blas = len(os.sched_getaffinity(0)), "blas"
+    T, d, f = wl.T, wl.d, wl.f
+    ds, fs = min(d_slice, d), min(f_slice, f)
+    h = lambda t: t.double().cpu().numpy()  # noqa: E731
+    x = h(inp["x"][:, :ds])
+    dy = h(inp["dy"][:, :ds])
+    w_gu = inp["w_gu"]
+    w_gu = h(torch_cat_gate_up(w_gu, f, fs, ds))
+    w2 = h(inp["w2"][:, :ds, :fs])
+    logits = h(inp["logits"])
+    act4 = wl.prec == "mxfp4"
+    t0 = time.perf_counter()
+    fwd = moe_mx.moe_forward_mx(x, logits, w_gu, w2, wl.k, act4=act4)
+    bwd = moe_mx.moe_backward_mx(fwd, dy, w_gu, w2)
+    moe_ref.routing_weight_backward(logits, fwd["idx"], fwd["p"], bwd["dp"],
+                                    wl.renorm)
+    dt = time.perf_counter() - t0
+    scale = (d * f) / (ds * fs)
+    return {"value": T / (dt * scale), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"all {T} tokens of the {wl.name} workload, fwd+bwd, "
+                       f"float64 numpy MX oracle on the first {ds} hidden and "
+                       f"{fs} intermediate features of every expert "
+                       f"({dt:.1f} s, {blas}, {threads} threads), scaled by "
+                       f"d*f/({ds}*{fs}) = {scale:.0f}, which scales the "
+                       f"oracle's per-token loops too: a lower bound on its "
+                       f"full-layer rate)")}
+
+
+def torch_cat_gate_up(w_gu, f, fs, ds):
+    """The gate rows [0, fs) and up rows [f, f + fs) of every expert, first
+    ds columns."""
+    import torch
+    return torch.cat([w_gu[:, :fs, :ds], w_gu[:, f:f + fs, :ds]], dim=1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,8 +387,9 @@ def main():
         gms = gs.elapsed_time(ge) / args.steps
         out["graph"] = {"ms_per_step": round(gms, 4),
                         "tokens_per_s": round(T / (gms / 1e3), 1)}
-    if not args.no_cpu_baseline and not mx:
-        out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_tokens, T))
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = (cpu_baseline_mx(inp, wl) if mx else
+                               cpu_baseline(inp, wl, min(args.cpu_tokens, T)))
     print(json.dumps(out), flush=True)
 
 

@@ -27,10 +27,13 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-// Two floats -> packed pair of bfloat16 (lo in bits 0..15).
+// Two floats -> packed pair of bfloat16 (lo in bits 0..15), round to
+// nearest even: one two-input hardware convert.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) |
-         (static_cast<uint32_t>(f2bf(hi)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) {

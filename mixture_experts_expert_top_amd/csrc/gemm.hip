@@ -478,6 +478,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   __shared__ int s_ord[MODE == kSegM ? 1 : kMaxExperts];
   __shared__ int s_stat[2];
   __shared__ float s_dp[C::WN * BM];
+  // kDSwiglu: the routing weights of the tile's rows
+  __shared__ float s_wrow[EPI == kDSwiglu ? BM : 1];
   // MX: scale dwords of the tile rows, [stage][A rows, B rows]
   __shared__ uint32_t s_scl[MX ? 2 * 2 * BM : 1];
 
@@ -1121,31 +1123,45 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     for (int m = 1; m < 64; m <<= 1) acc_p += __shfl_xor(acc_p, m, 64);
     pe = acc_p;
   }
-  // kDSwiglu: a lane's rows of a pass are r0 + it * kRowsPerPass.  Every
-  // AB read and routing weight of the pass is issued before the
-  // accumulators are staged, so the reads overlap the staging and each
-  // other instead of waiting one row at a time between dAB stores.
+  // kDSwiglu: a lane's rows of a pass are r0 + it * kRowsPerPass.  The AB
+  // values of a pass are all read ahead: pass 0's before the barrier below,
+  // pass h + 1's right after pass h's accumulators are staged (their
+  // registers are free then), so each read has a whole pass to land.  The
+  // tile's routing weights go to LDS once (a global read between two dAB
+  // stores would wait for them: the compiler cannot tell the two apart).
   constexpr int kDsIt = kEpiRows / kRowsPerPass;
   constexpr int kPre = EPI == kDSwiglu ? kDsIt : 1;
-#pragma unroll
-  for (int h = 0; h < TM / kEpiRows; ++h) {
-    const int row_base = m0 + wm * TM + h * kEpiRows;   // absolute row
-    uint2 pre_g[kPre], pre_u[kPre];
+  constexpr int kPasses = TM / kEpiRows;
+  uint2 pre_g[kPasses][kPre], pre_u[kPasses][kPre];
+  auto load_ab = [&](int h) {
     if constexpr (EPI == kDSwiglu) {
+      const int row_base = m0 + wm * TM + h * kEpiRows;
       const bf16_t* AB = P.AB + seg0 * static_cast<int64_t>(2 * f);
       const int col = n0 + wn * TN + (lane % kLanesPerRow) * 4;
 #pragma unroll
       for (int it = 0; it < kDsIt; ++it) {
         const int row = row_base + lane / kLanesPerRow + it * kRowsPerPass;
-        pre_g[it] = make_uint2(0u, 0u);
-        pre_u[it] = make_uint2(0u, 0u);
+        pre_g[h][it] = make_uint2(0u, 0u);
+        pre_u[h][it] = make_uint2(0u, 0u);
         if (row < Mvalid && col < f) {
           const bf16_t* src = AB + static_cast<int64_t>(row) * 2 * f + col;
-          pre_g[it] = *reinterpret_cast<const uint2*>(src);
-          pre_u[it] = *reinterpret_cast<const uint2*>(src + f);
+          pre_g[h][it] = *reinterpret_cast<const uint2*>(src);
+          pre_u[h][it] = *reinterpret_cast<const uint2*>(src + f);
         }
       }
     }
+  };
+  if constexpr (EPI == kDSwiglu) {
+    load_ab(0);
+    for (int lr = tid; lr < BM; lr += NT)
+      s_wrow[lr] = (w && m0 + lr < Mvalid) ? w[m0 + lr] : 1.0f;
+    __syncthreads();
+  }
+  // The passes are expanded at compile time (h indexes the accumulators;
+  // the unroller declines bodies this large).
+  auto epi_pass = [&](auto h_c) {
+    constexpr int h = decltype(h_c)::value;
+    const int row_base = m0 + wm * TM + h * kEpiRows;   // absolute row
 #pragma unroll
     for (int ii = 0; ii < kEpiRows / 32; ++ii)
 #pragma unroll
@@ -1156,6 +1172,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           stage[r * LD + j * 32 + fr] = acc[h * (kEpiRows / 32) + ii][j][v];
         }
     wave_lds_sync();
+    if (h + 1 < kPasses) load_ab(h + 1);
     if (EPI == kStore || EPI == kStoreF32) {
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
@@ -1194,11 +1211,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         const int row = row_base + lane / kLanesG + it * kRowsG;
         pre_wr[it] = (w && row < Mvalid && col < f) ? w[row] : 1.0f;
       }
-#pragma unroll
-      for (int it = 0; it < kItG; ++it) {
+      // Unchecked: every row of the pass and every gate column of the wave
+      // is inside the expert, so no lane needs a mask.
+      auto sw_iter = [&](int it, auto checked_c) {
+        constexpr bool kChecked = decltype(checked_c)::value;
         const int r = lane / kLanesG + it * kRowsG;
         const int row = row_base + r;
-        const bool ok = row < Mvalid && col < f;
+        const bool ok = !kChecked || (row < Mvalid && col < f);
         const int64_t ro = static_cast<int64_t>(row);
         const f32x4 g = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
         const f32x4 u =
@@ -1240,6 +1259,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             *reinterpret_cast<f32x4*>(stage + r * LD + c4) = sb;
           }
         }
+      };
+      const bool full = row_base + kEpiRows <= Mvalid &&
+                        n0g + wn * (TN / 2) + TN / 2 <= f;
+      if (full) {
+#pragma unroll
+        for (int it = 0; it < kItG; ++it) sw_iter(it, std::false_type{});
+      } else {
+#pragma unroll
+        for (int it = 0; it < kItG; ++it) sw_iter(it, std::true_type{});
       }
       if constexpr (kTokEpi) {
         if (tok) {
@@ -1276,23 +1304,32 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       bf16_t* dAB = P.C + cbase;
       const int c4 = (lane % kLanesPerRow) * 4;
       const int col = n0 + wn * TN + c4;
-#pragma unroll
-      for (int it = 0; it < kDsIt; ++it) {
-        const int r = lane / kLanesPerRow + it * kRowsPerPass;
+      // the lane's first row of the pass; row it is rstep elements on
+      const int r0 = lane / kLanesPerRow;
+      const int64_t rstep = static_cast<int64_t>(kRowsPerPass) * P.ldc;
+      bf16_t* drow = dAB + static_cast<int64_t>(row_base + r0) * P.ldc + col;
+      const int64_t qstep = static_cast<int64_t>(kRowsPerPass) * (2 * f);
+      const int64_t qrow = (seg0 + row_base + r0) * (2 * f);
+      // One row of the pass (it) for this lane: dSwiGLU of its 4 columns,
+      // the stores, and the row's share of the routing-weight gradient.
+      // Unchecked: every row of the pass and every column of the wave is
+      // inside the expert, so no lane needs a mask.
+      auto ds_iter = [&](int it, auto checked_c) {
+        constexpr bool kChecked = decltype(checked_c)::value;
+        const int r = r0 + it * kRowsPerPass;
         const int row = row_base + r;
         float part = 0.0f;
-        const bool ok = row < Mvalid && col < f;
-        const int64_t ro = static_cast<int64_t>(row);
+        const bool ok = !kChecked || (row < Mvalid && col < f);
         float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float du[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (ok) {
           const f32x4 ds = *reinterpret_cast<const f32x4*>(stage + r * LD + c4);
-          const uint2 gb = pre_g[it], ub = pre_u[it];
+          const uint2 gb = pre_g[h][it], ub = pre_u[h][it];
           const float g[4] = {bf_lo(gb.x), bf_hi(gb.x), bf_lo(gb.y),
                               bf_hi(gb.y)};
           const float u[4] = {bf_lo(ub.x), bf_hi(ub.x), bf_lo(ub.y),
                               bf_hi(ub.y)};
-          const float wr = w ? w[row] : 1.0f;
+          const float wr = s_wrow[row - m0];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const float sg = sigmoidf_(g[c]);
@@ -1306,8 +1343,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
             uint2 og, ou;
             og.x = pack_bf16x2(dg[0], dg[1]); og.y = pack_bf16x2(dg[2], dg[3]);
             ou.x = pack_bf16x2(du[0], du[1]); ou.y = pack_bf16x2(du[2], du[3]);
-            *reinterpret_cast<uint2*>(dAB + ro * P.ldc + col) = og;
-            *reinterpret_cast<uint2*>(dAB + ro * P.ldc + f + col) = ou;
+            bf16_t* dst = drow + it * rstep;
+            *reinterpret_cast<uint2*>(dst) = og;
+            *reinterpret_cast<uint2*>(dst + f) = ou;
           }
         }
         if constexpr (kTokEpi) {
@@ -1327,7 +1365,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           const uint32_t qg = mx_quant4(dg, ok, &sg_byte);
           const uint32_t qu = mx_quant4(du, ok, &su_byte);
           if (ok) {
-            const int64_t qr = (seg0 + ro) * (2 * f);
+            const int64_t qr = qrow + it * qstep;
             *reinterpret_cast<uint32_t*>(P.Qc + qr + col) = qg;
             *reinterpret_cast<uint32_t*>(P.Qc + qr + f + col) = qu;
             if ((lane & 7) == 0) {
@@ -1348,6 +1386,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         }
         if ((lane % kLanesPerRow) == 0)
           s_dp[wn * BM + wm * TM + h * kEpiRows + r] = part;
+      };
+      const bool full = row_base + kEpiRows <= Mvalid &&
+                        n0 + wn * TN + TN <= f;
+      if (full) {
+#pragma unroll
+        for (int it = 0; it < kDsIt; ++it) ds_iter(it, std::false_type{});
+      } else {
+#pragma unroll
+        for (int it = 0; it < kDsIt; ++it) ds_iter(it, std::true_type{});
       }
       if constexpr (kTokEpi) {
         if (tok) {
@@ -1396,7 +1443,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       }
     }
     wave_lds_sync();
-  }
+  };
+  static_assert(kPasses == 2, "two epilogue passes of 64 rows");
+  epi_pass(std::integral_constant<int, 0>{});
+  epi_pass(std::integral_constant<int, 1>{});
   if constexpr (kTokEpi) {
     // one scale dword (the wave's four 32-row blocks) per column
     if (tok && wrow0 < pad_len) {

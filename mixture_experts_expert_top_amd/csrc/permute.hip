@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * kRankWaves) void plan_rank_kernel(
     int rank = 0, grp = 0;
     while (active) {
       const int leader = __ffsll(static_cast<unsigned long long>(active)) - 1;
-      const int le = __shfl(e, leader, 64);
+      const int le = __builtin_amdgcn_readlane(e, leader);
       const uint64_t mask = __ballot(valid && e == le);
       if (valid && e == le) {
         rank = __popcll(mask & below);
