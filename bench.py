@@ -149,6 +149,258 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": 4 * n, "copies": 6}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Counter summaries (``--summarize-counters DIR``, no GPU needed).  DIR holds
+# the CSV output (``-d DIR/<run> -o run --output-format csv``) of these
+# rocprofv3 runs of this script, each in a process of its own:
+#   trace      --kernel-trace --stats              --steps 5 --warmup 1
+#   fetch      --pmc FETCH_SIZE --kernel-trace     --steps 2 --warmup 1
+#   write      --pmc WRITE_SIZE --kernel-trace     --steps 2 --warmup 1
+#   mfma       --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+#              GRBM_GUI_ACTIVE SQ_BUSY_CYCLES --kernel-trace
+#                                                  --steps 2 --warmup 1
+#   cal_fetch, cal_write   the same two counters over --copy-calibration
+# Each run's dispatches of this library are cut into steps at the router
+# score kernel; the first step of each run is dropped (cold caches) and the
+# rest are averaged per position in the step.
+
+# the library's kernels in the order one step launches them, per stage
+STEP_KERNELS = {
+    "bf16": [
+        ("router_logits", ["router_logits_kernel"]),
+        ("route", ["route_kernel"]),
+        ("permute", ["plan_rank_kernel", "plan_scan_kernel",
+                     "scatter_kernel"]),
+        ("gate_up_swiglu_fwd", ["grouped_gemm_kernel"]),
+        ("down_fwd", ["grouped_gemm_kernel"]),
+        ("unpermute_y", ["unpermute_kernel"]),
+        ("permute_dy", ["permute_rows_kernel"]),
+        ("down_swiglu_bwd", ["grouped_gemm_kernel"]),
+        ("dp_reduce", ["dp_reduce_kernel"]),
+        ("wgrad_down", ["grouped_gemm_kernel"]),
+        ("gate_up_dgrad", ["grouped_gemm_kernel"]),
+        ("wgrad_gate_up", ["grouped_gemm_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
+        ("router_backward", ["router_dlogits_kernel",
+                             "router_dwg_partial_kernel",
+                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_aux_final_kernel"]),
+    ],
+}
+
+# MFMA flops one SQ_INSTS_VALU_MFMA_MOPS_* count stands for
+MOPS_FLOPS = 512
+# SIMDs on the chip (256 CUs x 4), and XCDs (GRBM_GUI_ACTIVE is summed
+# over the XCDs' own copies)
+N_SIMDS, N_XCDS = 1024, 8
+
+
+def gemm_alg_bytes(stage, T, d, f, E, k, planes, ntiles):
+    """Algorithmic (read, write) HBM bytes of a bf16 GEMM stage: each
+    operand read once and each result written once (planes: fp32 partial
+    planes of the split-K outputs; ntiles: column tiles of the
+    routing-weight gradient partials)."""
+    Tk = T * k
+    return {
+        "gate_up_swiglu_fwd": (Tk * d * 2 + E * 2 * f * d * 2 + Tk * 4,
+                               Tk * 2 * f * 2 + Tk * f * 2),
+        "down_fwd": (Tk * f * 2 + E * d * f * 2, planes * Tk * d * 4),
+        "down_swiglu_bwd": (Tk * d * 2 + E * d * f * 2 + Tk * 2 * f * 2
+                            + Tk * 4,
+                            Tk * 2 * f * 2 + Tk * ntiles * 4),
+        "wgrad_down": (Tk * d * 2 + Tk * f * 2, E * d * f * 2),
+        "gate_up_dgrad": (Tk * 2 * f * 2 + E * 2 * f * d * 2,
+                          planes * Tk * d * 4),
+        "wgrad_gate_up": (Tk * 2 * f * 2 + Tk * d * 2, E * 2 * f * d * 2),
+    }.get(stage)
+
+
+def _base_kernel(name):
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    n = n.replace("moe::", "")
+    n = n.split("(")[0]
+    return n, n.split("<")[0]
+
+
+def _steps_of(path, counters):
+    """Dispatches of the library's kernels in a rocprofv3 CSV, cut into
+    steps: lists of dicts {name, base, grid, ns, <counter>: value}."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    by_disp = {}
+    for r in rows:
+        if "moe::" not in r["Kernel_Name"]:
+            continue
+        key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        ent = by_disp.get(key)
+        if ent is None:
+            full, base = _base_kernel(r["Kernel_Name"])
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X")
+            ent = {"name": full, "base": base, "grid": int(grid),
+                   "start": int(r["Start_Timestamp"]),
+                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])}
+            by_disp[key] = ent
+        if counters and r.get("Counter_Name") in counters:
+            ent[r["Counter_Name"]] = (ent.get(r["Counter_Name"], 0.0)
+                                      + float(r["Counter_Value"]))
+    seq = sorted(by_disp.values(), key=lambda e: e["start"])
+    steps, cur = [], None
+    for e in seq:
+        if e["base"] == "router_logits_kernel":
+            cur = []
+            steps.append(cur)
+        if cur is not None:
+            cur.append(e)
+    return steps
+
+
+def _average_steps(steps, keys):
+    """Per-position means over the steps after the first."""
+    use = steps[1:] if len(steps) > 1 else steps
+    n = min(len(s) for s in use)
+    out = []
+    for i in range(n):
+        e = dict(use[0][i])
+        for key in keys:
+            vals = [s[i][key] for s in use if key in s[i]]
+            if vals:
+                e[key] = sum(vals) / len(vals)
+        out.append(e)
+    return out
+
+
+def _label_stages(seq, family):
+    spec = [(st, b) for st, bases in STEP_KERNELS.get(family, [])
+            for b in bases]
+    p = 0
+    for e in seq:
+        if p < len(spec) and e["base"] == spec[p][1]:
+            e["stage"] = spec[p][0]
+            p += 1
+        else:
+            e["stage"] = "?"
+    return seq
+
+
+def _calibration(path, counter):
+    """KiB the counter reads for the plain 1 GiB copies (mean of the last
+    five of the six)."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "opy" in r["Kernel_Name"]]
+    vals = vals[-5:]
+    return sum(vals) / len(vals)
+
+
+def summarize_counters(root, workload):
+    """Print a markdown summary of the counter runs under ``root`` and
+    write the grouped-GEMM traffic record ``root/traffic.json`` (the form
+    profiles/traffic.json takes)."""
+    from mixture_experts_expert_top_amd import inputs, moe
+    wl = inputs.WORKLOADS[workload]
+    T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
+    mx = wl.prec in ("mxfp8", "mxfp4")
+    family = wl.prec
+    planes, ntiles = moe.row_planes(f), moe.moe_dp_tiles(f)
+    csvp = lambda run, kind: os.path.join(  # noqa: E731
+        root, run, f"run_{kind}.csv")
+    kt = _average_steps(_steps_of(csvp("trace", "kernel_trace"), None), [
+        "ns"])
+    fe = _average_steps(_steps_of(csvp("fetch", "counter_collection"),
+                                  {"FETCH_SIZE"}), ["FETCH_SIZE"])
+    wr = _average_steps(_steps_of(csvp("write", "counter_collection"),
+                                  {"WRITE_SIZE"}), ["WRITE_SIZE"])
+    mf_keys = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "ns"]
+    mf = _average_steps(_steps_of(csvp("mfma", "counter_collection"),
+                                  set(mf_keys)), mf_keys)
+    n = min(len(kt), len(fe), len(wr), len(mf))
+    for seq in (fe, wr, mf):
+        for i in range(n):
+            if seq[i]["base"] != kt[i]["base"]:
+                raise SystemExit(f"runs disagree at step position {i}: "
+                                 f"{kt[i]['name']} vs {seq[i]['name']}")
+    _label_stages(kt, family)
+    cal_f = _calibration(csvp("cal_fetch", "counter_collection"),
+                         "FETCH_SIZE")
+    cal_w = _calibration(csvp("cal_write", "counter_collection"),
+                         "WRITE_SIZE")
+    gib = float(1 << 30)
+    bf, bw = gib / cal_f, gib / cal_w
+    peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    lines = []
+    lines.append(f"Copy calibration: a plain 1 GiB device copy reads "
+                 f"FETCH_SIZE {cal_f:.0f} KiB and WRITE_SIZE {cal_w:.0f} KiB, "
+                 f"so one counted KiB stands for {bf:.1f} B read and "
+                 f"{bw:.1f} B written.")
+    lines.append("")
+    lines.append("| # | stage | kernel | grid | us | read MB | write MB | "
+                 "HBM GB/s | % of 8 TB/s | MFMA busy | counted TFLOP/s | "
+                 f"% of {peak_mfma / 1000:.1f} PF | clock GHz |")
+    lines.append("|---:|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"
+                 "---:|---:|")
+    stages = {}
+    step_us = 0.0
+    for i in range(n):
+        e = kt[i]
+        us = e["ns"] / 1e3
+        step_us += us
+        rd = fe[i].get("FETCH_SIZE", 0.0) * bf
+        wt = wr[i].get("WRITE_SIZE", 0.0) * bw
+        gbs = (rd + wt) / (e["ns"] * 1e-9) / 1e9
+        m = mf[i]
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        util = busy / (gui / N_XCDS * N_SIMDS) if gui else 0.0
+        mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        tfl = mops * MOPS_FLOPS / (m["ns"] * 1e-9) / 1e12 if mops else 0.0
+        clk = gui / N_XCDS / m["ns"] if m["ns"] else 0.0
+        is_gemm = e["base"] == "grouped_gemm_kernel"
+        short = e["name"].replace("grouped_gemm_kernel", "gg")
+        mfma_cols = (f"{util:.3f} | {tfl:.0f} | "
+                     f"{100 * tfl / peak_mfma:.1f} | {clk:.2f}"
+                     if is_gemm and not mx else
+                     (f"{util:.3f} | - | - | {clk:.2f}" if is_gemm
+                      else "- | - | - | -"))
+        lines.append(f"| {i} | {e['stage']} | `{short}` | {e['grid']} | "
+                     f"{us:.1f} | {rd / 1e6:.1f} | {wt / 1e6:.1f} | "
+                     f"{gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} | "
+                     f"{mfma_cols} |")
+        if is_gemm:
+            alg = None if mx else gemm_alg_bytes(e["stage"], T, d, f, E, k,
+                                                  planes, ntiles)
+            stages[e["stage"]] = {
+                "fetch_kib": fe[i].get("FETCH_SIZE", 0.0),
+                "write_kib": wr[i].get("WRITE_SIZE", 0.0),
+                "us": round(us, 1),
+                "mfma_busy": round(util, 4),
+                "counted_tflops": round(tfl, 1) if not mx else None,
+                "algorithmic_read_bytes": alg[0] if alg else None,
+                "algorithmic_write_bytes": alg[1] if alg else None,
+            }
+    lines.append("")
+    lines.append(f"Sum of the step's kernel times: {step_us / 1e3:.3f} ms.")
+    if not mx:
+        lines.append("")
+        lines.append("| GEMM stage | read GB | write GB | algorithmic read GB"
+                     " | algorithmic write GB | read / alg | write / alg |")
+        lines.append("|---|---:|---:|---:|---:|---:|---:|")
+        for st, v in stages.items():
+            rd = v["fetch_kib"] * bf
+            wt = v["write_kib"] * bw
+            ar, aw = v["algorithmic_read_bytes"], v["algorithmic_write_bytes"]
+            lines.append(f"| {st} | {rd / 1e9:.3f} | {wt / 1e9:.3f} | "
+                         f"{ar / 1e9:.3f} | {aw / 1e9:.3f} | {rd / ar:.2f} | "
+                         f"{wt / aw:.2f} |")
+    rec = {"workload": workload, "copy_bytes": 1 << 30,
+           "kernel_source_sha256": gemm_source_sha256(),
+           "copy_fetch_kib": cal_f, "copy_write_kib": cal_w,
+           "stages": stages}
+    with open(os.path.join(root, "traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print("\n".join(lines))
+
+
 def cpu_baseline(inp, wl, n_tokens):
     """The float64 oracle, untuned, on the first n_tokens tokens of the same
     workload (router scores, routing, experts, combine and backward)."""
@@ -260,6 +512,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates "
                          "the HBM traffic counters")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the summary of the rocprofv3 counter runs "
+                         "under DIR for --workload and write DIR/traffic.json"
+                         " (no GPU used)")
     args = ap.parse_args()
     if args.config:
         args.workload = CONFIGS[args.config]
@@ -270,6 +526,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
         return
 
     import torch

@@ -41,8 +41,8 @@
  *    f >= 8 and multiples of 8 (bf16) or of 32 (MXFP8).  Sizes are bound
  *    per buffer resource, not per tensor: one expert's weight, and for the
  *    weight gradients T*k rows of 2f (bf16) values, or a token-axis MX
- *    operand, must each stay within 4 GiB; x and the router weight within
- *    2 GiB.  (The Mixtral shape, d = 4096 and f = 14336, runs up to about
+ *    operand, must each stay within 4 GiB - 256 B; x and the router weight
+ *    within 2 GiB.  (The Mixtral shape, d = 4096 and f = 14336, runs up to about
  *    T*k = 74,000 rows a call.)
  *  - Deterministic: identical inputs give bitwise identical outputs (no
  *    floating-point atomics; all reductions run in a fixed order).

@@ -35,11 +35,12 @@ moe_status hip_status(hipError_t e, const char* where) {
 }
 
 constexpr int64_t kMaxBytes = (int64_t{1} << 31) - 1;
-// Largest byte range of one buffer resource (32-bit offsets).  The grouped
-// GEMMs bound each resource by what one workgroup touches: the rows of one
-// tile (row-segmented GEMMs), one expert's weight, one expert's rows of a
+// Largest byte range of one buffer resource: just under 4 GiB, so that the
+// kernels' masked-load offset lies past every range.  The grouped GEMMs
+// bound each resource by what one workgroup touches: the rows of one tile
+// (row-segmented GEMMs), one expert's weight, one expert's rows of a
 // weight-gradient operand, or one token-axis MX operand.
-constexpr int64_t kMaxRange = (int64_t{1} << 32) - 1;
+constexpr int64_t kMaxRange = moe::kMaxResourceBytes;
 
 bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;

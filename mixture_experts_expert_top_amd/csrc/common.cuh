@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace moe {
 
 typedef uint16_t bf16_t;  // IEEE bfloat16 bit pattern
@@ -44,10 +46,10 @@ __device__ __forceinline__ float bf_hi(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- buffers
-// Raw buffer resource over [base, base + bytes).  Loads whose offset falls
-// outside the range return zero, which implements tile masking.
+// Raw buffer resource over [base, base + bytes), bytes <= kOob (internal.h).
+// Loads whose offset falls outside the range return zero, which implements
+// tile masking.
 constexpr uint32_t kBufferWord3 = 0x00020000u;
-constexpr uint32_t kOob = 0x80000000u;  // an offset beyond every range
 
 // base and bytes must be the same on every lane of the wave: they are read
 // from the first active lane, which keeps the resource in scalar registers

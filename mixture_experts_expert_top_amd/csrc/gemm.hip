@@ -92,6 +92,7 @@ constexpr int kTileElems = BM * BK;       // one operand stage (A or B)
 constexpr int kStageElems = 2 * kTileElems;
 constexpr int kGroupN = 4;                // n-tiles per scheduling group
 constexpr int kGroupM = 8;                // m-tiles per block of a group
+constexpr int kGroupMOne = 12;            // ... or all, up to this many
 constexpr int kEpiRows = 64;              // rows per epilogue pass of a wave
 #ifndef MOE_INDEP_LOOP
 #define MOE_INDEP_LOOP 1
@@ -145,11 +146,12 @@ struct Params {
   const bf16_t* AB;  // kDSwiglu: saved [Tk][2f]
   float* dp_part;    // kDSwiglu: [Tk][ntn]
   int f;
-  // SegM split-K (kStoreF32 only): the reduction is cut into ksplit
-  // contiguous ranges; range s writes its partial sums to plane s of C
+  // SegM split-K (kStoreF32 only): the reduction is cut into ksplit (1 or
+  // 2) contiguous ranges; range s writes its partial sums to plane s of C
   // (plane = elements between planes).  The combine adds the planes.
   int ksplit;
   int64_t plane;
+  int xcd_cus;       // compute units of one XCD (split-K piece sizing)
   // MX operands: scale bytes [rows][lds_*] (one per 32 codes along K),
   // bs_stride = bytes between experts' B scales (SegM)
   const uint8_t* sA;
@@ -207,6 +209,29 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int q = nb >> 3, r = nb & 7;
   const int x = bid & 7, i = bid >> 3;
   return x * q + min(x, r) + i;
+}
+
+// k-steps of the second piece of a two-piece split reduction of nk steps,
+// on an XCD whose c CUs run ntx tiles: first all first pieces, then all
+// second pieces, each CU taking the next piece as it frees.  With b = ntx
+// mod c, b CUs run one first piece more than the others; second pieces of
+// 1/m of the reduction let both groups end together at ntx/c tiles' time
+// when m is a multiple of c / gcd(b, c) (and m >= 2).  m is kept to at
+// most 8: a shorter piece would be mostly fixed per-tile cost.  b = 0
+// needs no balancing and keeps two halves.
+__device__ __forceinline__ int split_second_steps(int ntx, int nk, int c) {
+  const int b = ntx % c;
+  int m = 2;
+  if (b != 0) {
+    int u = b, v = c;
+    while (v != 0) {
+      const int t = u % v;
+      u = v;
+      v = t;
+    }
+    m = max(2, min(8, c / u));
+  }
+  return max(1, (nk + m / 2) / m);
 }
 
 // One operand tile of 256 rows (M or N) x 64 k is moved by 256 threads
@@ -405,16 +430,20 @@ __device__ __forceinline__ void load_one(const M& mv, i32x4* v,
 // block may be narrower), m fastest inside a block.  Consecutive tiles --
 // which run together on one XCD -- then share kGroupN B column blocks and
 // kGroupM A row blocks in its L2, in both short (forward: a few m-tiles an
-// expert) and tall (weight gradients: M = d or 2f) grids.
+// expert) and tall (weight gradients: M = d or 2f) grids.  An expert of at
+// most kGroupMOne m-tiles is a single block: split in two, its last few
+// m-tiles would run a whole tile time after the first block and read every
+// B column block of the group from HBM again.
 __device__ __forceinline__ void tile_order(int local, int mtn, int ntn,
                                            int* mt, int* nt) {
   const int grp = local / (mtn * kGroupN);
   const int ng = min(kGroupN, ntn - grp * kGroupN);
   int rem = local - grp * mtn * kGroupN;
-  const int blk = rem / (kGroupM * ng);
-  const int mb = min(kGroupM, mtn - blk * kGroupM);
-  rem -= blk * kGroupM * ng;
-  *mt = blk * kGroupM + rem % mb;
+  const int gm = mtn <= kGroupMOne ? mtn : kGroupM;
+  const int blk = rem / (gm * ng);
+  const int mb = min(gm, mtn - blk * gm);
+  rem -= blk * gm * ng;
+  *mt = blk * gm + rem % mb;
   *nt = grp * kGroupN + rem / mb;
 }
 
@@ -534,18 +563,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     __syncthreads();
   }
   int split = 0;
+  int ksplit_at = 0;    // SegM, two pieces: first k of the second piece
   if (MODE == kSegM) {
-    // The grid holds ksplit copies of an upper bound on the tile count and
-    // only the first ksplit * total ids carry a tile (copy s, the slowest
-    // index, computes reduction range s).  The XCD-aware remap runs over
-    // those ids alone, so each XCD receives an equal share of real tiles;
-    // the surplus ids, dealt round-robin over the XCDs, exit at once.
+    // The grid holds an upper bound on the tile count (times two, rounded
+    // to 16, with a split reduction) and only the first ids of each XCD
+    // (the hardware deals ids round-robin over the 8 XCDs) carry a tile:
+    // XCD x owns a contiguous range of the tiles, the same share for
+    // every XCD, and the surplus ids exit at once.  A split reduction runs
+    // the first pieces of all the XCD's tiles, then their second pieces,
+    // whose length (split_second_steps) lets its CUs end together.
     const int total = s_pref[E] * P.ntn;
-    const int nreal = total * P.ksplit;
-    if (static_cast<int>(blockIdx.x) >= nreal) return;
-    const int lbid = xcd_remap(blockIdx.x, nreal);
-    split = lbid / total;
-    const int bid = lbid - split * total;
+    int bid;
+    if (P.ksplit == 1) {
+      if (static_cast<int>(blockIdx.x) >= total) return;
+      bid = xcd_remap(blockIdx.x, total);
+    } else {
+      const int q = total >> 3, r = total & 7;
+      const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+      const int ntx = q + (x < r ? 1 : 0);
+      if (i >= 2 * ntx) return;
+      split = i >= ntx ? 1 : 0;
+      bid = x * q + min(x, r) + i - split * ntx;
+      const int nkf = (P.K + BK - 1) / BK;
+      ksplit_at = (nkf - split_second_steps(ntx, nkf, P.xcd_cus)) * BK;
+    }
     e = find_segment(s_pref, E, bid / P.ntn);
     const int mte = s_pref[e + 1] - s_pref[e];
     tile_order(bid - s_pref[e] * P.ntn, mte, P.ntn, &mt, &nt);
@@ -609,12 +650,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int n0 = nt * BN;               // kSwiglu: gate column tile = nt*BN/2
   const int Mvalid = (MODE == kSegM) ? seg_len : P.M;
   // reduction range [kbeg, Kdim) of this workgroup
-  const int kchunk =
-      (MODE == kSegM) ? ((P.K + P.ksplit * BK - 1) / (P.ksplit * BK)) * BK : 0;
-  const int kbeg = (MODE == kSegM)    ? min(P.K, split * kchunk)
+  const bool two = MODE == kSegM && P.ksplit == 2;
+  const int kbeg = (MODE == kSegM)    ? (split ? min(P.K, ksplit_at) : 0)
                    : (MODE == kSegKT) ? s_pref[e]
                                       : 0;
-  const int Kdim = (MODE == kSegM)    ? min(P.K, kbeg + kchunk)
+  const int Kdim = (MODE == kSegM)    ? (two && !split ? min(P.K, ksplit_at)
+                                                       : P.K)
                    : (MODE == kSegKT) ? s_pref[e + 1]
                                       : seg_len;
 
@@ -1502,12 +1543,30 @@ using CfgWgrad = Cfg8;
 #endif
 using CfgMx = std::conditional_t<MOE_MX_WAVES == 4, Cfg4, Cfg8>;
 
+// Compute units of one XCD of the current device (8 XCDs), read once a
+// device.
+int xcd_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess || cus < 8)
+      cus = 256;
+    cached[dev] = cus / 8;
+  }
+  return cached[dev];
+}
+
 template <class C, int MODE, bool AKC, bool BKC, int EPI, bool MX = false,
           int FMT = 0>
 hipError_t launch(Params P, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (P.ksplit < 1) P.ksplit = 1;
-  grid *= P.ksplit;
+  if (P.ksplit != 2) P.ksplit = 1;
+  // two pieces a tile: every XCD needs twice its share of ids
+  if (P.ksplit == 2) grid = 16 * ((grid + 7) / 8);
+  P.xcd_cus = xcd_cus();
   hipLaunchKernelGGL((grouped_gemm_kernel<C, MODE, AKC, BKC, EPI, MX, FMT>),
                      dim3(grid), dim3(C::kThreads), 0, s, P);
   return hipGetLastError();

@@ -11,12 +11,16 @@ typedef uint16_t bf16_t;
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
-// fp32 row outputs of the down projection and of the gate_up data
-// gradient are written as this many partial-sum planes [planes][T*k][d]
-// (split reduction); the combine adds them in plane order.
+// Buffer resources address their range with 32-bit byte offsets, and a
+// load at an offset at or past the range returns zero (tile masking).
+// kOob is the offset the kernels give a masked load; every resource range
+// is at most kOob bytes, so a masked load never reads memory.
+constexpr uint32_t kOob = 0xffffff00u;
+constexpr int64_t kMaxResourceBytes = kOob;
 // Partial-sum planes of the fp32 row outputs (fc2's O and fc1's data
-// gradient dXp).  Their reductions (over f and 2f) are cut in two when f is
-// at least kSplitF, which pays while each half still spans many k-steps
+// gradient dXp), laid out [planes][T*k][d]; the combine adds them in plane
+// order.  Their reductions (over f and 2f) are cut in two when f is at
+// least kSplitF, which pays while each half still spans many k-steps
 // (measured at f = 14336).  With a narrower f one plane keeps the tiles
 // long and halves the combine's reads (measured at f = 1408).
 constexpr int64_t kSplitF = 4096;

@@ -84,7 +84,11 @@ __global__ __launch_bounds__(64 * kRankWaves) void plan_rank_kernel(
 // G lanes (G = 64 halved until G * E <= 1024): lane g sums its contiguous
 // range of chunks, the group scans those sums, and each lane rewrites its
 // range from its base.  An exclusive scan over experts then gives the
-// offsets.  Integer sums, so the result does not depend on the split.
+// offsets.  Integer sums, so the result does not depend on the split.  A
+// lane reads its range kScanBatch counts at a time, all loads in flight
+// together: the kernel is one workgroup's memory latency, so the number of
+// round trips is its time.
+constexpr int kScanBatch = 32;
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ chunk_counts, int nchunks, int E,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
@@ -96,10 +100,18 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   const int e = t / G, g = t - (t / G) * G;
   const int per = (nchunks + G - 1) / G;
   const int c0 = min(nchunks, g * per), c1 = min(nchunks, c0 + per);
+  int32_t* col = chunk_counts + e;
   int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c)
-      sum += chunk_counts[static_cast<int64_t>(c) * E + e];
+  if (e < E) {
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = cb + i < c1 ? col[static_cast<int64_t>(cb + i) * E] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) sum += v[i];
+    }
+  }
   int gincl = sum;
   for (int m = 1; m < G; m <<= 1) {
     const int o = __shfl_up(gincl, m, G);
@@ -107,11 +119,16 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   }
   if (e < E) {
     int run = gincl - sum;
-    for (int c = c0; c < c1; ++c) {
-      int32_t* p = chunk_counts + static_cast<int64_t>(c) * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = cb + i < c1 ? col[static_cast<int64_t>(cb + i) * E] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (cb + i < c1) col[static_cast<int64_t>(cb + i) * E] = run;
+        run += v[i];
+      }
     }
     if (g == G - 1) {
       s_cnt[e] = gincl;

@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.cuh"
 #include "internal.h"
@@ -18,16 +19,20 @@ namespace {
 
 // ---------------------------------------------------------------- logits
 // logits[t][e] = x[t] . w_g[e] (+ bias[e]); a skinny GEMM (N = E) on bf16
-// MFMA 32x32x16.  A workgroup owns 32 tokens x 32 experts; its 4 waves
-// split d into 4 contiguous quarters and their partial tiles are summed in
-// LDS in wave order (fixed, deterministic).
-constexpr int kLogitThreads = 256;
+// MFMA 32x32x16, bound by the one read of x.  A workgroup owns 32 tokens x
+// 32 experts; its 8 waves split d into 8 contiguous ranges and their
+// partial tiles are summed in LDS in wave order (fixed, deterministic).
+// Each wave issues the loads of kLogitAhead k-steps before their MFMAs so
+// that enough of x is in flight to keep HBM busy.
+constexpr int kLogitThreads = 512;
+constexpr int kLogitWaves = kLogitThreads / 64;
+constexpr int kLogitAhead = 8;
 
 __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int d, int E,
     float* __restrict__ logits) {
-  __shared__ float part[4][32 * 32];
+  __shared__ float part[kLogitWaves][32 * 32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
   const int row = lane & 31, kh = lane >> 5;
@@ -37,21 +42,30 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
       make_rsrc(wg, static_cast<uint32_t>(static_cast<int64_t>(E) * d * 2));
   const int tok = t0 + row, ex = e0 + row;
   const bool tok_ok = tok < T, ex_ok = ex < E;
-  // quarter of the reduction owned by this wave, in steps of 16
+  // the range of the reduction owned by this wave, in steps of 16
   const int steps = (d + 15) / 16;
-  const int q = (steps + 3) / 4;
+  const int q = (steps + kLogitWaves - 1) / kLogitWaves;
   const int s_begin = wave * q, s_end = min(steps, s_begin + q);
+  const int64_t xrow = static_cast<int64_t>(tok) * d;
+  const int64_t wrow = static_cast<int64_t>(ex) * d;
   f32x16 acc = {};
-  for (int s = s_begin; s < s_end; ++s) {
-    const int kk = s * 16 + kh * 8;
-    const bool kok = kk < d;
-    const uint32_t ox = (tok_ok && kok)
-        ? static_cast<uint32_t>((static_cast<int64_t>(tok) * d + kk) * 2) : kOob;
-    const uint32_t ow = (ex_ok && kok)
-        ? static_cast<uint32_t>((static_cast<int64_t>(ex) * d + kk) * 2) : kOob;
-    const bf16x8_v a = __builtin_bit_cast(bf16x8_v, buf_load16(rx, ox));
-    const bf16x8_v b = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  for (int s0 = s_begin; s0 < s_end; s0 += kLogitAhead) {
+    bf16x8_v a[kLogitAhead], b[kLogitAhead];
+#pragma unroll
+    for (int u = 0; u < kLogitAhead; ++u) {
+      // steps past the wave's range (or d) read zeros through kOob
+      const int kk = (s0 + u) * 16 + kh * 8;
+      const bool kok = s0 + u < s_end && kk < d;
+      const uint32_t ox = (tok_ok && kok)
+          ? static_cast<uint32_t>((xrow + kk) * 2) : kOob;
+      const uint32_t ow = (ex_ok && kok)
+          ? static_cast<uint32_t>((wrow + kk) * 2) : kOob;
+      a[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rx, ox));
+      b[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow));
+    }
+#pragma unroll
+    for (int u = 0; u < kLogitAhead; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
   }
   // acc[v] = C[token i][expert j], i = (v/4)*8 + kh*4 + v%4, j = lane%32
 #pragma unroll
@@ -65,9 +79,8 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
     const int t = t0 + i, e = e0 + j;
     if (t < T && e < E) {
       float s = part[0][idx];
-      s += part[1][idx];
-      s += part[2][idx];
-      s += part[3][idx];
+#pragma unroll
+      for (int w = 1; w < kLogitWaves; ++w) s += part[w][idx];
       if (bias) s += bias[e];
       logits[static_cast<int64_t>(t) * E + e] = s;
     }
@@ -249,29 +262,35 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
   }
 }
 
-// Partial dW_g over one chunk of 256 tokens, 512 columns and up to kExp
-// experts (8 when E <= 8, else 32 a block): part[chunk][e][c] = sum over
-// the chunk's tokens, in order, of dlogits[t][e] * x[t][c]; the y == 0
-// blocks also sum dlogits over the chunk (db).  With part == nullptr only
-// the db sums are made (x unread).  The x values of kAhead tokens are
-// loaded before any of them is used, so the loads overlap; the sums still
-// take the tokens one by one in order.
+// Partial dW_g over one chunk of 256 tokens, a block of columns and up to
+// kExp experts (8 when E <= 8, else 32 a block): part[chunk][e][c] = the
+// sum over the chunk's tokens of dlogits[t][e] * x[t][c].  The block's
+// four waves take a quarter of the chunk each (tokens added in order), a
+// lane kCpt adjacent columns (one 16-byte load a token when kCpt = 8), and
+// wave 0 adds the four quarter sums in wave order (fixed, deterministic).
+// The y == 0 blocks also sum dlogits over the chunk (db).  With part ==
+// nullptr only the db sums are made (x unread).  Each wave loads the x
+// values of kAhead tokens before using any of them, so the loads overlap.
 constexpr int kRbTok = 256;
 constexpr int kRbExp = 32;
-constexpr int kRbCols = 512;          // columns of a block, two a thread
-template <int kExp>
+template <int kExp, int kCpt>
 __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     const float* __restrict__ dlogits, const bf16_t* __restrict__ x, int T,
     int E, int d, float* __restrict__ part, float* __restrict__ db_part) {
-  constexpr int kRbExp = kExp;
-  __shared__ __attribute__((aligned(16))) float s_dl[kRbTok][kRbExp];
+  constexpr int kCols = 64 * kCpt;          // columns of a block
+  constexpr int kWaveTok = kRbTok / 4;      // tokens of a wave
+  constexpr int kAhead = 8;
+  static_assert(kWaveTok % kAhead == 0, "a wave's tokens come in kAhead");
+  __shared__ __attribute__((aligned(16))) float s_dl[kRbTok][kExp];
+  __shared__ __attribute__((aligned(16))) float s_red[3][kExp][kCols];
   const int tc = blockIdx.x;
-  const int c = blockIdx.y * kRbCols + threadIdx.x * 2;
-  const int e0 = blockIdx.z * kRbExp;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.y * kCols + lane * kCpt;
+  const int e0 = blockIdx.z * kExp;
   const int t0 = tc * kRbTok;
-  const int ne = min(kRbExp, E - e0), nt = min(kRbTok, T - t0);
-  for (int i = threadIdx.x; i < kRbTok * kRbExp; i += 256) {
-    const int tt = i / kRbExp, ee = i % kRbExp;
+  const int ne = min(kExp, E - e0), nt = min(kRbTok, T - t0);
+  for (int i = threadIdx.x; i < kRbTok * kExp; i += 256) {
+    const int tt = i / kExp, ee = i % kExp;
     s_dl[tt][ee] = (tt < nt && ee < ne)
         ? dlogits[static_cast<int64_t>(t0 + tt) * E + e0 + ee] : 0.0f;
   }
@@ -281,41 +300,76 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     for (int tt = 0; tt < nt; ++tt) acc += s_dl[tt][threadIdx.x];
     db_part[static_cast<int64_t>(tc) * E + e0 + threadIdx.x] = acc;
   }
-  if (part == nullptr || c >= d) return;
-  // columns c and c+1 (d is a multiple of 8), tokens added in order
-  float acc0[kRbExp], acc1[kRbExp];
+  if (part == nullptr) return;
+  // columns c .. c + kCpt - 1 (d is a multiple of 8, so all or none exist)
+  const bool col_ok = c < d;
+  float acc[kExp][kCpt];
 #pragma unroll
-  for (int ee = 0; ee < kRbExp; ++ee) { acc0[ee] = 0.0f; acc1[ee] = 0.0f; }
+  for (int ee = 0; ee < kExp; ++ee)
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) acc[ee][j] = 0.0f;
+  const int tw0 = wave * kWaveTok, tw1 = min(nt, tw0 + kWaveTok);
   const bf16_t* xc = x + static_cast<int64_t>(t0) * d + c;
-  constexpr int kAhead = 8;
-  for (int tb = 0; tb < nt; tb += kAhead) {
-    uint32_t xv[kAhead];
+  using Vec = typename std::conditional<kCpt == 8, i32x4, uint32_t>::type;
+  constexpr int kWords = kCpt / 2;
+  for (int tb = tw0; tb < tw1; tb += kAhead) {
+    Vec xv[kAhead];
 #pragma unroll
     for (int u = 0; u < kAhead; ++u)
-      xv[u] = (tb + u < nt) ? *reinterpret_cast<const uint32_t*>(
-                                  xc + static_cast<int64_t>(tb + u) * d)
-                            : 0u;
+      xv[u] = (col_ok && tb + u < tw1)
+          ? *reinterpret_cast<const Vec*>(xc + static_cast<int64_t>(tb + u) * d)
+          : Vec{};
+    // a token past the chunk adds exact zeros (its x and dlogits are 0)
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
-      if (tb + u >= nt) break;
       const int tt = tb + u;
-      const float x0 = bf_lo(xv[u]), x1 = bf_hi(xv[u]);
+      float xf[kCpt];
 #pragma unroll
-      for (int q = 0; q < kRbExp / 4; ++q) {
+      for (int w = 0; w < kWords; ++w) {
+        uint32_t word;
+        if constexpr (kCpt == 8) word = static_cast<uint32_t>(xv[u][w]);
+        else word = xv[u];
+        xf[2 * w] = bf_lo(word);
+        xf[2 * w + 1] = bf_hi(word);
+      }
+#pragma unroll
+      for (int q = 0; q < kExp / 4; ++q) {
         const f32x4 g = *reinterpret_cast<const f32x4*>(&s_dl[tt][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc0[4 * q + r] += g[r] * x0;
-          acc1[4 * q + r] += g[r] * x1;
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int j = 0; j < kCpt; ++j) acc[4 * q + r][j] += g[r] * xf[j];
       }
     }
   }
-  for (int ee = 0; ee < ne; ++ee) {
-    float2 o;
-    o.x = acc0[ee];
-    o.y = acc1[ee];
-    *reinterpret_cast<float2*>(part + (static_cast<int64_t>(tc) * E + e0 + ee) * d + c) = o;
+  if (wave > 0) {
+#pragma unroll
+    for (int ee = 0; ee < kExp; ++ee)
+#pragma unroll
+      for (int j = 0; j < kCpt; ++j)
+        s_red[wave - 1][ee][lane * kCpt + j] = acc[ee][j];
+  }
+  __syncthreads();
+  if (wave != 0 || !col_ok) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int ee = 0; ee < kExp; ++ee)
+#pragma unroll
+      for (int j = 0; j < kCpt; ++j) acc[ee][j] += s_red[w][ee][lane * kCpt + j];
+  // constant indices keep acc in registers
+#pragma unroll
+  for (int ee = 0; ee < kExp; ++ee) {
+    if (ee < ne) {
+      float* dst = part + (static_cast<int64_t>(tc) * E + e0 + ee) * d + c;
+#pragma unroll
+      for (int j = 0; j < kCpt; j += 2) {
+        float2 o;
+        o.x = acc[ee][j];
+        o.y = acc[ee][j + 1];
+        *reinterpret_cast<float2*>(dst + j) = o;
+      }
+    }
   }
 }
 
@@ -434,10 +488,19 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
   return hipGetLastError();
 }
 
+// Lanes that share one token in the routing kernels: the smallest power of
+// two that leaves each lane at most 8 experts (at most 64 lanes; 16 experts
+// a lane at E = 1024).  A lane's own experts are compared in registers, and
+// only log2(G) shuffle steps a round cross lanes.
+int route_lanes(int E) {
+  int G = 1;
+  while (G * 8 < E && G < 64) G <<= 1;
+  return G;
+}
+
 hipError_t launch_route(const float* logits, int64_t T, int E, int k,
                         int renorm, int32_t* idx, float* w, hipStream_t s) {
-  int G = 1;
-  while (G < E && G < 64) G <<= 1;
+  const int G = route_lanes(E);
   const int vpl_needed = (E + G - 1) / G;
   const int tokens_per_block = 256 / G;
   const unsigned grid =
@@ -484,8 +547,7 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
   float* db_part = reinterpret_cast<float*>(w);
   w += up(static_cast<size_t>(chunks * E * 4));
   float* q_part = reinterpret_cast<float*>(w);
-  int G = 1;
-  while (G < E && G < 64) G <<= 1;
+  const int G = route_lanes(E);
   const int vpl_needed = (E + G - 1) / G;
   const int tokens_per_block = 256 / G;
   const unsigned grid =
@@ -509,19 +571,22 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
   if (dw_g || db) {
     // without dw_g only the db sums are wanted: one column block, x unread
     const int64_t dd = dw_g ? d : 0;
-    // experts a block: 8 when they all fit, else 32 (grid.z covers E)
+    // experts a block: 8 (8 columns a lane) when they all fit, else 32
+    // (2 columns a lane); grid.z covers E
     const int eb = E <= 8 ? 8 : kRbExp;
+    const int cols = eb == 8 ? 64 * 8 : 64 * 2;
     dim3 g2(static_cast<unsigned>(chunks),
-            static_cast<unsigned>(dw_g ? (d + kRbCols - 1) / kRbCols : 1),
+            static_cast<unsigned>(dw_g ? (d + cols - 1) / cols : 1),
             static_cast<unsigned>((E + eb - 1) / eb));
     if (eb == 8)
-      hipLaunchKernelGGL(router_dwg_partial_kernel<8>, g2, dim3(256), 0, s,
-                         dlogits, x, Ti, E, static_cast<int>(dd),
-                         dw_g ? part : nullptr, db_part);
-    else
-      hipLaunchKernelGGL(router_dwg_partial_kernel<kRbExp>, g2, dim3(256), 0,
+      hipLaunchKernelGGL((router_dwg_partial_kernel<8, 8>), g2, dim3(256), 0,
                          s, dlogits, x, Ti, E, static_cast<int>(dd),
                          dw_g ? part : nullptr, db_part);
+    else
+      hipLaunchKernelGGL((router_dwg_partial_kernel<kRbExp, 2>), g2,
+                         dim3(256), 0, s, dlogits, x, Ti, E,
+                         static_cast<int>(dd), dw_g ? part : nullptr,
+                         db_part);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t n = std::max<int64_t>(static_cast<int64_t>(E) * dd, E);
     hipLaunchKernelGGL(router_dwg_reduce_kernel,
