@@ -144,4 +144,53 @@ __device__ __forceinline__ float dpp_group_max(float v) {
   return v;
 }
 
+
+// ---------------------------------------------------------------- [k][mn] tiles
+// An LDS tile of 64 k-rows x 256 bf16 columns kept as it lies in memory
+// (512-byte rows), the 16-byte chunk c of k-row r at chunk c ^ ((r & 3) << 2)
+// of its row: 64 lanes storing two rows' 32 chunks, and 64 lanes of a
+// transposed fragment read touching 8 rows x 4 chunks, both spread evenly
+// over the LDS banks.  kmn_off is the byte offset of chunk c of row r.
+__device__ __forceinline__ int kmn_off(int r, int c) {
+  return r * 512 + ((c ^ ((r & 3) << 2)) << 4);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA 32x32x16 fragment (lane l: column l % 32, k = 8 (l / 32) + 0..7 of
+// k-slice kk) of a [k][mn] LDS tile laid out by kmn_off, for the 32
+// columns starting at 32 * blk.  ds_read_b64_tr_b16 works on groups of 16
+// lanes: lane 4R + m of a group gives the address of 4 consecutive
+// elements, which become columns 4m..4m+3 of row R of a 4 x 16 block, and
+// lane j receives column j (rows 0..3).  Group g = l / 16 of the fragment
+// covers k-rows 8 (g / 2) + 0..3 (first read) and + 4..7 (second read,
+// 2048 bytes on) and columns 16 (g % 2) + 0..15.  lane_base and R come
+// from KmnLane.
+__device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
+                                            int R, int blk, int kk) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(tile) + lane_base +
+                     ((blk ^ R) << 6) + kk * 8192;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(p + 2048));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_v, v);
+}
+
+// The lane's fixed part of a frag_tr address (its row R and chunk inside a
+// 4 x 16 block, from its 16-lane group and position).
+struct KmnLane {
+  int base, R;
+  __device__ __forceinline__ explicit KmnLane(int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    R = j >> 2;
+    const int m = j & 3;
+    base = ((g >> 1) * 8 + R) * 512 + (2 * (g & 1) + (m >> 1)) * 16 +
+           (m & 1) * 8;
+  }
+};
+
 }  // namespace moe

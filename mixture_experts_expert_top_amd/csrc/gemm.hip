@@ -281,13 +281,10 @@ struct Mover<true> {
 };
 
 // MN-contiguous operand: 64 k-rows x 256 columns, kept in LDS as it lies
-// in memory ([k][mn], 512-byte rows) and transposed by the fragment reads
-// (ds_read_b64_tr_b16, see frag_tr).  Thread t moves the 16-byte column
-// chunk t % 32 of k-rows 8 (t / 32) + i, i = 0..7 (piece i); part 0 holds
-// pieces 0-3, part 1 pieces 4-7.  Chunk c of k-row r sits at chunk
-// c ^ ((r & 3) << 2) of its row: the 64 lanes of a store write two rows'
-// 32 chunks and the 64 lanes of a transposed read touch 8 rows x 4 chunks,
-// both spread evenly over the LDS banks.
+// in memory (the [k][mn] tile of kmn_off) and transposed by the fragment
+// reads (ds_read_b64_tr_b16, see frag_tr).  Thread t moves the 16-byte
+// column chunk t % 32 of k-rows 8 (t / 32) + i, i = 0..7 (piece i); part 0
+// holds pieces 0-3, part 1 pieces 4-7.
 template <>
 struct Mover<false> {
   uint32_t tpart;   // (kr*8 * ld + mc*8) * 2
@@ -312,36 +309,12 @@ struct Mover<false> {
 #pragma unroll
     for (int i = 4 * part; i < 4 * part + 4; ++i) {
       const int kr = kr0 + i;
-      *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(lds) + kr * 512 +
-                                ((cc ^ ((kr & 3) << 2)) << 4)) = v[i];
+      *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(lds) +
+                                kmn_off(kr, cc)) = v[i];
     }
   }
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// MFMA 32x32x16 fragment (lane l: column l % 32, k = 8 (l / 32) + 0..7 of
-// k-slice kk) of a [k][mn] LDS tile laid out by Mover<false>, for the 32
-// columns starting at 32 * blk.  ds_read_b64_tr_b16 works on groups of 16
-// lanes: lane 4R + m of a group gives the address of 4 consecutive
-// elements, which become columns 4m..4m+3 of row R of a 4 x 16 block, and
-// lane j receives column j (rows 0..3).  Group g = l / 16 of the fragment
-// covers k-rows 8 (g / 2) + 0..3 (first read) and + 4..7 (second read,
-// 2048 bytes on) and columns 16 (g % 2) + 0..15.  lane_base holds the
-// lane's part of the address (its row and chunk inside the block).
-__device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
-                                            int R, int blk, int kk) {
-  const uint8_t* p = reinterpret_cast<const uint8_t*>(tile) + lane_base +
-                     ((blk ^ R) << 6) + kk * 8192;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(p + 2048));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8_v, v);
-}
 
 // E2M1 codes two a byte -> E4M3 codes one a byte, exactly (every E2M1
 // value is an E4M3 value): through f16 with gfx950's scaled conversions at
@@ -749,10 +722,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
 
   // Transposed fragment reads (MN-contiguous operands): the lane's fixed
   // part of the address, see frag_tr.
-  const int tr_g = lane >> 4, tr_j = lane & 15;
-  const int tr_R = tr_j >> 2, tr_m = tr_j & 3;
-  const int tr_base = ((tr_g >> 1) * 8 + tr_R) * 512 +
-                      (2 * (tr_g & 1) + (tr_m >> 1)) * 16 + (tr_m & 1) * 8;
+  const KmnLane kl(lane);
+  const int tr_base = kl.base, tr_R = kl.R;
   // bf16 fragments of k-slice kk (16 wide) of one LDS stage.
   auto read_frags = [&](int st, int kk, bf16x8_v* af, bf16x8_v* bf) {
     const bf16_t* sa = atile(st);

@@ -81,58 +81,99 @@ __global__ __launch_bounds__(64 * kRankWaves) void plan_rank_kernel(
 
 // Pass 2: one workgroup.  Each expert's column of chunk counts is turned
 // into exclusive chunk bases (in place) and the expert total by a group of
-// G lanes (G = 64 halved until G * E <= 1024): lane g sums its contiguous
-// range of chunks, the group scans those sums, and each lane rewrites its
-// range from its base.  An exclusive scan over experts then gives the
-// offsets.  Integer sums, so the result does not depend on the split.  A
-// lane reads its range kScanBatch counts at a time, all loads in flight
-// together: the kernel is one workgroup's memory latency, so the number of
-// round trips is its time.
-constexpr int kScanBatch = 32;
+// G lanes (G = 64 halved until G * E <= 1024); an exclusive scan over the
+// experts' totals then gives the offsets.  Integer sums, so the result
+// does not depend on how the work is split.  The kernel is one
+// workgroup's latency.  A table that fits (kScanLds ints with its
+// padding) is copied into LDS expert-major, rows of nchunks + 17 ints,
+// with coalesced 16-byte loads all in flight together; the G lanes of an
+// expert then walk its row G chunks a round (lane g takes chunk r G + g:
+// a shuffle scan over the lanes plus the running carry), so the 64 lanes
+// of a wave read distinct banks; the row is written back the same way.
+// A larger table is scanned in place in global memory, lane g taking a
+// contiguous range of chunks.
+constexpr int kScanLds = 34816;       // ints of LDS table (136 KiB)
+constexpr int kScanIn = 8;            // 16-byte loads in flight a thread
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ chunk_counts, int nchunks, int E,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int wsum[16];
+  __shared__ int s_tab[kScanLds];
+  const int t = threadIdx.x;
+  const int n = nchunks * E;
+  const int n4 = (E & 3) == 0 ? n >> 2 : 0;    // 16-byte moves need E % 4
+  const int S = nchunks + 17;                   // LDS row stride (odd)
+  const bool in_lds = S * E <= kScanLds;
   int G = 64;
   while (G > 1 && G * E > 1024) G >>= 1;
-  const int t = threadIdx.x;
   const int e = t / G, g = t - (t / G) * G;
-  const int per = (nchunks + G - 1) / G;
-  const int c0 = min(nchunks, g * per), c1 = min(nchunks, c0 + per);
-  int32_t* col = chunk_counts + e;
-  int sum = 0;
-  if (e < E) {
-    for (int cb = c0; cb < c1; cb += kScanBatch) {
-      int v[kScanBatch];
+  if (in_lds) {
+    // [chunk][expert] in global -> [expert][chunk] in LDS
+    const i32x4* src = reinterpret_cast<const i32x4*>(chunk_counts);
+    for (int b = t; b < n4; b += 1024 * kScanIn) {
+      i32x4 v[kScanIn];
 #pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        v[i] = cb + i < c1 ? col[static_cast<int64_t>(cb + i) * E] : 0;
+      for (int u = 0; u < kScanIn; ++u)
+        v[u] = b + u * 1024 < n4 ? src[b + u * 1024] : i32x4{};
 #pragma unroll
-      for (int i = 0; i < kScanBatch; ++i) sum += v[i];
-    }
-  }
-  int gincl = sum;
-  for (int m = 1; m < G; m <<= 1) {
-    const int o = __shfl_up(gincl, m, G);
-    if (g >= m) gincl += o;
-  }
-  if (e < E) {
-    int run = gincl - sum;
-    for (int cb = c0; cb < c1; cb += kScanBatch) {
-      int v[kScanBatch];
+      for (int u = 0; u < kScanIn; ++u) {
+        const int i = 4 * (b + u * 1024);
+        if (i < n) {
+          const int c = i / E, e4 = i - c * E;
 #pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        v[i] = cb + i < c1 ? col[static_cast<int64_t>(cb + i) * E] : 0;
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i) {
-        if (cb + i < c1) col[static_cast<int64_t>(cb + i) * E] = run;
-        run += v[i];
+          for (int q = 0; q < 4; ++q) s_tab[(e4 + q) * S + c] = v[u][q];
+        }
       }
     }
-    if (g == G - 1) {
-      s_cnt[e] = gincl;
-      counts[e] = gincl;
+    for (int i = 4 * n4 + t; i < n; i += 1024)
+      s_tab[(i % E) * S + i / E] = chunk_counts[i];
+    __syncthreads();
+    int carry = 0;
+    if (e < E) {
+      int* row = s_tab + e * S;
+      for (int c0 = 0; c0 < nchunks; c0 += G) {
+        const int c = c0 + g;
+        const int v = c < nchunks ? row[c] : 0;
+        int incl = v;
+        for (int m = 1; m < G; m <<= 1) {
+          const int o = __shfl_up(incl, m, G);
+          if (g >= m) incl += o;
+        }
+        if (c < nchunks) row[c] = carry + incl - v;
+        carry += __shfl(incl, G - 1, G);
+      }
+      if (g == G - 1) {
+        s_cnt[e] = carry;
+        counts[e] = carry;
+      }
+    }
+    __syncthreads();
+    // back to [chunk][expert]
+    for (int i = t; i < n; i += 1024) chunk_counts[i] = s_tab[(i % E) * S + i / E];
+  } else {
+    const int per = (nchunks + G - 1) / G;
+    const int c0 = min(nchunks, g * per), c1 = min(nchunks, c0 + per);
+    int32_t* col = chunk_counts + e;
+    int sum = 0;
+    if (e < E)
+      for (int c = c0; c < c1; ++c) sum += col[static_cast<int64_t>(c) * E];
+    int gincl = sum;
+    for (int m = 1; m < G; m <<= 1) {
+      const int o = __shfl_up(gincl, m, G);
+      if (g >= m) gincl += o;
+    }
+    if (e < E) {
+      int run = gincl - sum;
+      for (int c = c0; c < c1; ++c) {
+        const int v = col[static_cast<int64_t>(c) * E];
+        col[static_cast<int64_t>(c) * E] = run;
+        run += v;
+      }
+      if (g == G - 1) {
+        s_cnt[e] = gincl;
+        counts[e] = gincl;
+      }
     }
   }
   __syncthreads();

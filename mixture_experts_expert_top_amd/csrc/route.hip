@@ -20,37 +20,42 @@ namespace {
 // ---------------------------------------------------------------- logits
 // logits[t][e] = x[t] . w_g[e] (+ bias[e]); a skinny GEMM (N = E) on bf16
 // MFMA 32x32x16, bound by the one read of x.  A workgroup owns 32 tokens x
-// 32 experts; its 8 waves split d into 8 contiguous ranges and their
-// partial tiles are summed in LDS in wave order (fixed, deterministic).
-// Each wave issues the loads of kLogitAhead k-steps before their MFMAs so
-// that enough of x is in flight to keep HBM busy.
+// 64 experts (two 32-expert blocks; one when the experts end sooner), so
+// x is read once for E <= 64; its 8 waves split d into 8 contiguous ranges
+// and their partial tiles are summed in LDS in wave order (fixed,
+// deterministic).  Each wave issues the loads of kLogitAhead k-steps
+// before their MFMAs so that enough of x is in flight to keep HBM busy.
 constexpr int kLogitThreads = 512;
 constexpr int kLogitWaves = kLogitThreads / 64;
 constexpr int kLogitAhead = 8;
+constexpr int kLogitExp = 64;
 
 __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int d, int E,
     float* __restrict__ logits) {
-  __shared__ float part[kLogitWaves][32 * 32];
+  __shared__ float part[kLogitWaves][2][32 * 32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * kLogitExp;
   const int row = lane & 31, kh = lane >> 5;
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc(x, static_cast<uint32_t>(static_cast<int64_t>(T) * d * 2));
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(wg, static_cast<uint32_t>(static_cast<int64_t>(E) * d * 2));
-  const int tok = t0 + row, ex = e0 + row;
-  const bool tok_ok = tok < T, ex_ok = ex < E;
+  const int tok = t0 + row;
+  const bool tok_ok = tok < T;
+  const bool two = e0 + 32 < E;           // uniform: second expert block
+  const bool ex_ok0 = e0 + row < E, ex_ok1 = e0 + 32 + row < E;
   // the range of the reduction owned by this wave, in steps of 16
   const int steps = (d + 15) / 16;
   const int q = (steps + kLogitWaves - 1) / kLogitWaves;
   const int s_begin = wave * q, s_end = min(steps, s_begin + q);
   const int64_t xrow = static_cast<int64_t>(tok) * d;
-  const int64_t wrow = static_cast<int64_t>(ex) * d;
-  f32x16 acc = {};
+  const int64_t wrow0 = static_cast<int64_t>(e0 + row) * d;
+  const int64_t wrow1 = wrow0 + static_cast<int64_t>(32) * d;
+  f32x16 acc0 = {}, acc1 = {};
   for (int s0 = s_begin; s0 < s_end; s0 += kLogitAhead) {
-    bf16x8_v a[kLogitAhead], b[kLogitAhead];
+    bf16x8_v a[kLogitAhead], b0[kLogitAhead], b1[kLogitAhead];
 #pragma unroll
     for (int u = 0; u < kLogitAhead; ++u) {
       // steps past the wave's range (or d) read zeros through kOob
@@ -58,29 +63,39 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
       const bool kok = s0 + u < s_end && kk < d;
       const uint32_t ox = (tok_ok && kok)
           ? static_cast<uint32_t>((xrow + kk) * 2) : kOob;
-      const uint32_t ow = (ex_ok && kok)
-          ? static_cast<uint32_t>((wrow + kk) * 2) : kOob;
+      const uint32_t ow0 = (ex_ok0 && kok)
+          ? static_cast<uint32_t>((wrow0 + kk) * 2) : kOob;
       a[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rx, ox));
-      b[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow));
+      b0[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow0));
+      if (two) {
+        const uint32_t ow1 = (ex_ok1 && kok)
+            ? static_cast<uint32_t>((wrow1 + kk) * 2) : kOob;
+        b1[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow1));
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kLogitAhead; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
+    for (int u = 0; u < kLogitAhead; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b0[u], acc0, 0, 0, 0);
+      if (two)
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b1[u], acc1, 0, 0,
+                                                       0);
+    }
   }
   // acc[v] = C[token i][expert j], i = (v/4)*8 + kh*4 + v%4, j = lane%32
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int i = (v >> 2) * 8 + kh * 4 + (v & 3);
-    part[wave][i * 32 + row] = acc[v];
+    part[wave][0][i * 32 + row] = acc0[v];
+    part[wave][1][i * 32 + row] = acc1[v];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 32 * 32; idx += kLogitThreads) {
-    const int i = idx >> 5, j = idx & 31;
-    const int t = t0 + i, e = e0 + j;
+  for (int idx = threadIdx.x; idx < 2 * 32 * 32; idx += kLogitThreads) {
+    const int h = idx >> 10, i = (idx >> 5) & 31, j = idx & 31;
+    const int t = t0 + i, e = e0 + 32 * h + j;
     if (t < T && e < E) {
-      float s = part[0][idx];
+      float s = part[0][h][idx & 1023];
 #pragma unroll
-      for (int w = 1; w < kLogitWaves; ++w) s += part[w][idx];
+      for (int w = 1; w < kLogitWaves; ++w) s += part[w][h][idx & 1023];
       if (bias) s += bias[e];
       logits[static_cast<int64_t>(t) * E + e] = s;
     }
@@ -262,114 +277,141 @@ __global__ __launch_bounds__(256) void router_dlogits_kernel(
   }
 }
 
-// Partial dW_g over one chunk of 256 tokens, a block of columns and up to
-// kExp experts (8 when E <= 8, else 32 a block): part[chunk][e][c] = the
-// sum over the chunk's tokens of dlogits[t][e] * x[t][c].  The block's
-// four waves take a quarter of the chunk each (tokens added in order), a
-// lane kCpt adjacent columns (one 16-byte load a token when kCpt = 8), and
-// wave 0 adds the four quarter sums in wave order (fixed, deterministic).
-// The y == 0 blocks also sum dlogits over the chunk (db).  With part ==
-// nullptr only the db sums are made (x unread).  Each wave loads the x
-// values of kAhead tokens before using any of them, so the loads overlap.
+// Partial dW_g over one chunk of kRbTok tokens on bf16 MFMA:
+// part[chunk][e][c] = the sum over the chunk's tokens of
+// dlogits[t][e] * x[t][c].  Each fp32 dlogits value is split into three
+// bf16 terms whose sum is the value exactly (the top 8 significant bits
+// rounded to nearest, then the next 8 of the remainder, then the last
+// 8), so every product with the bf16 x is exact in fp32 and the MFMA sums
+// them in fp32: the accuracy of an fp32 sum of the chunk's 3 * kRbTok
+// products, at matrix-core rate.  A block owns kDwCols columns, kDwExp
+// experts and the chunk; it stages kDwStep tokens at a time (x as a
+// [token][column] tile read transposed by frag_tr, dlogits as [expert]
+// [token]), and wave w keeps the 64 columns 64w.. x the 64 experts in four
+// 32 x 32 accumulators.  The y == 0 blocks also sum dlogits over the chunk
+// in token order (db).  With part == nullptr only the db sums are made (x
+// unread).
 constexpr int kRbTok = 256;
-constexpr int kRbExp = 32;
-template <int kExp, int kCpt>
+constexpr int kDwCols = 256;
+constexpr int kDwExp = 64;
+constexpr int kDwStep = 64;
+typedef float f32x8_v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf16x3(f32x8_v v, bf16x8_v* hi,
+                                             bf16x8_v* mid, bf16x8_v* lo) {
+  *hi = __builtin_convertvector(v, bf16x8_v);
+  const f32x8_v r1 = v - __builtin_convertvector(*hi, f32x8_v);
+  *mid = __builtin_convertvector(r1, bf16x8_v);
+  const f32x8_v r2 = r1 - __builtin_convertvector(*mid, f32x8_v);
+  *lo = __builtin_convertvector(r2, bf16x8_v);
+}
+
 __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
     const float* __restrict__ dlogits, const bf16_t* __restrict__ x, int T,
     int E, int d, float* __restrict__ part, float* __restrict__ db_part) {
-  constexpr int kCols = 64 * kCpt;          // columns of a block
-  constexpr int kWaveTok = kRbTok / 4;      // tokens of a wave
-  constexpr int kAhead = 8;
-  static_assert(kWaveTok % kAhead == 0, "a wave's tokens come in kAhead");
-  __shared__ __attribute__((aligned(16))) float s_dl[kRbTok][kExp];
-  __shared__ __attribute__((aligned(16))) float s_red[3][kExp][kCols];
+  __shared__ __attribute__((aligned(16))) bf16_t s_x[kDwStep * kDwCols];
+  // [expert][token], rows padded to 68 floats (16-byte aligned, and the
+  // transposing stores spread over the banks)
+  __shared__ __attribute__((aligned(16))) float s_dl[kDwExp][kDwStep + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tc = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.y * kCols + lane * kCpt;
-  const int e0 = blockIdx.z * kExp;
+  const int c0 = blockIdx.y * kDwCols, e0 = blockIdx.z * kDwExp;
   const int t0 = tc * kRbTok;
-  const int ne = min(kExp, E - e0), nt = min(kRbTok, T - t0);
-  for (int i = threadIdx.x; i < kRbTok * kExp; i += 256) {
-    const int tt = i / kExp, ee = i % kExp;
-    s_dl[tt][ee] = (tt < nt && ee < ne)
-        ? dlogits[static_cast<int64_t>(t0 + tt) * E + e0 + ee] : 0.0f;
-  }
-  __syncthreads();
-  if (blockIdx.y == 0 && threadIdx.x < ne) {
-    float acc = 0.0f;
-    for (int tt = 0; tt < nt; ++tt) acc += s_dl[tt][threadIdx.x];
-    db_part[static_cast<int64_t>(tc) * E + e0 + threadIdx.x] = acc;
-  }
-  if (part == nullptr) return;
-  // columns c .. c + kCpt - 1 (d is a multiple of 8, so all or none exist)
-  const bool col_ok = c < d;
-  float acc[kExp][kCpt];
+  const int nt = min(kRbTok, T - t0), ne = min(kDwExp, E - e0);
+  const bool want_x = part != nullptr;
+  const bool do_db = blockIdx.y == 0 && tid < ne;
+  const KmnLane kl(lane);
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int ee = 0; ee < kExp; ++ee)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < kCpt; ++j) acc[ee][j] = 0.0f;
-  const int tw0 = wave * kWaveTok, tw1 = min(nt, tw0 + kWaveTok);
-  const bf16_t* xc = x + static_cast<int64_t>(t0) * d + c;
-  using Vec = typename std::conditional<kCpt == 8, i32x4, uint32_t>::type;
-  constexpr int kWords = kCpt / 2;
-  for (int tb = tw0; tb < tw1; tb += kAhead) {
-    Vec xv[kAhead];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  float db = 0.0f;
+  for (int s0 = 0; s0 < nt; s0 += kDwStep) {
+    if (want_x) {
+      // thread t moves the 16-byte column chunk t % 32 of token rows
+      // 8 (t / 32) + i of the step
+      const int cc = tid & 31, kr0 = (tid >> 5) * 8;
+      const int col = c0 + cc * 8;
+      i32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < kAhead; ++u)
-      xv[u] = (col_ok && tb + u < tw1)
-          ? *reinterpret_cast<const Vec*>(xc + static_cast<int64_t>(tb + u) * d)
-          : Vec{};
-    // a token past the chunk adds exact zeros (its x and dlogits are 0)
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) {
-      const int tt = tb + u;
-      float xf[kCpt];
-#pragma unroll
-      for (int w = 0; w < kWords; ++w) {
-        uint32_t word;
-        if constexpr (kCpt == 8) word = static_cast<uint32_t>(xv[u][w]);
-        else word = xv[u];
-        xf[2 * w] = bf_lo(word);
-        xf[2 * w + 1] = bf_hi(word);
+      for (int i = 0; i < 8; ++i) {
+        const int row = s0 + kr0 + i;
+        v[i] = (row < nt && col < d)
+            ? *reinterpret_cast<const i32x4*>(
+                  x + static_cast<int64_t>(t0 + row) * d + col)
+            : i32x4{};
       }
 #pragma unroll
-      for (int q = 0; q < kExp / 4; ++q) {
-        const f32x4 g = *reinterpret_cast<const f32x4*>(&s_dl[tt][4 * q]);
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(s_x) +
+                                  kmn_off(kr0 + i, cc)) = v[i];
+    }
+    {
+      // thread t moves experts 16 (t % 4) + 0..15 of token t / 4
+      const int tt = tid >> 2, eb = (tid & 3) * 16;
+      const bool tok = s0 + tt < nt;
+      const float* src = dlogits + static_cast<int64_t>(t0 + s0 + tt) * E + e0;
+      float g[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+      for (int q = 0; q < 16; ++q)
+        g[q] = (tok && eb + q < ne) ? src[eb + q] : 0.0f;
 #pragma unroll
-          for (int j = 0; j < kCpt; ++j) acc[4 * q + r][j] += g[r] * xf[j];
+      for (int q = 0; q < 16; ++q) s_dl[eb + q][tt] = g[q];
+    }
+    __syncthreads();
+    if (do_db)
+      for (int tt = 0; tt < kDwStep; ++tt) db += s_dl[tid][tt];
+    if (want_x) {
+#pragma unroll
+      for (int kk = 0; kk < kDwStep / 16; ++kk) {
+        bf16x8_v a[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[i] = frag_tr(s_x, kl.base, kl.R, wave * 2 + i, kk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float* p = &s_dl[32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)];
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(p);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(p + 4);
+          const f32x8_v g = {g0[0], g0[1], g0[2], g0[3],
+                             g1[0], g1[1], g1[2], g1[3]};
+          bf16x8_v hi, mid, lo;
+          split_bf16x3(g, &hi, &mid, &lo);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a[i], hi, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a[i], mid, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a[i], lo, acc[i][j], 0, 0, 0);
+          }
+        }
       }
     }
+    __syncthreads();
   }
-  if (wave > 0) {
+  if (do_db) db_part[static_cast<int64_t>(tc) * E + e0 + tid] = db;
+  if (!want_x) return;
+  // acc[i][j][v] = column c0 + 64 wave + 32 i + 8 (v / 4) + 4 (lane / 32)
+  // + v % 4 (rows of the MFMA) for expert e0 + 32 j + lane % 32
 #pragma unroll
-    for (int ee = 0; ee < kExp; ++ee)
+  for (int j = 0; j < 2; ++j) {
+    const int e = 32 * j + (lane & 31);
+    if (e >= ne) continue;
+    float* dst = part + (static_cast<int64_t>(tc) * E + e0 + e) * d;
 #pragma unroll
-      for (int j = 0; j < kCpt; ++j)
-        s_red[wave - 1][ee][lane * kCpt + j] = acc[ee][j];
-  }
-  __syncthreads();
-  if (wave != 0 || !col_ok) return;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int ee = 0; ee < kExp; ++ee)
-#pragma unroll
-      for (int j = 0; j < kCpt; ++j) acc[ee][j] += s_red[w][ee][lane * kCpt + j];
-  // constant indices keep acc in registers
-#pragma unroll
-  for (int ee = 0; ee < kExp; ++ee) {
-    if (ee < ne) {
-      float* dst = part + (static_cast<int64_t>(tc) * E + e0 + ee) * d + c;
-#pragma unroll
-      for (int j = 0; j < kCpt; j += 2) {
-        float2 o;
-        o.x = acc[ee][j];
-        o.y = acc[ee][j + 1];
-        *reinterpret_cast<float2*>(dst + j) = o;
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + wave * 64 + 32 * i + 8 * q + 4 * (lane >> 5);
+        if (c < d) {
+          const f32x4 o = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(dst + c) = o;
+        }
       }
-    }
   }
 }
 
@@ -380,8 +422,18 @@ __global__ __launch_bounds__(256) void router_dwg_reduce_kernel(
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n = static_cast<int64_t>(E) * d;
   if (dw && i < n) {
+    // kAhead chunks' loads in flight at a time, added in chunk order
+    constexpr int kAhead = 8;
     float acc = 0.0f;
-    for (int tc = 0; tc < chunks; ++tc) acc += part[tc * n + i];
+    for (int tb = 0; tb < chunks; tb += kAhead) {
+      float v[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        v[u] = tb + u < chunks ? part[(tb + u) * n + i] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        if (tb + u < chunks) acc += v[u];
+    }
     dw[i] = acc;
   }
   if (db && i < E) {
@@ -425,23 +477,34 @@ __global__ __launch_bounds__(256) void router_dx_kernel(
       for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
     }
   }
-  for (int e = 0; e < E; ++e) {
-    const i32x4 w =
-        *reinterpret_cast<const i32x4*>(wg + static_cast<int64_t>(e) * d + c);
-    float wv[8];
+  // the w_g rows of kDxAhead experts are loaded before any is used
+  constexpr int kDxAhead = 4;
+  for (int eb = 0; eb < E; eb += kDxAhead) {
+    i32x4 wr[kDxAhead];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wv[2 * q] = bf_lo(static_cast<uint32_t>(w[q]));
-      wv[2 * q + 1] = bf_hi(static_cast<uint32_t>(w[q]));
+    for (int u = 0; u < kDxAhead; ++u)
+      wr[u] = eb + u < E ? *reinterpret_cast<const i32x4*>(
+                               wg + static_cast<int64_t>(eb + u) * d + c)
+                         : i32x4{};
+#pragma unroll
+    for (int u = 0; u < kDxAhead; ++u) {
+      if (eb + u >= E) break;
+      const int e = eb + u;
+      float wv[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wv[2 * q] = bf_lo(static_cast<uint32_t>(wr[u][q]));
+        wv[2 * q + 1] = bf_hi(static_cast<uint32_t>(wr[u][q]));
+      }
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok + 4);
+      const float g[kDxTok] = {g0[0], g0[1], g0[2], g0[3],
+                               g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+      for (int tt = 0; tt < kDxTok; ++tt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[tt][i] += g[tt] * wv[i];
     }
-    const f32x4 g0 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok);
-    const f32x4 g1 = *reinterpret_cast<const f32x4*>(s_dl + e * kDxTok + 4);
-    const float g[kDxTok] = {g0[0], g0[1], g0[2], g0[3],
-                             g1[0], g1[1], g1[2], g1[3]};
-#pragma unroll
-    for (int tt = 0; tt < kDxTok; ++tt)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[tt][i] += g[tt] * wv[i];
   }
 #pragma unroll
   for (int tt = 0; tt < kDxTok; ++tt) {
@@ -481,7 +544,7 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
                                 const float* bias, int64_t T, int64_t d, int E,
                                 float* logits, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((T + 31) / 32),
-            static_cast<unsigned>((E + 31) / 32));
+            static_cast<unsigned>((E + kLogitExp - 1) / kLogitExp));
   hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kLogitThreads), 0, s, x,
                      w_g, bias, static_cast<int>(T), static_cast<int>(d), E,
                      logits);
@@ -571,22 +634,12 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
   if (dw_g || db) {
     // without dw_g only the db sums are wanted: one column block, x unread
     const int64_t dd = dw_g ? d : 0;
-    // experts a block: 8 (8 columns a lane) when they all fit, else 32
-    // (2 columns a lane); grid.z covers E
-    const int eb = E <= 8 ? 8 : kRbExp;
-    const int cols = eb == 8 ? 64 * 8 : 64 * 2;
     dim3 g2(static_cast<unsigned>(chunks),
-            static_cast<unsigned>(dw_g ? (d + cols - 1) / cols : 1),
-            static_cast<unsigned>((E + eb - 1) / eb));
-    if (eb == 8)
-      hipLaunchKernelGGL((router_dwg_partial_kernel<8, 8>), g2, dim3(256), 0,
-                         s, dlogits, x, Ti, E, static_cast<int>(dd),
-                         dw_g ? part : nullptr, db_part);
-    else
-      hipLaunchKernelGGL((router_dwg_partial_kernel<kRbExp, 2>), g2,
-                         dim3(256), 0, s, dlogits, x, Ti, E,
-                         static_cast<int>(dd), dw_g ? part : nullptr,
-                         db_part);
+            static_cast<unsigned>(dw_g ? (d + kDwCols - 1) / kDwCols : 1),
+            static_cast<unsigned>((E + kDwExp - 1) / kDwExp));
+    hipLaunchKernelGGL(router_dwg_partial_kernel, g2, dim3(256), 0, s,
+                       dlogits, x, Ti, E, static_cast<int>(dd),
+                       dw_g ? part : nullptr, db_part);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t n = std::max<int64_t>(static_cast<int64_t>(E) * dd, E);
     hipLaunchKernelGGL(router_dwg_reduce_kernel,

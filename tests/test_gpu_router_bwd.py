@@ -145,13 +145,17 @@ def test_router_backward_parity(T, E, k, d, renorm, use_counts, bias):
 
     xn, wgn = h64(x), h64(w_g)
     dW, dB, dXr = R.router_backward(xn, wgn, dL)
-    chain = 258 + (T + 255) // 256
+    # dW_g: each chunk of 256 tokens is an fp32 sum of 3 * 256 exact
+    # products (every dlogits value split into three bf16 terms), in any
+    # order, then the chunks are added in order; db: 256 terms a chunk
+    chunks = (T + 255) // 256
+    chain = 3 * 256 + 2 + chunks
     ax = np.abs(xn)
     _check("dw_g", h64(dw_g), dW,
            chain * EPS * (np.abs(dL).T @ ax) + dl_bound.T @ ax + 1e-37)
     _check("db", h64(db), dB,
-           chain * EPS * np.abs(dL).sum(axis=0) + dl_bound.sum(axis=0)
-           + 1e-37)
+           (258 + chunks) * EPS * np.abs(dL).sum(axis=0)
+           + dl_bound.sum(axis=0) + 1e-37)
     ref_dx = h64(dx_in) + dXr
     fp32_err = (E + 2) * EPS * (np.abs(h64(dx_in)) + np.abs(dL) @ np.abs(wgn)) \
         + dl_bound @ np.abs(wgn)
