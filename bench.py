@@ -160,6 +160,7 @@ def copy_calibration():
 #              GRBM_GUI_ACTIVE SQ_BUSY_CYCLES --kernel-trace
 #                                                  --steps 2 --warmup 1
 #   cal_fetch, cal_write   the same two counters over --copy-calibration
+#                          (in DIR or in its parent)
 # Each run's dispatches of this library are cut into steps at the router
 # score kernel; the first step of each run is dropped (cold caches) and the
 # rest are averaged per position in the step.
@@ -179,6 +180,31 @@ STEP_KERNELS = {
         ("dp_reduce", ["dp_reduce_kernel"]),
         ("wgrad_down", ["grouped_gemm_kernel"]),
         ("gate_up_dgrad", ["grouped_gemm_kernel"]),
+        ("wgrad_gate_up", ["grouped_gemm_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
+        ("router_backward", ["router_dlogits_kernel",
+                             "router_dwg_partial_kernel",
+                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_aux_final_kernel"]),
+    ],
+    "mxfp8": [
+        ("router_logits", ["router_logits_kernel"]),
+        ("route", ["route_kernel"]),
+        ("quant_x", ["quant_rows_kernel"]),
+        ("permute", ["plan_rank_kernel", "plan_scan_kernel",
+                     "scatter_kernel"]),
+        ("quant_weights", ["quant_tokens_kernel", "quant_tokens_kernel"]),
+        ("gate_up_swiglu_fwd", ["grouped_gemm_kernel"]),
+        ("down_fwd", ["grouped_gemm_kernel"]),
+        ("unpermute_y", ["unpermute_kernel"]),
+        ("permute_dy", ["permute_rows_kernel"]),
+        ("permute_x", ["permute_rows_kernel"]),
+        ("quant_bwd_operands", ["quant_rows_kernel"]),
+        ("down_swiglu_bwd", ["grouped_gemm_kernel"]),
+        ("dp_reduce", ["dp_reduce_kernel"]),
+        ("gate_up_dgrad", ["grouped_gemm_kernel"]),
+        ("quant_tokens", ["quant_tokens_kernel", "quant_tokens_kernel"]),
+        ("wgrad_down", ["grouped_gemm_kernel"]),
         ("wgrad_gate_up", ["grouped_gemm_kernel"]),
         ("unpermute_dx", ["unpermute_kernel"]),
         ("router_backward", ["router_dlogits_kernel",
@@ -321,14 +347,58 @@ def summarize_counters(root, workload):
                 raise SystemExit(f"runs disagree at step position {i}: "
                                  f"{kt[i]['name']} vs {seq[i]['name']}")
     _label_stages(kt, family)
-    cal_f = _calibration(csvp("cal_fetch", "counter_collection"),
+    # the copy calibration runs sit beside the workload's runs or one up
+    cal_root = root if os.path.isdir(os.path.join(root, "cal_fetch")) \
+        else os.path.dirname(os.path.abspath(root))
+    cal_f = _calibration(os.path.join(cal_root, "cal_fetch",
+                                      "run_counter_collection.csv"),
                          "FETCH_SIZE")
-    cal_w = _calibration(csvp("cal_write", "counter_collection"),
+    cal_w = _calibration(os.path.join(cal_root, "cal_write",
+                                      "run_counter_collection.csv"),
                          "WRITE_SIZE")
     gib = float(1 << 30)
     bf, bw = gib / cal_f, gib / cal_w
     peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     lines = []
+    mode = "fwd+bwd" if wl.backward else "fwd"
+    lines.append(f"# Kernel time and counters, {workload} {mode} (T={T}, "
+                 f"d={d}, f={f}, E={E}, k={k}), {wl.prec}")
+    lines.append("")
+    lines.append("Made on one MI355X with these commands (from /tmp, "
+                 "TMPDIR=/tmp; <repo> is the repository root, <out> the "
+                 "output folder), then summarized by the last one, which "
+                 "uses no GPU:")
+    lines.append("")
+    lines.append("```")
+    run = (f"python3 <repo>/bench.py --workload {workload} "
+           "--no-cpu-baseline")
+    lines.append(f"rocprofv3 --kernel-trace --stats -d <out>/trace -o run "
+                 f"--output-format csv -- {run} --steps 5 --warmup 1")
+    for name, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
+                      ("mfma", "SQ_VALU_MFMA_BUSY_CYCLES "
+                               "SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE "
+                               "SQ_BUSY_CYCLES")):
+        lines.append(f"rocprofv3 --pmc {ctr} --kernel-trace -d <out>/{name} "
+                     f"-o run --output-format csv -- {run} --steps 2 "
+                     "--warmup 1")
+    for name, ctr in (("cal_fetch", "FETCH_SIZE"),
+                      ("cal_write", "WRITE_SIZE")):
+        lines.append(f"rocprofv3 --pmc {ctr} --kernel-trace -d <out>/{name} "
+                     f"-o run --output-format csv -- python3 <repo>/bench.py "
+                     "--copy-calibration")
+    lines.append(f"python3 <repo>/bench.py --summarize-counters <out> "
+                 f"--workload {workload}")
+    lines.append("```")
+    lines.append("")
+    lines.append("Per dispatch, averaged over the steps after the first. "
+                 "HBM GB/s = (read + write) / duration with the counters "
+                 "scaled by the copy calibration below.  MFMA busy = "
+                 "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+                 "SIMDs) (GRBM_GUI_ACTIVE sums the 8 XCDs' cycles); counted "
+                 "TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration "
+                 "(bf16 MFMAs only; tiles that pass an expert's last row "
+                 "are counted whole); clock = GRBM_GUI_ACTIVE / 8 / duration.")
+    lines.append("")
     lines.append(f"Copy calibration: a plain 1 GiB device copy reads "
                  f"FETCH_SIZE {cal_f:.0f} KiB and WRITE_SIZE {cal_w:.0f} KiB, "
                  f"so one counted KiB stands for {bf:.1f} B read and "
@@ -380,6 +450,24 @@ def summarize_counters(root, workload):
             }
     lines.append("")
     lines.append(f"Sum of the step's kernel times: {step_us / 1e3:.3f} ms.")
+    # every kernel of the traced run, this library's and torch's (input
+    # generation happens outside the timed steps)
+    import csv
+    stats = list(csv.DictReader(open(csvp("trace", "kernel_stats"))))
+    total_ns = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines.append("")
+    lines.append("Kernel time of the whole traced run (rocprofv3 --stats):")
+    lines.append("")
+    lines.append("| kernel | calls | avg us | total ms | % |")
+    lines.append("|---|---:|---:|---:|---:|")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        full, base = _base_kernel(r["Name"])
+        name = full if "grouped_gemm" in full or "moe" in r["Name"] \
+            else "torch:" + base.split("::")[-1][:40]
+        lines.append(f"| `{name}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total_ns:.2f} |")
     if not mx:
         lines.append("")
         lines.append("| GEMM stage | read GB | write GB | algorithmic read GB"

@@ -288,7 +288,13 @@ moe_status moe_grouped_mlp_fwd(moe_prec prec, const void* x_perm,
  *   that produces dAB (no bf16 dAB is stored).  With s_tok/s_tok_scales
  *   from the forward (ldt = moe_mxfp8_padded_rows(T*k, E)) S is not
  *   quantized again and s_saved may be NULL; for bf16 s_tok must be NULL.
- *   x_perm_scales is unused (NULL) for bf16 and MXFP8.
+ *   x_perm_scales is unused (NULL) for bf16 and MXFP8.  The weights' codes
+ *   along their columns may come in ready-made: w_gu_col_codes [d][E*2f]
+ *   with w_gu_col_scales [d][E*2f/32], and w2_col_codes [f][E*d] with
+ *   w2_col_scales [f][E*d/32], the col outputs of moe_mxfp8_quantize_weight
+ *   over w_gu viewed as [E*2f][d] and w2 viewed as [E*d][f] (as a training
+ *   forward makes them); the call then skips those two quantizations.
+ *   Each pair is given whole or NULL; all four are NULL for bf16.
  * prec == MOE_MXFP4: as MOE_MXFP8 except that x_perm is the forward's
  *   MXFP4 payload (codes [T*k][d/2], x_perm_scales [T*k][d/32]); the dW_gu
  *   GEMM reads it converted to MXFP4 blocks along each expert's tokens
@@ -306,6 +312,10 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                const void* ab_saved, const void* s_saved,
                                const uint8_t* s_tok,
                                const uint8_t* s_tok_scales, int64_t ldt,
+                               const uint8_t* w_gu_col_codes,
+                               const uint8_t* w_gu_col_scales,
+                               const uint8_t* w2_col_codes,
+                               const uint8_t* w2_col_scales,
                                const float* w_perm, void* dx_perm,
                                void* dw_gu, void* dw2, float* dp,
                                void* workspace, size_t workspace_bytes,

@@ -583,11 +583,25 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
                                const void* ab_saved, const void* s_saved,
                                const uint8_t* s_tok,
                                const uint8_t* s_tok_scales, int64_t ldt,
+                               const uint8_t* w_gu_col_codes,
+                               const uint8_t* w_gu_col_scales,
+                               const uint8_t* w2_col_codes,
+                               const uint8_t* w2_col_scales,
                                const float* w_perm, void* dx_perm,
                                void* dw_gu, void* dw2, float* dp,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   if (moe_status st = check_prec(prec)) return st;
+  REQUIRE_OPT_PTR(w_gu_col_codes);
+  REQUIRE_OPT_PTR(w_gu_col_scales);
+  REQUIRE_OPT_PTR(w2_col_codes);
+  REQUIRE_OPT_PTR(w2_col_scales);
+  REQUIRE(!w_gu_col_codes == !w_gu_col_scales &&
+              !w2_col_codes == !w2_col_scales,
+          MOE_ERR_INVALID_ARG,
+          "column codes and their scales come together or not at all");
+  REQUIRE(is_mx(prec) || (!w_gu_col_codes && !w2_col_codes),
+          MOE_ERR_INVALID_ARG, "column weight codes are an MX input");
   REQUIRE_PTR(dout_perm);
   REQUIRE_PTR(x_perm);
   REQUIRE_PTR(offsets);
@@ -641,27 +655,34 @@ moe_status moe_grouped_mlp_bwd(moe_prec prec, const void* dout_perm,
 #define MX_STEP(call, what)                                           \
     e = (call);                                                       \
     if (e != hipSuccess) return hip_status(e, "moe_grouped_mlp_bwd/" what)
-    // operands of the data gradients
+    // operands of the data gradients: the weights' column codes come in
+    // ready-made or are made here
     MX_STEP(moe::launch_mx_quant_rows(dO, Tk, d, ws + X.doq, ws + X.dos,
                                       stream), "quant_dO");
-    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w2),
-                                        nullptr, E * d, f, nullptr, 1,
-                                        ws + X.w2tq, ws + X.w2ts, E * d,
-                                        stream), "quant_W2");
-    MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w_gu),
-                                        nullptr, E * 2 * f, d, nullptr, 1,
-                                        ws + X.wgutq, ws + X.wguts,
-                                        E * 2 * f, stream), "quant_W_gu");
-    MX_STEP(moe::gemm_mx_fc2_dgrad(ws + X.doq, ws + X.dos, ws + X.w2tq,
-                                   ws + X.w2ts, E * d, offsets, E, Tk, d, f,
+    const uint8_t* w2tq = w2_col_codes ? w2_col_codes : ws + X.w2tq;
+    const uint8_t* w2ts = w2_col_scales ? w2_col_scales : ws + X.w2ts;
+    const uint8_t* wgutq = w_gu_col_codes ? w_gu_col_codes : ws + X.wgutq;
+    const uint8_t* wguts = w_gu_col_scales ? w_gu_col_scales : ws + X.wguts;
+    if (!w2_col_codes)
+      MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w2),
+                                          nullptr, E * d, f, nullptr, 1,
+                                          ws + X.w2tq, ws + X.w2ts, E * d,
+                                          stream), "quant_W2");
+    if (!w_gu_col_codes)
+      MX_STEP(moe::launch_mx_quant_tokens(static_cast<const bf16_t*>(w_gu),
+                                          nullptr, E * 2 * f, d, nullptr, 1,
+                                          ws + X.wgutq, ws + X.wguts,
+                                          E * 2 * f, stream), "quant_W_gu");
+    MX_STEP(moe::gemm_mx_fc2_dgrad(ws + X.doq, ws + X.dos, w2tq,
+                                   w2ts, E * d, offsets, E, Tk, d, f,
                                    static_cast<const bf16_t*>(ab_saved),
                                    w_perm, nullptr, ws + X.dabq, ws + X.dabs,
                                    ws + X.dabt, ws + X.dabts, tp, dp_part,
                                    stream), "mx_fc2_dgrad");
     MX_STEP(moe::launch_dp_reduce(dp_part, moe::gemm_dp_tiles(f), pos, T, k,
                                   dp, stream), "dp");
-    MX_STEP(moe::gemm_mx_fc1_dgrad(ws + X.dabq, ws + X.dabs, ws + X.wgutq,
-                                   ws + X.wguts, E * 2 * f, offsets, E, Tk, d,
+    MX_STEP(moe::gemm_mx_fc1_dgrad(ws + X.dabq, ws + X.dabs, wgutq,
+                                   wguts, E * 2 * f, offsets, E, Tk, d,
                                    f, static_cast<float*>(dx_perm), stream),
             "mx_fc1_dgrad");
     // token-axis operands of the weight gradients

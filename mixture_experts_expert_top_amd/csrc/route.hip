@@ -553,17 +553,20 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
 
 // Lanes that share one token in the routing kernels: the smallest power of
 // two that leaves each lane at most 8 experts (at most 64 lanes; 16 experts
-// a lane at E = 1024).  A lane's own experts are compared in registers, and
-// only log2(G) shuffle steps a round cross lanes.
-int route_lanes(int E) {
+// a lane at E = 1024) -- a lane's own experts are compared in registers and
+// only log2(G) shuffle steps a round cross lanes -- but more, up to one
+// expert a lane, while the grid (256 / G tokens a block) would leave
+// compute units idle.
+int route_lanes(int E, int64_t T) {
   int G = 1;
   while (G * 8 < E && G < 64) G <<= 1;
+  while (G < 64 && G < E && T * G < 256 * 256) G <<= 1;
   return G;
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k,
                         int renorm, int32_t* idx, float* w, hipStream_t s) {
-  const int G = route_lanes(E);
+  const int G = route_lanes(E, T);
   const int vpl_needed = (E + G - 1) / G;
   const int tokens_per_block = 256 / G;
   const unsigned grid =
@@ -610,7 +613,7 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx,
   float* db_part = reinterpret_cast<float*>(w);
   w += up(static_cast<size_t>(chunks * E * 4));
   float* q_part = reinterpret_cast<float*>(w);
-  const int G = route_lanes(E);
+  const int G = route_lanes(E, T);
   const int vpl_needed = (E + G - 1) / G;
   const int tokens_per_block = 256 / G;
   const unsigned grid =

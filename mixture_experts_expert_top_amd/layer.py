@@ -372,17 +372,22 @@ class MoEPathMX(MoEPath):
         xp, xps = ((self.xpq, self.xps) if self.act_fp4
                    else (self.x_perm, None))
         if timers is None:
+            # when training, the forward's column-wise weight codes go in
+            # ready-made
+            cols = ({"w_gu_col": (self.wgutq, self.wguts),
+                     "w2_col": (self.w2tq, self.w2ts)} if self.training
+                    else {})
             moe.moe_grouped_mlp_bwd(self.prec, self.dout_perm, xp,
                                     self.offsets, self.pos, w_gu, w2, self.ab,
                                     None, self.w_perm, self.dx_perm,
                                     self.dw_gu, self.dw2, self.dp,
                                     self.ws_bwd, s_tok=self.st,
                                     s_tok_scales=self.sts,
-                                    x_perm_scales=xps)
+                                    x_perm_scales=xps, **cols)
         else:
-            # the kernels of moe_grouped_mlp_bwd in its order, except that
-            # when training the column-wise weight codes come from the
-            # forward's quantize_weights
+            # the kernels of moe_grouped_mlp_bwd in its order (when
+            # training, the column-wise weight codes from the forward's
+            # quantize_weights, as the fused call is given them)
             tp = self.tk_pad
             with timers.around("quant_bwd_operands"):
                 moe.moe_mxfp8_quantize(self.dout_perm, 0, None, self.doq,

@@ -69,7 +69,7 @@ def _load():
                                       P]),
         "moe_grouped_mlp_bwd": (I32, [I32, P, P, P, P, P, I64, I32, I32,
                                       I64, I64, P, P, P, P, P, P, I64, P, P,
-                                      P, P, P, P, SZ, P]),
+                                      P, P, P, P, P, P, P, P, SZ, P]),
         "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
                                 P]),
         "moe_row_planes": (I32, [I64]),
@@ -315,9 +315,13 @@ def moe_grouped_mlp_fwd(prec, x_perm, x_perm_scales, offsets, w_gu,
 def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
                         ab_saved, s_saved, w_perm, dx_perm, dw_gu, dw2, dp,
                         workspace, stream=None, s_tok=None, s_tok_scales=None,
-                        x_perm_scales=None):
+                        x_perm_scales=None, w_gu_col=None, w2_col=None):
     """x_perm: bf16 rows (bf16 and MXFP8), or for MXFP4 the forward's
-    payload, E2M1 codes [T*k, d/2] with x_perm_scales [T*k, d/32]."""
+    payload, E2M1 codes [T*k, d/2] with x_perm_scales [T*k, d/32].
+    w_gu_col / w2_col (MX): (codes, scales) of the weights along their
+    columns as moe_mxfp8_quantize_weight makes them, codes [d, E*2f] /
+    [f, E*d], scales [d, E*2f/32] / [f, E*d/32]; None to quantize inside
+    the call."""
     Tk, d = dout_perm.shape
     T, k = pos.shape
     E, two_f, _ = w_gu.shape
@@ -339,13 +343,25 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
     _want(pos, "pos", torch.int32)
     _want(w_perm, "w_perm", torch.float32, (Tk,), allow_none=True)
     _want(dp, "dp", torch.float32, (T, k))
+    cols = {}
+    for n, pair, rows, width in (("w_gu_col", w_gu_col, d, E * 2 * f),
+                                 ("w2_col", w2_col, f, E * d)):
+        if pair is None:
+            cols[n] = (None, None)
+            continue
+        codes, scales = pair
+        _want(codes, n + " codes", torch.uint8, (rows, width))
+        _want(scales, n + " scales", torch.uint8, (rows, width // 32))
+        cols[n] = (codes, scales)
     nbytes = workspace.numel() * workspace.element_size() if workspace \
         is not None else 0
     _check("moe_grouped_mlp_bwd", lib.moe_grouped_mlp_bwd(
         prec, _p(dout_perm), _p(x_perm), _p(x_perm_scales), _p(offsets),
         _p(pos), T, k, E, d, f,
         _p(w_gu), _p(w2), _p(ab_saved), _p(s_saved), _p(s_tok),
-        _p(s_tok_scales), ldt, _p(w_perm), _p(dx_perm), _p(dw_gu), _p(dw2),
+        _p(s_tok_scales), ldt, _p(cols["w_gu_col"][0]),
+        _p(cols["w_gu_col"][1]), _p(cols["w2_col"][0]),
+        _p(cols["w2_col"][1]), _p(w_perm), _p(dx_perm), _p(dw_gu), _p(dw2),
         _p(dp), _p(workspace), nbytes, _stream(stream)))
 
 

@@ -124,12 +124,13 @@ def _fwd_args(prec=BF16, E=4, Tk=128, d=32, f=64, s=A, s_tok=None,
 
 
 def _bwd_args(prec=BF16, T=64, k=2, E=4, d=32, f=64, s=A, s_tok=None,
-              s_tok_scales=None, ldt=0, xs=None):
+              s_tok_scales=None, ldt=0, xs=None, cols=(None,) * 4):
     # prec, dout_perm, x_perm, x_perm_scales, offsets, pos, T, k, E, d, f,
-    # w_gu, w2, ab_saved, s_saved, s_tok, s_tok_scales, ldt, w_perm,
+    # w_gu, w2, ab_saved, s_saved, s_tok, s_tok_scales, ldt,
+    # w_gu_col_codes, w_gu_col_scales, w2_col_codes, w2_col_scales, w_perm,
     # dx_perm, dw_gu, dw2, dp, workspace
     return [prec, A, A, xs, A, A, T, k, E, d, f, A, A, A, s, s_tok,
-            s_tok_scales, ldt, A, A, A, A, A, A]
+            s_tok_scales, ldt, *cols, A, A, A, A, A, A]
 
 
 def test_mlp_fwd_validation():
@@ -183,6 +184,18 @@ def test_mx_mlp_validation():
     wsb = L.moe_workspace_bytes(2, MX, 64, 4, 2, 128, 128)
     args = _bwd_args(MX, d=128, f=128)
     assert b(*args, wsb - 1, None) == WS
+    # ready-made column codes of the weights: accepted in pairs (then only
+    # the workspace is short), refused without their scales or for bf16
+    assert b(*_bwd_args(MX, d=128, f=128, cols=(A, A, A, A)), wsb - 1,
+             None) == WS
+    assert b(*_bwd_args(MX, d=128, f=128, cols=(A, A, None, None)), wsb - 1,
+             None) == WS
+    assert b(*_bwd_args(MX, d=128, f=128, cols=(A, None, A, A)), wsb,
+             None) == INVALID
+    assert b(*_bwd_args(MX, d=128, f=128, cols=(MIS, A, None, None)), wsb,
+             None) == INVALID                                 # aligned
+    wsf = L.moe_workspace_bytes(2, BF16, 64, 4, 2, 32, 64)
+    assert b(*_bwd_args(cols=(A, A, None, None)), wsf, None) == INVALID
     args[9] = 160                                     # f % 128 != 0
     assert b(*args, wsb, None) == INVALID
 

@@ -543,3 +543,27 @@ def test_mx_fused_token_codes_equal_requantized():
     for a, b in ((dx_perm, path.dx_perm), (dw_gu, path.dw_gu),
                  (dw2, path.dw2), (dp, path.dp)):
         assert torch.equal(a, b)
+
+
+@gpu
+def test_mx_fused_bwd_ready_made_weight_codes():
+    """moe_grouped_mlp_bwd given the weights' column codes that the training
+    forward made (moe_mxfp8_quantize_weight) returns the same bits as when
+    it quantizes the weights along their columns itself."""
+    T, d, f, E, k = 300, 256, 384, 5, 2
+    inp, path = _run_mx_layer(T, d, f, E, k, False, 0.01, seed=7)
+    assert path.training
+    outs = []
+    for cols in ({}, {"w_gu_col": (path.wgutq, path.wguts),
+                      "w2_col": (path.w2tq, path.w2ts)}):
+        res = [torch.empty_like(t) for t in (path.dx_perm, path.dw_gu,
+                                             path.dw2, path.dp)]
+        moe.moe_grouped_mlp_bwd(moe.MOE_MXFP8, path.dout_perm, path.x_perm,
+                                path.offsets, path.pos, inp["w_gu"],
+                                inp["w2"], path.ab, None, path.w_perm, *res,
+                                path.ws_bwd, s_tok=path.st,
+                                s_tok_scales=path.sts, **cols)
+        outs.append(res)
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
