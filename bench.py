@@ -34,10 +34,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 (MX) MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
-# Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE and
-# WRITE_SIZE per dispatch, with the same counters' reading of a plain 1 GiB
-# device copy); valid only for the kernel source it was taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Measured HBM traffic of the grouped GEMMs of a workload (rocprofv3
+# FETCH_SIZE and WRITE_SIZE per dispatch, with the same counters' reading of
+# a plain 1 GiB device copy), one file a workload; valid only for the kernel
+# source it was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{}.json")
 # Recorded whole-chip MFMA ceiling with random operands (power-limited
 # clock): a measured figure, read as data.
 CEILING_FILE = os.path.join(ROOT, "profiles", "mfma_ceiling.json")
@@ -110,7 +111,7 @@ def measured_traffic(workload, stage):
     scaled by the copy calibration; None when there is no record for this
     workload and stage or the kernel source changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC_FILE.format(workload)) as fh:
             rec = json.load(fh)
         sha = gemm_source_sha256()
     except (OSError, ValueError):
@@ -204,6 +205,30 @@ STEP_KERNELS = {
         ("dp_reduce", ["dp_reduce_kernel"]),
         ("gate_up_dgrad", ["grouped_gemm_kernel"]),
         ("quant_tokens", ["quant_tokens_kernel", "quant_tokens_kernel"]),
+        ("wgrad_down", ["grouped_gemm_kernel"]),
+        ("wgrad_gate_up", ["grouped_gemm_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
+        ("router_backward", ["router_dlogits_kernel",
+                             "router_dwg_partial_kernel",
+                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_aux_final_kernel"]),
+    ],
+    "mxfp4": [
+        ("router_logits", ["router_logits_kernel"]),
+        ("route", ["route_kernel"]),
+        ("quant_x", ["quant_rows4_kernel"]),
+        ("permute", ["plan_rank_kernel", "plan_scan_kernel",
+                     "scatter_kernel"]),
+        ("quant_weights", ["quant_tokens_kernel", "quant_tokens_kernel"]),
+        ("gate_up_swiglu_fwd", ["grouped_gemm_kernel"]),
+        ("down_fwd", ["grouped_gemm_kernel"]),
+        ("unpermute_y", ["unpermute_kernel"]),
+        ("permute_dy", ["permute_rows_kernel"]),
+        ("quant_bwd_operands", ["quant_rows_kernel"]),
+        ("down_swiglu_bwd", ["grouped_gemm_kernel"]),
+        ("dp_reduce", ["dp_reduce_kernel"]),
+        ("gate_up_dgrad", ["grouped_gemm_kernel"]),
+        ("quant_tokens", ["quant_tokens_kernel", "quant_tokens4_kernel"]),
         ("wgrad_down", ["grouped_gemm_kernel"]),
         ("wgrad_gate_up", ["grouped_gemm_kernel"]),
         ("unpermute_dx", ["unpermute_kernel"]),
@@ -320,8 +345,8 @@ def _calibration(path, counter):
 
 def summarize_counters(root, workload):
     """Print a markdown summary of the counter runs under ``root`` and
-    write the grouped-GEMM traffic record ``root/traffic.json`` (the form
-    profiles/traffic.json takes)."""
+    write the grouped-GEMM traffic record ``root/traffic_<workload>.json``
+    (the form of profiles/traffic_<workload>.json)."""
     from mixture_experts_expert_top_amd import inputs, moe
     wl = inputs.WORKLOADS[workload]
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
@@ -484,7 +509,7 @@ def summarize_counters(root, workload):
            "kernel_source_sha256": gemm_source_sha256(),
            "copy_fetch_kib": cal_f, "copy_write_kib": cal_w,
            "stages": stages}
-    with open(os.path.join(root, "traffic.json"), "w") as fh:
+    with open(os.path.join(root, f"traffic_{workload}.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print("\n".join(lines))
 
@@ -602,8 +627,8 @@ def main():
                          "the HBM traffic counters")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print the summary of the rocprofv3 counter runs "
-                         "under DIR for --workload and write DIR/traffic.json"
-                         " (no GPU used)")
+                         "under DIR for --workload and write "
+                         "DIR/traffic_<workload>.json (no GPU used)")
     args = ap.parse_args()
     if args.config:
         args.workload = CONFIGS[args.config]
