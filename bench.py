@@ -5,9 +5,9 @@ backward: router scores (x . W_g), top-k routing, permutation, the grouped
 gate_up GEMM with the fused ScaledSwiGLU epilogue, the grouped down GEMM,
 the combine, the permutation of dY, the fused down-projection backward
 (dS, dSwiGLU, routing-weight gradient partials), their reduction, both
-variable-K weight-gradient GEMMs, the gate_up data gradient, the combine
-of dX (fp32) and the router backward (score gradient with the balancing
-term, dW_g, db, and the router's share of dX added before its rounding).
+variable-K weight-gradient GEMMs, the gate_up data gradient, the router
+backward (score gradient with the balancing term, dW_g, db) and the combine
+of dX with the router's share of it added before its one rounding.
 Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer,
@@ -67,7 +67,7 @@ def stage_flops(name, T, d, f, E, k):
     Tk = T * k
     return {
         "router_logits": 2.0 * T * d * E,
-        "router_backward": 4.0 * T * d * E,
+        "router_backward": 2.0 * T * d * E,     # dW_g (dX's share: combine)
         "gate_up_swiglu_fwd": 4.0 * Tk * d * f,
         "down_fwd": 2.0 * Tk * d * f,
         "down_swiglu_bwd": 2.0 * Tk * d * f,
@@ -92,9 +92,12 @@ def stage_bytes(name, T, d, f, E, k, planes=1, mx=False, act4=False):
         "unpermute_y": Tk * 4 + planes * Tk * d * 4 + T * d * 2,
         "permute_dy": Tk * 4 + T * d * 2 + Tk * d * 2,
         "permute_x": Tk * 4 + T * d * 2 + Tk * d * 2,
-        "unpermute_dx": Tk * 4 + planes * Tk * d * 4 + T * d * 4,
-        "router_backward": (T * E * 4 * 3 + Tk * 12 + T * d * 2 + E * d * 2
-                            + T * d * 4 + T * d * 2 + E * d * 4),
+        # dX leaves in bf16 with the router's share (its score gradients
+        # and weight) added
+        "unpermute_dx": (Tk * 4 + planes * Tk * d * 4 + T * d * 2
+                         + T * E * 4 + E * d * 2),
+        "router_backward": (T * E * 4 * 3 + Tk * 12 + T * d * 2
+                            + E * d * 4),
         "quant_x": T * d * (2 + xb),
         # training: both MX layouts of each weight from one bf16 read
         "quant_weights": 3 * E * d * f * (2 + 2 * q),
@@ -182,11 +185,11 @@ STEP_KERNELS = {
         ("wgrad_down", ["grouped_gemm_kernel"]),
         ("gate_up_dgrad", ["grouped_gemm_kernel"]),
         ("wgrad_gate_up", ["grouped_gemm_kernel"]),
-        ("unpermute_dx", ["unpermute_kernel"]),
         ("router_backward", ["router_dlogits_kernel",
                              "router_dwg_partial_kernel",
-                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_dwg_reduce_kernel",
                              "router_aux_final_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
     ],
     "mxfp8": [
         ("router_logits", ["router_logits_kernel"]),
@@ -207,11 +210,11 @@ STEP_KERNELS = {
         ("quant_tokens", ["quant_tokens_kernel", "quant_tokens_kernel"]),
         ("wgrad_down", ["grouped_gemm_kernel"]),
         ("wgrad_gate_up", ["grouped_gemm_kernel"]),
-        ("unpermute_dx", ["unpermute_kernel"]),
         ("router_backward", ["router_dlogits_kernel",
                              "router_dwg_partial_kernel",
-                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_dwg_reduce_kernel",
                              "router_aux_final_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
     ],
     "mxfp4": [
         ("router_logits", ["router_logits_kernel"]),
@@ -231,11 +234,11 @@ STEP_KERNELS = {
         ("quant_tokens", ["quant_tokens_kernel", "quant_tokens4_kernel"]),
         ("wgrad_down", ["grouped_gemm_kernel"]),
         ("wgrad_gate_up", ["grouped_gemm_kernel"]),
-        ("unpermute_dx", ["unpermute_kernel"]),
         ("router_backward", ["router_dlogits_kernel",
                              "router_dwg_partial_kernel",
-                             "router_dwg_reduce_kernel", "router_dx_kernel",
+                             "router_dwg_reduce_kernel",
                              "router_aux_final_kernel"]),
+        ("unpermute_dx", ["unpermute_kernel"]),
     ],
 }
 

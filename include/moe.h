@@ -451,11 +451,18 @@ moe_status moe_mx_grouped_wgrad(const uint8_t* aq, const uint8_t* as,
  * rounding.  o_perm [o_planes][T*k][d] fp32 (o_fp32 != 0; a row is the
  * sum of its planes, added in plane order) or [T*k][d] bf16 (o_fp32 == 0,
  * o_planes must be 1); y [T][d] bf16 (y_fp32 == 0) or fp32 (y_fp32 != 0).
+ * With dlogits (fp32 [T][E], the router score gradients moe_router_backward
+ * returns) the router's share of the input gradient is added before the
+ * rounding: y[t] += sum over e, in order, of dlogits[t][e] * w_g[e]
+ * (w_g bf16 [E][d], 1 <= E <= 1024), the same arithmetic as that entry's
+ * dx_in/dx_out, so the backward's dX leaves in one pass; dlogits NULL
+ * ignores w_g and E.
  */
 moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
                          int32_t o_planes, const int32_t* pos, const float* w,
                          int64_t T, int32_t k, int64_t d, int32_t y_fp32,
-                         void* y, hipStream_t stream);
+                         void* y, const float* dlogits, const void* w_g,
+                         int32_t E, hipStream_t stream);
 
 /* Number of partial-sum planes P in out_perm and dx_perm for intermediate
  * width f: 2 when f >= 4096 (fc2's reduction over f and fc1's data-gradient

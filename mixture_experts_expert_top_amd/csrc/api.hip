@@ -756,11 +756,20 @@ int32_t moe_row_planes(int64_t f) { return f >= 1 ? moe::out_planes(f) : 0; }
 moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
                          int32_t o_planes, const int32_t* pos, const float* w,
                          int64_t T, int32_t k, int64_t d, int32_t y_fp32,
-                         void* y, hipStream_t stream) {
+                         void* y, const float* dlogits, const void* w_g,
+                         int32_t E, hipStream_t stream) {
   REQUIRE_PTR(o_perm);
   REQUIRE_PTR(pos);
   REQUIRE_OPT_PTR(w);
   REQUIRE_PTR(y);
+  REQUIRE_OPT_PTR(dlogits);
+  if (dlogits) {
+    REQUIRE_PTR(w_g);
+    REQUIRE(E >= 1 && E <= moe::kMaxExperts, MOE_ERR_INVALID_ARG,
+            "E must be in [1, %d] with dlogits", moe::kMaxExperts);
+    REQUIRE(E * d * 2 <= kMaxBytes, MOE_ERR_UNSUPPORTED,
+            "router weight larger than 2 GiB");
+  }
   REQUIRE(T >= 1, MOE_ERR_INVALID_ARG, "T must be >= 1");
   REQUIRE(k >= 1 && k <= moe::kMaxTopK, MOE_ERR_INVALID_ARG,
           "k must be in [1, %d]", moe::kMaxTopK);
@@ -770,10 +779,12 @@ moe_status moe_unpermute(const void* o_perm, int32_t o_fp32,
           "o_planes must be in [1, 8] (1 for bf16 rows), got %d", o_planes);
   REQUIRE(T * k * d * 4 <= kMaxBytes * 2, MOE_ERR_UNSUPPORTED,
           "plane larger than 4 GiB");
-  return hip_status(moe::launch_unpermute(o_perm, o_fp32 ? 1 : 0, o_planes,
-                                          pos, w, T, k, d, y_fp32 ? 1 : 0, y,
-                                          stream),
-                    "moe_unpermute");
+  return hip_status(
+      moe::launch_unpermute(o_perm, o_fp32 ? 1 : 0, o_planes, pos, w, T, k, d,
+                            y_fp32 ? 1 : 0, y, dlogits,
+                            static_cast<const bf16_t*>(w_g),
+                            dlogits ? E : 0, stream),
+      "moe_unpermute");
 }
 
 int32_t moe_dp_tiles(int64_t f) {

@@ -56,6 +56,7 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
 hipError_t launch_unpermute(const void* o, int o_fp32, int o_planes,
                             const int32_t* pos, const float* w, int64_t T,
                             int k, int64_t d, int y_fp32, void* y,
+                            const float* dl, const bf16_t* wg, int E,
                             hipStream_t s);
 hipError_t launch_dp_reduce(const float* dp_part, int ntn, const int32_t* pos,
                             int64_t T, int k, float* dp, hipStream_t s);

@@ -293,63 +293,148 @@ __device__ __forceinline__ void load8(const void* o, int64_t row, int64_t d,
   }
 }
 
-template <bool OF32>
+// slot of flattened (slot, plane) row r: planes is 1 or 2 in practice,
+// which needs no division
+__device__ __forceinline__ int slot_of(int r, int planes) {
+  return planes == 1 ? r : planes == 2 ? (r >> 1) : r / planes;
+}
+
+// With dl (router score gradients [T][E] fp32) and wg (router weight
+// [E][d] bf16), the router's share of the token's input gradient,
+// sum over e in order of dl[t][e] * wg[e], is added to the fp32 sum before
+// the one rounding, as moe_router_backward adds it to a given fp32 dx.  A
+// workgroup takes TPB consecutive tokens, so each w_g row it loads serves
+// TPB tokens (many experts would otherwise read w_g once per token).
+template <bool OF32, int TPB>
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const void* __restrict__ o, int planes, int64_t plane,
     const int32_t* __restrict__ pos, const float* __restrict__ w, int k,
-    int64_t d, int y_fp32, void* __restrict__ y) {
-  __shared__ int s_pos[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
-  const int64_t t = blockIdx.x;
-  if (threadIdx.x == 0) {
+    int64_t T, int64_t d, int y_fp32, void* __restrict__ y,
+    const float* __restrict__ dl, const bf16_t* __restrict__ wg, int E) {
+  __shared__ int s_pos[TPB][kMaxTopK];
+  __shared__ float s_w[TPB][kMaxTopK];
+  __shared__ float s_dl[TPB > 1 ? TPB : 1][kMaxExperts];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPB;
+  const int nt = static_cast<int>(T - t0 < TPB ? T - t0 : TPB);
+  if (dl)
+    for (int i = threadIdx.x; i < nt * E; i += blockDim.x)
+      s_dl[i / E][i % E] = dl[t0 * E + i];
+  if (threadIdx.x < nt) {
     // insertion sort of the token's k rows (k <= 32)
+    const int tt = threadIdx.x;
+    const int64_t t = t0 + tt;
     for (int j = 0; j < k; ++j) {
       const int p = pos[t * k + j];
       const float wj = w ? w[t * k + j] : 1.0f;
       int i = j;
-      while (i > 0 && s_pos[i - 1] > p) {
-        s_pos[i] = s_pos[i - 1];
-        s_w[i] = s_w[i - 1];
+      while (i > 0 && s_pos[tt][i - 1] > p) {
+        s_pos[tt][i] = s_pos[tt][i - 1];
+        s_w[tt][i] = s_w[tt][i - 1];
         --i;
       }
-      s_pos[i] = p;
-      s_w[i] = wj;
+      s_pos[tt][i] = p;
+      s_w[tt][i] = wj;
     }
   }
   __syncthreads();
+  // A token's rows, taken as (slot, plane) pairs in order (slots
+  // ascending, a slot's planes in plane order), are loaded kUnBatch at a
+  // time with every load of a batch in flight before any is added; the
+  // additions keep that order.
+  constexpr int kUnBatch = 8;
+  const int nrow = k * planes;
   const int64_t n8 = d >> 3;
   for (int64_t q = threadIdx.x; q < n8; q += blockDim.x) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      float v[8];
-      load8<OF32>(o, s_pos[j], d, q, v);
-      // further partial-sum planes of the same row, in plane order
-      for (int pl = 1; pl < planes; ++pl) {
-        float u[8];
-        load8<OF32>(static_cast<const float*>(o) + pl * plane, s_pos[j], d, q,
-                    u);
+    float acc[TPB][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] += u[c];
-      }
-      if (w) {
-        const float wj = s_w[j];
+    for (int tt = 0; tt < TPB; ++tt) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] += wj * v[c];
-      } else {
+      for (int c = 0; c < 8; ++c) acc[tt][c] = 0.0f;
+      if (tt >= nt) continue;
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int r0 = 0; r0 < nrow; r0 += kUnBatch) {
+        float u[kUnBatch][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] += v[c];
+        for (int b = 0; b < kUnBatch; ++b) {
+          const int r = r0 + b;
+          if (r < nrow) {
+            const int j = slot_of(r, planes), pl = r - j * planes;
+            load8<OF32>(OF32 ? static_cast<const void*>(
+                                   static_cast<const float*>(o) + pl * plane)
+                             : o,
+                        s_pos[tt][j], d, q, u[b]);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kUnBatch; ++b) {
+          const int r = r0 + b;
+          if (r >= nrow) break;
+          const int j = slot_of(r, planes), pl = r - j * planes;
+          if (pl == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = u[b][c];
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] += u[b][c];
+          }
+          if (pl == planes - 1) {
+            if (w) {
+              const float wj = s_w[tt][j];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[tt][c] += wj * v[c];
+            } else {
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[tt][c] += v[c];
+            }
+          }
+        }
       }
     }
-    if (y_fp32) {
-      f32x4* yp = reinterpret_cast<f32x4*>(static_cast<float*>(y) + t * d) + 2 * q;
-      yp[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      yp[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    } else {
-      i32x4 out;
+    if (dl) {
+      // w_g rows of kUnBatch experts in flight at a time, experts in order
+      const int64_t col = q * 8;
+      for (int e0 = 0; e0 < E; e0 += kUnBatch) {
+        i32x4 wr[kUnBatch];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        out[c] = static_cast<int>(pack_bf16x2(acc[2 * c], acc[2 * c + 1]));
-      reinterpret_cast<i32x4*>(static_cast<bf16_t*>(y) + t * d)[q] = out;
+        for (int b = 0; b < kUnBatch; ++b)
+          wr[b] = e0 + b < E ? *reinterpret_cast<const i32x4*>(
+                                   wg + static_cast<int64_t>(e0 + b) * d + col)
+                             : i32x4{};
+#pragma unroll
+        for (int b = 0; b < kUnBatch; ++b) {
+          if (e0 + b >= E) break;
+          float wv[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            wv[2 * c] = bf_lo(static_cast<uint32_t>(wr[b][c]));
+            wv[2 * c + 1] = bf_hi(static_cast<uint32_t>(wr[b][c]));
+          }
+#pragma unroll
+          for (int tt = 0; tt < TPB; ++tt) {
+            const float g = s_dl[TPB > 1 ? tt : 0][e0 + b];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[tt][c] += g * wv[c];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt) {
+      if (tt >= nt) break;
+      const int64_t t = t0 + tt;
+      if (y_fp32) {
+        f32x4* yp =
+            reinterpret_cast<f32x4*>(static_cast<float*>(y) + t * d) + 2 * q;
+        yp[0] = f32x4{acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
+        yp[1] = f32x4{acc[tt][4], acc[tt][5], acc[tt][6], acc[tt][7]};
+      } else {
+        i32x4 out;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          out[c] = static_cast<int>(
+              pack_bf16x2(acc[tt][2 * c], acc[tt][2 * c + 1]));
+        reinterpret_cast<i32x4*>(static_cast<bf16_t*>(y) + t * d)[q] = out;
+      }
     }
   }
 }
@@ -361,8 +446,16 @@ __global__ __launch_bounds__(256) void dp_reduce_kernel(
   const int64_t s = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (s >= TK) return;
   const float* p = part + static_cast<int64_t>(pos[s]) * ntn;
+  // 8 tiles' loads in flight at a time, added in tile order
   float acc = 0.0f;
-  for (int n = 0; n < ntn; ++n) acc += p[n];
+  for (int n0 = 0; n0 < ntn; n0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) v[b] = n0 + b < ntn ? p[n0 + b] : 0.0f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      if (n0 + b < ntn) acc += v[b];
+  }
   dp[s] = acc;
 }
 
@@ -433,15 +526,32 @@ hipError_t launch_permute_rows(const int32_t* pos, int64_t T, int k,
 hipError_t launch_unpermute(const void* o, int o_fp32, int o_planes,
                             const int32_t* pos, const float* w, int64_t T,
                             int k, int64_t d, int y_fp32, void* y,
+                            const float* dl, const bf16_t* wg, int E,
                             hipStream_t s) {
   const int64_t plane = T * k * d;
+  const int planes = o_fp32 ? o_planes : 1;
+  // with the router's share of many experts, 4 tokens a workgroup share
+  // each w_g row they load
+  if (dl && E > 8) {
+    constexpr int kTpb = 4;
+    const dim3 grid(static_cast<unsigned>((T + kTpb - 1) / kTpb));
+    if (o_fp32)
+      hipLaunchKernelGGL((unpermute_kernel<true, kTpb>), grid, dim3(256), 0,
+                         s, o, planes, plane, pos, w, k, T, d, y_fp32, y, dl,
+                         wg, E);
+    else
+      hipLaunchKernelGGL((unpermute_kernel<false, kTpb>), grid, dim3(256), 0,
+                         s, o, planes, plane, pos, w, k, T, d, y_fp32, y, dl,
+                         wg, E);
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>(T));
   if (o_fp32)
-    hipLaunchKernelGGL(unpermute_kernel<true>, dim3(static_cast<unsigned>(T)),
-                       dim3(256), 0, s, o, o_planes, plane, pos, w, k, d,
-                       y_fp32, y);
+    hipLaunchKernelGGL((unpermute_kernel<true, 1>), grid, dim3(256), 0, s, o,
+                       planes, plane, pos, w, k, T, d, y_fp32, y, dl, wg, E);
   else
-    hipLaunchKernelGGL(unpermute_kernel<false>, dim3(static_cast<unsigned>(T)),
-                       dim3(256), 0, s, o, 1, plane, pos, w, k, d, y_fp32, y);
+    hipLaunchKernelGGL((unpermute_kernel<false, 1>), grid, dim3(256), 0, s, o,
+                       planes, plane, pos, w, k, T, d, y_fp32, y, dl, wg, E);
   return hipGetLastError();
 }
 

@@ -5,10 +5,11 @@ with torch, reused every step) and issues the library calls in order:
 
   forward : moe_router_logits -> moe_route -> moe_permute
             -> moe_grouped_mlp_fwd -> moe_unpermute
-  backward: moe_permute_rows (dY) -> moe_grouped_mlp_bwd -> moe_unpermute
+  backward: moe_permute_rows (dY) -> moe_grouped_mlp_bwd
             -> moe_router_backward (when the forward computed the router
-               scores: dlogits with the balancing term, dW_g, db, and the
-               router's share added to dx before its one rounding)
+               scores: dlogits with the balancing term, dW_g, db)
+            -> moe_unpermute (dX, with the router's share added before its
+               one rounding)
 
 With a ``timers`` object (see ``StageTimers``) the GEMMs are issued
 through the per-GEMM stage entry points instead of the fused ones, with
@@ -119,7 +120,6 @@ class MoEPath:
         self.ws_bwd = torch.empty(max(ws_b, 16), dtype=torch.uint8,
                                   device=dev)
         # router backward
-        self.dx_f32 = torch.empty(T, d, dtype=torch.float32, device=dev)
         self.dlogits = torch.empty(T, E, dtype=torch.float32, device=dev)
         self.dw_g = torch.empty(E, d, dtype=torch.float32, device=dev)
         self.db = torch.empty(E, dtype=torch.float32, device=dev)
@@ -199,20 +199,23 @@ class MoEPath:
         return self.dx, self.dw_gu, self.dw2, self.dp
 
     def _finish_dx(self, timers):
-        """Combine dX; with a router, add its share before the rounding."""
+        """Combine dX; with a router, its backward runs first (score
+        gradients, dW_g, db, the balancing loss) and the combine adds the
+        router's share of dX before the one rounding."""
         if self._router is None:
             with _around(timers, "unpermute_dx"):
                 moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx)
             return
         x, w_g, bias = self._router
-        with _around(timers, "unpermute_dx"):
-            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx_f32)
         with _around(timers, "router_backward"):
             moe.moe_router_backward(
                 self._logits_used, self.topk_idx, self.topk_w, self.dp,
                 self.counts, self.aux_coef, self.renorm, x, w_g,
                 self.dlogits, self.dw_g, self.db if bias is not None else None,
-                self.dx_f32, self.dx, self.aux_loss, self.ws_router)
+                None, None, self.aux_loss, self.ws_router)
+        with _around(timers, "unpermute_dx"):
+            moe.moe_unpermute(self.dx_perm, self.pos, None, self.dx,
+                              dlogits=self.dlogits, w_g=w_g)
 
 
 class StepGraph:

@@ -71,7 +71,7 @@ def _load():
                                       I64, I64, P, P, P, P, P, P, I64, P, P,
                                       P, P, P, P, P, P, P, P, SZ, P]),
         "moe_unpermute": (I32, [P, I32, I32, P, P, I64, I32, I64, I32, P,
-                                P]),
+                                P, P, I32, P]),
         "moe_row_planes": (I32, [I64]),
         "moe_mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, I64, P]),
         "moe_mxfp8_quantize_weight": (I32, [P, I64, I64, P, P, P, P, P]),
@@ -365,8 +365,10 @@ def moe_grouped_mlp_bwd(prec, dout_perm, x_perm, offsets, pos, w_gu, w2,
         _p(dp), _p(workspace), nbytes, _stream(stream)))
 
 
-def moe_unpermute(o_perm, pos, w, y, stream=None):
-    """o_perm: bf16 [T*k, d] rows, or fp32 [T*k, d] / [planes, T*k, d]."""
+def moe_unpermute(o_perm, pos, w, y, stream=None, dlogits=None, w_g=None):
+    """o_perm: bf16 [T*k, d] rows, or fp32 [T*k, d] / [planes, T*k, d].
+    dlogits (fp32 [T, E]) with w_g (bf16 [E, d]): add the router's share
+    of the input gradient before the rounding."""
     T, k = pos.shape
     d = o_perm.shape[-1]
     if o_perm.dtype not in (torch.bfloat16, torch.float32):
@@ -379,10 +381,16 @@ def moe_unpermute(o_perm, pos, w, y, stream=None):
     if y.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("y must be bfloat16 or float32")
     _want(y, "y", y.dtype, (T, d))
+    E = 0
+    if dlogits is not None:
+        E = dlogits.shape[1]
+        _want(dlogits, "dlogits", torch.float32, (T, E))
+        _want(w_g, "w_g", torch.bfloat16, (E, d))
     _check("moe_unpermute", lib.moe_unpermute(
         _p(o_perm), 1 if o_perm.dtype == torch.float32 else 0, planes,
         _p(pos), _p(w), T, k, d,
-        1 if y.dtype == torch.float32 else 0, _p(y), _stream(stream)))
+        1 if y.dtype == torch.float32 else 0, _p(y), _p(dlogits),
+        _p(w_g) if dlogits is not None else None, E, _stream(stream)))
 
 
 def moe_mxfp8_padded_rows(rows, nseg):

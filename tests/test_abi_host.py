@@ -247,14 +247,26 @@ def test_mx_stage_validation():
                                   64, A, None) == INVALID
 
 
+def _unpermute(o_fp32=0, planes=1, pos=A, T=8, k=2, d=64, dl=None, wg=None,
+               E=0):
+    # o_perm, o_fp32, o_planes, pos, w, T, k, d, y_fp32, y, dlogits, w_g, E,
+    # stream
+    return L.moe_unpermute(A, o_fp32, planes, pos, None, T, k, d, 0, A, dl,
+                           wg, E, None)
+
+
 def test_unpermute_validation():
-    assert L.moe_unpermute(A, 0, 1, A, None, 8, 0, 64, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, 1, 1, A, None, 8, 2, 60, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, 0, 1, None, None, 8, 2, 64, 0, A,
-                           None) == INVALID
+    assert _unpermute(k=0) == INVALID
+    assert _unpermute(o_fp32=1, d=60) == INVALID
+    assert _unpermute(pos=None) == INVALID
     # bf16 rows come as one plane; planes must be in [1, 8]
-    assert L.moe_unpermute(A, 0, 2, A, None, 8, 2, 64, 0, A, None) == INVALID
-    assert L.moe_unpermute(A, 1, 0, A, None, 8, 2, 64, 0, A, None) == INVALID
+    assert _unpermute(planes=2) == INVALID
+    assert _unpermute(o_fp32=1, planes=0) == INVALID
+    # the router's share of dX: dlogits needs w_g and E in [1, 1024]
+    assert _unpermute(dl=A, wg=None, E=8) == INVALID
+    assert _unpermute(dl=A, wg=A, E=0) == INVALID
+    assert _unpermute(dl=A, wg=A, E=1025) == INVALID
+    assert _unpermute(dl=MIS, wg=A, E=8) == INVALID
     # two fp32 partial planes for a wide intermediate width, one otherwise
     assert L.moe_row_planes(14336) == 2
     assert L.moe_row_planes(4096) == 2

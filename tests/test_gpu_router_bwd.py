@@ -7,9 +7,10 @@ element, against the float64 oracle on the same seeded inputs:
   * dlogits: |err| <= 128 * 2^-24 * M, with M the sum of the magnitudes of
     the terms the element is made of (softmax values, exp/sum and the
     k-term sum s each cost a few ulps);
-  * dW_g and db: a chain of at most 256 + T/256 + 2 fp32 additions per
-    element, so |err| <= (258 + T/256) * 2^-24 * (|dL|^T |x|) plus the
-    dlogits error carried through;
+  * dW_g: each 256-token chunk is an fp32 sum of 3 * 256 exact products
+    (every dlogits value split into three bf16 terms), then the chunks are
+    added in order, so |err| <= (770 + T/256) * 2^-24 * (|dL|^T |x|) plus
+    the dlogits error carried through; db: 256 + T/256 + 2 additions;
   * dx_out (bf16): one rounding of the fp32 sum, |err| <= 2^-8 |ref| plus
     twice the fp32 error of the E-term sum;
   * aux_loss: positive terms only, relative error <= (chain + 64) * 2^-24.
@@ -259,3 +260,47 @@ def test_layer_with_router(T, d, f, E, k, bias):
     bad = {n: v for n, v in res.items() if not v <= 2e-2}
     assert not bad, bad
     assert abs(path.aux_loss.item() - loss) <= 1e-5 * abs(loss)
+
+
+@gpu
+@pytest.mark.parametrize("T,E,k,d,planes", [
+    (1000, 8, 2, 264, 2), (2048, 64, 8, 512, 1), (300, 7, 3, 136, 2)])
+def test_combine_with_router_share_bitexact(T, E, k, d, planes):
+    """moe_unpermute given the score gradients adds the router's share of dX
+    exactly as moe_router_backward adds it to a given fp32 dX: the combine
+    in one pass equals combine-to-fp32 then the router's dx_in/dx_out, bit
+    for bit."""
+    dev = _dev()
+    wl = I.Workload("rc", T, d, 8, E, k)
+    inp = I.make_inputs(wl, seed=T + E, device=dev, with_weights=False,
+                        with_dy=False)
+    dp = I.make_tensor((T, k), seed=T + 1, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    moe.moe_route(inp["logits"], k, True, idx, w)
+    # any one-to-one map of the token slots onto rows serves the combine
+    g = torch.Generator().manual_seed(T)
+    pos = torch.randperm(T * k, generator=g).to(torch.int32).view(T, k)
+    pos = pos.to(dev)
+    dxp = I.make_tensor((planes, T * k, d), seed=T + 2, dtype=torch.float32,
+                        device=dev)
+    ws = torch.empty(moe.moe_workspace_bytes(MOE_ENTRY_ROUTER_BWD, MOE_BF16,
+                                             T, E, k, d, 0),
+                     dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    # two steps: the combine to fp32, then the router adds its share
+    dx32 = torch.empty(T, d, **f32)
+    moe.moe_unpermute(dxp, pos, None, dx32)
+    dl_a, dx_a = torch.empty(T, E, **f32), torch.empty(T, d, **bf)
+    moe.moe_router_backward(inp["logits"], idx, w, dp, None, 0.0, True, None,
+                            inp["w_g"], dl_a, None, None, dx32, dx_a, None,
+                            ws)
+    # one pass: the router's gradients first, the combine adds the share
+    dl_b, dx_b = torch.empty(T, E, **f32), torch.empty(T, d, **bf)
+    moe.moe_router_backward(inp["logits"], idx, w, dp, None, 0.0, True, None,
+                            None, dl_b, None, None, None, None, None, ws)
+    moe.moe_unpermute(dxp, pos, None, dx_b, dlogits=dl_b, w_g=inp["w_g"])
+    torch.cuda.synchronize()
+    assert torch.equal(dl_a, dl_b)
+    assert torch.equal(dx_a, dx_b)
