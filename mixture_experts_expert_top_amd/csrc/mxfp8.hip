@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 
 
 // Workgroup = one 128-row tile of the padded layout x kTokTiles runs of 64
-// columns (a tile never straddles a segment: segments start on multiples
-// of 128), each run in three steps:
+// columns (kTokTilesRows with the row-wise outputs; a tile never straddles
+// a segment: segments start on multiples of 128), each run in three steps:
 //   1. 256 threads load the tile's source rows with 16-byte loads (8
 //      columns each; rows past the segment read as zero) into LDS;
 //   2. thread (block b = t/64, column c = t%64) quantizes its 32-row block
@@ -69,11 +69,16 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // With kRows (one segment, no gather: a weight quantized for both of its
 // GEMMs from one read) thread (row t/2, half t%2) also quantizes its 32
 // columns of the tile along the row, as quant_rows_kernel does, into
-// row_codes [rows][cols] and row_scales [rows][cols/32].
+// row_codes [rows][cols] and row_scales [rows][cols/32].  Those are kept in
+// LDS over the workgroup's column runs and leave at the end as whole rows
+// of the runs (128 code bytes, 8 lanes a row, and one 4-byte scale word a
+// row), so the row-wise outputs go out in full lines instead of 64-byte
+// pieces and single bytes.
 constexpr int kTokRows = 128;
 constexpr int kTokCols = 64;
 constexpr int kTokLd = kTokCols + 8;       // bf16 row stride of the tile
 constexpr int kTokTiles = 4;               // column runs per workgroup
+constexpr int kTokTilesRows = 2;           // ... with the row-wise outputs
 
 template <bool kRows>
 __global__ __launch_bounds__(256) void quant_tokens_kernel(
@@ -86,6 +91,13 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t tile[kTokRows * kTokLd];
   __shared__ __attribute__((aligned(16))) uint8_t out[kTokCols][kTokRows];
   __shared__ uint32_t sc_out[kTokCols];
+  constexpr int kRuns = kRows ? kTokTilesRows : kTokTiles;
+  // kRows: the row-wise codes and scales of all the column runs
+  constexpr int kRowBytes = kTokCols * kRuns;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t rcodes[kRows ? kTokRows : 1][kRows ? kRowBytes : 16];
+  __shared__ __attribute__((aligned(4)))
+  uint8_t rscales[kRows ? kTokRows : 1][kRows ? kRowBytes / kMxBlock : 4];
   padded_prefix(seg, nseg, rows, s_pad);
   const int t = threadIdx.x;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kTokRows;
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   i32x4 nxt[kTokRows / 32];
   auto load_run = [&](int ct) {
     const int64_t c0 =
-        (static_cast<int64_t>(blockIdx.y) * kTokTiles + ct) * kTokCols;
+        (static_cast<int64_t>(blockIdx.y) * kRuns + ct) * kTokCols;
     const bool col_ok = c0 + cc < cols;            // cols % 8 == 0
 #pragma unroll
     for (int i = 0; i < kTokRows / 32; ++i) {
@@ -123,9 +135,9 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     }
   };
   load_run(0);
-  for (int ct = 0; ct < kTokTiles; ++ct) {
+  for (int ct = 0; ct < kRuns; ++ct) {
     const int64_t c0 =
-        (static_cast<int64_t>(blockIdx.y) * kTokTiles + ct) * kTokCols;
+        (static_cast<int64_t>(blockIdx.y) * kRuns + ct) * kTokCols;
     if (c0 >= cols) break;
     if (ct > 0) __syncthreads();                   // LDS of the previous run
 #pragma unroll
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
       *reinterpret_cast<i32x4*>(tile + ((t >> 3) + 32 * i) * kTokLd + cc) =
           nxt[i];
     __syncthreads();
-    if (ct + 1 < kTokTiles) load_run(ct + 1);
+    if (ct + 1 < kRuns) load_run(ct + 1);
     if constexpr (kRows) {
       // along the row: 32 columns of row t/2 (c0 is a multiple of 64)
       const int rr = t >> 1, half = t & 1;
@@ -161,12 +173,11 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
           w[q >> 2][q & 3] = static_cast<int>(
               e4m3_pack4(v[q * 4] * inv, v[q * 4 + 1] * inv,
                          v[q * 4 + 2] * inv, v[q * 4 + 3] * inv));
-        const int64_t cb = c0 + 32 * half;
-        i32x4* o = reinterpret_cast<i32x4*>(row_codes + r * cols + cb);
+        const int lc = ct * kTokCols + 32 * half;     // column in the runs
+        i32x4* o = reinterpret_cast<i32x4*>(&rcodes[rr][lc]);
         o[0] = w[0];
         o[1] = w[1];
-        row_scales[r * (cols / kMxBlock) + cb / kMxBlock] =
-            static_cast<uint8_t>(e + 127);
+        rscales[rr][lc / kMxBlock] = static_cast<uint8_t>(e + 127);
       }
     }
     // 2. quantize one 32-row block of one column
@@ -208,6 +219,37 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
       *reinterpret_cast<uint32_t*>(scales + (c0 + t) * (rows_pad / kMxBlock) +
                                    p0 / kMxBlock) = sc_out[t];
   }
+  if constexpr (kRows) {
+    // the runs' row-wise codes: kChunks lanes a row, 16 bytes each; scales:
+    // kRowBytes / 32 bytes a row (cols is a multiple of 64, so a run is all
+    // in or all out)
+    __syncthreads();
+    constexpr int kChunks = kRowBytes / 16;
+    const int64_t cw0 = static_cast<int64_t>(blockIdx.y) * kRowBytes;
+    const int64_t ncols = cols - cw0 < kRowBytes ? cols - cw0 : kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kTokRows * kChunks / 256; ++j) {
+      const int id = t + 256 * j;
+      const int rr = id / kChunks, ch = id % kChunks;
+      const int64_t r = r0 + rr;
+      if (r < r_end && ch * 16 < ncols)
+        *reinterpret_cast<i32x4*>(row_codes + r * cols + cw0 + ch * 16) =
+            *reinterpret_cast<const i32x4*>(&rcodes[rr][ch * 16]);
+    }
+    if (t < kTokRows) {
+      const int64_t r = r0 + t;
+      const int nsc = static_cast<int>(ncols / kMxBlock);
+      uint8_t* dst = row_scales + r * (cols / kMxBlock) + cw0 / kMxBlock;
+      if (r < r_end) {
+        if (nsc == 4 && kRowBytes / kMxBlock == 4 &&
+            ((reinterpret_cast<uintptr_t>(dst) & 3) == 0))
+          *reinterpret_cast<uint32_t*>(dst) =
+              *reinterpret_cast<const uint32_t*>(&rscales[t][0]);
+        else
+          for (int i = 0; i < nsc; ++i) dst[i] = rscales[t][i];
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -242,8 +284,8 @@ hipError_t launch_mx_quant_both(const bf16_t* src, int64_t rows,
                                 uint8_t* row_scales, uint8_t* col_codes,
                                 uint8_t* col_scales, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(rows / kTokRows),
-            static_cast<unsigned>((cols + kTokCols * kTokTiles - 1) /
-                                  (kTokCols * kTokTiles)));
+            static_cast<unsigned>((cols + kTokCols * kTokTilesRows - 1) /
+                                  (kTokCols * kTokTilesRows)));
   hipLaunchKernelGGL(quant_tokens_kernel<true>, grid, dim3(256), 0, s, src,
                      nullptr, rows, cols, nullptr, 1, col_codes, col_scales,
                      rows, row_codes, row_scales);
