@@ -202,25 +202,62 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
 }
 
 // ---------------------------------------------------------------- rows
-// Copy one row of `bytes` (multiple of 16) from src to the k rows
-// dst_base + rows[j] * stride.  rows[] lives in LDS.
-__device__ __forceinline__ void copy_row16(const uint8_t* __restrict__ src,
-                                           uint8_t* __restrict__ dst_base,
-                                           const int* rows, int k,
-                                           int64_t bytes) {
-  const int64_t n16 = bytes >> 4;
-  for (int64_t q = threadIdx.x; q < n16; q += blockDim.x) {
-    const i32x4 v = reinterpret_cast<const i32x4*>(src)[q];
-    for (int j = 0; j < k; ++j)
-      reinterpret_cast<i32x4*>(dst_base + static_cast<int64_t>(rows[j]) *
-                                              bytes)[q] = v;
+// A token's row of `bytes` (a multiple of 16) goes to the k rows
+// dst_base + rows[j] * bytes (rows[] in LDS).  The first kRowPre 16-byte
+// pieces of each thread are loaded before the destinations are known
+// (RowPre::load, issued ahead of the position work) and stored after
+// (RowPre::store); the rest of a long row is copied in a plain loop.
+constexpr int kRowPre = 4;
+struct RowPre {
+  i32x4 v[kRowPre];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ src,
+                                       int64_t bytes) {
+    const int64_t n16 = bytes >> 4;
+#pragma unroll
+    for (int i = 0; i < kRowPre; ++i) {
+      const int64_t q = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+      if (q < n16) v[i] = reinterpret_cast<const i32x4*>(src)[q];
+    }
   }
-}
+  __device__ __forceinline__ void store(const uint8_t* __restrict__ src,
+                                        uint8_t* __restrict__ dst_base,
+                                        const int* rows, int k,
+                                        int64_t bytes) const {
+    const int64_t n16 = bytes >> 4;
+#pragma unroll
+    for (int i = 0; i < kRowPre; ++i) {
+      const int64_t q = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+      if (q < n16)
+        for (int j = 0; j < k; ++j)
+          reinterpret_cast<i32x4*>(dst_base + static_cast<int64_t>(rows[j]) *
+                                                  bytes)[q] = v[i];
+    }
+    for (int64_t q = threadIdx.x + static_cast<int64_t>(kRowPre) * blockDim.x;
+         q < n16; q += blockDim.x) {
+      const i32x4 w = reinterpret_cast<const i32x4*>(src)[q];
+      for (int j = 0; j < k; ++j)
+        reinterpret_cast<i32x4*>(dst_base + static_cast<int64_t>(rows[j]) *
+                                                bytes)[q] = w;
+    }
+  }
+};
 
-__device__ __forceinline__ void copy_row1(const uint8_t* __restrict__ src,
+// Side bytes (MX scales) of a row: 16 bytes at a time when the row length
+// allows, else byte by byte.
+__device__ __forceinline__ void copy_side(const uint8_t* __restrict__ src,
                                           uint8_t* __restrict__ dst_base,
                                           const int* rows, int k,
                                           int64_t bytes) {
+  if ((bytes & 15) == 0) {
+    const int64_t n16 = bytes >> 4;
+    for (int64_t q = threadIdx.x; q < n16; q += blockDim.x) {
+      const i32x4 v = reinterpret_cast<const i32x4*>(src)[q];
+      for (int j = 0; j < k; ++j)
+        reinterpret_cast<i32x4*>(dst_base + static_cast<int64_t>(rows[j]) *
+                                                bytes)[q] = v;
+    }
+    return;
+  }
   for (int64_t q = threadIdx.x; q < bytes; q += blockDim.x) {
     const uint8_t v = src[q];
     for (int j = 0; j < k; ++j)
@@ -240,6 +277,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     uint8_t* __restrict__ side_p) {
   __shared__ int s_pos[kMaxTopK];
   const int64_t t = blockIdx.x;
+  RowPre row;
+  row.load(x + t * row_bytes, row_bytes);
   if (threadIdx.x < k) {
     const int j = threadIdx.x;
     const int64_t s = t * k + j;
@@ -252,8 +291,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     s_pos[j] = p;
   }
   __syncthreads();
-  copy_row16(x + t * row_bytes, xp, s_pos, k, row_bytes);
-  if (side) copy_row1(side + t * side_bytes, side_p, s_pos, k, side_bytes);
+  row.store(x + t * row_bytes, xp, s_pos, k, row_bytes);
+  if (side) copy_side(side + t * side_bytes, side_p, s_pos, k, side_bytes);
 }
 
 __global__ __launch_bounds__(256) void permute_rows_kernel(
@@ -263,10 +302,12 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
     uint8_t* __restrict__ side_p) {
   __shared__ int s_pos[kMaxTopK];
   const int64_t t = blockIdx.x;
+  RowPre row;
+  row.load(x + t * row_bytes, row_bytes);
   if (threadIdx.x < k) s_pos[threadIdx.x] = pos[t * k + threadIdx.x];
   __syncthreads();
-  copy_row16(x + t * row_bytes, xp, s_pos, k, row_bytes);
-  if (side) copy_row1(side + t * side_bytes, side_p, s_pos, k, side_bytes);
+  row.store(x + t * row_bytes, xp, s_pos, k, row_bytes);
+  if (side) copy_side(side + t * side_bytes, side_p, s_pos, k, side_bytes);
 }
 
 // ---------------------------------------------------------------- combine
