@@ -113,12 +113,22 @@ def measured_traffic(workload, stage):
     """HBM bytes per launch of ``stage`` from the recorded counter runs,
     scaled by the copy calibration; None when there is no record for this
     workload and stage or the kernel source changed since."""
-    try:
-        with open(TRAFFIC_FILE.format(workload)) as fh:
-            rec = json.load(fh)
-        sha = gemm_source_sha256()
-    except (OSError, ValueError):
+    # a forward-only workload runs the forward kernels of the fwd+bwd
+    # workload of the same name, whose record covers them
+    names = [workload] + ([workload[:-4]] if workload.endswith("_fwd")
+                          else [])
+    rec = None
+    for name in names:
+        try:
+            with open(TRAFFIC_FILE.format(name)) as fh:
+                rec = json.load(fh)
+            workload = name
+            break
+        except (OSError, ValueError):
+            continue
+    if rec is None:
         return None
+    sha = gemm_source_sha256()
     st = rec.get("stages", {}).get(stage)
     if (rec.get("workload") != workload or st is None
             or rec.get("kernel_source_sha256") != sha):
