@@ -135,7 +135,7 @@ def test_quantize_tokens_segments(offs):
 
 
 @gpu
-@pytest.mark.parametrize("R,C", [(128, 64), (256, 320), (384, 1024)])
+@pytest.mark.parametrize("R,C", [(128, 64), (256, 320), (384, 1024), (128, 576)])
 def test_quantize_weight_both_layouts(R, C):
     """moe_mxfp8_quantize_weight: the row-wise codes equal the oracle's row
     blocks and the column-wise (transposed) codes its one-segment blocks
