@@ -5,14 +5,15 @@ the Mixtral expert shape
 100 (their router scores too).  GPU forward and backward through MoEPathMX
 against the MX-emulating oracle (oracle/moe_mx.py) evaluated for sampled
 outputs, gated at max|err| / rms(ref) <= 6e-2 per sampled group:
-  * y of tokens routed to experts {0, 1} (ordinary and outlier tokens
-    scored separately, since the outliers' rows are ~1e4 times larger);
-  * the rows of dXp (the gate_up data gradient) and dp at expert 0 for
-    the same tokens;
+  * y of tokens routed to experts {0, 1}, and of tokens routed to {4, 7}
+    (ordinary and outlier tokens scored separately, since the outliers'
+    rows are ~1e4 times larger);
+  * the rows of dXp (the gate_up data gradient) and dp at experts 0 and 4
+    for the same tokens;
   * columns of dW2 and rows of dW_gu (gate and up) of several experts.
 Routing is checked bit-exact against the oracle's on the same scores.
-The oracle quantizes experts 0 and 1 in full, which takes a minute or two
-of CPU time.
+The oracle quantizes experts 0, 1, 4 and 7 in full, which takes a few
+minutes of CPU time.
 """
 
 import numpy as np
@@ -35,9 +36,16 @@ def h64(t):
 
 
 def rel(got, ref):
+    """max|got - ref| / rms(ref); an all-zero reference must be met
+    exactly (0.0, else inf)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
+    assert np.all(np.isfinite(got)), "non-finite GPU values"
+    err = float(np.max(np.abs(got - ref)))
+    den = float(np.sqrt(np.mean(ref * ref)))
+    if den == 0.0:
+        return 0.0 if err == 0.0 else float("inf")
+    return err / den
 
 
 @gpu
@@ -59,41 +67,51 @@ def test_mx_full_size_sampled(act4):
     counts, offsets, pos, src = R.dispatch_plan(idx, E)
     np.testing.assert_array_equal(path.pos.cpu().numpy(), pos)
     outl = set(inp["outlier_rows"].cpu().numpy().tolist())
-    pair = [t for t in range(T) if set(idx[t].tolist()) == {0, 1}]
-    normal = [t for t in pair if t not in outl][:6]
-    big = [t for t in pair if t in outl][:2]
-    tokens = normal + big
-    assert len(normal) == 6
-
     x = inp["x"]
     dy = inp["dy"]
-    xt = h64(x[tokens])
-    dyt = h64(dy[tokens])
-    W = {0: X.expert_weights_mx(h64(inp["w_gu"][0]), h64(inp["w2"][0]),
-                                backward=True),
-         1: X.expert_weights_mx(h64(inp["w_gu"][1]), h64(inp["w2"][1]))}
-    y_gpu = h64(path.y[tokens])
-    dxp_gpu = h64(path.dx_perm.sum(dim=0)[pos[tokens, :][idx[tokens] == 0]])
+    y_all = h64(path.y)
+    dxp_sum = path.dx_perm.sum(dim=0)
     dp_gpu = path.dp.cpu().numpy()
     results = {}
-    y_ref = np.stack([X.token_forward_mx(xt[i], idx[t], p[t], W, act4)
-                      for i, t in enumerate(tokens)])
-    dxp_ref, dp_ref, dp_got = [], [], []
-    for i, t in enumerate(tokens):
-        j = int(np.nonzero(idx[t] == 0)[0][0])
-        g, dpv = X.row_backward_mx(xt[i], dyt[i], p[t, j], W[0], act4)
-        dxp_ref.append(g)
-        dp_ref.append(dpv)
-        dp_got.append(dp_gpu[t, j])
-    dxp_ref = np.stack(dxp_ref)
-    nn = len(normal)
-    results["y"] = rel(y_gpu[:nn], y_ref[:nn])
-    results["dxp"] = rel(dxp_gpu[:nn], dxp_ref[:nn])
-    if big:
-        results["y_outlier"] = rel(y_gpu[nn:], y_ref[nn:])
-        results["dxp_outlier"] = rel(dxp_gpu[nn:], dxp_ref[nn:])
-    results["dp"] = rel(np.array(dp_got), np.array(dp_ref))
-    del W
+    # two expert pairs: tokens routed to exactly {a, b}; y against the
+    # forward of both experts, dXp and dp at expert a
+    for a, b, n_norm, n_big in ((0, 1, 6, 2), (4, 7, 4, 1)):
+        pair = [t for t in range(T) if set(idx[t].tolist()) == {a, b}]
+        normal = [t for t in pair if t not in outl][:n_norm]
+        # outlier scores are 100 times larger, so one of the two weights is
+        # often far below fp32's range: take outliers that weight expert a
+        big = [t for t in pair if t in outl and
+               p[t, int(np.nonzero(idx[t] == a)[0][0])] > 1e-3][:n_big]
+        tokens = normal + big
+        assert len(normal) == n_norm
+        xt = h64(x[tokens])
+        dyt = h64(dy[tokens])
+        W = {a: X.expert_weights_mx(h64(inp["w_gu"][a]), h64(inp["w2"][a]),
+                                    backward=True),
+             b: X.expert_weights_mx(h64(inp["w_gu"][b]), h64(inp["w2"][b]))}
+        y_gpu = y_all[tokens]
+        rows_a = [int(pos[t, int(np.nonzero(idx[t] == a)[0][0])])
+                  for t in tokens]
+        dxp_gpu = h64(dxp_sum[rows_a])
+        y_ref = np.stack([X.token_forward_mx(xt[i], idx[t], p[t], W, act4)
+                          for i, t in enumerate(tokens)])
+        dxp_ref, dp_ref, dp_got = [], [], []
+        for i, t in enumerate(tokens):
+            j = int(np.nonzero(idx[t] == a)[0][0])
+            g, dpv = X.row_backward_mx(xt[i], dyt[i], p[t, j], W[a], act4)
+            dxp_ref.append(g)
+            dp_ref.append(dpv)
+            dp_got.append(dp_gpu[t, j])
+        dxp_ref = np.stack(dxp_ref)
+        nn = len(normal)
+        tag = f"{{{a},{b}}}"
+        results[f"y{tag}"] = rel(y_gpu[:nn], y_ref[:nn])
+        results[f"dxp{tag}"] = rel(dxp_gpu[:nn], dxp_ref[:nn])
+        if big:
+            results[f"y_outlier{tag}"] = rel(y_gpu[nn:], y_ref[nn:])
+            results[f"dxp_outlier{tag}"] = rel(dxp_gpu[nn:], dxp_ref[nn:])
+        results[f"dp{tag}"] = rel(np.array(dp_got), np.array(dp_ref))
+        del W
 
     # weight gradients: sampled columns of dW2, rows of dW_gu
     for e, cols, rows in ((0, (0, 5000, f - 1), (3, f + 3)),
