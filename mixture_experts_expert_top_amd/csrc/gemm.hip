@@ -1411,10 +1411,17 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       if constexpr (kTokEpi) {
         if (tok) {
           // lane = dS column of the wave; both 32-row blocks of the pass,
-          // gate (low half) and up (high half) of the packed pairs
+          // gate (low half) and up (high half) of the packed pairs.  The
+          // codes go out through the wave's LDS region: lane c leaves its
+          // column's 64 codes of the pass (four 16-byte chunks, gate at
+          // byte 0, up at 4096, chunk k of column c in slot (k + c/4) % 4 of
+          // the column's 64 bytes, so that 16 lanes of a write hit 64
+          // distinct banks), then four lanes write each column's 64-byte
+          // run: 16 runs a store instead of 64 pieces of 16 bytes.
           wave_lds_sync();
           const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
-          const int col = n0 + wn * TN + lane;
+          uint8_t* gb = reinterpret_cast<uint8_t*>(stage);
+          auto slot = [](int c, int k) { return ((k + (c >> 2)) & 3) * 16; };
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             uint32_t pk[kMxBlock];
@@ -1438,18 +1445,40 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
                   bf_hi(p4[0]) * iu, bf_hi(p4[1]) * iu, bf_hi(p4[2]) * iu,
                   bf_hi(p4[3]) * iu));
             }
-            const int trow = wrow0 + h * kEpiRows + cb * kMxBlock;
-            if (trow < pad_len && col < f) {
-              uint8_t* dg_dst = P.Tc + static_cast<int64_t>(col) * P.ldt + pe +
-                                trow;
-              uint8_t* du_dst = dg_dst + static_cast<int64_t>(f) * P.ldt;
-              *reinterpret_cast<i32x4*>(dg_dst) = qg[0];
-              *reinterpret_cast<i32x4*>(dg_dst + 16) = qg[1];
-              *reinterpret_cast<i32x4*>(du_dst) = qu[0];
-              *reinterpret_cast<i32x4*>(du_dst + 16) = qu[1];
-            }
+            // rows 0-31 of the region (block 0's pairs) are read by every
+            // lane before block 0's codes overwrite its first 8 KB; block
+            // 1 reads rows 32-63, past them
+            if (cb == 0) wave_lds_sync();
+            uint8_t* gc = gb + lane * 64;
+            *reinterpret_cast<i32x4*>(gc + slot(lane, 2 * cb)) = qg[0];
+            *reinterpret_cast<i32x4*>(gc + slot(lane, 2 * cb + 1)) = qg[1];
+            *reinterpret_cast<i32x4*>(gc + 4096 + slot(lane, 2 * cb)) = qu[0];
+            *reinterpret_cast<i32x4*>(gc + 4096 + slot(lane, 2 * cb + 1)) =
+                qu[1];
             tsc[0] |= static_cast<uint32_t>(eg + 127) << (8 * (2 * h + cb));
             tsc[1] |= static_cast<uint32_t>(eu + 127) << (8 * (2 * h + cb));
+          }
+          wave_lds_sync();
+          // wrow0 and pad_len are multiples of 128: the pass is all in or
+          // all out
+          if (wrow0 < pad_len) {
+            const int j = lane & 3;
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) {
+              const int c = 16 * sg + (lane >> 2);
+              const i32x4 vg =
+                  *reinterpret_cast<const i32x4*>(gb + c * 64 + slot(c, j));
+              const i32x4 vu = *reinterpret_cast<const i32x4*>(
+                  gb + 4096 + c * 64 + slot(c, j));
+              const int col = n0 + wn * TN + c;
+              if (col < f) {
+                uint8_t* dg_dst = P.Tc + static_cast<int64_t>(col) * P.ldt +
+                                  pe + wrow0 + h * kEpiRows + 16 * j;
+                *reinterpret_cast<i32x4*>(dg_dst) = vg;
+                *reinterpret_cast<i32x4*>(
+                    dg_dst + static_cast<int64_t>(f) * P.ldt) = vu;
+              }
+            }
           }
         }
       }
