@@ -138,7 +138,11 @@ def test_route_bitexact(T, E, k, renorm, kind):
     (1, 4, 4, 64, "randn"), (513, 1024, 32, 8, "randn"),
     # the plan's column scan splits each expert over 64 / 16 / 4 / 2 / 1
     # lanes by E; E = 130 and 300 take the 4- and 2-lane groups
-    (700, 130, 7, 64, "randn"), (400, 300, 9, 32, "randn")])
+    (700, 130, 7, 64, "randn"), (400, 300, 9, 32, "randn"),
+    # tokens whose slots straddle two chunks (k = 6, 5, 3) at several
+    # expert counts
+    (1000, 16, 6, 64, "randn"), (700, 128, 5, 32, "tied"),
+    (1000, 256, 3, 32, "randn"), (2500, 32, 3, 64, "randn")])
 def test_permute_bitexact(T, E, k, d, kind):
     dev = _dev()
     L = _logits(kind, T, E, seed=7 * T + E)
