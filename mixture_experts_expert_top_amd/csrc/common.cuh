@@ -79,6 +79,21 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r,
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// The same with a wave-uniform part of the offset in soffset (a scalar
+// register, added without a vector instruction).  Callers keep every term
+// that can reach past the resource in voff, so the range check holds
+// whether or not the hardware counts soffset in it, and keep voff + soff
+// below 2^32.
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r,
+                                            uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r,
+                                              uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------- math
 // 1 / (1 + e^-a) with the hardware reciprocal (about 1 ulp) in place of an
 // IEEE division: the result feeds bf16 or E4M3 values, and the division's
@@ -167,10 +182,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // covers k-rows 8 (g / 2) + 0..3 (first read) and + 4..7 (second read,
 // 2048 bytes on) and columns 16 (g % 2) + 0..15.  lane_base and R come
 // from KmnLane.
-__device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
-                                            int R, int blk, int kk) {
-  const uint8_t* p = reinterpret_cast<const uint8_t*>(tile) + lane_base +
-                     ((blk ^ R) << 6) + kk * 8192;
+// frag_tr_at takes the lane's whole block offset, lane_base + ((blk ^ R)
+// << 6), so a caller can compute it once for every k-slice and stage.
+__device__ __forceinline__ bf16x8_v frag_tr_at(const uint8_t* tile,
+                                               int lane_off, int kk) {
+  const uint8_t* p = tile + lane_off + kk * 8192;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -178,6 +194,12 @@ __device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_v, v);
+}
+
+__device__ __forceinline__ bf16x8_v frag_tr(const bf16_t* tile, int lane_base,
+                                            int R, int blk, int kk) {
+  return frag_tr_at(reinterpret_cast<const uint8_t*>(tile),
+                    lane_base + ((blk ^ R) << 6), kk);
 }
 
 // The lane's fixed part of a frag_tr address (its row R and chunk inside a

@@ -174,7 +174,13 @@ struct Params {
   int64_t ldt;
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// 16-byte chunk swizzle of a [row][64 k] bf16 operand tile (128-byte
+// rows): chunk c of row r sits at chunk c ^ swz(r).  A fragment read (one
+// chunk of 32 consecutive rows) and a mover store (all 8 chunks of 8 rows)
+// are then spread evenly over the LDS banks, and swz is the same for rows
+// 16 apart, so the 32-row blocks of a tile differ by a constant offset and
+// every per-lane address is computed once per tile.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // Instruction classes for the scheduling-group hints of the K-loop.
 constexpr int kSgMfma = 0x008;
@@ -187,6 +193,8 @@ constexpr int kSgDsWrite = 0x200;
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * BK + ((chunk ^ swz(row)) << 3);
 }
+constexpr int kTileBytes = kTileElems * 2;
+constexpr int kBlkBytes = 32 * BK * 2;     // one 32-row block of a tile
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo,
                                              uint32_t sel) {
@@ -240,7 +248,16 @@ __device__ __forceinline__ int split_second_steps(int ntx, int nk, int c) {
 // (part 0: pieces 0-3, part 1: pieces 4-7) so the traffic can be spread
 // over the k-slices of the pipeline.  Byte offsets are split into a
 // per-thread part, computed once, and a per-piece part that is the same
-// for the whole workgroup.
+// for the whole workgroup; LDS offsets are per-thread bases plus
+// constants.  init's tile_bytes places the operand's tile (A at 0, B at
+// 2 kTileBytes) inside a stage; store takes the stage's base.
+//
+// Loads come in two forms.  The masked form tests every lane's k range
+// against kmax, for the one stage that may end inside a tile.  The full
+// form serves a stage that lies wholly inside [0, kmax) or wholly past it
+// (its data is never read): no mask, the k offset in soffset (clamped to
+// 0 past kmax, so the load stays inside the buffer), and rows past the
+// buffer still caught by the range check on voffset.
 constexpr int kMoveThreads = 256;
 
 template <bool KC>
@@ -253,30 +270,38 @@ template <>
 struct Mover<true> {
   uint32_t tpart;   // (t/8) * ld * 2 + (t%8) * 16
   int koff;         // (t%8) * 8
-  __device__ __forceinline__ void init(int t, int64_t ld) {
+  int lds0;         // LDS byte offset of piece 0 in a stage
+  __device__ __forceinline__ void init(int t, int64_t ld, int tile_bytes) {
     tpart = static_cast<uint32_t>(((t >> 3) * ld + (t & 7) * 8) * 2);
     koff = (t & 7) * 8;
+    lds0 = tile_bytes + lds_off(t >> 3, t & 7) * 2;
   }
-  template <typename Blk>
+  template <bool kFull, typename Blk>
   __device__ __forceinline__ void load(i32x4* v, __amdgpu_buffer_rsrc_t rs,
                                        int64_t ld, int k0, int kmax, Blk blk,
                                        int part) const {
-    const bool kok = k0 + koff < kmax;
+    if constexpr (kFull) {
+      const uint32_t ks = k0 < kmax ? static_cast<uint32_t>(k0) * 2 : 0u;
 #pragma unroll
-    for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const uint32_t off =
-          tpart + static_cast<uint32_t>((blk(i) * ld + k0) * 2);
-      v[i] = buf_load16(rs, kok ? off : kOob);
+      for (int i = 4 * part; i < 4 * part + 4; ++i)
+        v[i] = buf_load16(rs, tpart + static_cast<uint32_t>(blk(i) * ld * 2),
+                          ks);
+    } else {
+      const bool kok = k0 + koff < kmax;
+#pragma unroll
+      for (int i = 4 * part; i < 4 * part + 4; ++i) {
+        const uint32_t off =
+            tpart + static_cast<uint32_t>((blk(i) * ld + k0) * 2);
+        v[i] = buf_load16(rs, kok ? off : kOob);
+      }
     }
   }
-  __device__ __forceinline__ static void store(const i32x4* v, bf16_t* lds,
-                                               int t, int part) {
-    const int chunk = t & 7;
+  // rows t/8 + 32 i share the swizzle: piece i is 32 rows on
+  __device__ __forceinline__ void store(const i32x4* v, uint8_t* stage,
+                                        int part) const {
 #pragma unroll
-    for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      *reinterpret_cast<i32x4*>(lds + lds_off(row, chunk)) = v[i];
-    }
+    for (int i = 4 * part; i < 4 * part + 4; ++i)
+      *reinterpret_cast<i32x4*>(stage + lds0 + i * kBlkBytes) = v[i];
   }
 };
 
@@ -284,34 +309,48 @@ struct Mover<true> {
 // in memory (the [k][mn] tile of kmn_off) and transposed by the fragment
 // reads (ds_read_b64_tr_b16, see frag_tr).  Thread t moves the 16-byte
 // column chunk t % 32 of k-rows 8 (t / 32) + i, i = 0..7 (piece i); part 0
-// holds pieces 0-3, part 1 pieces 4-7.
+// holds pieces 0-3, part 1 pieces 4-7.  A full load keeps the k-row in
+// voffset: on a segment's last k-row, the chunks past the last column are
+// past the buffer's end.
 template <>
 struct Mover<false> {
   uint32_t tpart;   // (kr*8 * ld + mc*8) * 2
   int krow;         // kr * 8
-  __device__ __forceinline__ void init(int t, int64_t ld) {
+  int lds0[4];      // LDS byte offsets of pieces 0-3 in a stage
+  __device__ __forceinline__ void init(int t, int64_t ld, int tile_bytes) {
     krow = (t >> 5) * 8;
     tpart = static_cast<uint32_t>((krow * ld + (t & 31) * 8) * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lds0[q] = tile_bytes + kmn_off(krow + q, t & 31);
   }
+  template <bool kFull>
   __device__ __forceinline__ void load(i32x4* v, __amdgpu_buffer_rsrc_t rs,
                                        int64_t ld, int k0, int kmax,
                                        int64_t colbase, int part) const {
+    if constexpr (kFull) {
+      const int kc = k0 < kmax ? k0 : 0;
 #pragma unroll
-    for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const uint32_t off =
-          tpart + static_cast<uint32_t>(((k0 + i) * ld + colbase) * 2);
-      v[i] = buf_load16(rs, (k0 + krow + i < kmax) ? off : kOob);
+      for (int i = 4 * part; i < 4 * part + 4; ++i)
+        v[i] = buf_load16(
+            rs, tpart + static_cast<uint32_t>(((kc + i) * ld + colbase) * 2),
+            0u);
+    } else {
+#pragma unroll
+      for (int i = 4 * part; i < 4 * part + 4; ++i) {
+        const uint32_t off =
+            tpart + static_cast<uint32_t>(((k0 + i) * ld + colbase) * 2);
+        v[i] = buf_load16(rs, (k0 + krow + i < kmax) ? off : kOob);
+      }
     }
   }
-  __device__ __forceinline__ static void store(const i32x4* v, bf16_t* lds,
-                                               int t, int part) {
-    const int kr0 = (t >> 5) * 8, cc = t & 31;
+  // k-row krow + i: the chunk XOR repeats every 4 rows (krow is a multiple
+  // of 8)
+  __device__ __forceinline__ void store(const i32x4* v, uint8_t* stage,
+                                        int part) const {
 #pragma unroll
-    for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const int kr = kr0 + i;
-      *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(lds) +
-                                kmn_off(kr, cc)) = v[i];
-    }
+    for (int i = 4 * part; i < 4 * part + 4; ++i)
+      *reinterpret_cast<i32x4*>(stage + lds0[i & 3] + (i & ~3) * 512) = v[i];
   }
 };
 
@@ -352,50 +391,71 @@ struct Mover4 {
   uint32_t tpart;   // (t/8) * row bytes + (t%8) * 8
   uint32_t ldb;     // operand row stride in bytes
   int koff;         // (t%8) * 8 code pairs
-  __device__ __forceinline__ void init(int t, int64_t ld_units) {
+  int lds0;         // LDS byte offset of piece 0 in a stage
+  __device__ __forceinline__ void init(int t, int64_t ld_units,
+                                       int tile_bytes) {
     ldb = static_cast<uint32_t>(ld_units * 2);
     tpart = static_cast<uint32_t>(t >> 3) * ldb +
             static_cast<uint32_t>((t & 7) * 8);
     koff = (t & 7) * 8;
+    lds0 = tile_bytes + lds_off(t >> 3, t & 7) * 2;
   }
-  template <typename Blk>
+  template <bool kFull, typename Blk>
   __device__ __forceinline__ void load(i32x4* v, __amdgpu_buffer_rsrc_t rs,
                                        int k0, int kmax, Blk blk,
                                        int part) const {
     const bool kok = k0 + koff < kmax;
+    const uint32_t ks = k0 < kmax ? static_cast<uint32_t>(k0) : 0u;
 #pragma unroll
     for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const uint32_t off = tpart + static_cast<uint32_t>(blk(i)) * ldb +
-                           static_cast<uint32_t>(k0);
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, kok ? off : kOob,
-                                                          0, 0);
+      const uint32_t row = tpart + static_cast<uint32_t>(blk(i)) * ldb;
+      const auto w =
+          kFull ? __builtin_amdgcn_raw_buffer_load_b64(rs, row, ks, 0)
+                : __builtin_amdgcn_raw_buffer_load_b64(
+                      rs, kok ? row + static_cast<uint32_t>(k0) : kOob, 0, 0);
       v[i] = i32x4{static_cast<int>(w[0]), static_cast<int>(w[1]), 0, 0};
     }
   }
-  __device__ __forceinline__ static void store(const i32x4* v, bf16_t* lds,
-                                               int t, int part) {
-    const int chunk = t & 7;
+  __device__ __forceinline__ void store(const i32x4* v, uint8_t* stage,
+                                        int part) const {
 #pragma unroll
-    for (int i = 4 * part; i < 4 * part + 4; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      *reinterpret_cast<i32x4*>(lds + lds_off(row, chunk)) =
+    for (int i = 4 * part; i < 4 * part + 4; ++i)
+      *reinterpret_cast<i32x4*>(stage + lds0 + i * kBlkBytes) =
           e2m1x16_to_e4m3(static_cast<uint32_t>(v[i][0]),
                           static_cast<uint32_t>(v[i][1]));
-    }
   }
 };
 
 // Load part `part` of one operand with the mover of its layout: K-contig
 // movers take the block map, MN-contig movers the first column.
-template <bool KC, typename M, typename Blk>
+template <bool KC, bool kFull, typename M, typename Blk>
 __device__ __forceinline__ void load_one(const M& mv, i32x4* v,
                                          __amdgpu_buffer_rsrc_t rs, int64_t ld,
                                          int k0, int part, Blk blk,
                                          int64_t colbase, int kmax) {
   if constexpr (KC)
-    mv.load(v, rs, ld, k0, kmax, blk, part);
+    mv.template load<kFull>(v, rs, ld, k0, kmax, blk, part);
   else
-    mv.load(v, rs, ld, k0, kmax, colbase, part);
+    mv.template load<kFull>(v, rs, ld, k0, kmax, colbase, part);
+}
+
+// Runs k-steps 0 .. nk-1 of a K-loop whose iteration kt reads LDS stage
+// kt & 1 and prefetches stage kt + 2, as step(kt, stage, full): pairs
+// (even kt, kt + 1) with the stage a compile-time constant and full loads
+// up to kt_part, the iteration that prefetches a last stage ending inside
+// its tile (-1: none), then single steps with a run-time stage and masked
+// loads (at most four).  One loop of pairs and one of single steps: a loop
+// that picks between the two forms each time round keeps both forms'
+// registers live and spills.
+template <typename Step>
+__device__ __forceinline__ void run_ksteps(int nk, int kt_part, Step&& step) {
+  const int kf = kt_part >= 0 ? min(nk, kt_part) : nk;
+  int kt = 0;
+  for (; kt + 1 < kf; kt += 2) {
+    step(kt, 0, std::true_type{});
+    step(kt + 1, 1, std::true_type{});
+  }
+  for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{});
 }
 
 // Tile order inside one expert's mt x nt tile grid: groups of kGroupN
@@ -699,13 +759,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int nk = (Kdim - kbeg + BK - 1) / BK;
   Mover<AKC> ma;
   Mover<BKC> mb;
-  ma.init(lt, P.lda);
-  mb.init(lt, P.ldb);
+  ma.init(lt, P.lda, 0);
+  mb.init(lt, P.ldb, 2 * kTileBytes);
   // with 8 waves and one layout for both operands, one mover serves either
   const __amdgpu_buffer_rsrc_t rs_own = mv_a ? rsA : rsB;
   const int64_t ld_own = mv_a ? P.lda : P.ldb;
+  const int own_tile = mv_a ? 0 : 2 * kTileBytes;
   Mover<AKC> mown;
-  mown.init(lt, ld_own);
+  mown.init(lt, ld_own, own_tile);
 
   f32x16 acc[BI][BJ];
 #pragma unroll
@@ -716,36 +777,53 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   const int fr = lane & 31;      // fragment row inside a 32-block
   const int fk = lane >> 5;      // which half of the fragment's k range
 
-  // LDS tiles: [A stage 0][A stage 1][B stage 0][B stage 1].
-  auto atile = [&](int st) { return smem + st * kTileElems; };
-  auto btile = [&](int st) { return smem + (2 + st) * kTileElems; };
+  // LDS tiles: [A stage 0][A stage 1][B stage 0][B stage 1]; stage st
+  // of A starts at byte st * kTileBytes and of B 2 kTileBytes later.
+  uint8_t* const smem8 = reinterpret_cast<uint8_t*>(smem);
 
-  // Transposed fragment reads (MN-contiguous operands): the lane's fixed
-  // part of the address, see frag_tr.
+  // Per-lane LDS byte offsets of the fragment reads, relative to a stage's
+  // A tile; a stage, a 32-row block and (transposed) a k-slice add
+  // constants, so that inside the unrolled K-loop every read address is
+  // one of these registers plus an immediate.
+  //  * K-contiguous: chunk 2 kk + fk of row fr of the wave's first block
+  //    (swz is the same for rows 16 apart), kk = 0..3.
+  //  * MN-contiguous: the frag_tr offset of each of the wave's blocks.
+  int fa[4], fb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = lds_off(fr, 2 * kk + fk) * 2;
+    fa[kk] = wm * TM * BK * 2 + c;
+    fb[kk] = 2 * kTileBytes + wn * TN * BK * 2 + c;
+  }
   const KmnLane kl(lane);
-  const int tr_base = kl.base, tr_R = kl.R;
+  int ta[BI], tb[BJ];
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+    ta[i] = kl.base + (((wm * BI + i) ^ kl.R) << 6);
+#pragma unroll
+  for (int j = 0; j < BJ; ++j)
+    tb[j] = 2 * kTileBytes + kl.base + (((wn * BJ + j) ^ kl.R) << 6);
+
   // bf16 fragments of k-slice kk (16 wide) of one LDS stage.
   auto read_frags = [&](int st, int kk, bf16x8_v* af, bf16x8_v* bf) {
-    const bf16_t* sa = atile(st);
-    const bf16_t* sb = btile(st);
-    const int chunk = kk * 2 + fk;
+    const uint8_t* s8 = smem8 + st * kTileBytes;
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       if constexpr (AKC)
         af[i] = __builtin_bit_cast(
-            bf16x8_v, *reinterpret_cast<const i32x4*>(
-                          sa + lds_off(wm * TM + i * 32 + fr, chunk)));
+            bf16x8_v,
+            *reinterpret_cast<const i32x4*>(s8 + fa[kk] + i * kBlkBytes));
       else
-        af[i] = frag_tr(sa, tr_base, tr_R, wm * (TM / 32) + i, kk);
+        af[i] = frag_tr_at(s8, ta[i], kk);
     }
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
       if constexpr (BKC)
         bf[j] = __builtin_bit_cast(
-            bf16x8_v, *reinterpret_cast<const i32x4*>(
-                          sb + lds_off(wn * TN + j * 32 + fr, chunk)));
+            bf16x8_v,
+            *reinterpret_cast<const i32x4*>(s8 + fb[kk] + j * kBlkBytes));
       else
-        bf[j] = frag_tr(sb, tr_base, tr_R, wn * (TN / 32) + j, kk);
+        bf[j] = frag_tr_at(s8, tb[j], kk);
     }
   };
   auto mfmas = [&](const bf16x8_v* af, const bf16x8_v* bf) {
@@ -759,42 +837,51 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   };
   i32x4 va[8];
   i32x4 vb[C::kSplitLoad ? 1 : 8];
-  // part p of this thread's operand(s): global -> registers, and
-  // registers -> LDS stage st
-  auto gload = [&](int k0, int part) {
+  // part p of this thread's operand(s): global -> registers (full: a
+  // std::bool_constant, see the movers), and registers -> LDS stage st
+  auto gload = [&](int k0, int part, auto full) {
+    constexpr bool kF = decltype(full)::value;
     if (C::kSplitLoad) {
       if constexpr (AKC)
-        mown.load(va, rs_own, ld_own, k0, Kdim,
-                  [&](int i) { return mv_a ? blk_a(i) : blk_b(i); }, part);
+        mown.template load<kF>(
+            va, rs_own, ld_own, k0, Kdim,
+            [&](int i) { return mv_a ? blk_a(i) : blk_b(i); }, part);
       else
-        mown.load(va, rs_own, ld_own, k0, Kdim, mv_a ? m0 : n0, part);
+        mown.template load<kF>(va, rs_own, ld_own, k0, Kdim, mv_a ? m0 : n0,
+                               part);
     } else {
-      load_one<AKC>(ma, va, rsA, P.lda, k0, part, blk_a, m0, Kdim);
-      load_one<BKC>(mb, vb, rsB, P.ldb, k0, part, blk_b, n0, Kdim);
+      load_one<AKC, kF>(ma, va, rsA, P.lda, k0, part, blk_a, m0, Kdim);
+      load_one<BKC, kF>(mb, vb, rsB, P.ldb, k0, part, blk_b, n0, Kdim);
     }
   };
   auto lstore = [&](int st, int part) {
     if (C::kSplitLoad) {
-      Mover<AKC>::store(va, mv_a ? atile(st) : btile(st), lt, part);
+      mown.store(va, smem8 + st * kTileBytes, part);
     } else {
-      Mover<AKC>::store(va, atile(st), lt, part);
-      Mover<BKC>::store(vb, btile(st), lt, part);
+      ma.store(va, smem8 + st * kTileBytes, part);
+      mb.store(vb, smem8 + st * kTileBytes, part);
     }
   };
   // 8 waves with different layouts: each wave role gets its own copy of
   // the K-loop, so neither carries the other's mover state
-  auto gload_a = [&](int k0, int part) {
-    load_one<AKC>(ma, va, rsA, P.lda, k0, part, blk_a, m0, Kdim);
+  auto gload_a = [&](int k0, int part, auto full) {
+    load_one<AKC, decltype(full)::value>(ma, va, rsA, P.lda, k0, part, blk_a,
+                                         m0, Kdim);
   };
   auto lstore_a = [&](int st, int part) {
-    Mover<AKC>::store(va, atile(st), lt, part);
+    ma.store(va, smem8 + st * kTileBytes, part);
   };
-  auto gload_b = [&](int k0, int part) {
-    load_one<BKC>(mb, va, rsB, P.ldb, k0, part, blk_b, n0, Kdim);
+  auto gload_b = [&](int k0, int part, auto full) {
+    load_one<BKC, decltype(full)::value>(mb, va, rsB, P.ldb, k0, part, blk_b,
+                                         n0, Kdim);
   };
   auto lstore_b = [&](int st, int part) {
-    Mover<BKC>::store(va, btile(st), lt, part);
+    mb.store(va, smem8 + st * kTileBytes, part);
   };
+
+  // the iteration that prefetches the last stage when that stage ends
+  // inside its tile (the reduction length is not a multiple of BK)
+  const int kt_part = ((Kdim - kbeg) % BK != 0) ? nk - 3 : -1;
 
   // Software pipeline over k-steps of BK.  At iteration kt the mover
   // registers hold stage kt+1 (loaded one iteration earlier) and go to the
@@ -811,8 +898,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
   //     last MFMAs.
   // Both movers keep the halves of a stage in separate registers, so the
   // first schedule serves every layout.
-  // Loads past K return zeros and the one stray store of the last
-  // iteration lands in the buffer no one reads any more.
+  // Iterations run in pairs with the stage index a compile-time constant
+  // (every LDS address an immediate off a per-lane register) and full
+  // loads, then singly with a run-time stage and masked loads: the last
+  // one when nk is odd, and, when the last stage ends inside the tile,
+  // the iteration that prefetches it and those after (run_ksteps).  Loads
+  // past K return zeros (masked) or data never read (full), and the one
+  // stray store of the last iteration lands in the buffer no one reads
+  // any more.
   auto kloop = [&](auto&& gload, auto&& lstore, auto indep_halves) {
     constexpr bool kIndep = decltype(indep_halves)::value;
     constexpr int kMf = BI * BJ;                   // MFMAs per k-slice
@@ -822,25 +915,26 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     // more after each of the first kRd % kMf)
     constexpr int kRdLo = kRd / kMf, kRdHi = kRdLo + 1, kRdN = kRd % kMf;
     constexpr int kMv = C::kSplitLoad ? 4 : 8;     // moves per half stage
+    const std::false_type masked{};
     bf16x8_v a0[BI], b0[BJ], a1[BI], b1[BJ];
     if (nk > 0) {
-      gload(kbeg, 0);
-      gload(kbeg, 1);
+      gload(kbeg, 0, masked);
+      gload(kbeg, 1, masked);
       lstore(0, 0);
       lstore(0, 1);
-      gload(kbeg + BK, 0);
-      gload(kbeg + BK, 1);
+      gload(kbeg + BK, 0, masked);
+      gload(kbeg + BK, 1, masked);
       __syncthreads();
       read_frags(0, 0, a0, b0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cs = kt & 1, ns = cs ^ 1;
+    auto step = [&](int kt, int cs, auto full) {
+      const int ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
       // slices 0 and 1: MFMAs; reads of the next slice; half p of stage
       // kt+1 to LDS (and, K-contiguous, half p of stage kt+2 loaded)
       read_frags(cs, 1, a1, b1);
       lstore(ns, 0);
-      if constexpr (kIndep) gload(k2, 0);
+      if constexpr (kIndep) gload(k2, 0, full);
       mfmas(a0, b0);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
@@ -853,7 +947,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       __builtin_amdgcn_sched_barrier(0);
       read_frags(cs, 2, a0, b0);
       lstore(ns, 1);
-      if constexpr (kIndep) gload(k2, 1);
+      if constexpr (kIndep) gload(k2, 1, full);
       mfmas(a1, b1);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
@@ -866,7 +960,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       __builtin_amdgcn_sched_barrier(0);
       // slice 2: MFMAs on (a0,b0); reads of slice 3
       read_frags(cs, 3, a1, b1);
-      if constexpr (!kIndep) gload(k2, 0);
+      if constexpr (!kIndep) gload(k2, 0, full);
       mfmas(a0, b0);
   #pragma unroll
       for (int i = 0; i < kMf; ++i) {
@@ -891,7 +985,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // slice 3: MFMAs on (a1,b1); second half of stage kt+2
-        gload(k2, 1);
+        gload(k2, 1, full);
         mfmas(a1, b1);
   #pragma unroll
         for (int i = 0; i < kMf; ++i) {
@@ -902,7 +996,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         __syncthreads();
         read_frags(ns, 0, a0, b0);
       }
-    }
+    };
+    run_ksteps(nk, kt_part, step);
   };
 
   // MX K-loop: two 64-code k-slices per stage.  The stage's movers work
@@ -931,27 +1026,37 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     uint32_t vsa = 0, vsb = 0;
     // an E2M1 operand has its own mover (half the bytes a stage)
     Mover4 m4;
-    if constexpr (kRole4) m4.init(lt, ld_own);
-    auto gload_ops = [&](int k0, int part) {
+    if constexpr (kRole4) m4.init(lt, ld_own, own_tile);
+    auto gload_ops = [&](int k0, int part, auto full) {
       if constexpr (kRole4) {
         auto blk = [&](int i) { return mv_a ? blk_a(i) : blk_b(i); };
-        m4.load(va, rs_own, k0, Kdim, blk, part);
+        m4.template load<decltype(full)::value>(va, rs_own, k0, Kdim, blk,
+                                                part);
       } else {
-        gload(k0, part);
+        gload(k0, part, full);
       }
     };
     auto lstore_ops = [&](int st, int part) {
       if constexpr (kRole4)
-        Mover4::store(va, mv_a ? atile(st) : btile(st), lt, part);
+        m4.store(va, smem8 + st * kTileBytes, part);
       else
         lstore(st, part);
     };
-    auto gload_mx = [&](int k0, int part) {
-      gload_ops(k0, part);
+    auto gload_mx = [&](int k0, int part, auto full) {
+      gload_ops(k0, part, full);
       if (part == 0) {
         const bool ok = k0 < Kdim;
         const uint32_t kb = static_cast<uint32_t>(k0 >> 4);   // 32-blocks
-        if (C::kSplitLoad) {
+        if constexpr (decltype(full)::value) {
+          const uint32_t ks = ok ? kb : 0u;
+          if (C::kSplitLoad) {
+            vsa = mv_a ? buf_load4(rsSA, srow_a, ks)
+                       : buf_load4(rsSB, srow_b, ks);
+          } else {
+            vsa = buf_load4(rsSA, srow_a, ks);
+            vsb = buf_load4(rsSB, srow_b, ks);
+          }
+        } else if (C::kSplitLoad) {
           vsa = mv_a ? buf_load4(rsSA, ok ? srow_a + kb : kOob)
                      : buf_load4(rsSB, ok ? srow_b + kb : kOob);
         } else {
@@ -987,38 +1092,39 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     // (scaled by the byte that lanes 0-31 supply) and bytes 16-31 from the
     // second (scaled by lanes 32-63), so lane half fk holds 16 codes of each
     // block: chunks 4 kk + fk and 4 kk + 2 + fk.
-    auto frag = [&](const bf16_t* tile, int row, int kk) {
-      const int c0 = kk * 4 + fk;
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(tile + lds_off(row, c0));
-      const i32x4 hi =
-          *reinterpret_cast<const i32x4*>(tile + lds_off(row, c0 + 2));
+    // Chunks 4 kk + fk and 4 kk + 2 + fk are the bf16 loop's chunk pairs
+    // 2 kk and 2 kk + 1 (offsets fa, fb).
+    auto frag = [&](int st, const int* fo, int blk, int kk) {
+      const uint8_t* p = smem8 + st * kTileBytes + blk * kBlkBytes;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(p + fo[2 * kk]);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + fo[2 * kk + 1]);
       return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     auto read_a = [&](int st, int kk, int h, i32x8* af) {
 #pragma unroll
-      for (int i = 0; i < kAH; ++i)
-        af[i] = frag(atile(st), wm * TM + (h * kAH + i) * 32 + fr, kk);
+      for (int i = 0; i < kAH; ++i) af[i] = frag(st, fa, h * kAH + i, kk);
     };
     auto read_b = [&](int st, int kk, i32x8* bf) {
 #pragma unroll
-      for (int j = 0; j < BJ; ++j)
-        bf[j] = frag(btile(st), wn * TN + j * 32 + fr, kk);
+      for (int j = 0; j < BJ; ++j) bf[j] = frag(st, fb, j, kk);
     };
     i32x8 af[kAH], bf[BJ];
     uint32_t sa[BI], sb[BJ];
+    const std::false_type masked{};
     if (nk > 0) {
-      gload_mx(kbeg, 0);
-      gload_mx(kbeg, 1);
+      gload_mx(kbeg, 0, masked);
+      gload_mx(kbeg, 1, masked);
       lstore_mx(0, 0);
       lstore_mx(0, 1);
-      gload_mx(kbeg + BK, 0);
-      gload_mx(kbeg + BK, 1);
+      gload_mx(kbeg + BK, 0, masked);
+      gload_mx(kbeg + BK, 1, masked);
       __syncthreads();
       read_b(0, 0, bf);
       read_a(0, 0, 0, af);
       read_scales(0, sa, sb);
     }
-    auto step = [&](int cs, int ns, int kt) {
+    auto step = [&](int kt, int cs, auto full) {
+      const int ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
       // slice 0 (fragments of half 0 already read): stores of stage kt+1
       if constexpr (kHalves == 1) {
@@ -1053,7 +1159,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       // slice 1: loads of stage kt+2
       read_b(cs, 1, bf);
       read_a(cs, 1, 0, af);
-      gload_mx(k2, 0);
+      gload_mx(k2, 0, full);
       mx_mfmas<2, 0, kAH>(acc, af, bf, sa, sb);
       sched_group(kSgDsRead, 2 * (kAH + BJ));
 #pragma unroll
@@ -1064,7 +1170,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kHalves == 2) {
         read_a(cs, 1, 1, af);
-        gload_mx(k2, 1);
+        gload_mx(k2, 1, full);
         mx_mfmas<2, kAH, kAH>(acc, af, bf, sa, sb);
         sched_group(kSgDsRead, 2 * kAH);
 #pragma unroll
@@ -1073,7 +1179,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           if (i < kMv) sched_group(kSgVmemRead, 1);
         }
       } else {
-        gload_mx(k2, 1);
+        gload_mx(k2, 1, full);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -1081,7 +1187,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       read_a(ns, 0, 0, af);
       read_scales(ns, sa, sb);
     };
-    for (int kt = 0; kt < nk; ++kt) step(kt & 1, (kt & 1) ^ 1, kt);
+    run_ksteps(nk, kt_part, step);
   };
 
   if constexpr (MX) {
