@@ -45,6 +45,15 @@ __device__ __forceinline__ float bf_hi(uint32_t w) {
   return __uint_as_float(w & 0xffff0000u);
 }
 
+// Workgroup id -> logical id so that the workgroups one XCD receives (the
+// hardware hands out ids round-robin over the 8 XCDs) form a contiguous
+// range of logical ids, which share data in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  const int q = nb >> 3, r = nb & 7;
+  const int x = bid & 7, i = bid >> 3;
+  return x * q + min(x, r) + i;
+}
+
 // ---------------------------------------------------------------- buffers
 // Raw buffer resource over [base, base + bytes), bytes <= kOob (internal.h).
 // Loads whose offset falls outside the range return zero, which implements

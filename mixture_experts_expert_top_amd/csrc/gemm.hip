@@ -210,14 +210,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Workgroup id -> logical tile id so that the blocks one XCD receives
-// (hardware hands out ids round-robin over the 8 XCDs) form a contiguous
-// range of tiles that share operands in that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
-  const int q = nb >> 3, r = nb & 7;
-  const int x = bid & 7, i = bid >> 3;
-  return x * q + min(x, r) + i;
-}
 
 // k-steps of the second piece of a two-piece split reduction of nk steps,
 // on an XCD whose c CUs run ntx tiles: first all first pieces, then all

@@ -100,7 +100,17 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   uint8_t rscales[kRows ? kTokRows : 1][kRows ? kRowBytes / kMxBlock : 4];
   padded_prefix(seg, nseg, rows, s_pad);
   const int t = threadIdx.x;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kTokRows;
+  // Workgroup order: each XCD takes a contiguous range of (row tile,
+  // column group) pairs, column group fastest, so the 4-byte scale pieces
+  // that neighbouring workgroups write into one 32-byte sector (row-wise:
+  // the column groups of a row tile; along tokens: consecutive row tiles)
+  // leave one XCD close together and can merge in its L2.
+  const int ngy = static_cast<int>(gridDim.y);
+  const int lin = xcd_remap(
+      static_cast<int>(blockIdx.y * gridDim.x + blockIdx.x),
+      static_cast<int>(gridDim.x) * ngy);
+  const int bx = lin / ngy, by = lin % ngy;
+  const int64_t p0 = static_cast<int64_t>(bx) * kTokRows;
   // segment holding this tile: largest s with s_pad[s] <= p0
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   i32x4 nxt[kTokRows / 32];
   auto load_run = [&](int ct) {
     const int64_t c0 =
-        (static_cast<int64_t>(blockIdx.y) * kRuns + ct) * kTokCols;
+        (static_cast<int64_t>(by) * kRuns + ct) * kTokCols;
     const bool col_ok = c0 + cc < cols;            // cols % 8 == 0
 #pragma unroll
     for (int i = 0; i < kTokRows / 32; ++i) {
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
   load_run(0);
   for (int ct = 0; ct < kRuns; ++ct) {
     const int64_t c0 =
-        (static_cast<int64_t>(blockIdx.y) * kRuns + ct) * kTokCols;
+        (static_cast<int64_t>(by) * kRuns + ct) * kTokCols;
     if (c0 >= cols) break;
     if (ct > 0) __syncthreads();                   // LDS of the previous run
 #pragma unroll
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
     // in or all out)
     __syncthreads();
     constexpr int kChunks = kRowBytes / 16;
-    const int64_t cw0 = static_cast<int64_t>(blockIdx.y) * kRowBytes;
+    const int64_t cw0 = static_cast<int64_t>(by) * kRowBytes;
     const int64_t ncols = cols - cw0 < kRowBytes ? cols - cw0 : kRowBytes;
 #pragma unroll
     for (int j = 0; j < kTokRows * kChunks / 256; ++j) {
