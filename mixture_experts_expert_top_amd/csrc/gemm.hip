@@ -1132,47 +1132,50 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
           if (i < 2 * kMv + 2) sched_group(kSgDsWrite, 1);
         }
       } else {
+        // with 8 waves, half p of stage kt+2 is loaded right after half p
+        // of stage kt+1 leaves the same registers for LDS, so the loads
+        // have a whole step to land
         lstore_mx(ns, 0);
+        gload_mx(k2, 0, full);
         mx_mfmas<0, 0, kAH>(acc, af, bf, sa, sb);
 #pragma unroll
         for (int i = 0; i < kMfH; ++i) {
           sched_group(kSgMfma, 1);
           if (i < kMv + 1) sched_group(kSgDsWrite, 1);
+          if (i < kMv + 1) sched_group(kSgVmemRead, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         read_a(cs, 0, 1, af);
         lstore_mx(ns, 1);
+        gload_mx(k2, 1, full);
         mx_mfmas<0, kAH, kAH>(acc, af, bf, sa, sb);
         sched_group(kSgDsRead, 2 * kAH);
 #pragma unroll
         for (int i = 0; i < kMfH; ++i) {
           sched_group(kSgMfma, 1);
           if (i < kMv) sched_group(kSgDsWrite, 1);
+          if (i < kMv) sched_group(kSgVmemRead, 1);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // slice 1: loads of stage kt+2
+      // slice 1 (4 waves: loads of stage kt+2)
       read_b(cs, 1, bf);
       read_a(cs, 1, 0, af);
-      gload_mx(k2, 0, full);
+      if constexpr (kHalves == 1) gload_mx(k2, 0, full);
       mx_mfmas<2, 0, kAH>(acc, af, bf, sa, sb);
       sched_group(kSgDsRead, 2 * (kAH + BJ));
 #pragma unroll
       for (int i = 0; i < kMfH; ++i) {
         sched_group(kSgMfma, 1);
-        if (i < kMv + 1) sched_group(kSgVmemRead, 1);
+        if (kHalves == 1 && i < kMv + 1) sched_group(kSgVmemRead, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kHalves == 2) {
         read_a(cs, 1, 1, af);
-        gload_mx(k2, 1, full);
         mx_mfmas<2, kAH, kAH>(acc, af, bf, sa, sb);
         sched_group(kSgDsRead, 2 * kAH);
 #pragma unroll
-        for (int i = 0; i < kMfH; ++i) {
-          sched_group(kSgMfma, 1);
-          if (i < kMv) sched_group(kSgVmemRead, 1);
-        }
+        for (int i = 0; i < kMfH; ++i) sched_group(kSgMfma, 1);
       } else {
         gload_mx(k2, 1, full);
       }
