@@ -450,6 +450,28 @@ __device__ __forceinline__ void run_ksteps(int nk, int kt_part, Step&& step) {
   for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{});
 }
 
+// run_ksteps for a loop that also needs kt mod 4, as step(kt, stage,
+// full, kt % 4): quads of steps with both as compile-time constants and
+// full loads up to kt_part, then single steps with run-time values and
+// masked loads.
+template <typename Step>
+__device__ __forceinline__ void run_ksteps4(int nk, int kt_part,
+                                            Step&& step) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  const int kf = kt_part >= 0 ? min(nk, kt_part) : nk;
+  int kt = 0;
+  for (; kt + 3 < kf; kt += 4) {
+    step(kt, 0, std::true_type{}, I0{});
+    step(kt + 1, 1, std::true_type{}, I1{});
+    step(kt + 2, 0, std::true_type{}, I2{});
+    step(kt + 3, 1, std::true_type{}, I3{});
+  }
+  for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{}, kt & 3);
+}
+
 // Tile order inside one expert's mt x nt tile grid: groups of kGroupN
 // n-tiles; inside a group, blocks of kGroupM m-tiles (the last group and
 // block may be narrower), m fastest inside a block.  Consecutive tiles --
@@ -1018,7 +1040,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     const uint32_t srow_a = static_cast<uint32_t>((a_row0 + lt) * P.lds_a);
     const uint32_t srow_b =
         static_cast<uint32_t>((blk_b(lt >> 5) + (lt & 31)) * P.lds_b);
-    uint32_t vsa = 0, vsb = 0;
+    // scale dwords (4 blocks of 32 codes, one stage) of the thread's tile
+    // row for 4 consecutive stages, loaded together every fourth stage:
+    // one 16-byte load per row instead of four 4-byte ones, each of which
+    // touches a cache line of its own for every lane.  A group that runs
+    // past the end of the resource reads zeros there (the range check is
+    // per dword) and those stages are never stored.
+    i32x4 vsg{}, vsgb{};
     // an E2M1 operand has its own mover (half the bytes a stage)
     Mover4 m4;
     if constexpr (kRole4) m4.init(lt, ld_own, own_tile);
@@ -1037,38 +1065,40 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       else
         lstore(st, part);
     };
-    auto gload_mx = [&](int k0, int part, auto full) {
+    // qs: the loaded stage's index mod 4 (its place in its scale group)
+    auto gload_mx = [&](int k0, int part, auto full, int qs) {
       gload_ops(k0, part, full);
-      if (part == 0) {
+      if (part == 0 && qs == 0) {
         const bool ok = k0 < Kdim;
         const uint32_t kb = static_cast<uint32_t>(k0 >> 4);   // 32-blocks
         if constexpr (decltype(full)::value) {
           const uint32_t ks = ok ? kb : 0u;
           if (C::kSplitLoad) {
-            vsa = mv_a ? buf_load4(rsSA, srow_a, ks)
-                       : buf_load4(rsSB, srow_b, ks);
+            vsg = mv_a ? buf_load16(rsSA, srow_a, ks)
+                       : buf_load16(rsSB, srow_b, ks);
           } else {
-            vsa = buf_load4(rsSA, srow_a, ks);
-            vsb = buf_load4(rsSB, srow_b, ks);
+            vsg = buf_load16(rsSA, srow_a, ks);
+            vsgb = buf_load16(rsSB, srow_b, ks);
           }
         } else if (C::kSplitLoad) {
-          vsa = mv_a ? buf_load4(rsSA, ok ? srow_a + kb : kOob)
-                     : buf_load4(rsSB, ok ? srow_b + kb : kOob);
+          vsg = mv_a ? buf_load16(rsSA, ok ? srow_a + kb : kOob)
+                     : buf_load16(rsSB, ok ? srow_b + kb : kOob);
         } else {
-          vsa = buf_load4(rsSA, ok ? srow_a + kb : kOob);
-          vsb = buf_load4(rsSB, ok ? srow_b + kb : kOob);
+          vsg = buf_load16(rsSA, ok ? srow_a + kb : kOob);
+          vsgb = buf_load16(rsSB, ok ? srow_b + kb : kOob);
         }
       }
     };
-    auto lstore_mx = [&](int st, int part) {
+    // qs: the stored stage's index mod 4
+    auto lstore_mx = [&](int st, int part, int qs) {
       lstore_ops(st, part);
       if (part == 0) {
         uint32_t* sc = s_scl + st * (2 * BM);
         if (C::kSplitLoad) {
-          sc[(mv_a ? 0 : BM) + lt] = vsa;
+          sc[(mv_a ? 0 : BM) + lt] = static_cast<uint32_t>(vsg[qs]);
         } else {
-          sc[lt] = vsa;
-          sc[BM + lt] = vsb;
+          sc[lt] = static_cast<uint32_t>(vsg[qs]);
+          sc[BM + lt] = static_cast<uint32_t>(vsgb[qs]);
         }
       }
     };
@@ -1107,24 +1137,26 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     uint32_t sa[BI], sb[BJ];
     const std::false_type masked{};
     if (nk > 0) {
-      gload_mx(kbeg, 0, masked);
-      gload_mx(kbeg, 1, masked);
-      lstore_mx(0, 0);
-      lstore_mx(0, 1);
-      gload_mx(kbeg + BK, 0, masked);
-      gload_mx(kbeg + BK, 1, masked);
+      gload_mx(kbeg, 0, masked, 0);
+      gload_mx(kbeg, 1, masked, 0);
+      lstore_mx(0, 0, 0);
+      lstore_mx(0, 1, 0);
+      gload_mx(kbeg + BK, 0, masked, 1);
+      gload_mx(kbeg + BK, 1, masked, 1);
       __syncthreads();
       read_b(0, 0, bf);
       read_a(0, 0, 0, af);
       read_scales(0, sa, sb);
     }
-    auto step = [&](int kt, int cs, auto full) {
+    // q: kt mod 4 (a compile-time constant in the unrolled quads)
+    auto step = [&](int kt, int cs, auto full, int q) {
       const int ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
+      const int q1 = (q + 1) & 3, q2 = (q + 2) & 3;
       // slice 0 (fragments of half 0 already read): stores of stage kt+1
       if constexpr (kHalves == 1) {
-        lstore_mx(ns, 0);
-        lstore_mx(ns, 1);
+        lstore_mx(ns, 0, q1);
+        lstore_mx(ns, 1, q1);
         mx_mfmas<0, 0, kAH>(acc, af, bf, sa, sb);
 #pragma unroll
         for (int i = 0; i < kMfH; ++i) {
@@ -1135,8 +1167,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         // with 8 waves, half p of stage kt+2 is loaded right after half p
         // of stage kt+1 leaves the same registers for LDS, so the loads
         // have a whole step to land
-        lstore_mx(ns, 0);
-        gload_mx(k2, 0, full);
+        lstore_mx(ns, 0, q1);
+        gload_mx(k2, 0, full, q2);
         mx_mfmas<0, 0, kAH>(acc, af, bf, sa, sb);
 #pragma unroll
         for (int i = 0; i < kMfH; ++i) {
@@ -1146,8 +1178,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
         read_a(cs, 0, 1, af);
-        lstore_mx(ns, 1);
-        gload_mx(k2, 1, full);
+        lstore_mx(ns, 1, q1);
+        gload_mx(k2, 1, full, q2);
         mx_mfmas<0, kAH, kAH>(acc, af, bf, sa, sb);
         sched_group(kSgDsRead, 2 * kAH);
 #pragma unroll
@@ -1161,7 +1193,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       // slice 1 (4 waves: loads of stage kt+2)
       read_b(cs, 1, bf);
       read_a(cs, 1, 0, af);
-      if constexpr (kHalves == 1) gload_mx(k2, 0, full);
+      if constexpr (kHalves == 1) gload_mx(k2, 0, full, q2);
       mx_mfmas<2, 0, kAH>(acc, af, bf, sa, sb);
       sched_group(kSgDsRead, 2 * (kAH + BJ));
 #pragma unroll
@@ -1177,7 +1209,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < kMfH; ++i) sched_group(kSgMfma, 1);
       } else {
-        gload_mx(k2, 1, full);
+        gload_mx(k2, 1, full, q2);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -1185,7 +1217,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       read_a(ns, 0, 0, af);
       read_scales(ns, sa, sb);
     };
-    run_ksteps(nk, kt_part, step);
+    run_ksteps4(nk, kt_part, step);
   };
 
   if constexpr (MX) {
