@@ -98,6 +98,13 @@ constexpr int kEpiRows = 64;              // rows per epilogue pass of a wave
 #define MOE_INDEP_LOOP 1
 #endif
 constexpr bool kIndepLoop = MOE_INDEP_LOOP != 0;
+#ifndef MOE_SCALE_GROUP
+#define MOE_SCALE_GROUP 4
+#endif
+// MX K-loop: stages whose scale dwords one thread loads together (a power
+// of two; 4 measured best: 8, with the loop unrolled eight times, made
+// the MXFP8 step 8% slower)
+constexpr int kScaleGroup = MOE_SCALE_GROUP;
 
 enum Mode { kSegM = 0, kSegK = 1, kSegKT = 2 };
 enum Epi { kStore = 0, kSwiglu = 1, kDSwiglu = 2, kStoreF32 = 3 };
@@ -450,26 +457,24 @@ __device__ __forceinline__ void run_ksteps(int nk, int kt_part, Step&& step) {
   for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{});
 }
 
-// run_ksteps for a loop that also needs kt mod 4, as step(kt, stage,
-// full, kt % 4): quads of steps with both as compile-time constants and
-// full loads up to kt_part, then single steps with run-time values and
-// masked loads.
-template <typename Step>
-__device__ __forceinline__ void run_ksteps4(int nk, int kt_part,
-                                            Step&& step) {
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
+// run_ksteps for a loop that also needs kt mod G, as step(kt, stage,
+// full, kt % G): groups of G steps with both as compile-time constants
+// and full loads up to kt_part, then single steps with run-time values
+// and masked loads.
+template <int G, typename Step, int... Is>
+__device__ __forceinline__ void ksteps_group(int kt, Step&& step,
+                                             std::integer_sequence<int, Is...>) {
+  (step(kt + Is, Is & 1, std::true_type{}, std::integral_constant<int, Is>{}),
+   ...);
+}
+template <int G, typename Step>
+__device__ __forceinline__ void run_ksteps_g(int nk, int kt_part,
+                                             Step&& step) {
   const int kf = kt_part >= 0 ? min(nk, kt_part) : nk;
   int kt = 0;
-  for (; kt + 3 < kf; kt += 4) {
-    step(kt, 0, std::true_type{}, I0{});
-    step(kt + 1, 1, std::true_type{}, I1{});
-    step(kt + 2, 0, std::true_type{}, I2{});
-    step(kt + 3, 1, std::true_type{}, I3{});
-  }
-  for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{}, kt & 3);
+  for (; kt + G - 1 < kf; kt += G)
+    ksteps_group<G>(kt, step, std::make_integer_sequence<int, G>{});
+  for (; kt < nk; ++kt) step(kt, kt & 1, std::false_type{}, kt & (G - 1));
 }
 
 // Tile order inside one expert's mt x nt tile grid: groups of kGroupN
@@ -1041,12 +1046,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
     const uint32_t srow_b =
         static_cast<uint32_t>((blk_b(lt >> 5) + (lt & 31)) * P.lds_b);
     // scale dwords (4 blocks of 32 codes, one stage) of the thread's tile
-    // row for 4 consecutive stages, loaded together every fourth stage:
-    // one 16-byte load per row instead of four 4-byte ones, each of which
-    // touches a cache line of its own for every lane.  A group that runs
+    // row for kScaleGroup consecutive stages, loaded together once a
+    // group: a 16-byte load per 4 stages instead of four 4-byte ones, each
+    // of which touches a cache line of its own for every lane.  A group that runs
     // past the end of the resource reads zeros there (the range check is
     // per dword) and those stages are never stored.
-    i32x4 vsg{}, vsgb{};
+    constexpr int kSg4 = kScaleGroup / 4;    // 16-byte loads a group
+    i32x4 vsg[kSg4] = {}, vsgb[kSg4] = {};
     // an E2M1 operand has its own mover (half the bytes a stage)
     Mover4 m4;
     if constexpr (kRole4) m4.init(lt, ld_own, own_tile);
@@ -1065,40 +1071,46 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       else
         lstore(st, part);
     };
-    // qs: the loaded stage's index mod 4 (its place in its scale group)
+    // qs: the loaded stage's index mod kScaleGroup (its place in its
+    // scale group)
     auto gload_mx = [&](int k0, int part, auto full, int qs) {
       gload_ops(k0, part, full);
       if (part == 0 && qs == 0) {
         const bool ok = k0 < Kdim;
-        const uint32_t kb = static_cast<uint32_t>(k0 >> 4);   // 32-blocks
-        if constexpr (decltype(full)::value) {
-          const uint32_t ks = ok ? kb : 0u;
-          if (C::kSplitLoad) {
-            vsg = mv_a ? buf_load16(rsSA, srow_a, ks)
-                       : buf_load16(rsSB, srow_b, ks);
+#pragma unroll
+        for (int g = 0; g < kSg4; ++g) {
+          const uint32_t kb =
+              static_cast<uint32_t>(k0 >> 4) + 16u * g;      // 32-blocks
+          if constexpr (decltype(full)::value) {
+            const uint32_t ks = ok ? kb : 16u * g;
+            if (C::kSplitLoad) {
+              vsg[g] = mv_a ? buf_load16(rsSA, srow_a, ks)
+                            : buf_load16(rsSB, srow_b, ks);
+            } else {
+              vsg[g] = buf_load16(rsSA, srow_a, ks);
+              vsgb[g] = buf_load16(rsSB, srow_b, ks);
+            }
+          } else if (C::kSplitLoad) {
+            vsg[g] = mv_a ? buf_load16(rsSA, ok ? srow_a + kb : kOob)
+                          : buf_load16(rsSB, ok ? srow_b + kb : kOob);
           } else {
-            vsg = buf_load16(rsSA, srow_a, ks);
-            vsgb = buf_load16(rsSB, srow_b, ks);
+            vsg[g] = buf_load16(rsSA, ok ? srow_a + kb : kOob);
+            vsgb[g] = buf_load16(rsSB, ok ? srow_b + kb : kOob);
           }
-        } else if (C::kSplitLoad) {
-          vsg = mv_a ? buf_load16(rsSA, ok ? srow_a + kb : kOob)
-                     : buf_load16(rsSB, ok ? srow_b + kb : kOob);
-        } else {
-          vsg = buf_load16(rsSA, ok ? srow_a + kb : kOob);
-          vsgb = buf_load16(rsSB, ok ? srow_b + kb : kOob);
         }
       }
     };
-    // qs: the stored stage's index mod 4
+    // qs: the stored stage's index mod kScaleGroup
     auto lstore_mx = [&](int st, int part, int qs) {
       lstore_ops(st, part);
       if (part == 0) {
         uint32_t* sc = s_scl + st * (2 * BM);
         if (C::kSplitLoad) {
-          sc[(mv_a ? 0 : BM) + lt] = static_cast<uint32_t>(vsg[qs]);
+          sc[(mv_a ? 0 : BM) + lt] =
+              static_cast<uint32_t>(vsg[qs >> 2][qs & 3]);
         } else {
-          sc[lt] = static_cast<uint32_t>(vsg[qs]);
-          sc[BM + lt] = static_cast<uint32_t>(vsgb[qs]);
+          sc[lt] = static_cast<uint32_t>(vsg[qs >> 2][qs & 3]);
+          sc[BM + lt] = static_cast<uint32_t>(vsgb[qs >> 2][qs & 3]);
         }
       }
     };
@@ -1148,11 +1160,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       read_a(0, 0, 0, af);
       read_scales(0, sa, sb);
     }
-    // q: kt mod 4 (a compile-time constant in the unrolled quads)
+    // q: kt mod kScaleGroup (a compile-time constant in the unrolled
+    // groups)
     auto step = [&](int kt, int cs, auto full, int q) {
       const int ns = cs ^ 1;
       const int k2 = kbeg + (kt + 2) * BK;
-      const int q1 = (q + 1) & 3, q2 = (q + 2) & 3;
+      const int q1 = (q + 1) & (kScaleGroup - 1);
+      const int q2 = (q + 2) & (kScaleGroup - 1);
       // slice 0 (fragments of half 0 already read): stores of stage kt+1
       if constexpr (kHalves == 1) {
         lstore_mx(ns, 0, q1);
@@ -1217,7 +1231,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void grouped_gemm_kernel(
       read_a(ns, 0, 0, af);
       read_scales(ns, sa, sb);
     };
-    run_ksteps4(nk, kt_part, step);
+    run_ksteps_g<kScaleGroup>(nk, kt_part, step);
   };
 
   if constexpr (MX) {
