@@ -23,13 +23,16 @@ namespace {
 // 64 experts (two 32-expert blocks; one when the experts end sooner), so
 // x is read once for E <= 64; its 8 waves split d into 8 contiguous ranges
 // and their partial tiles are summed in LDS in wave order (fixed,
-// deterministic).  Each wave issues the loads of kLogitAhead k-steps
-// before their MFMAs so that enough of x is in flight to keep HBM busy.
+// deterministic).  Each wave issues the loads of AH k-steps before their
+// MFMAs so that enough of x is in flight to keep HBM busy: 16 when E <= 32
+// (one expert block, so the registers of the second serve the loads), else
+// 8.  The workgroups are one per CU at these token counts, so the loads
+// in flight are what sets the rate.
 constexpr int kLogitThreads = 512;
 constexpr int kLogitWaves = kLogitThreads / 64;
-constexpr int kLogitAhead = 8;
 constexpr int kLogitExp = 64;
 
+template <int AH, bool TWO>
 __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int d, int E,
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
       make_rsrc(wg, static_cast<uint32_t>(static_cast<int64_t>(E) * d * 2));
   const int tok = t0 + row;
   const bool tok_ok = tok < T;
-  const bool two = e0 + 32 < E;           // uniform: second expert block
+  const bool two = TWO && e0 + 32 < E;    // uniform: second expert block
   const bool ex_ok0 = e0 + row < E, ex_ok1 = e0 + 32 + row < E;
   // the range of the reduction owned by this wave, in steps of 16
   const int steps = (d + 15) / 16;
@@ -54,10 +57,10 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
   const int64_t wrow0 = static_cast<int64_t>(e0 + row) * d;
   const int64_t wrow1 = wrow0 + static_cast<int64_t>(32) * d;
   f32x16 acc0 = {}, acc1 = {};
-  for (int s0 = s_begin; s0 < s_end; s0 += kLogitAhead) {
-    bf16x8_v a[kLogitAhead], b0[kLogitAhead], b1[kLogitAhead];
+  for (int s0 = s_begin; s0 < s_end; s0 += AH) {
+    bf16x8_v a[AH], b0[AH], b1[TWO ? AH : 1];
 #pragma unroll
-    for (int u = 0; u < kLogitAhead; ++u) {
+    for (int u = 0; u < AH; ++u) {
       // steps past the wave's range (or d) read zeros through kOob
       const int kk = (s0 + u) * 16 + kh * 8;
       const bool kok = s0 + u < s_end && kk < d;
@@ -70,15 +73,17 @@ __global__ __launch_bounds__(kLogitThreads) void router_logits_kernel(
       if (two) {
         const uint32_t ow1 = (ex_ok1 && kok)
             ? static_cast<uint32_t>((wrow1 + kk) * 2) : kOob;
-        b1[u] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow1));
+        b1[TWO ? u : 0] = __builtin_bit_cast(bf16x8_v, buf_load16(rw, ow1));
       }
     }
+    // every load of the group is issued before the first MFMA waits
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kLogitAhead; ++u) {
+    for (int u = 0; u < AH; ++u) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b0[u], acc0, 0, 0, 0);
       if (two)
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b1[u], acc1, 0, 0,
-                                                       0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b1[TWO ? u : 0],
+                                                       acc1, 0, 0, 0);
     }
   }
   // acc[v] = C[token i][expert j], i = (v/4)*8 + kh*4 + v%4, j = lane%32
@@ -327,13 +332,16 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   float db = 0.0f;
-  for (int s0 = 0; s0 < nt; s0 += kDwStep) {
+  // thread t moves the 16-byte column chunk t % 32 of token rows
+  // 8 (t / 32) + i of a step, and experts 16 (t % 4) + 0..15 of token t / 4;
+  // a step's values are loaded into registers during the step before
+  const int cc = tid & 31, kr0 = (tid >> 5) * 8;
+  const int col = c0 + cc * 8;
+  const int tt4 = tid >> 2, eb = (tid & 3) * 16;
+  i32x4 v[8];
+  float g[16];
+  auto load_step = [&](int s0) {
     if (want_x) {
-      // thread t moves the 16-byte column chunk t % 32 of token rows
-      // 8 (t / 32) + i of the step
-      const int cc = tid & 31, kr0 = (tid >> 5) * 8;
-      const int col = c0 + cc * 8;
-      i32x4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = s0 + kr0 + i;
@@ -342,24 +350,27 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
                   x + static_cast<int64_t>(t0 + row) * d + col)
             : i32x4{};
       }
+    }
+    const bool tok = s0 + tt4 < nt;
+    const float* src = dlogits + static_cast<int64_t>(t0 + s0 + tt4) * E + e0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      g[q] = (tok && eb + q < ne) ? src[eb + q] : 0.0f;
+  };
+  load_step(0);
+  for (int s0 = 0; s0 < nt; s0 += kDwStep) {
+    if (want_x) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(s_x) +
                                   kmn_off(kr0 + i, cc)) = v[i];
     }
-    {
-      // thread t moves experts 16 (t % 4) + 0..15 of token t / 4
-      const int tt = tid >> 2, eb = (tid & 3) * 16;
-      const bool tok = s0 + tt < nt;
-      const float* src = dlogits + static_cast<int64_t>(t0 + s0 + tt) * E + e0;
-      float g[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        g[q] = (tok && eb + q < ne) ? src[eb + q] : 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) s_dl[eb + q][tt] = g[q];
-    }
+    for (int q = 0; q < 16; ++q) s_dl[eb + q][tt4] = g[q];
     __syncthreads();
+    if (s0 + kDwStep < nt) load_step(s0 + kDwStep);
+    // the next step's loads stay ahead of this step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     if (do_db)
       for (int tt = 0; tt < kDwStep; ++tt) db += s_dl[tid][tt];
     if (want_x) {
@@ -545,9 +556,14 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w_g,
                                 float* logits, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((T + 31) / 32),
             static_cast<unsigned>((E + kLogitExp - 1) / kLogitExp));
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kLogitThreads), 0, s, x,
-                     w_g, bias, static_cast<int>(T), static_cast<int>(d), E,
-                     logits);
+  if (E <= 32)
+    hipLaunchKernelGGL((router_logits_kernel<16, false>), grid,
+                       dim3(kLogitThreads), 0, s, x, w_g, bias,
+                       static_cast<int>(T), static_cast<int>(d), E, logits);
+  else
+    hipLaunchKernelGGL((router_logits_kernel<8, true>), grid,
+                       dim3(kLogitThreads), 0, s, x, w_g, bias,
+                       static_cast<int>(T), static_cast<int>(d), E, logits);
   return hipGetLastError();
 }
 
