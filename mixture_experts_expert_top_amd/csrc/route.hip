@@ -382,6 +382,7 @@ __global__ __launch_bounds__(256) void router_dwg_partial_kernel(
           a[i] = frag_tr(s_x, kl.base, kl.R, wave * 2 + i, kk);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+          if (32 * j >= ne) break;              // no expert in this block
           const float* p = &s_dl[32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)];
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(p);
           const f32x4 g1 = *reinterpret_cast<const f32x4*>(p + 4);
